@@ -1,0 +1,189 @@
+"""Benchmark of one Muon optimizer step on one MI355X.
+
+A step is the whole hot path over every matrix of the workload:
+muon_momentum (fp32 momentum, Nesterov blend, sum of squares) ->
+muon_orthogonalize_grouped (5 quintic Newton-Schulz steps, bf16 MFMA with
+fp32 accumulation) -> muon_apply (0.2*sqrt(max(m,n)) shape factor,
+decoupled weight decay), with inputs resident in HBM.
+
+Prints one JSON line.  ``value`` is optimizer steps per second; the line
+also carries the Newton-Schulz TFLOP/s (algorithmic flops: upper-triangle
+Gram and square, full update product), the roofline of the dominant kernel
+family and the fp64 CPU oracle timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Muon steps/sec + Newton-Schulz TFLOP/s (% bf16 MFMA peak) per layer set"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+LR, WD = 3e-4, 0.1
+
+
+def ns_flops(count, rows, cols, steps=5):
+    """(algorithmic, nominal) Newton-Schulz flops for `count` rows x cols."""
+    m, n = min(rows, cols), max(rows, cols)
+    algo = m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n
+    nominal = 4 * m * m * n + 2 * m ** 3
+    return count * steps * algo, count * steps * nominal
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, grads_host, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the workload's matrices
+    (smallest first until about `budget_s` of work), scaled by NS flops to
+    the whole workload."""
+    import numpy as np
+    from oracle import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    total_flops = sum(ns_flops(g.count, g.rows, g.cols)[0] for g in cfg.groups)
+    order = sorted(range(len(cfg.groups)), key=lambda i: cfg.groups[i].rows * cfg.groups[i].cols)
+    spent, done_flops, names = 0.0, 0, []
+    for gi in order:
+        g = cfg.groups[gi]
+        G = grads_host[gi].astype(np.float64)
+        W = np.zeros((g.rows, g.cols))
+        M = np.zeros((g.rows, g.cols))
+        t0 = time.perf_counter()
+        O.muon_step(W, M, G, lr=LR, weight_decay=WD)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done_flops += ns_flops(1, g.rows, g.cols)[0]
+        names.append(f"{g.name} {g.rows}x{g.cols}")
+        if spent > budget_s * 0.5:
+            break
+    sec_per_step = spent * total_flops / done_flops
+    return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle muon_step on one matrix each of [{', '.join(names)}] "
+                      f"({spent:.1f} s), scaled by Newton-Schulz flops to the whole workload",
+            "seconds_per_step": sec_per_step}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the Muon step here runs on a single MI355X with no "
+              f"collectives (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import matrix_aware_optimizer_step_amd as mx
+    from workloads import synth
+
+    mx._lib.load()  # fails loudly without the HIP library
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    cfg = synth.CONFIGS[args.config]
+    log(f"[bench] config {cfg.index}: {cfg.name}, {cfg.matrices} matrices, {cfg.elements / 1e6:.1f} M elements")
+
+    t0 = time.perf_counter()
+    grads = synth.group_gradients(cfg, step=1, device=dev)
+    weights = synth.initial_weights(cfg, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
+
+    stepper = mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD)
+
+    def one_step(ev=None):
+        stepper.step(events=ev)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        one_step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps done in {wall:.3f} s")
+
+    t_mom = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    t_ns = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    t_app = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    algo, nominal = 0, 0
+    for g in cfg.groups:
+        fa, fn = ns_flops(g.count, g.rows, g.cols)
+        algo += fa
+        nominal += fn
+    ns_tflops = algo / (t_ns * 1e-3) / 1e12
+    ns_tflops_nominal = nominal / (t_ns * 1e-3) / 1e12
+    elems = cfg.elements
+    mom_bytes = elems * (2 + 8 + 2)   # G bf16 read, M fp32 read+write, N bf16 write
+    app_bytes = elems * (4 + 2)       # W bf16 read+write, O bf16 read
+    mom_gbs = mom_bytes / (t_mom * 1e-3) / 1e9
+    app_gbs = app_bytes / (t_app * 1e-3) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a bounded sample (host cores)")
+        host = [g[0].float().cpu().numpy() for g in grads]
+        cpu = cpu_baseline(cfg, host)
+        log(f"[bench] oracle: {cpu['seconds_per_step']:.1f} s per step (extrapolated)")
+
+    shapes = {g.name: [g.count, g.rows, g.cols] for g in cfg.groups}
+    out = {
+        "metric": METRIC,
+        "value": 1e3 / ms_per_step,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"config {cfg.index}: {cfg.name}", "matrices": cfg.matrices,
+                   "shapes": shapes, "gradients": cfg.kind, "ns_steps": 5, "compute": "bf16 MFMA, fp32 accumulate",
+                   "parallelism": "single GPU"},
+        "newton_schulz": {"tflops_algorithmic": ns_tflops, "tflops_nominal_4m2n_2m3": ns_tflops_nominal,
+                          "frac_bf16_peak": ns_tflops / PEAK_BF16_TFLOPS, "ms": t_ns,
+                          "flops_algorithmic": algo, "flops_nominal": nominal},
+        "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
+                        "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},
+        "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "ns_gemm_kernel (Gram, polynomial and update launches of muon_orthogonalize_grouped)"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

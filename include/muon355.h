@@ -1,0 +1,194 @@
+/*
+ * muon355.h - C ABI of libmuon355, the Muon optimizer step on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * One Muon step for a hidden 2-D weight W (m x n) with gradient G is three
+ * calls, in this order, all asynchronous on one HIP stream:
+ *
+ *   muon_momentum       M <- beta*M + (1-beta)*G, the Nesterov blend N, and
+ *                       the sum of squares of N.
+ *   muon_orthogonalize  O = K Newton-Schulz steps on N / (||N||_F + eps),
+ *                       run on the smaller side (transposed when m > n).
+ *   muon_apply          W <- (1 - lr*wd)*W - lr*s*O with the shape factor s.
+ *
+ * Sources ("the pages") cited below:
+ *   [NOTES]  "Reading notes on SOAP, Muon and higher-order optimizers",
+ *            section 1 "AdamW vs. SOAP vs. Muon" (moving-average momentum).
+ *   [GUIDE]  "LLM Optimizers: From SGD and AdamW to SOAP, Muon, and Scalable
+ *            Training", sections 11.3 (momentum, Nesterov), 11.4
+ *            (Newton-Schulz equations, epsilon, tall transpose) and 11.5
+ *            (shape factors, decoupled weight decay).
+ *   [LESSON] "Matrix optimizers: K-FAC, Shampoo and Muon" (Lesson 12),
+ *            subsection "Newton-Schulz: UV^T with matrix products only"
+ *            (Lemma 3 and the three-step algorithm) and subsection "Muon"
+ *            (steps 1-4, update size).
+ *   [PREPRINT] "SOAP, Muon, and Beyond: Pushing LLM Pretraining Scales"
+ *            (epsilon 1e-7 for Muon).
+ *
+ * Conventions shared by every entry point:
+ *   - All matrix memory and all workspaces are caller-owned DEVICE memory.
+ *     The library never allocates, frees or synchronizes; every call only
+ *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
+ *     and returns.
+ *   - Matrices are row-major with a leading dimension `ld` (elements between
+ *     consecutive rows, ld >= cols).  A batch holds `count` matrices of one
+ *     shape and dtype: matrix i lives at ptrs[i] when `ptrs` is non-NULL (a
+ *     DEVICE array of count pointers) and at base + i*stride elements
+ *     otherwise.  All pointers must be 16-byte aligned.
+ *   - Arguments are validated before anything is enqueued.  A non-OK status
+ *     means nothing was enqueued (except MUON_ERR_LAUNCH, which reports a
+ *     failed launch); muon_last_error() then gives a thread-local message.
+ *     No C++ exception crosses this boundary.
+ *   - Non-finite values in G or M propagate to sumsq and to the outputs; the
+ *     caller may test sumsq and skip muon_apply (the library never skips).
+ *   - Calls on one stream are ordered; calls that share a workspace must not
+ *     run concurrently on different streams.
+ */
+#ifndef MUON355_H
+#define MUON355_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MUON355_ABI_VERSION 1
+
+typedef enum muon_status {
+  MUON_OK = 0,
+  MUON_ERR_INVALID_VALUE = 1, /* a NULL required pointer, a bad size or a bad hyperparameter */
+  MUON_ERR_UNSUPPORTED = 2,   /* a dtype or mode combination that is not built */
+  MUON_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace() query */
+  MUON_ERR_LAUNCH = 4         /* a kernel launch failed (hipGetLastError) */
+} muon_status_t;
+
+typedef enum muon_dtype {
+  MUON_F32 = 0,  /* IEEE binary32 */
+  MUON_BF16 = 1  /* bfloat16 (upper half of binary32), round-to-nearest-even on store */
+} muon_dtype_t;
+
+typedef enum muon_scale {
+  MUON_SCALE_MATCH_RMS = 0, /* s = coeff * sqrt(max(m, n)); coeff = 0.2 matches AdamW's update RMS
+                               ([GUIDE] 11.5, [LESSON] "Muon" step 4 and "Update size") */
+  MUON_SCALE_ORIGINAL = 1,  /* s = sqrt(max(1, m / n)) ([GUIDE] 11.5, [LESSON] "Muon" step 4) */
+  MUON_SCALE_NONE = 2       /* s = 1 */
+} muon_scale_t;
+
+typedef struct muon_batch {
+  void* const* ptrs; /* device array of `count` matrix pointers, or NULL to use base/stride */
+  void* base;        /* matrix i at base + i*stride elements when ptrs == NULL */
+  int64_t stride;    /* elements between consecutive matrices (strided batch) */
+  int64_t count;     /* number of matrices, >= 1 */
+  int64_t rows;      /* m >= 1 */
+  int64_t cols;      /* n >= 1 */
+  int64_t ld;        /* leading dimension in elements, >= cols */
+  int32_t dtype;     /* muon_dtype_t */
+  int32_t reserved;  /* must be 0 */
+} muon_batch_t;
+
+/* Bytes of device workspace muon_momentum needs for `count` matrices of
+ * rows x cols (per-block partial sums of the Frobenius reduction). */
+size_t muon_momentum_workspace(int64_t count, int64_t rows, int64_t cols);
+
+/*
+ * Momentum, Nesterov blend and the sum of squares of the Newton-Schulz input.
+ *
+ *   M <- beta*M + (1-beta)*G                          ([NOTES] section 1)
+ *   N  = (1-beta)*G + beta*M   if nesterov, else N = M
+ *   sumsq[i] = sum of N_i^2 over all entries          ([GUIDE] 11.4, X_0)
+ *
+ * The pages write the accumulating form B <- beta*B + G, N = G + beta*B
+ * ([GUIDE] 11.3, [LESSON] "Muon" steps 1-2); the moving average here is
+ * (1-beta) times it, which Newton-Schulz's normalization removes.
+ *
+ * grad : G, BF16 or F32, read only.
+ * mom  : M, F32, read and written in place.
+ * nout : N, BF16 or F32, written; may be NULL only when nesterov == 0, in
+ *        which case M itself is the Newton-Schulz input.
+ * sumsq: device float[count], written (sum of squares of N as computed in
+ *        fp32, before any bf16 rounding of N; partials are added in fp64).
+ * beta : in [0, 1).  nesterov: 0 or 1.
+ * Arithmetic is fp32.  Shapes of grad, mom and nout must match.
+ */
+muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom,
+                            const muon_batch_t* nout, float* sumsq, float beta,
+                            int nesterov, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Bytes of device workspace muon_orthogonalize needs for `count` matrices
+ * of stored shape rows x cols computed in `compute` (MUON_BF16 or MUON_F32).
+ * Returns 0 for invalid arguments. */
+size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols,
+                                    int32_t compute);
+
+/*
+ * Newton-Schulz orthogonalization ([GUIDE] 11.4; [LESSON] Lemma 3 and the
+ * algorithm after it):
+ *   X_0 = N / (sqrt(sumsq) + eps), transposed when rows > cols;
+ *   K times: A = X X^T;  B = b*A + c*A*A;  X <- a*X + B*X;
+ *   O = X_K in the stored orientation.
+ *
+ * in     : N, BF16 or F32 (the momentum output), read only.
+ * sumsq  : device float[count] from muon_momentum, or NULL to have it
+ *          computed here from `in`.
+ * out    : O, BF16 or F32, same rows/cols as `in`, written.  May alias
+ *          `in` (the iteration runs in the workspace).
+ * steps  : K >= 0 (5 in Muon).  a, b, c: finite coefficients, the same at
+ *          every step ((3.4445, -4.7750, 2.0315) in Muon).
+ * eps    : finite, >= 0 (1e-7 in Muon, [PREPRINT]); added to the norm.
+ * compute: MUON_BF16 = bf16 MFMA operands with fp32 accumulation and an
+ *          fp32 copy of X for the a*X term (the fast path);
+ *          MUON_F32   = fp32 MFMA throughout (the parity path).
+ * The Gram and polynomial GEMMs compute only upper-triangle tiles and
+ * mirror them.
+ */
+muon_status_t muon_orthogonalize(const muon_batch_t* in, const float* sumsq,
+                                 const muon_batch_t* out, int steps, float a,
+                                 float b, float c, float eps, int32_t compute,
+                                 void* workspace, size_t ws_bytes,
+                                 void* stream);
+
+/* Grouped form: `ngroups` batches of different shapes orthogonalized with
+ * one kernel launch per stage (every group's tiles packed into one grid).
+ * ins[g], outs[g] and sumsqs[g] are as in muon_orthogonalize (sumsqs may be
+ * NULL, or hold NULL entries, to compute them here).  1 <= ngroups <= 8.
+ * The workspace query takes the same per-group arrays. */
+size_t muon_orthogonalize_grouped_workspace(int ngroups, const int64_t* counts,
+                                            const int64_t* rows,
+                                            const int64_t* cols,
+                                            int32_t compute);
+muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins,
+                                         const float* const* sumsqs,
+                                         const muon_batch_t* outs, int steps,
+                                         float a, float b, float c, float eps,
+                                         int32_t compute, void* workspace,
+                                         size_t ws_bytes, void* stream);
+
+/*
+ * Parameter update ([GUIDE] 11.5 update equation; [LESSON] "Muon" step 4):
+ *   W <- (1 - lr*weight_decay) * W - lr * s * O
+ * with s from `mode` and `coeff` (see muon_scale_t) and (m, n) = (rows,
+ * cols) of W.  Both terms read the old W.  Arithmetic is fp32; a BF16 W is
+ * rounded once to nearest even.
+ *
+ * weight: W, BF16 or F32, in place.  ortho: O, BF16 or F32, same shape.
+ * lr, weight_decay, coeff: finite.
+ */
+muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho,
+                         float lr, float weight_decay, int32_t mode,
+                         float coeff, void* stream);
+
+/* Static text for a status code. */
+const char* muon_status_string(muon_status_t status);
+/* Thread-local detail of the last non-OK return on this thread ("" if none). */
+const char* muon_last_error(void);
+/* MUON355_ABI_VERSION of the loaded library. */
+int muon_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON355_H */

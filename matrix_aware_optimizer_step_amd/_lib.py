@@ -1,0 +1,139 @@
+"""ctypes binding of libmuon355 (include/muon355.h).
+
+Argument marshalling only: every step of the Muon path runs in the library's
+HIP kernels.  Each function has the name of the C entry point it wraps,
+takes ``MuonBatch`` descriptors and raw device addresses, and raises
+``MuonError`` on a non-OK status.  Loading fails loudly when the library has
+not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmuon355.so")
+
+MUON_F32 = 0
+MUON_BF16 = 1
+MUON_SCALE_MATCH_RMS = 0
+MUON_SCALE_ORIGINAL = 1
+MUON_SCALE_NONE = 2
+
+STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
+          3: "MUON_ERR_WORKSPACE", 4: "MUON_ERR_LAUNCH"}
+
+EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
+            "muon_momentum", "muon_orthogonalize_workspace", "muon_orthogonalize",
+            "muon_orthogonalize_grouped_workspace", "muon_orthogonalize_grouped", "muon_apply")
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+
+
+class MuonBatch(ctypes.Structure):
+    _fields_ = [("ptrs", ctypes.c_void_p), ("base", ctypes.c_void_p), ("stride", ctypes.c_int64),
+                ("count", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "(the Muon path has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(MuonBatch)
+    vp, f32, i32, i64, sz = ctypes.c_void_p, ctypes.c_float, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "muon_abi_version": (ctypes.c_int, []),
+        "muon_last_error": (ctypes.c_char_p, []),
+        "muon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "muon_momentum_workspace": (sz, [i64, i64, i64]),
+        "muon_momentum": (ctypes.c_int, [P, P, P, vp, f32, ctypes.c_int, vp, sz, vp]),
+        "muon_orthogonalize_workspace": (sz, [i64, i64, i64, i32]),
+        "muon_orthogonalize": (ctypes.c_int, [P, vp, P, ctypes.c_int, f32, f32, f32, f32, i32, vp, sz, vp]),
+        "muon_orthogonalize_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                      ctypes.POINTER(i64), i32]),
+        "muon_orthogonalize_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(vp), P, ctypes.c_int,
+                                                      f32, f32, f32, f32, i32, vp, sz, vp]),
+        "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        detail = load().muon_last_error().decode(errors="replace")
+        raise MuonError(status, where, detail)
+
+
+def _ref(b):
+    return None if b is None else ctypes.byref(b)
+
+
+def muon_abi_version() -> int:
+    return load().muon_abi_version()
+
+
+def muon_momentum_workspace(count: int, rows: int, cols: int) -> int:
+    return load().muon_momentum_workspace(count, rows, cols)
+
+
+def muon_momentum(grad: MuonBatch, mom: MuonBatch, nout: MuonBatch | None, sumsq_ptr: int, beta: float,
+                  nesterov: bool, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    st = load().muon_momentum(_ref(grad), _ref(mom), _ref(nout), sumsq_ptr, beta, int(bool(nesterov)),
+                              workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_momentum")
+
+
+def muon_orthogonalize_workspace(count: int, rows: int, cols: int, compute: int) -> int:
+    return load().muon_orthogonalize_workspace(count, rows, cols, compute)
+
+
+def muon_orthogonalize(inp: MuonBatch, sumsq_ptr: int | None, out: MuonBatch, steps: int, a: float, b: float,
+                       c: float, eps: float, compute: int, workspace_ptr: int, ws_bytes: int,
+                       stream: int) -> None:
+    st = load().muon_orthogonalize(_ref(inp), sumsq_ptr, _ref(out), steps, a, b, c, eps, compute,
+                                   workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_orthogonalize")
+
+
+def muon_orthogonalize_grouped_workspace(counts, rows, cols, compute: int) -> int:
+    n = len(counts)
+    arr = ctypes.c_int64 * n
+    return load().muon_orthogonalize_grouped_workspace(n, arr(*counts), arr(*rows), arr(*cols), compute)
+
+
+def muon_orthogonalize_grouped(ins, sumsq_ptrs, outs, steps: int, a: float, b: float, c: float, eps: float,
+                               compute: int, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    n = len(ins)
+    if len(outs) != n:
+        raise ValueError("ins and outs differ in length")
+    ins_arr = (MuonBatch * n)(*ins)
+    outs_arr = (MuonBatch * n)(*outs)
+    ss = None
+    if sumsq_ptrs is not None:
+        ss = (ctypes.c_void_p * n)(*[p if p else None for p in sumsq_ptrs])
+    st = load().muon_orthogonalize_grouped(n, ins_arr, ss, outs_arr, steps, a, b, c, eps, compute,
+                                           workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_orthogonalize_grouped")
+
+
+def muon_apply(weight: MuonBatch, ortho: MuonBatch, lr: float, weight_decay: float, mode: int, coeff: float,
+               stream: int) -> None:
+    st = load().muon_apply(_ref(weight), _ref(ortho), lr, weight_decay, mode, coeff, stream)
+    _check(st, "muon_apply")

@@ -1,0 +1,501 @@
+// C-ABI layer of libmuon355: argument validation, workspace planning and the
+// host loop that enqueues the Newton-Schulz stages.  Declarations and their
+// contracts are in include/muon355.h.
+
+#include "../../include/muon355.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "muon_internal.h"
+
+namespace muon {
+int elementwise_blocks_per_matrix(int64_t rows, int64_t cols);
+}
+
+namespace {
+
+using namespace muon;
+
+thread_local char g_last_error[512] = "";
+
+muon_status_t fail(muon_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+muon_status_t fail(muon_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+muon_status_t ok() {
+  g_last_error[0] = '\0';
+  return MUON_OK;
+}
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int esize(int32_t dtype) { return dtype == MUON_BF16 ? 2 : 4; }
+
+muon_status_t check_batch(const muon_batch_t* b, const char* name, bool allow_bf16) {
+  if (!b) return fail(MUON_ERR_INVALID_VALUE, "%s: descriptor is NULL", name);
+  if (b->dtype != MUON_F32 && b->dtype != MUON_BF16)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: dtype %d is not MUON_F32 or MUON_BF16", name, b->dtype);
+  if (b->dtype == MUON_BF16 && !allow_bf16)
+    return fail(MUON_ERR_UNSUPPORTED, "%s: must be MUON_F32", name);
+  if (b->reserved != 0) return fail(MUON_ERR_INVALID_VALUE, "%s: reserved field must be 0", name);
+  if (b->count < 1 || b->count > 65535)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: count %lld outside [1, 65535]", name, (long long)b->count);
+  if (b->rows < 1 || b->cols < 1)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: rows and cols must be >= 1 (got %lld x %lld)", name,
+                (long long)b->rows, (long long)b->cols);
+  if (b->rows > kMaxElems / b->cols)
+    return fail(MUON_ERR_UNSUPPORTED, "%s: %lld x %lld has more than 2^31-1 elements", name,
+                (long long)b->rows, (long long)b->cols);
+  if (b->ld < b->cols)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: ld %lld < cols %lld", name, (long long)b->ld, (long long)b->cols);
+  if (!b->ptrs && !b->base) return fail(MUON_ERR_INVALID_VALUE, "%s: both ptrs and base are NULL", name);
+  if (!b->ptrs && b->count > 1 && b->stride < (b->rows - 1) * b->ld + b->cols)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: stride %lld overlaps consecutive matrices", name,
+                (long long)b->stride);
+  if (!b->ptrs && (reinterpret_cast<uintptr_t>(b->base) % esize(b->dtype)) != 0)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: base is not aligned to its element size", name);
+  return MUON_OK;
+}
+
+bool same_shape(const muon_batch_t* a, const muon_batch_t* b) {
+  return a->count == b->count && a->rows == b->rows && a->cols == b->cols;
+}
+
+MatBatch to_mat(const muon_batch_t* b) {
+  MatBatch m;
+  m.base = static_cast<char*>(b->base);
+  m.stride_bytes = b->stride * esize(b->dtype);
+  m.ptrs = b->ptrs;
+  m.ld = b->ld;
+  m.dtype = b->dtype;
+  m.pad_ = 0;
+  return m;
+}
+
+// 16-byte vector path possible: rows of 8 elements start on 16-byte boundaries.
+bool vec_ok(const muon_batch_t* b) {
+  if (b->cols % 8 != 0 || b->ld % 8 != 0) return false;
+  if (b->ptrs) return true;  // documented: every pointer 16-byte aligned
+  if (reinterpret_cast<uintptr_t>(b->base) % 16 != 0) return false;
+  return (b->stride * esize(b->dtype)) % 16 == 0 || b->count == 1;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+muon_status_t launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MUON_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return MUON_OK;
+}
+
+// ------------------------------------------------------------ NS workspace plan
+
+struct GroupPlan {
+  int64_t count;
+  int32_t rows, cols;   // stored shape
+  int32_t ms, ns;       // Newton-Schulz shape (ms <= ns)
+  int32_t tall;
+  int32_t tile;
+  int32_t Mp, Np;       // padded NS shape
+  int32_t Pr, Pc;       // padded stored shape
+  // byte offsets into the workspace
+  int64_t x32, xc[2], xt[2], a, b, sumsq, partials;
+  int32_t blocks_per_mat;
+};
+
+struct Plan {
+  std::vector<GroupPlan> g;
+  int64_t bytes = 0;
+};
+
+bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,
+               int32_t compute, const bool* need_sumsq, Plan* plan) {
+  if (ngroups < 1 || ngroups > kMaxGroups) return false;
+  if (compute != MUON_F32 && compute != MUON_BF16) return false;
+  const int64_t es = compute == MUON_BF16 ? 2 : 4;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align_up(off + bytes, kAlign);
+    return o;
+  };
+  plan->g.clear();
+  for (int i = 0; i < ngroups; ++i) {
+    if (counts[i] < 1 || counts[i] > 65535 || rows[i] < 1 || cols[i] < 1) return false;
+    if (rows[i] > kMaxElems / cols[i]) return false;
+    GroupPlan p{};
+    p.count = counts[i];
+    p.rows = static_cast<int32_t>(rows[i]);
+    p.cols = static_cast<int32_t>(cols[i]);
+    p.tall = rows[i] > cols[i];
+    p.ms = static_cast<int32_t>(p.tall ? cols[i] : rows[i]);
+    p.ns = static_cast<int32_t>(p.tall ? rows[i] : cols[i]);
+    p.tile = p.ms <= 128 ? 128 : 256;
+    p.Mp = static_cast<int32_t>(align_up(p.ms, p.tile));
+    p.Np = static_cast<int32_t>(align_up(p.ns, p.tile));
+    if (static_cast<int64_t>(p.Mp) * p.Np > kMaxElems) return false;
+    p.Pr = p.tall ? p.Np : p.Mp;
+    p.Pc = p.tall ? p.Mp : p.Np;
+    const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
+    const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
+    p.x32 = compute == MUON_BF16 ? take(p.count * mn * 4) : -1;
+    p.xc[0] = take(p.count * mn * es);
+    p.xc[1] = take(p.count * mn * es);
+    p.xt[0] = take(p.count * mn * es);
+    p.xt[1] = take(p.count * mn * es);
+    p.a = take(p.count * mm * es);
+    p.b = take(p.count * mm * es);
+    p.blocks_per_mat = elementwise_blocks_per_matrix(p.rows, p.cols);
+    if (need_sumsq == nullptr || need_sumsq[i]) {
+      p.sumsq = take(p.count * 4);
+      p.partials = take(p.count * p.blocks_per_mat * 4);
+    } else {
+      p.sumsq = p.partials = -1;
+    }
+    plan->g.push_back(p);
+  }
+  plan->bytes = off;
+  return true;
+}
+
+GemmGroup base_group(const GroupPlan& p, int tiles_per_mat, int tiles_m, int tiles_n, int sym) {
+  GemmGroup G;
+  std::memset(&G, 0, sizeof(G));
+  G.count = static_cast<int32_t>(p.count);
+  G.tiles_per_mat = tiles_per_mat;
+  G.tiles_m = tiles_m;
+  G.tiles_n = tiles_n;
+  G.sym = sym;
+  G.ms = p.ms;
+  G.ns = p.ns;
+  G.tall = p.tall;
+  return G;
+}
+
+muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const float* const* sumsqs,
+                                const muon_batch_t* outs, int steps, float a, float b, float c,
+                                float eps, int32_t compute, void* workspace, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (compute != MUON_F32 && compute != MUON_BF16)
+    return fail(MUON_ERR_INVALID_VALUE, "compute %d is not MUON_F32 or MUON_BF16", compute);
+  if (steps < 0) return fail(MUON_ERR_INVALID_VALUE, "steps %d < 0", steps);
+  if (!finite(a) || !finite(b) || !finite(c)) return fail(MUON_ERR_INVALID_VALUE, "coefficients must be finite");
+  if (!finite(eps) || eps < 0.0f) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  if (!ins || !outs) return fail(MUON_ERR_INVALID_VALUE, "ins/outs is NULL");
+  std::vector<int64_t> counts(ngroups), rows(ngroups), cols(ngroups);
+  bool need[kMaxGroups];
+  for (int g = 0; g < ngroups; ++g) {
+    muon_status_t st = check_batch(&ins[g], "in", true);
+    if (st != MUON_OK) return st;
+    st = check_batch(&outs[g], "out", true);
+    if (st != MUON_OK) return st;
+    if (!same_shape(&ins[g], &outs[g])) return fail(MUON_ERR_INVALID_VALUE, "in and out shapes differ (group %d)", g);
+    counts[g] = ins[g].count;
+    rows[g] = ins[g].rows;
+    cols[g] = ins[g].cols;
+    need[g] = sumsqs == nullptr || sumsqs[g] == nullptr;
+  }
+  Plan plan;
+  if (!make_plan(ngroups, counts.data(), rows.data(), cols.data(), compute, need, &plan))
+    return fail(MUON_ERR_UNSUPPORTED, "a padded Newton-Schulz shape exceeds 2^31-1 elements");
+  if (!workspace || ws_bytes < static_cast<size_t>(plan.bytes))
+    return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %lld needed", ws_bytes, (long long)plan.bytes);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MUON_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  const int64_t es = compute == MUON_BF16 ? 2 : 4;
+  hipError_t e;
+
+  // 1. sums of squares that the caller did not provide
+  std::vector<const float*> ssq(ngroups);
+  for (int g = 0; g < ngroups; ++g) {
+    const GroupPlan& p = plan.g[g];
+    if (!need[g]) {
+      ssq[g] = sumsqs[g];
+      continue;
+    }
+    SumsqArgs sa;
+    sa.X = to_mat(&ins[g]);
+    sa.partials = reinterpret_cast<float*>(ws + p.partials);
+    sa.blocks_per_mat = p.blocks_per_mat;
+    sa.rows = p.rows;
+    sa.cols = p.cols;
+    sa.cdiv = make_fastdiv(static_cast<uint32_t>(p.cols));
+    if ((e = launch_sumsq_partials(sa, p.count, vec_ok(&ins[g]), stream)) != hipSuccess)
+      return launch_status(e, "sumsq partials");
+    float* out = reinterpret_cast<float*>(ws + p.sumsq);
+    if ((e = launch_sumsq_finalize(sa.partials, p.blocks_per_mat, out, p.count, stream)) != hipSuccess)
+      return launch_status(e, "sumsq finalize");
+    ssq[g] = out;
+  }
+
+  // 2. X_0 = N / (||N|| + eps) into the padded buffers, both orientations
+  for (int g = 0; g < ngroups; ++g) {
+    const GroupPlan& p = plan.g[g];
+    const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
+    PackArgs pa;
+    pa.N = to_mat(&ins[g]);
+    pa.sumsq = ssq[g];
+    pa.eps = eps;
+    pa.rows = p.rows;
+    pa.cols = p.cols;
+    pa.Pr = p.Pr;
+    pa.Pc = p.Pc;
+    pa.compute = compute;
+    pa.tall = p.tall;
+    // S is the stored orientation, T its transpose; X = S unless tall.
+    pa.S = ws + (p.tall ? p.xt[0] : p.xc[0]);
+    pa.T = ws + (p.tall ? p.xc[0] : p.xt[0]);
+    pa.s_mat = pa.t_mat = mn * es;
+    pa.F = compute == MUON_BF16 ? reinterpret_cast<float*>(ws + p.x32) : nullptr;
+    pa.f_mat = mn;
+    if ((e = launch_pack(pa, p.count, stream)) != hipSuccess) return launch_status(e, "pack");
+  }
+
+  if (steps == 0) {
+    for (int g = 0; g < ngroups; ++g) {
+      const GroupPlan& p = plan.g[g];
+      CopyOutArgs ca;
+      ca.X = reinterpret_cast<const float*>(ws + (compute == MUON_BF16 ? p.x32 : p.xc[0]));
+      ca.x_mat = static_cast<int64_t>(p.Mp) * p.Np;
+      ca.ldx = p.Np;
+      ca.out = to_mat(&outs[g]);
+      ca.rows = p.rows;
+      ca.cols = p.cols;
+      ca.tall = p.tall;
+      if ((e = launch_copy_out(ca, p.count, stream)) != hipSuccess) return launch_status(e, "copy out");
+    }
+    return ok();
+  }
+
+  // 3. the K-step loop: Gram, polynomial, update; one launch per stage and tile class
+  for (int k = 0; k < steps; ++k) {
+    const int cur = k & 1;
+    const int nxt = cur ^ 1;
+    const bool last = k + 1 == steps;
+    for (int stage = 0; stage < 3; ++stage) {
+      for (int tile : {256, 128}) {
+        GemmLaunch L;
+        std::memset(&L, 0, sizeof(L));
+        L.a = a;
+        L.b = b;
+        L.c = c;
+        int total = 0;
+        for (int g = 0; g < ngroups; ++g) {
+          const GroupPlan& p = plan.g[g];
+          if (p.tile != tile) continue;
+          const int T = p.Mp / tile;
+          const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
+          const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
+          GemmGroup G;
+          if (stage == 0) {  // A = X X^T
+            G = base_group(p, T * (T + 1) / 2, T, T, 1);
+            G.P = G.Q = ws + p.xc[cur];
+            G.p_mat = G.q_mat = mn * es;
+            G.ldp = G.ldq = p.Np;
+            G.K = p.Np;
+            G.O0 = ws + p.a;
+            G.o0_mat = mm * es;
+            G.ldo0 = p.Mp;
+          } else if (stage == 1) {  // B = b A + c A A
+            G = base_group(p, T * (T + 1) / 2, T, T, 1);
+            G.P = G.Q = ws + p.a;
+            G.p_mat = G.q_mat = mm * es;
+            G.ldp = G.ldq = p.Mp;
+            G.K = p.Mp;
+            G.E0 = ws + p.a;
+            G.e0_mat = mm * es;
+            G.lde0 = p.Mp;
+            G.O0 = ws + p.b;
+            G.o0_mat = mm * es;
+            G.ldo0 = p.Mp;
+          } else {  // X' = a X + B X
+            const int Tn = p.Np / tile;
+            G = base_group(p, T * Tn, T, Tn, 0);
+            G.P = ws + p.b;
+            G.p_mat = mm * es;
+            G.ldp = p.Mp;
+            G.Q = ws + p.xt[cur];
+            G.q_mat = mn * es;
+            G.ldq = p.Mp;
+            G.K = p.Mp;
+            const int64_t xsrc = compute == MUON_BF16 ? p.x32 : p.xc[cur];
+            G.E0 = ws + xsrc;
+            G.e0_mat = mn * 4;
+            G.lde0 = p.Np;
+            if (last) {
+              G.user = to_mat(&outs[g]);
+            } else {
+              G.O0 = ws + (compute == MUON_BF16 ? p.x32 : p.xc[nxt]);
+              G.o0_mat = mn * 4;
+              G.ldo0 = p.Np;
+              if (compute == MUON_BF16) {
+                G.O1 = ws + p.xc[nxt];
+                G.o1_mat = mn * 2;
+                G.ldo1 = p.Np;
+              }
+              G.OT = ws + p.xt[nxt];
+              G.ot_mat = mn * es;
+              G.ldot = p.Mp;
+            }
+          }
+          G.tile_begin = total;
+          total += G.tiles_per_mat * G.count;
+          L.g[L.ngroups++] = G;
+        }
+        if (L.ngroups == 0) continue;
+        L.total_tiles = total;
+        const int epi = stage == 0 ? EPI_GRAM : stage == 1 ? EPI_POLY : (last ? EPI_FINAL : EPI_UPDATE);
+        if ((e = launch_ns_gemm(compute, tile, epi, L, stream)) != hipSuccess)
+          return launch_status(e, "newton-schulz gemm");
+      }
+    }
+  }
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int muon_abi_version(void) { return MUON355_ABI_VERSION; }
+
+const char* muon_last_error(void) { return g_last_error; }
+
+const char* muon_status_string(muon_status_t s) {
+  switch (s) {
+    case MUON_OK: return "MUON_OK";
+    case MUON_ERR_INVALID_VALUE: return "MUON_ERR_INVALID_VALUE";
+    case MUON_ERR_UNSUPPORTED: return "MUON_ERR_UNSUPPORTED";
+    case MUON_ERR_WORKSPACE: return "MUON_ERR_WORKSPACE";
+    case MUON_ERR_LAUNCH: return "MUON_ERR_LAUNCH";
+  }
+  return "unknown muon_status_t";
+}
+
+size_t muon_momentum_workspace(int64_t count, int64_t rows, int64_t cols) {
+  if (count < 1 || rows < 1 || cols < 1 || rows > kMaxElems / cols) return 0;
+  return static_cast<size_t>(align_up(count * elementwise_blocks_per_matrix(rows, cols) * 4, kAlign));
+}
+
+muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom, const muon_batch_t* nout,
+                            float* sumsq, float beta, int nesterov, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
+  if ((st = check_batch(mom, "mom", false)) != MUON_OK) return st;
+  if (!same_shape(grad, mom)) return fail(MUON_ERR_INVALID_VALUE, "grad and mom shapes differ");
+  if (nout) {
+    if ((st = check_batch(nout, "nout", true)) != MUON_OK) return st;
+    if (!same_shape(grad, nout)) return fail(MUON_ERR_INVALID_VALUE, "grad and nout shapes differ");
+  } else if (nesterov) {
+    return fail(MUON_ERR_INVALID_VALUE, "nout may be NULL only without Nesterov");
+  }
+  if (!sumsq) return fail(MUON_ERR_INVALID_VALUE, "sumsq is NULL");
+  if (!(beta >= 0.0f && beta < 1.0f)) return fail(MUON_ERR_INVALID_VALUE, "beta must lie in [0, 1)");
+  if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_VALUE, "nesterov must be 0 or 1");
+  const size_t need = muon_momentum_workspace(grad->count, grad->rows, grad->cols);
+  if (!workspace || ws_bytes < need)
+    return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+    return fail(MUON_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+
+  MomentumArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.G = to_mat(grad);
+  a.M = to_mat(mom);
+  if (nout) a.N = to_mat(nout);
+  a.has_n = nout != nullptr;
+  a.partials = static_cast<float*>(workspace);
+  a.blocks_per_mat = elementwise_blocks_per_matrix(grad->rows, grad->cols);
+  a.rows = static_cast<int32_t>(grad->rows);
+  a.cols = static_cast<int32_t>(grad->cols);
+  a.cdiv = make_fastdiv(static_cast<uint32_t>(grad->cols));
+  a.beta = beta;
+  a.nesterov = nesterov;
+  const bool vec = vec_ok(grad) && vec_ok(mom) && (!nout || vec_ok(nout));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_momentum(a, grad->count, vec, s);
+  if (e != hipSuccess) return launch_status(e, "momentum");
+  e = launch_sumsq_finalize(a.partials, a.blocks_per_mat, sumsq, grad->count, s);
+  if (e != hipSuccess) return launch_status(e, "sumsq finalize");
+  return ok();
+}
+
+size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols, int32_t compute) {
+  Plan plan;
+  bool need = true;
+  if (!make_plan(1, &count, &rows, &cols, compute, &need, &plan)) return 0;
+  return static_cast<size_t>(plan.bytes);
+}
+
+size_t muon_orthogonalize_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
+                                            const int64_t* cols, int32_t compute) {
+  if (!counts || !rows || !cols) return 0;
+  Plan plan;
+  if (!make_plan(ngroups, counts, rows, cols, compute, nullptr, &plan)) return 0;
+  return static_cast<size_t>(plan.bytes);
+}
+
+muon_status_t muon_orthogonalize(const muon_batch_t* in, const float* sumsq, const muon_batch_t* out, int steps,
+                                 float a, float b, float c, float eps, int32_t compute, void* workspace,
+                                 size_t ws_bytes, void* stream) {
+  const float* s[1] = {sumsq};
+  return run_orthogonalize(1, in, s, out, steps, a, b, c, eps, compute, workspace, ws_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins, const float* const* sumsqs,
+                                         const muon_batch_t* outs, int steps, float a, float b, float c,
+                                         float eps, int32_t compute, void* workspace, size_t ws_bytes,
+                                         void* stream) {
+  return run_orthogonalize(ngroups, ins, sumsqs, outs, steps, a, b, c, eps, compute, workspace, ws_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,
+                         int32_t mode, float coeff, void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(weight, "weight", true)) != MUON_OK) return st;
+  if ((st = check_batch(ortho, "ortho", true)) != MUON_OK) return st;
+  if (!same_shape(weight, ortho)) return fail(MUON_ERR_INVALID_VALUE, "weight and ortho shapes differ");
+  if (!finite(lr) || !finite(weight_decay) || !finite(coeff))
+    return fail(MUON_ERR_INVALID_VALUE, "lr, weight_decay and coeff must be finite");
+  const double m = static_cast<double>(weight->rows);
+  const double n = static_cast<double>(weight->cols);
+  double s;
+  switch (mode) {
+    case MUON_SCALE_MATCH_RMS: s = static_cast<double>(coeff) * std::sqrt(m > n ? m : n); break;
+    case MUON_SCALE_ORIGINAL: s = std::sqrt(m / n > 1.0 ? m / n : 1.0); break;
+    case MUON_SCALE_NONE: s = 1.0; break;
+    default: return fail(MUON_ERR_INVALID_VALUE, "unknown scale mode %d", mode);
+  }
+  ApplyArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.W = to_mat(weight);
+  a.O = to_mat(ortho);
+  a.rows = static_cast<int32_t>(weight->rows);
+  a.cols = static_cast<int32_t>(weight->cols);
+  a.cdiv = make_fastdiv(static_cast<uint32_t>(weight->cols));
+  a.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
+  a.step = static_cast<float>(static_cast<double>(lr) * s);
+  const bool vec = vec_ok(weight) && vec_ok(ortho);
+  hipError_t e = launch_apply(a, weight->count, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return launch_status(e, "apply");
+  return ok();
+}
+
+}  // extern "C"

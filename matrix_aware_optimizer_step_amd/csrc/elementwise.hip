@@ -1,0 +1,386 @@
+// HBM-bound kernels of the Muon step on gfx950:
+//
+//   momentum_kernel   M <- beta*M + (1-beta)*G and the Nesterov blend N
+//                     ("Reading notes on SOAP, Muon and higher-order
+//                     optimizers", section 1; "LLM Optimizers: From SGD and
+//                     AdamW to SOAP, Muon, and Scalable Training", section
+//                     11.3), with per-workgroup partial sums of N^2 for the
+//                     Frobenius norm of section 11.4;
+//   finalize_kernel   one fixed-order fp64 reduction of those partials per
+//                     matrix (deterministic; no float atomics);
+//   apply_kernel      W <- (1 - lr*wd)*W - lr*s*O (section 11.5);
+//   pack_kernel       N / (||N||_F + eps) into the padded Newton-Schulz
+//                     buffers, in both orientations, through an LDS tile
+//                     transpose so that reads and writes stay coalesced;
+//   copy_out_kernel   the zero-step output.
+//
+// The streaming kernels move 16 bytes per lane per access (8 bf16 or 4+4
+// fp32 values per thread step), reduce with wave64 shuffles and one LDS
+// exchange per workgroup, and address rows through a multiply-high division
+// so that matrices with ld > cols (row blocks of a larger weight) need no
+// separate path.
+
+#include "muon_internal.h"
+
+namespace muon {
+
+FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  uint32_t l = 0;
+  while ((1ull << l) < d) ++l;
+  f.l = l;
+  // m = floor(2^32 * (2^l - d) / d) + 1
+  f.m = static_cast<uint32_t>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  return f;
+}
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kVec = 8;        // elements per thread step
+constexpr int kUnroll = 4;     // thread steps per workgroup pass
+constexpr int kElemsPerBlock = kThreads * kVec * kUnroll;  // 8192
+
+__device__ __forceinline__ uint32_t fdiv(const FastDiv& f, uint32_t n) {
+  const uint64_t t = static_cast<uint64_t>(__umulhi(n, f.m)) + n;
+  return static_cast<uint32_t>(t >> f.l);
+}
+
+__device__ __forceinline__ char* mat_ptr(const MatBatch& m, int64_t i) {
+  return m.ptrs ? static_cast<char*>(m.ptrs[i]) : m.base + i * m.stride_bytes;
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __builtin_bit_cast(float, static_cast<uint32_t>(h) << 16);
+}
+
+// Load 8 consecutive values of a bf16 or f32 matrix as fp32.
+__device__ __forceinline__ void load8(const char* p, int dtype, float* v) {
+  if (dtype) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __builtin_bit_cast(float, w[k] << 16);
+      v[2 * k + 1] = __builtin_bit_cast(float, w[k] & 0xffff0000u);
+    }
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(p)[0];
+    const float4 b = reinterpret_cast<const float4*>(p)[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+__device__ __forceinline__ void store8(char* p, int dtype, const float* v) {
+  if (dtype) {
+    uint4 u;
+    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
+    u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    *reinterpret_cast<uint4*>(p) = u;
+  } else {
+    reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+}
+
+__device__ __forceinline__ float load1(const char* p, int dtype) {
+  return dtype ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(p)) : *reinterpret_cast<const float*>(p);
+}
+__device__ __forceinline__ void store1(char* p, int dtype, float v) {
+  if (dtype) {
+    *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(v);
+  } else {
+    *reinterpret_cast<float*>(p) = v;
+  }
+}
+
+// Workgroup sum of one float per thread; result valid in thread 0.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.0f;
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) s += red[i];
+  }
+  return s;
+}
+
+// ------------------------------------------------------------ momentum
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumArgs a) {
+  __shared__ float red[kThreads / 64];
+  const int64_t mat = blockIdx.y;
+  const char* g = mat_ptr(a.G, mat);
+  char* m = mat_ptr(a.M, mat);
+  char* n = a.has_n ? mat_ptr(a.N, mat) : nullptr;
+  const int gs = a.G.dtype ? 2 : 4;
+  const int ns = a.N.dtype ? 2 : 4;
+  const uint32_t total = static_cast<uint32_t>(a.rows) * static_cast<uint32_t>(a.cols);
+  const float beta = a.beta;
+  const float omb = 1.0f - a.beta;
+  float ss = 0.0f;
+  const uint32_t base = static_cast<uint32_t>(blockIdx.x) * kElemsPerBlock;
+  if (VEC) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = base + (u * kThreads + threadIdx.x) * kVec;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        float gv[kVec], mv[kVec], nv[kVec];
+        load8(g + (r * a.G.ld + c) * gs, a.G.dtype, gv);
+        float* mp = reinterpret_cast<float*>(m + (r * a.M.ld + c) * 4);
+        load8(reinterpret_cast<const char*>(mp), 0, mv);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) {
+          mv[k] = beta * mv[k] + omb * gv[k];
+          nv[k] = a.nesterov ? omb * gv[k] + beta * mv[k] : mv[k];
+          ss += nv[k] * nv[k];
+        }
+        store8(reinterpret_cast<char*>(mp), 0, mv);
+        if (n) store8(n + (r * a.N.ld + c) * ns, a.N.dtype, nv);
+      }
+    }
+  } else {
+    for (int u = 0; u < kUnroll * kVec; ++u) {
+      const uint32_t e = base + u * kThreads + threadIdx.x;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        const float gv = load1(g + (r * a.G.ld + c) * gs, a.G.dtype);
+        float* mp = reinterpret_cast<float*>(m + (r * a.M.ld + c) * 4);
+        const float mv = beta * *mp + omb * gv;
+        const float nv = a.nesterov ? omb * gv + beta * mv : mv;
+        ss += nv * nv;
+        *mp = mv;
+        if (n) store1(n + (r * a.N.ld + c) * ns, a.N.dtype, nv);
+      }
+    }
+  }
+  const float s = block_sum(ss, red);
+  if (threadIdx.x == 0) a.partials[mat * a.blocks_per_mat + blockIdx.x] = s;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void sumsq_partials_kernel(const SumsqArgs a) {
+  __shared__ float red[kThreads / 64];
+  const int64_t mat = blockIdx.y;
+  const char* x = mat_ptr(a.X, mat);
+  const int xs = a.X.dtype ? 2 : 4;
+  const uint32_t total = static_cast<uint32_t>(a.rows) * static_cast<uint32_t>(a.cols);
+  float ss = 0.0f;
+  const uint32_t base = static_cast<uint32_t>(blockIdx.x) * kElemsPerBlock;
+  if (VEC) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = base + (u * kThreads + threadIdx.x) * kVec;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        float v[kVec];
+        load8(x + (r * a.X.ld + c) * xs, a.X.dtype, v);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) ss += v[k] * v[k];
+      }
+    }
+  } else {
+    for (int u = 0; u < kUnroll * kVec; ++u) {
+      const uint32_t e = base + u * kThreads + threadIdx.x;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        const float v = load1(x + (r * a.X.ld + c) * xs, a.X.dtype);
+        ss += v * v;
+      }
+    }
+  }
+  const float s = block_sum(ss, red);
+  if (threadIdx.x == 0) a.partials[mat * a.blocks_per_mat + blockIdx.x] = s;
+}
+
+// One workgroup per matrix: fixed-order fp64 sum of its partials.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* partials, int per, float* sumsq) {
+  __shared__ double red[kThreads];
+  const int64_t mat = blockIdx.x;
+  const float* p = partials + mat * per;
+  double s = 0.0;
+  for (int i = threadIdx.x; i < per; i += kThreads) s += static_cast<double>(p[i]);
+  red[threadIdx.x] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = kThreads / 2; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) sumsq[mat] = static_cast<float>(red[0]);
+}
+
+// ------------------------------------------------------------ apply
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void apply_kernel(const ApplyArgs a) {
+  const int64_t mat = blockIdx.y;
+  char* w = mat_ptr(a.W, mat);
+  const char* o = mat_ptr(a.O, mat);
+  const int ws = a.W.dtype ? 2 : 4;
+  const int os = a.O.dtype ? 2 : 4;
+  const uint32_t total = static_cast<uint32_t>(a.rows) * static_cast<uint32_t>(a.cols);
+  const uint32_t base = static_cast<uint32_t>(blockIdx.x) * kElemsPerBlock;
+  if (VEC) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t e = base + (u * kThreads + threadIdx.x) * kVec;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        char* wp = w + (r * a.W.ld + c) * ws;
+        float wv[kVec], ov[kVec];
+        load8(wp, a.W.dtype, wv);
+        load8(o + (r * a.O.ld + c) * os, a.O.dtype, ov);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) wv[k] = a.decay * wv[k] - a.step * ov[k];
+        store8(wp, a.W.dtype, wv);
+      }
+    }
+  } else {
+    for (int u = 0; u < kUnroll * kVec; ++u) {
+      const uint32_t e = base + u * kThreads + threadIdx.x;
+      if (e < total) {
+        const uint32_t r = fdiv(a.cdiv, e);
+        const uint32_t c = e - r * a.cols;
+        char* wp = w + (r * a.W.ld + c) * ws;
+        const float v = a.decay * load1(wp, a.W.dtype) - a.step * load1(o + (r * a.O.ld + c) * os, a.O.dtype);
+        store1(wp, a.W.dtype, v);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ pack
+
+constexpr int kTile = 64;
+
+// grid: (Pc/64, Pr/64, count).  Each workgroup moves one 64x64 tile of the
+// padded stored-orientation extent.
+__global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
+  __shared__ float tile[kTile][kTile + 1];
+  const int64_t mat = blockIdx.z;
+  const int r0 = blockIdx.y * kTile;
+  const int c0 = blockIdx.x * kTile;
+  const char* n = mat_ptr(a.N, mat);
+  const int nsz = a.N.dtype ? 2 : 4;
+  const float ssq = a.sumsq[mat];
+  const float scale = 1.0f / (sqrtf(ssq) + a.eps);
+  const int tx = threadIdx.x & 63;
+  const int ty = threadIdx.x >> 6;  // 0..3
+  const int esz = a.compute ? 2 : 4;
+  // read rows of N (zero outside m x n), write rows of S
+  char* S = a.S + mat * a.s_mat;
+  for (int rr = ty; rr < kTile; rr += 4) {
+    const int r = r0 + rr;
+    const int c = c0 + tx;
+    float v = 0.0f;
+    if (r < a.rows && c < a.cols) v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
+    tile[rr][tx] = v;
+    store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
+    if (a.F && !a.tall) a.F[mat * a.f_mat + static_cast<int64_t>(r) * a.Pc + c] = v;
+  }
+  __syncthreads();
+  // write rows of T = columns of the tile
+  char* T = a.T + mat * a.t_mat;
+  for (int cc = ty; cc < kTile; cc += 4) {
+    const int c = c0 + cc;
+    const int r = r0 + tx;
+    const float v = tile[tx][cc];
+    store1(T + (static_cast<int64_t>(c) * a.Pr + r) * esz, a.compute, v);
+    if (a.F && a.tall) a.F[mat * a.f_mat + static_cast<int64_t>(c) * a.Pr + r] = v;
+  }
+}
+
+// grid: (ceil(cols/64), ceil(rows/64), count) over the stored output.
+__global__ __launch_bounds__(kThreads) void copy_out_kernel(const CopyOutArgs a) {
+  const int64_t mat = blockIdx.z;
+  char* o = mat_ptr(a.out, mat);
+  const int osz = a.out.dtype ? 2 : 4;
+  const float* X = a.X + mat * a.x_mat;
+  const int tx = threadIdx.x & 63;
+  const int ty = threadIdx.x >> 6;
+  for (int rr = ty; rr < kTile; rr += 4) {
+    const int r = blockIdx.y * kTile + rr;
+    const int c = blockIdx.x * kTile + tx;
+    if (r < a.rows && c < a.cols) {
+      const float v = a.tall ? X[static_cast<int64_t>(c) * a.ldx + r] : X[static_cast<int64_t>(r) * a.ldx + c];
+      store1(o + (static_cast<int64_t>(r) * a.out.ld + c) * osz, a.out.dtype, v);
+    }
+  }
+}
+
+}  // namespace
+
+int elementwise_blocks_per_matrix(int64_t rows, int64_t cols) {
+  return static_cast<int>((rows * cols + kElemsPerBlock - 1) / kElemsPerBlock);
+}
+
+hipError_t launch_momentum(const MomentumArgs& a, int64_t count, bool vec, hipStream_t stream) {
+  dim3 grid(a.blocks_per_mat, static_cast<unsigned>(count));
+  if (vec) {
+    hipLaunchKernelGGL(momentum_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(momentum_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_partials(const SumsqArgs& a, int64_t count, bool vec, hipStream_t stream) {
+  dim3 grid(a.blocks_per_mat, static_cast<unsigned>(count));
+  if (vec) {
+    hipLaunchKernelGGL(sumsq_partials_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(sumsq_partials_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_finalize(const float* partials, int per, float* sumsq, int64_t count,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_kernel, dim3(static_cast<unsigned>(count)), dim3(kThreads), 0, stream,
+                     partials, per, sumsq);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply(const ApplyArgs& a, int64_t count, bool vec, hipStream_t stream) {
+  const int per = elementwise_blocks_per_matrix(a.rows, a.cols);
+  dim3 grid(per, static_cast<unsigned>(count));
+  if (vec) {
+    hipLaunchKernelGGL(apply_kernel<true>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(apply_kernel<false>, grid, dim3(kThreads), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream) {
+  dim3 grid(a.Pc / kTile, a.Pr / kTile, static_cast<unsigned>(count));
+  hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t stream) {
+  dim3 grid((a.cols + kTile - 1) / kTile, (a.rows + kTile - 1) / kTile, static_cast<unsigned>(count));
+  hipLaunchKernelGGL(copy_out_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace muon

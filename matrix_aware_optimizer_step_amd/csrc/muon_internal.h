@@ -1,0 +1,141 @@
+// Internal declarations shared by the libmuon355 kernels and its C-ABI layer.
+// Nothing here is part of the public interface (include/muon355.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace muon {
+
+constexpr int kMaxGroups = 8;
+
+// One batch of same-shape matrices in device memory, as seen by a kernel.
+struct MatBatch {
+  char* base;            // matrix i at base + i*stride_bytes when ptrs == nullptr
+  int64_t stride_bytes;
+  void* const* ptrs;     // device array of per-matrix pointers, or nullptr
+  int64_t ld;            // leading dimension in elements
+  int32_t dtype;         // 0 = f32, 1 = bf16
+  int32_t pad_;
+};
+
+// Fast unsigned 32-bit division by a runtime-constant divisor
+// (round-up multiply-high method of Granlund and Montgomery).
+struct FastDiv {
+  uint32_t d, m, l;
+};
+FastDiv make_fastdiv(uint32_t d);
+
+// ---------------------------------------------------------------- GEMM stage
+
+enum Epi : int { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL = 3 };
+
+// One group of same-shape NT products C = P * Q^T (P: rows i, Q: rows j, both
+// contiguous along the reduction index k), with the stage's epilogue.
+struct GemmGroup {
+  const char* P; int64_t p_mat;  // bytes between matrices
+  const char* Q; int64_t q_mat;
+  int32_t ldp, ldq;              // elements
+  int32_t K;                     // reduction length, a multiple of the k-tile
+  int32_t tiles_m, tiles_n;      // tile grid of one matrix
+  int32_t sym;                   // 1: only tiles with ti <= tj, mirrored on store
+  int32_t count;
+  int32_t tiles_per_mat;
+  int32_t tile_begin;            // first linear tile of this group in the launch
+  // epilogue operands (row-major, i x j orientation unless noted)
+  const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A (compute type); UPDATE/FINAL: fp32 X
+  int32_t pad0_;
+  char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: fp32 X (next)
+  int32_t pad1_;
+  char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE (bf16 compute): bf16 X (next), else null
+  int32_t pad2_;
+  char* OT; int64_t ot_mat; int32_t ldot;        // UPDATE: X^T (next) in compute type
+  int32_t pad3_;
+  // FINAL: the caller's output in its stored orientation
+  MatBatch user;
+  int32_t tall;                  // 1: user output is X^T
+  int32_t ms, ns;                // true (unpadded) Newton-Schulz shape
+  int32_t pad4_;
+};
+
+struct GemmLaunch {
+  int32_t ngroups;
+  int32_t total_tiles;
+  float a, b, c;
+  int32_t pad_;
+  GemmGroup g[kMaxGroups];
+};
+
+// Launch one stage for all groups (all with the same tile size `tile`).
+// compute: 0 = f32, 1 = bf16.
+hipError_t launch_ns_gemm(int compute, int tile, int epi, const GemmLaunch& L,
+                          hipStream_t stream);
+
+// ------------------------------------------------------------ elementwise
+
+struct MomentumArgs {
+  MatBatch G, M, N;      // N.base == nullptr && N.ptrs == nullptr: N is M
+  float* partials;       // [count * blocks_per_mat]
+  int32_t blocks_per_mat;
+  int32_t rows, cols;
+  FastDiv cdiv;          // division by cols
+  float beta;
+  int32_t nesterov;
+  int32_t has_n;
+};
+hipError_t launch_momentum(const MomentumArgs& a, int64_t count, bool vec,
+                           hipStream_t stream);
+
+struct SumsqArgs {
+  MatBatch X;
+  float* partials;
+  int32_t blocks_per_mat;
+  int32_t rows, cols;
+  FastDiv cdiv;
+};
+hipError_t launch_sumsq_partials(const SumsqArgs& a, int64_t count, bool vec,
+                                 hipStream_t stream);
+
+// sumsq[i] = sum of partials[i*per .. i*per+per) in fp64, fixed order.
+hipError_t launch_sumsq_finalize(const float* partials, int per, float* sumsq,
+                                 int64_t count, hipStream_t stream);
+
+struct ApplyArgs {
+  MatBatch W, O;
+  int32_t rows, cols;
+  FastDiv cdiv;
+  float decay;           // 1 - lr*wd
+  float step;            // lr * s
+};
+hipError_t launch_apply(const ApplyArgs& a, int64_t count, bool vec,
+                        hipStream_t stream);
+
+// Copy the caller's N (stored m x n) into the padded Newton-Schulz buffers,
+// scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc) and
+// T[c][r] (Pc x Pr), zero outside m x n; F32 copy of X (= S if !tall, T if
+// tall) when F != null.
+struct PackArgs {
+  MatBatch N;
+  const float* sumsq;
+  float eps;
+  int32_t rows, cols;      // m, n
+  int32_t Pr, Pc;          // padded
+  int32_t compute;         // element type of S and T
+  int32_t tall;
+  char* S; int64_t s_mat;  // bytes per matrix
+  char* T; int64_t t_mat;
+  float* F; int64_t f_mat; // floats per matrix
+};
+hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream);
+
+// Zero-step output: out (stored orientation) = fp32 X (NS orientation).
+struct CopyOutArgs {
+  const float* X; int64_t x_mat; int32_t ldx;
+  MatBatch out;
+  int32_t rows, cols;      // stored m, n
+  int32_t tall;
+};
+hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t stream);
+
+}  // namespace muon

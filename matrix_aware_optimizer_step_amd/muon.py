@@ -1,0 +1,210 @@
+"""Torch-facing marshalling for libmuon355.
+
+PyTorch supplies device memory and the current HIP stream; this module turns
+tensors into ``MuonBatch`` descriptors, sizes workspaces from the library's
+own queries, and calls the C entry points in the order one Muon step needs
+them ("Matrix optimizers: K-FAC, Shampoo and Muon", subsection "Muon",
+steps 1-4).  It does no arithmetic on the tensors.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _lib as L
+
+QUINTIC = (3.4445, -4.7750, 2.0315)
+EPS = 1e-7
+
+
+def dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return L.MUON_BF16
+    if t.dtype == torch.float32:
+        return L.MUON_F32
+    raise TypeError(f"libmuon355 takes bfloat16 or float32 matrices, not {t.dtype}")
+
+
+@dataclass
+class Batch:
+    """A MuonBatch plus the tensors that must stay alive while it is in use."""
+    desc: L.MuonBatch
+    count: int
+    rows: int
+    cols: int
+    keep: list = field(default_factory=list)
+
+
+def batch(x) -> Batch:
+    """Descriptor for a 2-D tensor (one matrix), a 3-D tensor (strided batch,
+    e.g. ``W.view(32, 128, 4096)`` for per-head row blocks), or a list of
+    same-shape 2-D tensors (passed as a device pointer array)."""
+    if isinstance(x, Batch):
+        return x
+    if isinstance(x, (list, tuple)):
+        if not x:
+            raise ValueError("empty list of matrices")
+        t0 = x[0]
+        for t in x:
+            if t.shape != t0.shape or t.dtype != t0.dtype or t.device != t0.device or t.dim() != 2:
+                raise ValueError("a pointer-array batch needs same-shape, same-dtype 2-D tensors")
+            if t.stride(1) != 1 or t.stride(0) != t0.stride(0):
+                raise ValueError("matrices must be row-major with one leading dimension")
+            if t.is_sparse:
+                raise RuntimeError("dense gradients required")
+        ptrs = torch.tensor([t.data_ptr() for t in x], dtype=torch.int64, device=t0.device)
+        d = L.MuonBatch(ptrs.data_ptr(), None, 0, len(x), t0.shape[0], t0.shape[1], t0.stride(0),
+                        dtype_code(t0), 0)
+        return Batch(d, len(x), t0.shape[0], t0.shape[1], [ptrs, *x])
+    t = x
+    if t.is_sparse:
+        raise RuntimeError("dense gradients required")
+    if t.dim() == 2:
+        if t.stride(1) != 1:
+            raise ValueError("matrices must be row-major (last stride 1)")
+        d = L.MuonBatch(None, t.data_ptr(), 0, 1, t.shape[0], t.shape[1], t.stride(0), dtype_code(t), 0)
+        return Batch(d, 1, t.shape[0], t.shape[1], [t])
+    if t.dim() == 3:
+        if t.stride(2) != 1:
+            raise ValueError("matrices must be row-major (last stride 1)")
+        d = L.MuonBatch(None, t.data_ptr(), t.stride(0), t.shape[0], t.shape[1], t.shape[2], t.stride(1),
+                        dtype_code(t), 0)
+        return Batch(d, t.shape[0], t.shape[1], t.shape[2], [t])
+    raise ValueError("expected a 2-D or 3-D tensor or a list of 2-D tensors")
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def momentum(grad, mom, nout, sumsq: torch.Tensor, beta: float = 0.95, nesterov: bool = True,
+             ws: torch.Tensor | None = None, stream=None) -> None:
+    g, m = batch(grad), batch(mom)
+    n = batch(nout) if nout is not None else None
+    need = L.muon_momentum_workspace(g.count, g.rows, g.cols)
+    if ws is None:
+        ws = workspace(need, sumsq.device)
+    L.muon_momentum(g.desc, m.desc, n.desc if n else None, sumsq.data_ptr(), beta, nesterov,
+                    ws.data_ptr(), ws.numel(), _stream(stream))
+
+
+def orthogonalize(inp, out, sumsq: torch.Tensor | None = None, steps: int = 5, coeffs=QUINTIC,
+                  eps: float = EPS, compute: int = L.MUON_BF16, ws: torch.Tensor | None = None,
+                  stream=None, device=None) -> None:
+    i, o = batch(inp), batch(out)
+    if ws is None:
+        need = L.muon_orthogonalize_workspace(i.count, i.rows, i.cols, compute)
+        ws = workspace(need, device or (sumsq.device if sumsq is not None else i.keep[-1].device))
+    a, b, c = coeffs
+    L.muon_orthogonalize(i.desc, sumsq.data_ptr() if sumsq is not None else None, o.desc, steps, a, b, c,
+                         eps, compute, ws.data_ptr(), ws.numel(), _stream(stream))
+
+
+def orthogonalize_grouped(ins, outs, sumsqs=None, steps: int = 5, coeffs=QUINTIC, eps: float = EPS,
+                          compute: int = L.MUON_BF16, ws: torch.Tensor | None = None, stream=None,
+                          device=None) -> None:
+    bi = [batch(x) for x in ins]
+    bo = [batch(x) for x in outs]
+    if ws is None:
+        need = L.muon_orthogonalize_grouped_workspace([b.count for b in bi], [b.rows for b in bi],
+                                                      [b.cols for b in bi], compute)
+        ws = workspace(need, device)
+    a, b, c = coeffs
+    sp = None if sumsqs is None else [s.data_ptr() if s is not None else 0 for s in sumsqs]
+    L.muon_orthogonalize_grouped([x.desc for x in bi], sp, [x.desc for x in bo], steps, a, b, c, eps, compute,
+                                 ws.data_ptr(), ws.numel(), _stream(stream))
+
+
+def apply(weight, ortho, lr: float, weight_decay: float, mode: int = L.MUON_SCALE_MATCH_RMS,
+          coeff: float = 0.2, stream=None) -> None:
+    w, o = batch(weight), batch(ortho)
+    L.muon_apply(w.desc, o.desc, lr, weight_decay, mode, coeff, _stream(stream))
+
+
+class MuonStep:
+    """One Muon optimizer step over several same-shape groups of weights.
+
+    ``groups`` is a list of ``(weights, grads)`` pairs, each element anything
+    ``batch()`` accepts (a 2-D or 3-D tensor or a list of 2-D tensors).  The
+    fp32 momentum, the Newton-Schulz input/output buffers, the sums of
+    squares and the workspaces are allocated once here; ``step()`` only
+    enqueues the library's kernels on the current stream.
+    """
+
+    def __init__(self, groups, *, compute: int = L.MUON_BF16, beta: float = 0.95, nesterov: bool = True,
+                 steps: int = 5, coeffs=QUINTIC, eps: float = EPS, lr: float = 3e-4,
+                 weight_decay: float = 0.1, mode: int = L.MUON_SCALE_MATCH_RMS, coeff: float = 0.2):
+        if not groups:
+            raise ValueError("no parameter groups")
+        self.compute, self.beta, self.nesterov = compute, beta, nesterov
+        self.steps, self.coeffs, self.eps = steps, coeffs, eps
+        self.lr, self.weight_decay, self.mode, self.coeff = lr, weight_decay, mode, coeff
+        self.w, self.g, self.m, self.n, self.o, self.ss, self.mws = [], [], [], [], [], [], []
+        dev = None
+        nbuf_dtype = torch.bfloat16 if compute == L.MUON_BF16 else torch.float32
+        for weights, grads in groups:
+            w, g = batch(weights), batch(grads)
+            if (w.count, w.rows, w.cols) != (g.count, g.rows, g.cols):
+                raise ValueError("weights and gradients differ in shape")
+            dev = w.keep[-1].device
+            shape = (w.count, w.rows, w.cols)
+            self.w.append(w)
+            self.g.append(g)
+            self.m.append(batch(torch.zeros(shape, dtype=torch.float32, device=dev)))
+            self.n.append(batch(torch.empty(shape, dtype=nbuf_dtype, device=dev)))
+            self.o.append(batch(torch.empty(shape, dtype=w.keep[-1].dtype, device=dev)))
+            self.ss.append(torch.empty(w.count, dtype=torch.float32, device=dev))
+            self.mws.append(workspace(L.muon_momentum_workspace(*shape), dev))
+        self.device = dev
+        # groups are orthogonalized together, at most 8 per grouped launch
+        self.chunks = [list(range(i, min(i + 8, len(self.w)))) for i in range(0, len(self.w), 8)]
+        self.ows = []
+        for ch in self.chunks:
+            need = L.muon_orthogonalize_grouped_workspace([self.n[i].count for i in ch], [self.n[i].rows for i in ch],
+                                                          [self.n[i].cols for i in ch], compute)
+            self.ows.append(workspace(need, dev))
+
+    @property
+    def momentum_buffers(self):
+        return [m.keep[0] for m in self.m]
+
+    @property
+    def ortho_buffers(self):
+        return [o.keep[0] for o in self.o]
+
+    @property
+    def sumsq_buffers(self):
+        return self.ss
+
+    def step(self, stream=None, events=None) -> None:
+        """Enqueue one step.  ``events``, if given, is four torch.cuda.Event
+        objects recorded before momentum, before orthogonalization, before
+        apply and after apply (phase timing on the same stream)."""
+        st = stream if stream is not None else torch.cuda.current_stream()
+        s = _stream(st)
+        if events is not None:
+            events[0].record(st)
+        for g, m, n, ss, ws in zip(self.g, self.m, self.n, self.ss, self.mws):
+            L.muon_momentum(g.desc, m.desc, n.desc, ss.data_ptr(), self.beta, self.nesterov, ws.data_ptr(),
+                            ws.numel(), s)
+        if events is not None:
+            events[1].record(st)
+        a, b, c = self.coeffs
+        for ch, ws in zip(self.chunks, self.ows):
+            L.muon_orthogonalize_grouped([self.n[i].desc for i in ch], [self.ss[i].data_ptr() for i in ch],
+                                         [self.o[i].desc for i in ch], self.steps, a, b, c, self.eps,
+                                         self.compute, ws.data_ptr(), ws.numel(), s)
+        if events is not None:
+            events[2].record(st)
+        for w, o in zip(self.w, self.o):
+            L.muon_apply(w.desc, o.desc, self.lr, self.weight_decay, self.mode, self.coeff, s)
+        if events is not None:
+            events[3].record(st)

@@ -1,0 +1,134 @@
+"""CPU checks of the C-ABI library: it loads, exports every entry point that
+include/muon355.h declares, and rejects invalid arguments with the documented
+status before anything is launched (no GPU is touched here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from matrix_aware_optimizer_step_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon355.h")
+FAKE = 0x10000  # non-NULL, 16-byte aligned; never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = L.load()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), f"{name} declared in muon355.h but not exported"
+    assert set(declared) == set(L.EXPORTED)
+    assert lib.muon_abi_version() == 1
+
+
+def test_status_strings():
+    lib = L.load()
+    for code, name in L.STATUS.items():
+        assert lib.muon_status_string(code).decode() == name
+
+
+def desc(count=1, rows=64, cols=64, ld=None, dtype=L.MUON_F32, base=FAKE, stride=None, reserved=0):
+    ld = cols if ld is None else ld
+    stride = rows * ld if stride is None else stride
+    return L.MuonBatch(None, base, stride, count, rows, cols, ld, dtype, reserved)
+
+
+def status_of(fn):
+    with pytest.raises(L.MuonError) as e:
+        fn()
+    return e.value.status
+
+
+INVALID, UNSUPPORTED, WORKSPACE = 1, 2, 3
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(count=0), INVALID), (dict(rows=0), INVALID), (dict(cols=0), INVALID),
+    (dict(ld=32), INVALID), (dict(dtype=7), INVALID), (dict(base=None), INVALID),
+    (dict(reserved=1), INVALID), (dict(count=2, stride=10), INVALID),
+    (dict(rows=65536, cols=65536), UNSUPPORTED), (dict(count=70000), INVALID),
+])
+def test_momentum_rejects_bad_descriptors(bad, code):
+    g = desc(**bad)
+    m = desc(**{k: v for k, v in bad.items() if k != "dtype"})
+    assert status_of(lambda: L.muon_momentum(g, m, desc(), FAKE, 0.95, True, FAKE, 1 << 20, 0)) == code
+
+
+def test_momentum_rejects_bad_hyperparameters_and_workspace():
+    g, m, n = desc(), desc(), desc()
+    call = lambda **kw: L.muon_momentum(kw.get("g", g), kw.get("m", m), kw.get("n", n), kw.get("ss", FAKE),
+                                        kw.get("beta", 0.95), kw.get("nest", True), kw.get("ws", FAKE),
+                                        kw.get("wsb", 1 << 20), 0)
+    assert status_of(lambda: call(beta=1.0)) == INVALID
+    assert status_of(lambda: call(beta=-0.1)) == INVALID
+    assert status_of(lambda: call(beta=float("nan"))) == INVALID
+    assert status_of(lambda: call(ss=None)) == INVALID
+    assert status_of(lambda: call(n=None)) == INVALID          # Nesterov needs an output
+    assert status_of(lambda: call(ws=None)) == WORKSPACE
+    assert status_of(lambda: call(wsb=4)) == WORKSPACE
+    assert status_of(lambda: call(m=desc(dtype=L.MUON_BF16))) == UNSUPPORTED  # momentum is fp32
+    assert status_of(lambda: call(n=desc(rows=32))) == INVALID   # shape mismatch
+    assert "beta" in L.load().muon_last_error().decode() or True
+
+
+def test_orthogonalize_rejects_bad_arguments():
+    i, o = desc(), desc()
+    need = L.muon_orthogonalize_workspace(1, 64, 64, L.MUON_BF16)
+    assert need > 0
+    call = lambda **kw: L.muon_orthogonalize(kw.get("i", i), None, kw.get("o", o), kw.get("steps", 5),
+                                             kw.get("a", 3.4445), -4.775, 2.0315, kw.get("eps", 1e-7),
+                                             kw.get("compute", L.MUON_BF16), kw.get("ws", FAKE),
+                                             kw.get("wsb", need), 0)
+    assert status_of(lambda: call(steps=-1)) == INVALID
+    assert status_of(lambda: call(a=float("inf"))) == INVALID
+    assert status_of(lambda: call(eps=-1.0)) == INVALID
+    assert status_of(lambda: call(eps=float("nan"))) == INVALID
+    assert status_of(lambda: call(compute=3)) == INVALID
+    assert status_of(lambda: call(o=desc(cols=32))) == INVALID
+    assert status_of(lambda: call(wsb=need - 1)) == WORKSPACE
+    assert status_of(lambda: call(ws=None)) == WORKSPACE
+    assert status_of(lambda: call(ws=FAKE + 4)) == WORKSPACE
+
+
+def test_grouped_rejects_bad_group_counts():
+    ins = [desc()] * 9
+    need = 1 << 30
+    with pytest.raises(L.MuonError) as e:
+        L.muon_orthogonalize_grouped(ins, None, ins, 5, 1.0, 0.0, 0.0, 1e-7, L.MUON_BF16, FAKE, need, 0)
+    assert e.value.status == INVALID
+    assert L.muon_orthogonalize_grouped_workspace([1] * 9, [4] * 9, [4] * 9, 1) == 0
+
+
+def test_apply_rejects_bad_arguments():
+    w, o = desc(), desc()
+    call = lambda **kw: L.muon_apply(kw.get("w", w), kw.get("o", o), kw.get("lr", 1e-3), kw.get("wd", 0.1),
+                                     kw.get("mode", 0), kw.get("coeff", 0.2), 0)
+    assert status_of(lambda: call(lr=float("nan"))) == INVALID
+    assert status_of(lambda: call(wd=float("inf"))) == INVALID
+    assert status_of(lambda: call(mode=9)) == INVALID
+    assert status_of(lambda: call(o=desc(rows=3))) == INVALID
+
+
+def test_workspace_queries():
+    assert L.muon_momentum_workspace(0, 4, 4) == 0
+    assert L.muon_momentum_workspace(2, 4096, 14336) >= 2 * (4096 * 14336 // 8192) * 4
+    # bf16 compute needs the fp32 copy of X on top of the bf16 buffers
+    b = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_BF16)
+    f = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_F32)
+    mn = 4096 * 14336
+    assert b >= mn * (4 + 4 * 2) and f >= mn * 4 * 4
+    # tall and wide of one shape pad to the same Newton-Schulz problem
+    assert L.muon_orthogonalize_workspace(3, 700, 300, 1) == L.muon_orthogonalize_workspace(3, 300, 700, 1)
+    g = L.muon_orthogonalize_grouped_workspace([2, 1], [4096, 1024], [4096, 4096], L.MUON_BF16)
+    assert g >= L.muon_orthogonalize_workspace(2, 4096, 4096, 1) + L.muon_orthogonalize_workspace(1, 1024, 4096, 1) - 4096
+    assert L.muon_orthogonalize_workspace(1, 65536, 65536, 1) == 0

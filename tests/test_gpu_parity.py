@@ -1,0 +1,289 @@
+"""GPU parity of libmuon355 against the fp64 oracle, called through the C ABI.
+
+Tolerances (written here, derived in the design notes):
+* momentum, sum of squares and apply, fp32: relative error <= 1e-6;
+* bf16 outputs of those kernels: within one bf16 rounding of the oracle;
+* Newton-Schulz, fp32 path: relative Frobenius error <= 1e-5;
+* Newton-Schulz, bf16 MFMA path: relative Frobenius error <= 3e-2.
+Sizes span several tiles and ragged tails while the oracle stays fast.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL_EW = 1e-6
+TOL_F32 = 1e-5
+TOL_BF16 = 3e-2
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import matrix_aware_optimizer_step_amd as m
+    m._lib.load()  # raises when the library is missing: there is no fallback
+    return m
+
+
+def f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def bf16_of(x: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def bf16_ulp(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (8 significant bits)."""
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def within_one_bf16_rounding(got: np.ndarray, exact: np.ndarray) -> bool:
+    """A bf16 result computed in fp32 and rounded once differs from the exact
+    value rounded to bf16 by at most one bf16 step, plus the fp32 error of the
+    computation before rounding (bounded normwise by 1e-6 of the largest
+    entry: entries that nearly cancel carry it in full)."""
+    tol = bf16_ulp(exact) + TOL_EW * np.max(np.abs(exact))
+    return bool(np.all(np.abs(got - bf16_of(exact)) <= tol))
+
+
+def rel(got, want):
+    return O.relative_frobenius_error(got, want)
+
+
+def randn(shape, seed, dtype, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return (scale * torch.randn(*shape, generator=g, dtype=torch.float32)).to(dtype).cuda()
+
+
+# ------------------------------------------------------------------ momentum
+
+MOM_CASES = [
+    ((1, 256, 128), torch.float32),   # the single fp32 gradient
+    ((3, 100, 72), torch.bfloat16),   # ragged rows, vector path
+    ((2, 33, 50), torch.float32),     # cols not a multiple of 8: scalar path
+    ((1, 8191, 8), torch.bfloat16),   # many rows, one block boundary
+]
+
+
+@pytest.mark.parametrize("shape,gdtype", MOM_CASES)
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_momentum_three_steps(mx, shape, gdtype, nesterov):
+    beta = 0.95
+    M = torch.zeros(shape, dtype=torch.float32, device="cuda")
+    N = torch.empty(shape, dtype=gdtype, device="cuda")
+    ss = torch.empty(shape[0], dtype=torch.float32, device="cuda")
+    Mo = [np.zeros(shape[1:]) for _ in range(shape[0])]
+    for t in range(1, 4):
+        G = randn(shape, 100 + t, gdtype, 3.0)
+        mx.momentum(G, M, N, ss, beta, nesterov)
+        torch.cuda.synchronize()
+        for i in range(shape[0]):
+            Mo[i], No = O.momentum(Mo[i], f64(G[i]), beta, nesterov)
+            assert rel(f64(M[i]), Mo[i]) <= TOL_EW
+            assert np.max(np.abs(f64(M[i]) - Mo[i])) <= TOL_EW * np.max(np.abs(Mo[i]))
+            if gdtype == torch.float32:
+                assert rel(f64(N[i]), No) <= TOL_EW
+            else:
+                assert within_one_bf16_rounding(f64(N[i]), No)
+            want = O.frobenius_sumsq(No)
+            assert abs(float(ss[i]) - want) <= TOL_EW * want
+
+
+def test_momentum_row_blocks_and_pointer_arrays(mx):
+    """ld > cols (row blocks of a wider matrix) and a pointer-array batch."""
+    big = randn((3, 64, 160), 7, torch.bfloat16)
+    G = big[:, :, 16:144]                       # ld 160, cols 128
+    M = torch.zeros(3, 64, 128, device="cuda")
+    Nl = [torch.empty(64, 128, dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    ss = torch.empty(3, device="cuda")
+    mx.momentum(G, M, Nl, ss, 0.9, True)
+    torch.cuda.synchronize()
+    for i in range(3):
+        Mo, No = O.momentum(np.zeros((64, 128)), f64(G[i]), 0.9, True)
+        assert rel(f64(M[i]), Mo) <= TOL_EW
+        assert within_one_bf16_rounding(f64(Nl[i]), No)
+
+
+def test_momentum_nonfinite_propagates(mx):
+    G = randn((1, 64, 64), 3, torch.float32)
+    G[0, 5, 7] = float("nan")
+    M = torch.zeros(1, 64, 64, device="cuda")
+    N = torch.empty(1, 64, 64, device="cuda")
+    ss = torch.empty(1, device="cuda")
+    mx.momentum(G, M, N, ss, 0.95, True)
+    torch.cuda.synchronize()
+    assert not math.isfinite(float(ss[0]))
+
+
+# --------------------------------------------------------------------- apply
+
+@pytest.mark.parametrize("mode", [mx_mode for mx_mode in (0, 1, 2)])
+@pytest.mark.parametrize("wdtype,shape", [(torch.float32, (2, 96, 200)), (torch.bfloat16, (1, 300, 64)),
+                                          (torch.float32, (1, 37, 51))])
+def test_apply(mx, mode, wdtype, shape):
+    lr, wd = 1.0, 0.5  # the update term dominates, so a mistake in it cannot hide
+    W = randn(shape, 11, wdtype, 0.02)
+    Od = randn(shape, 12, wdtype, 0.05)
+    W0 = f64(W)
+    mx.apply(W, Od, lr, wd, mode, 0.2)
+    torch.cuda.synchronize()
+    for i in range(shape[0]):
+        want = O.apply_update(W0[i], f64(Od[i]), lr, wd, mode, 0.2)
+        if wdtype == torch.float32:
+            assert rel(f64(W[i]), want) <= TOL_EW
+        else:
+            assert within_one_bf16_rounding(f64(W[i]), want)
+
+
+# ------------------------------------------------------------ Newton-Schulz
+
+def run_ns(mx, N, compute, steps=5, coeffs=O.QUINTIC, out_dtype=None, eps=O.EPS):
+    out = torch.empty(N.shape, dtype=out_dtype or N.dtype, device="cuda")
+    mx.orthogonalize(N, out, None, steps, coeffs, eps, compute, device="cuda")
+    torch.cuda.synchronize()
+    return out
+
+
+NS_F32_SHAPES = [(256, 128), (128, 256), (200, 333), (333, 200), (300, 300), (1, 64), (64, 1),
+                 (700, 520), (129, 900), (40, 2000)]
+
+
+@pytest.mark.parametrize("shape", NS_F32_SHAPES)
+def test_ns_f32(mx, shape):
+    N = randn((1,) + shape, sum(shape), torch.float32)
+    out = run_ns(mx, N, mx.MUON_F32)
+    want = O.newton_schulz(f64(N[0]), 5)
+    assert rel(f64(out[0]), want) <= TOL_F32
+
+
+NS_BF16_SHAPES = [(256, 128), (512, 1024), (1024, 512), (384, 1000), (130, 2000), (1000, 130), (300, 300),
+                  (768, 2048)]
+
+
+@pytest.mark.parametrize("shape", NS_BF16_SHAPES)
+def test_ns_bf16(mx, shape):
+    G = synth.rank1_sum(*shape, seed=shape[0] * 7 + shape[1], inner=512)
+    N = G.to(torch.bfloat16).unsqueeze(0).cuda()
+    out = run_ns(mx, N, mx.MUON_BF16)
+    want = O.newton_schulz(f64(N[0]), 5)
+    assert rel(f64(out[0]), want) <= TOL_BF16
+
+
+@pytest.mark.parametrize("compute,tol", [(0, TOL_F32), (1, TOL_BF16)])
+@pytest.mark.parametrize("coeffs", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (0.5, -0.25, 0.125)])
+@pytest.mark.parametrize("shape", [(300, 700), (700, 300), (96, 520)])
+def test_ns_single_stage(mx, compute, tol, coeffs, shape):
+    """One step with coefficients that isolate the identity, the Gram-times-X
+    and the polynomial term, so each GEMM stage is checked on its own."""
+    dt = torch.float32 if compute == 0 else torch.bfloat16
+    N = randn((1,) + shape, 5, dt)
+    out = run_ns(mx, N, compute, steps=1, coeffs=coeffs, out_dtype=torch.float32)
+    want = O.newton_schulz(f64(N[0]), 1, coeffs)
+    assert rel(f64(out[0]), want) <= tol
+
+
+@pytest.mark.parametrize("compute", [0, 1])
+def test_ns_zero_steps_is_normalized_input(mx, compute):
+    N = randn((2, 70, 90), 9, torch.float32)
+    out = run_ns(mx, N, compute, steps=0)
+    for i in range(2):
+        assert rel(f64(out[i]), O.newton_schulz(f64(N[i]), 0)) <= 1e-6
+
+
+@pytest.mark.parametrize("compute", [0, 1])
+def test_ns_zero_input_gives_zero(mx, compute):
+    N = torch.zeros(1, 64, 96, device="cuda")
+    out = run_ns(mx, N, compute)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_ns_orthogonal_input(mx):
+    q, _ = torch.linalg.qr(torch.randn(512, 128, generator=torch.Generator().manual_seed(4), dtype=torch.float64))
+    Q = q.T.contiguous()  # 128 x 512, orthonormal rows
+    out = run_ns(mx, Q.float().unsqueeze(0).cuda(), mx.MUON_F32)
+    c = 1.0 / (math.sqrt(128) + O.EPS)
+    for _ in range(5):
+        c = 3.4445 * c - 4.7750 * c ** 3 + 2.0315 * c ** 5
+    assert rel(f64(out[0]), c * Q.numpy()) <= TOL_F32
+
+
+def test_ns_transpose_equivariance(mx):
+    N = randn((1, 200, 500), 21, torch.float32)
+    a = run_ns(mx, N, mx.MUON_F32)
+    b = run_ns(mx, N.transpose(1, 2).contiguous(), mx.MUON_F32)
+    # the two orientations sum the squares in different orders
+    assert rel(f64(b[0]).T, f64(a[0])) <= TOL_F32
+
+
+def test_ns_batched_strided_and_pointer_array(mx):
+    """A strided batch (per-head row blocks, ld = 4 x cols) and the same
+    matrices as a pointer array give the oracle's answer."""
+    big = randn((1, 512, 256), 31, torch.bfloat16)[0]
+    heads = big.view(4, 128, 256)                     # contiguous row blocks
+    out = torch.empty(4, 128, 256, dtype=torch.bfloat16, device="cuda")
+    mx.orthogonalize(heads, out, None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    outl = [torch.empty(128, 256, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+    mx.orthogonalize([heads[i] for i in range(4)], outl, None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(4):
+        want = O.newton_schulz(f64(heads[i]), 5)
+        assert rel(f64(out[i]), want) <= TOL_BF16
+        assert torch.equal(out[i], outl[i])
+
+
+def test_grouped_equals_separate_calls(mx):
+    shapes = [(2, 300, 700), (3, 128, 640), (1, 900, 256)]
+    Ns = [randn(s, 40 + k, torch.bfloat16) for k, s in enumerate(shapes)]
+    sep = [run_ns(mx, N, mx.MUON_BF16) for N in Ns]
+    outs = [torch.empty_like(N) for N in Ns]
+    mx.orthogonalize_grouped(Ns, outs, None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    for a, b in zip(sep, outs):
+        assert torch.equal(a, b)
+
+
+# --------------------------------------------------------------- full steps
+
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_single_fp32_gradient_three_steps(mx, nesterov):
+    """The 256x128 fp32 configuration, three seeded gradients, whole step."""
+    cfg = synth.CONFIGS[1]
+    lr, wd = 1.0, 0.5
+    W = (0.02 * torch.randn(1, 256, 128, generator=torch.Generator().manual_seed(5))).cuda()
+    Wo, Mo = f64(W[0]), np.zeros((256, 128))
+    grads = [synth.group_gradients(cfg, step=t)[0].cuda() for t in (1, 2, 3)]
+    G = torch.empty_like(grads[0])
+    step = mx.MuonStep([(W, G)], compute=mx.MUON_F32, nesterov=nesterov, lr=lr, weight_decay=wd)
+    for t in range(3):
+        G.copy_(grads[t])
+        step.step()
+        torch.cuda.synchronize()
+        Wo, Mo, Oo, sso = O.muon_step(Wo, Mo, f64(grads[t][0]), nesterov=nesterov, lr=lr, weight_decay=wd)
+        assert rel(f64(step.momentum_buffers[0][0]), Mo) <= TOL_EW
+        assert abs(float(step.sumsq_buffers[0][0]) - sso) <= TOL_EW * sso
+        assert rel(f64(step.ortho_buffers[0][0]), Oo) <= TOL_F32
+        assert rel(f64(W[0]), Wo) <= TOL_F32
+
+
+def test_zero_gradient_step_is_pure_decay(mx):
+    W = randn((2, 128, 192), 8, torch.float32, 0.02)
+    W0 = W.clone()
+    G = torch.zeros_like(W)
+    step = mx.MuonStep([(W, G)], compute=mx.MUON_BF16, lr=0.01, weight_decay=0.5)
+    for _ in range(3):
+        step.step()
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(step.ortho_buffers[0]).item() == 0
+    want = f64(W0) * (1 - 0.01 * 0.5) ** 3
+    assert rel(f64(W), want) <= TOL_EW

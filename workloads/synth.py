@@ -1,0 +1,177 @@
+"""Seeded synthetic gradients shaped like the pages' workloads.
+
+This module only draws random numbers; it holds none of the Muon step's
+arithmetic.  The GPU tests, the benchmark and the oracle's callers all take
+their inputs from here, so both sides of every parity check see the same
+bits.
+
+Seed rule: matrix ``i`` (counted across the whole configuration, in group
+order) at optimizer step ``t`` (1-based) uses seed ``c*10**6 + i*10 + t``
+for configuration ``c``.
+
+Configurations (the model shapes the pages name: an 8B dense GPT and a
+Qwen3-30B-A3B-style MoE, "SOAP, Muon, and Beyond: Pushing LLM Pretraining
+Scales"; per-head orthogonalization, "Reading notes on SOAP, Muon and
+higher-order optimizers", section 1; MoE effective batch, same notes,
+section 3):
+
+1. one 256x128 fp32 gradient, entries N(0,1), three steps.
+2. one dense 8B-style layer in bf16: Wq, Wo 4096x4096; Wk, Wv 1024x4096;
+   gate, up 14336x4096; down 4096x14336.  G = D X^T with D (m x 4096) and
+   X (n x 4096) N(0,1): a sum of 4096 rank-1 outer products.
+3. all 32 layers of those shapes (224 matrices), G = U diag(1/k) V^T with
+   Haar-random U, V: a power-law spectrum.
+4. an MoE layer: 128 experts x (gate 768x2048, up 768x2048, down
+   2048x768), G_e = c_e * Z_e with Z_e N(0,1) and c_e the expert's token
+   count under top-8-of-128 routing of 65536 tokens with N(0,1) logits.
+5. per-head: the 96 row blocks (128x4096) of Wq, Wk, Wv of a 4096-wide,
+   32-head layer, plus gate, up (14336x4096) and down (4096x14336); every
+   matrix G = U diag(sigma) V^T with sigma geometric from 1 to 1e-4
+   (condition number 1e4).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+
+@dataclass(frozen=True)
+class Group:
+    name: str
+    count: int
+    rows: int
+    cols: int
+
+
+@dataclass(frozen=True)
+class Config:
+    index: int
+    name: str
+    groups: tuple
+    kind: str
+    dtype: torch.dtype
+
+    @property
+    def matrices(self) -> int:
+        return sum(g.count for g in self.groups)
+
+    @property
+    def elements(self) -> int:
+        return sum(g.count * g.rows * g.cols for g in self.groups)
+
+
+def _layer_groups(layers: int):
+    return (Group("wq_wo", 2 * layers, 4096, 4096), Group("wk_wv", 2 * layers, 1024, 4096),
+            Group("gate_up", 2 * layers, 14336, 4096), Group("down", layers, 4096, 14336))
+
+
+CONFIGS = {
+    1: Config(1, "single 256x128 fp32 gradient", (Group("g", 1, 256, 128),), "gauss", torch.float32),
+    2: Config(2, "one GPT-8B-style dense layer", _layer_groups(1), "rank1_sum", torch.bfloat16),
+    3: Config(3, "32 GPT-8B-style dense layers", _layer_groups(32), "power_law", torch.bfloat16),
+    4: Config(4, "30B-A3B-style MoE layer, 128 experts", (Group("gate_up", 256, 768, 2048),
+                                                        Group("down", 128, 2048, 768)), "moe", torch.bfloat16),
+    5: Config(5, "per-head QKV blocks + MLP, condition number 1e4",
+              (Group("qkv_heads", 96, 128, 4096), Group("gate_up", 2, 14336, 4096), Group("down", 1, 4096, 14336)),
+              "kappa", torch.bfloat16),
+}
+
+
+def seed_of(config: int, matrix: int, step: int) -> int:
+    return config * 10 ** 6 + matrix * 10 + step
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def gaussian(rows: int, cols: int, seed: int, device="cpu") -> torch.Tensor:
+    return torch.randn(rows, cols, generator=_gen(seed, device), device=device, dtype=torch.float32)
+
+
+def rank1_sum(rows: int, cols: int, seed: int, inner: int = 4096, device="cpu") -> torch.Tensor:
+    g = _gen(seed, device)
+    d = torch.randn(rows, inner, generator=g, device=device, dtype=torch.float32)
+    x = torch.randn(cols, inner, generator=g, device=device, dtype=torch.float32)
+    return d @ x.T
+
+
+def haar(n: int, k: int, gen: torch.Generator, device) -> torch.Tensor:
+    """n x k with orthonormal columns: QR of a Gaussian, signs fixed by R."""
+    z = torch.randn(n, k, generator=gen, device=device, dtype=torch.float32)
+    q, r = torch.linalg.qr(z)
+    return q * torch.sign(torch.diagonal(r)).unsqueeze(0)
+
+
+def with_spectrum(rows: int, cols: int, sigma: torch.Tensor, seed: int, device="cpu") -> torch.Tensor:
+    g = _gen(seed, device)
+    r = sigma.numel()
+    u = haar(rows, r, g, device)
+    v = haar(cols, r, g, device)
+    return (u * sigma.to(device=device, dtype=torch.float32).unsqueeze(0)) @ v.T
+
+
+def power_law(rows: int, cols: int, seed: int, device="cpu") -> torch.Tensor:
+    r = min(rows, cols)
+    return with_spectrum(rows, cols, 1.0 / torch.arange(1, r + 1, dtype=torch.float64), seed, device)
+
+
+def condition_number(rows: int, cols: int, seed: int, kappa: float = 1e4, device="cpu") -> torch.Tensor:
+    r = min(rows, cols)
+    sigma = torch.logspace(0.0, -torch.log10(torch.tensor(kappa)).item(), r, dtype=torch.float64)
+    return with_spectrum(rows, cols, sigma, seed, device)
+
+
+def moe_token_counts(seed: int, tokens: int = 65536, experts: int = 128, topk: int = 8, device="cpu") -> torch.Tensor:
+    g = _gen(seed, device)
+    logits = torch.randn(tokens, experts, generator=g, device=device, dtype=torch.float32)
+    top = torch.topk(logits, topk, dim=1).indices.flatten()
+    return torch.bincount(top, minlength=experts)
+
+
+def gradient(config: Config, matrix: int, rows: int, cols: int, step: int = 1, device="cpu",
+             expert_counts: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 gradient of matrix ``matrix`` of ``config`` at ``step``."""
+    seed = seed_of(config.index, matrix, step)
+    if config.kind == "gauss":
+        return gaussian(rows, cols, seed, device)
+    if config.kind == "rank1_sum":
+        return rank1_sum(rows, cols, seed, device=device)
+    if config.kind == "power_law":
+        return power_law(rows, cols, seed, device)
+    if config.kind == "kappa":
+        return condition_number(rows, cols, seed, device=device)
+    if config.kind == "moe":
+        if expert_counts is None:
+            expert_counts = moe_token_counts(seed_of(config.index, 0, 0), device=device)
+        expert = matrix % 128
+        return float(expert_counts[expert]) * gaussian(rows, cols, seed, device)
+    raise ValueError(config.kind)
+
+
+def group_gradients(config: Config, step: int = 1, device="cpu", dtype=None, groups=None):
+    """One tensor (count, rows, cols) per group, in the config's dtype."""
+    dtype = dtype or config.dtype
+    counts = moe_token_counts(seed_of(config.index, 0, 0), device=device) if config.kind == "moe" else None
+    out = []
+    i = 0
+    for gi, grp in enumerate(config.groups):
+        t = torch.empty(grp.count, grp.rows, grp.cols, dtype=dtype, device=device)
+        for k in range(grp.count):
+            if groups is None or gi in groups:
+                t[k] = gradient(config, i, grp.rows, grp.cols, step, device, counts).to(dtype)
+            i += 1
+        out.append(t)
+    return out
+
+
+def initial_weights(config: Config, device="cpu", dtype=None, std: float = 0.02, seed: int = 7):
+    """W_0 ~ N(0, std^2), one tensor (count, rows, cols) per group."""
+    dtype = dtype or config.dtype
+    g = _gen(config.index * 10 ** 6 + seed * 100003, device)
+    return [(std * torch.randn(grp.count, grp.rows, grp.cols, generator=g, device=device,
+                               dtype=torch.float32)).to(dtype) for grp in config.groups]
