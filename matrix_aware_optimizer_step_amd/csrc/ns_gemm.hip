@@ -49,6 +49,7 @@ struct Elem;
 template <>
 struct Elem<uint16_t> {  // bf16 storage
   static constexpr int kPerChunk = 8;
+  static constexpr int kMfmaPerChunk = 1;
   __device__ __forceinline__ static void mma(f32x16_t& acc, const Chunk& a, const Chunk& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
@@ -58,6 +59,15 @@ struct Elem<uint16_t> {  // bf16 storage
   }
   __device__ __forceinline__ static void store(char* p, float v) {
     *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(v);
+  }
+  // eight consecutive elements (16 bytes)
+  __device__ __forceinline__ static void store8(char* p, const float4& a, const float4& b) {
+    uint4 u;
+    u.x = static_cast<uint32_t>(f32_to_bf16(a.x)) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16);
+    u.y = static_cast<uint32_t>(f32_to_bf16(a.z)) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16);
+    u.z = static_cast<uint32_t>(f32_to_bf16(b.x)) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16);
+    u.w = static_cast<uint32_t>(f32_to_bf16(b.z)) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16);
+    *reinterpret_cast<uint4*>(p) = u;
   }
   // four consecutive elements
   __device__ __forceinline__ static void store4(char* p, float v0, float v1, float v2, float v3) {
@@ -71,6 +81,7 @@ struct Elem<uint16_t> {  // bf16 storage
 template <>
 struct Elem<float> {
   static constexpr int kPerChunk = 4;
+  static constexpr int kMfmaPerChunk = 4;
   // Bit-cast the whole chunk, then index it: bit-casting a single component
   // of an ext_vector (v.y) is miscompiled to read component x.
   __device__ __forceinline__ static void mma(f32x16_t& acc, const Chunk& a, const Chunk& b) {
@@ -88,6 +99,10 @@ struct Elem<float> {
   __device__ __forceinline__ static void store4(char* p, float v0, float v1, float v2, float v3) {
     *reinterpret_cast<float4*>(p) = make_float4(v0, v1, v2, v3);
   }
+  __device__ __forceinline__ static void store8(char* p, const float4& a, const float4& b) {
+    reinterpret_cast<float4*>(p)[0] = a;
+    reinterpret_cast<float4*>(p)[1] = b;
+  }
 };
 
 __device__ __forceinline__ char* user_ptr(const MatBatch& m, int mat) {
@@ -103,28 +118,93 @@ __device__ __forceinline__ void store_user(const MatBatch& u, char* base, int64_
   }
 }
 
-constexpr int kRowBytes = 128;  // one k-tile row in LDS: 8 chunks of 16 bytes
+// Physical 16-byte slot of logical chunk c in an LDS row of RC chunks.  A
+// ds_read_b128 from 16 consecutive rows at one logical chunk is one cycle of
+// the 64-bank (256-byte) gfx950 LDS when the 16 slots are distinct modulo
+// 256 bytes: rows sharing a 256-byte phase (row mod 16/RC) get different
+// chunks.  SWZ = 0 is the 32-bank pattern (8 consecutive rows distinct).
+template <int SWZ, int RC>
+__device__ __forceinline__ int swizzle(int row, int c) {
+  constexpr int kPhase = 16 / RC;  // rows per 256 bytes
+  return SWZ ? (c ^ ((row / kPhase) & (RC - 1))) : (c ^ (row & (RC - 1)));
+}
+
+__device__ __forceinline__ void lds_dma16(const char* g, char* l) {
+  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
+                                   (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14,
+  // expcnt (7) in bits 6:4 and lgkmcnt (15) in bits 11:8 left unconstrained.
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Workgroup barrier that keeps later-issued DMA loads in flight: wait for
+// this wave's LDS reads (lgkmcnt 0) and for all but the newest N vector
+// loads, then s_barrier.  (__syncthreads() would wait for every load.)
+template <int N>
+__device__ __forceinline__ void barrier_keep_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+  __builtin_amdgcn_s_barrier();
+}
 
 // BM x BM output tile per workgroup; WGM x WGN waves, each owning a
 // (BM/WGM) x (BM/WGN) sub-tile of 32x32 MFMA blocks.
-template <typename T, int BM, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(64 * WGM * WGN)
+//   RC:     16-byte chunks per LDS row (k-tile = RC*16 bytes of k).
+//   STAGES: LDS ring depth; k-tile t+STAGES-1 is in flight while t is used.
+//   SWZ:    LDS swizzle (see swizzle()).
+//   DMA:    1 = operand tiles go global -> LDS with global_load_lds_dwordx4
+//           (no staging registers); 0 = through VGPRs (two stages only).
+//   XCD:    1 = renumber workgroups so each of the 8 XCDs (which receive
+//           workgroup ids round-robin) works on a contiguous tile range.
+//   SCHED:  0 = compiler schedule; 1 = pin the order of MFMAs and the next
+//           substep's LDS reads.
+//   GM:     tiles of a non-symmetric product are numbered in groups of GM
+//           tile rows, column by column inside a group, so that workgroups
+//           running together (one XCD's range under XCD = 1) share GM row
+//           blocks of P and a few column blocks of Q in L2.
+template <typename T, int BM, int WGM, int WGN, int EPI, int RC = 4, int STAGES = 4, int SWZ = 1, int DMA = 1,
+          int XCD = 0, int SCHED = 0, int GM = 1, int BN = BM>
+__global__ __launch_bounds__(64 * WGM * WGN, 2)  // at least two waves per SIMD
 void ns_gemm_kernel(const GemmLaunch L) {
-  constexpr int NT = 64 * WGM * WGN;     // threads
+  constexpr int NW = WGM * WGN;          // waves
+  constexpr int NT = 64 * NW;            // threads
   constexpr int WTM = BM / WGM;          // wave sub-tile rows
-  constexpr int WTN = BM / WGN;          // wave sub-tile cols
+  constexpr int WTN = BN / WGN;          // wave sub-tile cols
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
   constexpr int CH = Elem<T>::kPerChunk;  // elements per 16-byte chunk
-  constexpr int BK = 8 * CH;             // elements per k-tile
-  constexpr int RPP = NT / 8;            // tile rows loaded per pass
-  constexpr int LOADS = BM / RPP;        // chunks per thread per operand
-  constexpr int OPB = BM * kRowBytes;    // bytes of one operand tile
-  static_assert(LOADS * RPP == BM, "tile rows must split evenly over the threads");
-  __shared__ __attribute__((aligned(16))) char smem[2 * 2 * OPB];
+  constexpr int ROWB = RC * 16;          // bytes per LDS row
+  constexpr int BK = RC * CH;            // elements per k-tile
+  constexpr int SUB = RC / 2;            // MFMA substeps per k-tile (2 chunks each)
+  constexpr int RPP = NT / RC;           // tile rows per register-path pass
+  constexpr int LOADS = BM / RPP;        // P chunks per thread (register path)
+  constexpr int LOADSQ = BN / RPP;       // Q chunks per thread (register path)
+  constexpr int RPI = 64 / RC;           // rows per DMA instruction (64 lanes x 16 bytes)
+  constexpr int IPW = BM / (RPI * NW);   // P DMA instructions per wave
+  constexpr int IPWQ = BN / (RPI * NW);  // Q DMA instructions per wave
+  constexpr int OPB = BM * ROWB;         // bytes of the P tile (the Q tile follows)
+  constexpr int STB = (BM + BN) * ROWB;  // bytes of one stage
+  static_assert(DMA || STAGES == 2, "the register path is double-buffered");
+  static_assert(LOADS * RPP == BM && LOADSQ * RPP == BN, "tile rows must split evenly over the threads");
+  static_assert(IPW * RPI * NW == BM && IPWQ * RPI * NW == BN, "tile rows must split evenly over the waves");
+  constexpr int EPI_BYTES = NW * 64 * 68 * 4;  // transposed-store staging
+  constexpr int SMEM = STAGES * STB > EPI_BYTES ? STAGES * STB : EPI_BYTES;
+  static_assert(SMEM <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   // ---- which tile of which matrix of which group
-  const int t = blockIdx.x;
+  int t = blockIdx.x;
+  if (XCD) {
+    const int n = L.total_tiles;
+    const int per = n >> 3, rem = n & 7;
+    const int x = t & 7;
+    t = x * per + (x < rem ? x : rem) + (t >> 3);
+  }
   int gi = 0;
   while (gi + 1 < L.ngroups && t >= L.g[gi + 1].tile_begin) ++gi;
   const GemmGroup& G = L.g[gi];
@@ -132,16 +212,26 @@ void ns_gemm_kernel(const GemmLaunch L) {
   const int mat = lt / G.tiles_per_mat;
   int tt = lt - mat * G.tiles_per_mat;
   int ti, tj;
+  constexpr int R = BM / BN;  // column tiles per row tile
+  static_assert(R * BN == BM, "BN must divide BM");
   if (G.sym) {
+    // upper tiles only: row tile ti keeps column tiles tj >= R*ti
     ti = 0;
-    while (tt >= G.tiles_n - ti) {
-      tt -= G.tiles_n - ti;
+    while (tt >= G.tiles_n - R * ti) {
+      tt -= G.tiles_n - R * ti;
       ++ti;
     }
-    tj = ti + tt;
-  } else {
+    tj = R * ti + tt;
+  } else if (GM == 1) {
     ti = tt / G.tiles_n;
     tj = tt - ti * G.tiles_n;
+  } else {
+    const int span = GM * G.tiles_n;          // tiles in one full group of GM rows
+    const int grp = tt / span;
+    const int in = tt - grp * span;
+    const int rows = min(GM, G.tiles_m - grp * GM);  // the last group may be shorter
+    tj = in / rows;
+    ti = grp * GM + (in - tj * rows);
   }
 
   const int tid = threadIdx.x;
@@ -152,33 +242,87 @@ void ns_gemm_kernel(const GemmLaunch L) {
 
   const int ldp = G.ldp;
   const int ldq = G.ldq;
-  const int lrow = tid >> 3;  // 0..RPP-1
-  const int lch = tid & 7;    // chunk within the row
-  const char* Pl = G.P + mat * G.p_mat +
-                   (static_cast<int64_t>(ti * BM + lrow) * ldp + lch * CH) * sizeof(T);
-  const char* Ql = G.Q + mat * G.q_mat +
-                   (static_cast<int64_t>(tj * BM + lrow) * ldq + lch * CH) * sizeof(T);
-  const int64_t pstep = static_cast<int64_t>(RPP) * ldp * sizeof(T);
-  const int64_t qstep = static_cast<int64_t>(RPP) * ldq * sizeof(T);
-  int soff[LOADS];
+  const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T);
+  const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * ldq * sizeof(T);
+  const int nk = G.K / BK;
+
+  // ---- operand staging
+  uint32_t dofs_p[DMA ? IPW : 1], dofs_q[DMA ? IPWQ : 1];  // DMA: lane byte offsets within the tile
+  int soff[DMA ? 1 : LOADS];                               // register path: LDS slot offsets
+  Chunk pr[DMA ? 1 : LOADS], qr[DMA ? 1 : LOADSQ];
+  const char* Pl = nullptr;
+  const char* Ql = nullptr;
+  int64_t pstep = 0, qstep = 0;
+  if constexpr (DMA) {
 #pragma unroll
-  for (int r = 0; r < LOADS; ++r) {
-    const int row = lrow + RPP * r;
-    soff[r] = row * kRowBytes + ((lch ^ (row & 7)) << 4);
+    for (int r = 0; r < IPW; ++r) {
+      const int row = (wave * IPW + r) * RPI + lane / RC;
+      const int c = swizzle<SWZ, RC>(row, lane % RC);
+      dofs_p[r] = static_cast<uint32_t>((row * ldp + c * CH) * static_cast<int>(sizeof(T)));
+    }
+#pragma unroll
+    for (int r = 0; r < IPWQ; ++r) {
+      const int row = (wave * IPWQ + r) * RPI + lane / RC;
+      const int c = swizzle<SWZ, RC>(row, lane % RC);
+      dofs_q[r] = static_cast<uint32_t>((row * ldq + c * CH) * static_cast<int>(sizeof(T)));
+    }
+  } else {
+    const int lrow = tid / RC;
+    const int lch = tid % RC;
+    Pl = Pt + (static_cast<int64_t>(lrow) * ldp + lch * CH) * sizeof(T);
+    Ql = Qt + (static_cast<int64_t>(lrow) * ldq + lch * CH) * sizeof(T);
+    pstep = static_cast<int64_t>(RPP) * ldp * sizeof(T);
+    qstep = static_cast<int64_t>(RPP) * ldq * sizeof(T);
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int row = lrow + RPP * r;
+      soff[r] = row * ROWB + (swizzle<SWZ, RC>(row, lch) << 4);
+    }
   }
 
-  Chunk pr[LOADS], qr[LOADS];
+  // DMA: issue k-tile kt into LDS stage st (lands asynchronously; vmcnt).
+  auto dma_issue = [&](int kt, int st) {
+    const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
+    const char* pk = Pt + kb;
+    const char* qk = Qt + kb;
+    char* lp = smem + st * STB + wave * IPW * 1024;
+    char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
-  for (int r = 0; r < LOADS; ++r) {
-    pr[r] = *reinterpret_cast<const Chunk*>(Pl + r * pstep);
-    qr[r] = *reinterpret_cast<const Chunk*>(Ql + r * qstep);
-  }
+    for (int r = 0; r < IPW; ++r) lds_dma16(pk + dofs_p[r], lp + r * 1024);
 #pragma unroll
-  for (int r = 0; r < LOADS; ++r) {
-    *reinterpret_cast<Chunk*>(smem + soff[r]) = pr[r];
-    *reinterpret_cast<Chunk*>(smem + OPB + soff[r]) = qr[r];
+    for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
+  };
+  auto reg_load = [&](int kt) {
+    const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) pr[r] = *reinterpret_cast<const Chunk*>(Pl + kb + r * pstep);
+#pragma unroll
+    for (int r = 0; r < LOADSQ; ++r) qr[r] = *reinterpret_cast<const Chunk*>(Ql + kb + r * qstep);
+  };
+  auto reg_store = [&](int st) {
+    char* dp = smem + st * STB;
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) *reinterpret_cast<Chunk*>(dp + soff[r]) = pr[r];
+#pragma unroll
+    for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
+  };
+
+  constexpr int kPerTile = IPW + IPWQ;  // DMA instructions per wave per k-tile
+  static_assert(SUB % 2 == 0, "fragment double buffer assumes an even substep count");
+  if constexpr (DMA) {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) dma_issue(s, s);
+    if (nk >= STAGES - 1) {
+      barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile 0 has landed
+    } else {
+      barrier_keep_vm<0>();
+    }
+  } else {
+    reg_load(0);
+    reg_store(0);
+    __syncthreads();
   }
-  __syncthreads();
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -190,164 +334,265 @@ void ns_gemm_kernel(const GemmLaunch L) {
 
   const int frow = lane & 31;
   const int half = lane >> 5;
-  const int nk = G.K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int64_t kb = static_cast<int64_t>(kt + 1) * BK * sizeof(T);
+  int fa_off[FM], fb_off[FN], fa_row[FM], fb_row[FN];
 #pragma unroll
-      for (int r = 0; r < LOADS; ++r) {
-        pr[r] = *reinterpret_cast<const Chunk*>(Pl + kb + r * pstep);
-        qr[r] = *reinterpret_cast<const Chunk*>(Ql + kb + r * qstep);
-      }
-    }
-    const char* sp = smem + (kt & 1) * 2 * OPB;
-    const char* sq = sp + OPB;
+  for (int f = 0; f < FM; ++f) {
+    fa_row[f] = wm * WTM + f * 32 + frow;
+    fa_off[f] = fa_row[f] * ROWB;
+  }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int ch = 2 * s + half;
-      Chunk af[FM], bfr[FN];
-#pragma unroll
-      for (int f = 0; f < FM; ++f) {
-        const int ra = wm * WTM + f * 32 + frow;
-        af[f] = *reinterpret_cast<const Chunk*>(sp + ra * kRowBytes + ((ch ^ (ra & 7)) << 4));
-      }
-#pragma unroll
-      for (int f = 0; f < FN; ++f) {
-        const int rb = wn * WTN + f * 32 + frow;
-        bfr[f] = *reinterpret_cast<const Chunk*>(sq + rb * kRowBytes + ((ch ^ (rb & 7)) << 4));
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) Elem<T>::mma(acc[i][j], af[i], bfr[j]);
-    }
-    if (more) {
-      char* dp = smem + ((kt + 1) & 1) * 2 * OPB;
-#pragma unroll
-      for (int r = 0; r < LOADS; ++r) {
-        *reinterpret_cast<Chunk*>(dp + soff[r]) = pr[r];
-        *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
-      }
-    }
-    __syncthreads();
+  for (int f = 0; f < FN; ++f) {
+    fb_row[f] = wn * WTN + f * 32 + frow;
+    fb_off[f] = OPB + fb_row[f] * ROWB;
   }
 
+  // Main loop.  Fragments of substep s+1 are read while the MFMAs of
+  // substep s run; at the last substep of k-tile kt the wave waits for its
+  // own DMA of k-tile kt+1, joins the barrier, and reads k-tile kt+1's first
+  // fragments before issuing kt's last MFMAs, so the barrier and the LDS
+  // latency overlap matrix work.  The barrier also retires every read of
+  // k-tile kt's stage, which the DMA issued next iteration overwrites.
+  Chunk af[2][FM], bfr[2][FN];
+  auto frags = [&](const char* sb, int s, Chunk* a, Chunk* b) {
+    const int ch = 2 * s + half;
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+      a[f] = *reinterpret_cast<const Chunk*>(sb + fa_off[f] + (swizzle<SWZ, RC>(fa_row[f], ch) << 4));
+#pragma unroll
+    for (int f = 0; f < FN; ++f)
+      b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
+  };
+  frags(smem, 0, af[0], bfr[0]);
+  int st = 0;  // stage holding k-tile kt
+  for (int kt = 0; kt < nk; ++kt) {
+    const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
+    if (issue) {
+      if constexpr (DMA) {
+        int sn = st + STAGES - 1;
+        if (sn >= STAGES) sn -= STAGES;
+        dma_issue(kt + STAGES - 1, sn);
+      } else {
+        reg_load(kt + 1);
+      }
+    }
+    const char* sb = smem + st * STB;
+    const int stn = (st + 1 == STAGES) ? 0 : st + 1;
+    auto mma_range = [&](int cur, int q0, int q1) {
+#pragma unroll
+      for (int q = q0; q < q1; ++q) Elem<T>::mma(acc[q / FN][q % FN], af[cur][q / FN], bfr[cur][q % FN]);
+    };
+    constexpr int NQ = FM * FN;
+    constexpr int kMf = Elem<T>::kMfmaPerChunk;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      const int cur = s & 1;  // SUB is even: k-tile kt+1 starts in buffer 0 again
+      if (s + 1 < SUB) {
+        frags(sb, s + 1, af[cur ^ 1], bfr[cur ^ 1]);
+        mma_range(cur, 0, NQ);
+        if constexpr (SCHED == 1) {
+          // two MFMAs (their operands' wait comes first), the next substep's
+          // reads, then the remaining MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMf, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, (NQ - 2) * kMf, 0);
+        }
+      } else {
+        // Half of the last substep's MFMAs go before the barrier so the MFMA
+        // pipe stays busy while the wave waits in it.  The barrier and the
+        // next k-tile's first reads are unconditional, also after the last
+        // k-tile (the reads are then unused but in bounds): a branch would
+        // merge two different counts of outstanding LDS reads and force a
+        // full lgkmcnt wait.
+        mma_range(cur, 0, NQ / 2);
+        if constexpr (DMA) {
+          if (kt + STAGES - 1 < nk) {
+            barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile kt+1 has landed for this wave
+          } else {
+            barrier_keep_vm<0>();
+          }
+        } else {
+          if (issue) reg_store(stn);
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS stores done
+          __builtin_amdgcn_s_barrier();
+        }
+        frags(smem + stn * STB, 0, af[cur ^ 1], bfr[cur ^ 1]);
+        mma_range(cur, NQ / 2, NQ);
+        if constexpr (SCHED == 1) {
+          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, (NQ - NQ / 2) * kMf, 0);
+        }
+      }
+    }
+    st = stn;
+  }
   // ---- epilogue.  acc[fi][fj][4q+e] holds C[i][j] with
   //   i = ti*BM + wm*WTM + fi*32 + 8q + 4*half + e
   //   j = tj*BM + wn*WTN + fj*32 + lane%32
-  const int i_base = ti * BM + wm * WTM + 4 * half;
-  const int j_base = tj * BM + wn * WTN + frow;
+  // Each value is finished in registers (v replaces acc) and stored
+  // row-major straight from the MFMA layout: 32 lanes cover 32 consecutive
+  // columns of one row.  Transposed outputs (X'^T, the mirror tile of a
+  // symmetric product, a tall caller output) are staged per wave through LDS
+  // in 64-row halves, column-major with a 68-float stride (conflict-free for
+  // the 16-byte writes of 4 rows and the 16-byte reads of 8 rows), and leave
+  // as 128-byte row segments.
+  const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
+  const int gj0 = tj * BN + wn * WTN;  // first column
+  const int i_base = gi0 + 4 * half;
+  const int j_base = gj0 + frow;
 
-  if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
-    char* Om = G.O0 + mat * G.o0_mat;
-    const int ldo = G.ldo0;
-    const char* Em = (EPI == EPI_POLY) ? G.E0 + mat * G.e0_mat : nullptr;
-    const int lde = G.lde0;
-    const bool mirror = (ti != tj);
+  // 1. finish the values and store them row-major, one 32x32 block at a
+  //    time.  The epilogue operand (fp32 X, or A for the polynomial) of the
+  //    next PF blocks is loaded ahead, in registers the main loop no longer
+  //    needs, so several blocks' loads are in flight at once.
+  constexpr int NB = FM * FN;  // 32x32 blocks per wave
+  constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
+  constexpr bool kHasE = (EPI != EPI_GRAM);
+  float ebuf[kHasE ? PF + 1 : 1][16];
+  auto eload = [&](int blk, float* e) {
+    const int fi = blk / FN, fj = blk % FN;
+    const int j = j_base + fj * 32;
+    if constexpr (EPI == EPI_POLY) {
+      const char* Em = G.E0 + mat * G.e0_mat;
+      const int64_t lde = G.lde0;
 #pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
+      for (int r = 0; r < 16; ++r)
+        e[r] = Elem<T>::load(Em + ((i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * lde + j) * sizeof(T));
+    } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
+      const float* Em = reinterpret_cast<const float*>(G.E0 + mat * G.e0_mat);  // fp32 X
+      const int64_t lde = G.lde0;
 #pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
+      for (int r = 0; r < 16; ++r) e[r] = Em[(i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * lde + j];
+    }
+  };
+  if constexpr (kHasE) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i0 = i_base + fi * 32 + 8 * q;
-          const int j = j_base + fj * 32;
-          float v0 = acc[fi][fj][4 * q + 0];
-          float v1 = acc[fi][fj][4 * q + 1];
-          float v2 = acc[fi][fj][4 * q + 2];
-          float v3 = acc[fi][fj][4 * q + 3];
-          if constexpr (EPI == EPI_POLY) {
-            const char* e = Em + (static_cast<int64_t>(i0) * lde + j) * sizeof(T);
-            const int64_t rs = static_cast<int64_t>(lde) * sizeof(T);
-            v0 = L.b * Elem<T>::load(e) + L.c * v0;
-            v1 = L.b * Elem<T>::load(e + rs) + L.c * v1;
-            v2 = L.b * Elem<T>::load(e + 2 * rs) + L.c * v2;
-            v3 = L.b * Elem<T>::load(e + 3 * rs) + L.c * v3;
-          }
-          // C[j][i0..i0+3] = C[i0..i0+3][j] by symmetry: one contiguous store
-          Elem<T>::store4(Om + (static_cast<int64_t>(j) * ldo + i0) * sizeof(T), v0, v1, v2, v3);
-          if (mirror) {
-            char* o = Om + (static_cast<int64_t>(i0) * ldo + j) * sizeof(T);
-            const int64_t rs = static_cast<int64_t>(ldo) * sizeof(T);
-            Elem<T>::store(o, v0);
-            Elem<T>::store(o + rs, v1);
-            Elem<T>::store(o + 2 * rs, v2);
-            Elem<T>::store(o + 3 * rs, v3);
-          }
-        }
-  } else if constexpr (EPI == EPI_UPDATE) {
-    const float* Em = reinterpret_cast<const float*>(G.E0 + mat * G.e0_mat);  // fp32 X
-    const int lde = G.lde0;
-    float* O0m = reinterpret_cast<float*>(G.O0 + mat * G.o0_mat);           // fp32 X'
-    const int ldo0 = G.ldo0;
-    uint16_t* O1m = G.O1 ? reinterpret_cast<uint16_t*>(G.O1 + mat * G.o1_mat) : nullptr;
-    const int ldo1 = G.ldo1;
-    char* OTm = G.OT + mat * G.ot_mat;                                      // X'^T
-    const int ldot = G.ldot;
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i0 = i_base + fi * 32 + 8 * q;
-          const int j = j_base + fj * 32;
-          float v[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            v[e] = L.a * Em[static_cast<int64_t>(i0 + e) * lde + j] + acc[fi][fj][4 * q + e];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            O0m[static_cast<int64_t>(i0 + e) * ldo0 + j] = v[e];
-            if (O1m) O1m[static_cast<int64_t>(i0 + e) * ldo1 + j] = f32_to_bf16(v[e]);
-          }
-          Elem<T>::store4(OTm + (static_cast<int64_t>(j) * ldot + i0) * sizeof(T), v[0], v[1], v[2], v[3]);
-        }
-  } else {  // EPI_FINAL: a*X + B*X into the caller's output, clipped to ms x ns
-    const float* Em = reinterpret_cast<const float*>(G.E0 + mat * G.e0_mat);
-    const int lde = G.lde0;
-    char* U = user_ptr(G.user, mat);
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int i0 = i_base + fi * 32 + 8 * q;
-          const int j = j_base + fj * 32;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            const float v = L.a * Em[static_cast<int64_t>(i) * lde + j] + acc[fi][fj][4 * q + e];
-            if (i < G.ms && j < G.ns) {
-              if (G.tall) {
-                store_user(G.user, U, j, i, v);
-              } else {
-                store_user(G.user, U, i, j, v);
-              }
-            }
-          }
-        }
+    for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
   }
+#pragma unroll
+  for (int blk = 0; blk < NB; ++blk) {
+    const int fi = blk / FN, fj = blk % FN;
+    const int j = j_base + fj * 32;
+    if constexpr (kHasE) {
+      if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
+      const float* e = ebuf[blk % (PF + 1)];
+      if constexpr (EPI == EPI_POLY) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
+      }
+    }
+    if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
+      char* Om = G.O0 + mat * G.o0_mat;
+      const int64_t ldo = G.ldo0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        Elem<T>::store(Om + ((i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * ldo + j) * sizeof(T), acc[fi][fj][r]);
+    } else if constexpr (EPI == EPI_UPDATE) {
+      float* O0m = reinterpret_cast<float*>(G.O0 + mat * G.o0_mat);  // fp32 X'
+      const int64_t ldo0 = G.ldo0;
+      uint16_t* O1m = G.O1 ? reinterpret_cast<uint16_t*>(G.O1 + mat * G.o1_mat) : nullptr;  // bf16 X'
+      const int64_t ldo1 = G.ldo1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+        O0m[i * ldo0 + j] = acc[fi][fj][r];
+        if (O1m) O1m[i * ldo1 + j] = f32_to_bf16(acc[fi][fj][r]);
+      }
+    } else {  // EPI_FINAL: caller output in the Newton-Schulz orientation
+      if (!G.tall) {
+        char* U = user_ptr(G.user, mat);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          if (i < G.ms && j < G.ns) store_user(G.user, U, i, j, acc[fi][fj][r]);
+        }
+      }
+    }
+  }
+
+  // 3. transposed stores through LDS
+  bool transposed;
+  if constexpr (EPI == EPI_UPDATE) {
+    transposed = true;
+  } else if constexpr (EPI == EPI_FINAL) {
+    transposed = G.tall != 0;
+  } else {
+    transposed = tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
+  }
+  if (!transposed) return;  // uniform over the workgroup
+  static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
+  constexpr int ES = 68;  // floats per staged column
+  __syncthreads();        // every wave is done with the operand stages
+  float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
+  char* OTm;
+  int64_t ldot;
+  if constexpr (EPI == EPI_UPDATE) {
+    OTm = G.OT + mat * G.ot_mat;
+    ldot = G.ldot;
+  } else if constexpr (EPI == EPI_FINAL) {
+    OTm = user_ptr(G.user, mat);
+    ldot = G.user.ld;
+  } else {
+    OTm = G.O0 + mat * G.o0_mat;
+    ldot = G.ldo0;
+  }
+#pragma unroll
+  for (int h = 0; h < WTM / 64; ++h) {
+    // registers -> LDS column-major: 4 consecutive rows of one column per write
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = f * 32 + 8 * q + 4 * half;
+          const int c = fj * 32 + frow;
+          const int fi = 2 * h + f;
+          *reinterpret_cast<float4*>(wl + c * ES + r) =
+              make_float4(acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
+        }
+    // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = (lane >> 3) + 8 * k;
+      const int rc = (lane & 7) * 8;
+      const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
+      const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
+      const int64_t orow = gj0 + c;            // output row = this tile's column
+      const int64_t ocol = gi0 + h * 64 + rc;  // output column = this tile's row
+      if constexpr (EPI == EPI_FINAL) {
+        if (orow < G.ns) {
+          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (ocol + e < G.ms) store_user(G.user, OTm, orow, ocol + e, xv[e]);
+        }
+      } else {
+        Elem<T>::store8(OTm + (orow * ldot + ocol) * sizeof(T), x0, x1);
+      }
+    }
+  }
+}
+
+// Measured on MI355X (config-2 shapes): 64-element k-tiles moved by LDS DMA
+// through a two-stage ring, the 64-bank swizzle, XCD-contiguous tile ranges
+// and groups of four tile rows for the non-symmetric product.
+template <typename T, int BM, int WGM, int WGN, int EPI>
+void launch_one(const GemmLaunch& L, hipStream_t stream) {
+  constexpr int RC = 8, STAGES = 2, SWZ = 1, DMA = 1, XCD = 1, SCHED = 0, GM = 4;
+  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM>),
+                     dim3(L.total_tiles), dim3(64 * WGM * WGN), 0, stream, L);
 }
 
 template <typename T, int BM, int WGM, int WGN>
 hipError_t launch_t(int epi, const GemmLaunch& L, hipStream_t stream) {
-  dim3 grid(L.total_tiles), block(64 * WGM * WGN);
   switch (epi) {
-    case EPI_GRAM:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI_GRAM>), grid, block, 0, stream, L);
-      break;
-    case EPI_POLY:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI_POLY>), grid, block, 0, stream, L);
-      break;
-    case EPI_UPDATE:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI_UPDATE>), grid, block, 0, stream, L);
-      break;
-    default:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI_FINAL>), grid, block, 0, stream, L);
-      break;
+    case EPI_GRAM: launch_one<T, BM, WGM, WGN, EPI_GRAM>(L, stream); break;
+    case EPI_POLY: launch_one<T, BM, WGM, WGN, EPI_POLY>(L, stream); break;
+    case EPI_UPDATE: launch_one<T, BM, WGM, WGN, EPI_UPDATE>(L, stream); break;
+    default: launch_one<T, BM, WGM, WGN, EPI_FINAL>(L, stream); break;
   }
   return hipGetLastError();
 }
