@@ -4,6 +4,7 @@
 
 #include "../../include/muon355.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -352,11 +353,16 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
               G.ldot = p.Mp;
             }
           }
-          G.tile_begin = total;
-          total += G.tiles_per_mat * G.count;
           L.g[L.ngroups++] = G;
         }
         if (L.ngroups == 0) continue;
+        // Longest tiles first (reduction length decides a tile's cost), so
+        // the short ones fill in at the end of the launch.
+        std::stable_sort(L.g, L.g + L.ngroups, [](const GemmGroup& x, const GemmGroup& y) { return x.K > y.K; });
+        for (int q = 0; q < L.ngroups; ++q) {
+          L.g[q].tile_begin = total;
+          total += L.g[q].tiles_per_mat * L.g[q].count;
+        }
         L.total_tiles = total;
         const int epi = stage == 0 ? EPI_GRAM : stage == 1 ? EPI_POLY : (last ? EPI_FINAL : EPI_UPDATE);
         if ((e = launch_ns_gemm(compute, tile, epi, L, stream)) != hipSuccess)

@@ -160,7 +160,8 @@ __device__ __forceinline__ void barrier_keep_vm() {
 //   DMA:    1 = operand tiles go global -> LDS with global_load_lds_dwordx4
 //           (no staging registers); 0 = through VGPRs (two stages only).
 //   XCD:    1 = renumber workgroups so each of the 8 XCDs (which receive
-//           workgroup ids round-robin) works on a contiguous tile range.
+//           workgroup ids round-robin) works on a contiguous tile range of
+//           every group.
 //   SCHED:  0 = compiler schedule; 1 = pin the order of MFMAs and the next
 //           substep's LDS reads.
 //   GM:     tiles of a non-symmetric product are numbered in groups of GM
@@ -198,17 +199,23 @@ void ns_gemm_kernel(const GemmLaunch L) {
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
   // ---- which tile of which matrix of which group
-  int t = blockIdx.x;
-  if (XCD) {
-    const int n = L.total_tiles;
-    const int per = n >> 3, rem = n & 7;
-    const int x = t & 7;
-    t = x * per + (x < rem ? x : rem) + (t >> 3);
-  }
+  const int t = blockIdx.x;
   int gi = 0;
   while (gi + 1 < L.ngroups && t >= L.g[gi + 1].tile_begin) ++gi;
   const GemmGroup& G = L.g[gi];
-  const int lt = t - G.tile_begin;
+  int lt = t - G.tile_begin;  // position within the group
+  if (XCD) {
+    // Workgroup ids reach the 8 XCDs round-robin.  Inside each group, the
+    // positions that land on one XCD are renumbered to one contiguous range
+    // of the group's tiles: every XCD keeps a proportional share of every
+    // group (groups of unequal tile cost stay balanced across XCDs) and
+    // neighbouring tiles on an XCD share its L2.
+    const int n = G.tiles_per_mat * G.count;
+    const int f = (t - G.tile_begin) & 7;  // first in-group position on this XCD
+    int start = 0;
+    for (int e = 0; e < f; ++e) start += (n - e + 7) >> 3;  // positions on XCDs ranked before
+    lt = start + ((lt - f) >> 3);
+  }
   const int mat = lt / G.tiles_per_mat;
   int tt = lt - mat * G.tiles_per_mat;
   int ti, tj;
