@@ -45,6 +45,26 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(cfg_index):
+    """HBM bytes per step of the Newton-Schulz GEMM launches, from the
+    rocprofv3 FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when that
+    summary was taken on a different version of the kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"ns_gemm_config{cfg_index}_hbm_traffic.md")
+    src = os.path.join(ROOT, "matrix_aware_optimizer_step_amd", "csrc", "ns_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("traffic-record: "):
+            rec = json.loads(line[len("traffic-record: "):])
+    if rec is None:
+        return None
+    if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    return rec["ns_gemm_bytes_per_step"]
+
+
 def cpu_baseline(cfg, grads_host, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the workload's matrices
     (smallest first until about `budget_s` of work), scaled by NS flops to
@@ -86,6 +106,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB device-to-device copy before the warmup, so that profiler byte counters "
+                         "can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the Muon step here runs on a single MI355X with no "
@@ -112,6 +135,13 @@ def main():
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
 
     stepper = mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] 1 GiB calibration copy done")
 
     def one_step(ev=None):
         stepper.step(events=ev)
@@ -178,7 +208,7 @@ def main():
         "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
                         "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.index),
                      "kernel": "ns_gemm_kernel (Gram, polynomial and update launches of muon_orthogonalize_grouped)"},
         "cpu_baseline": cpu,
     }
