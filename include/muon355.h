@@ -142,7 +142,9 @@ size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols,
  *          fp32 copy of X for the a*X term (the fast path);
  *          MUON_F32   = fp32 MFMA throughout (the parity path).
  * The Gram and polynomial GEMMs compute only upper-triangle tiles and
- * mirror them.
+ * mirror them.  The Newton-Schulz shape padded to the tile size (128 or
+ * 256) may hold at most 2^30 elements; larger shapes return
+ * MUON_ERR_UNSUPPORTED.
  */
 muon_status_t muon_orthogonalize(const muon_batch_t* in, const float* sumsq,
                                  const muon_batch_t* out, int steps, float a,

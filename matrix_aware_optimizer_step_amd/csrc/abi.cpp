@@ -144,7 +144,9 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.tile = p.ms <= 128 ? 128 : 256;
     p.Mp = static_cast<int32_t>(align_up(p.ms, p.tile));
     p.Np = static_cast<int32_t>(align_up(p.ns, p.tile));
-    if (static_cast<int64_t>(p.Mp) * p.Np > kMaxElems) return false;
+    // per-matrix byte offsets inside the GEMM kernels are 32-bit: an fp32
+    // padded matrix must stay below 4 GiB
+    if (static_cast<int64_t>(p.Mp) * p.Np > (int64_t{1} << 30)) return false;
     p.Pr = p.tall ? p.Np : p.Mp;
     p.Pc = p.tall ? p.Mp : p.Np;
     const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
@@ -210,7 +212,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
   }
   Plan plan;
   if (!make_plan(ngroups, counts.data(), rows.data(), cols.data(), compute, need, &plan))
-    return fail(MUON_ERR_UNSUPPORTED, "a padded Newton-Schulz shape exceeds 2^31-1 elements");
+    return fail(MUON_ERR_UNSUPPORTED, "a padded Newton-Schulz shape exceeds 2^30 elements");
   if (!workspace || ws_bytes < static_cast<size_t>(plan.bytes))
     return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %lld needed", ws_bytes, (long long)plan.bytes);
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)

@@ -314,6 +314,41 @@ void ns_gemm_kernel(const GemmLaunch L) {
     for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
   };
 
+  // ---- accumulators.  For the update product the fp32 a*X term is the
+  // starting value (X' = a*X + B*X), loaded here so that its latency overlaps
+  // the operand prologue and the epilogue only stores.
+  const int frow = lane & 31;
+  const int half = lane >> 5;
+  const int i_base = ti * BM + wm * WTM + 4 * half;  // acc[fi][fj][4q+e]: row i_base + fi*32 + 8q + e
+  const int j_base = tj * BN + wn * WTN + frow;      //                    col j_base + fj*32
+  f32x16_t acc[FM][FN];
+  if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
+    const char* Em = G.E0 + mat * G.e0_mat;  // fp32 X; per-matrix byte offsets fit in 32 bits
+    const uint32_t lde = G.lde0;
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          acc[fi][fj][r] = *reinterpret_cast<const float*>(Em + (i * lde + j_base + fj * 32) * 4u);
+        }
+#pragma unroll
+    for (int fi = 0; fi < FM; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fi][fj][r] *= L.a;
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  }
+
   constexpr int kPerTile = IPW + IPWQ;  // DMA instructions per wave per k-tile
   static_assert(SUB % 2 == 0, "fragment double buffer assumes an even substep count");
   if constexpr (DMA) {
@@ -331,16 +366,6 @@ void ns_gemm_kernel(const GemmLaunch L) {
     __syncthreads();
   }
 
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  const int frow = lane & 31;
-  const int half = lane >> 5;
   int fa_off[FM], fb_off[FN], fa_row[FM], fb_row[FN];
 #pragma unroll
   for (int f = 0; f < FM; ++f) {
@@ -444,8 +469,6 @@ void ns_gemm_kernel(const GemmLaunch L) {
   // as 128-byte row segments.
   const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
   const int gj0 = tj * BN + wn * WTN;  // first column
-  const int i_base = gi0 + 4 * half;
-  const int j_base = gj0 + frow;
 
   // 1. finish the values and store them row-major, one 32x32 block at a
   //    time.  The epilogue operand (fp32 X, or A for the polynomial) of the
@@ -453,22 +476,19 @@ void ns_gemm_kernel(const GemmLaunch L) {
   //    needs, so several blocks' loads are in flight at once.
   constexpr int NB = FM * FN;  // 32x32 blocks per wave
   constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
-  constexpr bool kHasE = (EPI != EPI_GRAM);
+  constexpr bool kHasE = (EPI == EPI_POLY);  // the update's a*X is already in acc
   float ebuf[kHasE ? PF + 1 : 1][16];
   auto eload = [&](int blk, float* e) {
     const int fi = blk / FN, fj = blk % FN;
     const int j = j_base + fj * 32;
     if constexpr (EPI == EPI_POLY) {
       const char* Em = G.E0 + mat * G.e0_mat;
-      const int64_t lde = G.lde0;
+      const uint32_t lde = G.lde0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        e[r] = Elem<T>::load(Em + ((i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * lde + j) * sizeof(T));
-    } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
-      const float* Em = reinterpret_cast<const float*>(G.E0 + mat * G.e0_mat);  // fp32 X
-      const int64_t lde = G.lde0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = Em[(i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * lde + j];
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+        e[r] = Elem<T>::load(Em + (i * lde + j) * static_cast<uint32_t>(sizeof(T)));
+      }
     }
   };
   if constexpr (kHasE) {
@@ -482,30 +502,27 @@ void ns_gemm_kernel(const GemmLaunch L) {
     if constexpr (kHasE) {
       if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
       const float* e = ebuf[blk % (PF + 1)];
-      if constexpr (EPI == EPI_POLY) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
-      }
+      for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
     }
     if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
       char* Om = G.O0 + mat * G.o0_mat;
-      const int64_t ldo = G.ldo0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        Elem<T>::store(Om + ((i_base + fi * 32 + 8 * (r >> 2) + (r & 3)) * ldo + j) * sizeof(T), acc[fi][fj][r]);
-    } else if constexpr (EPI == EPI_UPDATE) {
-      float* O0m = reinterpret_cast<float*>(G.O0 + mat * G.o0_mat);  // fp32 X'
-      const int64_t ldo0 = G.ldo0;
-      uint16_t* O1m = G.O1 ? reinterpret_cast<uint16_t*>(G.O1 + mat * G.o1_mat) : nullptr;  // bf16 X'
-      const int64_t ldo1 = G.ldo1;
+      const uint32_t ldo = G.ldo0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-        O0m[i * ldo0 + j] = acc[fi][fj][r];
-        if (O1m) O1m[i * ldo1 + j] = f32_to_bf16(acc[fi][fj][r]);
+        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+        Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
+      }
+    } else if constexpr (EPI == EPI_UPDATE) {
+      char* O0m = G.O0 + mat * G.o0_mat;  // fp32 X'
+      const uint32_t ldo0 = G.ldo0;
+      char* O1m = G.O1 ? G.O1 + mat * G.o1_mat : nullptr;  // bf16 X'
+      const uint32_t ldo1 = G.ldo1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+        *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
+        if (O1m) *reinterpret_cast<uint16_t*>(O1m + (i * ldo1 + j) * 2u) = f32_to_bf16(acc[fi][fj][r]);
       }
     } else {  // EPI_FINAL: caller output in the Newton-Schulz orientation
       if (!G.tall) {
@@ -567,8 +584,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
       const int rc = (lane & 7) * 8;
       const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
       const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
-      const int64_t orow = gj0 + c;            // output row = this tile's column
-      const int64_t ocol = gi0 + h * 64 + rc;  // output column = this tile's row
+      const int orow = gj0 + c;            // output row = this tile's column
+      const int ocol = gi0 + h * 64 + rc;  // output column = this tile's row
       if constexpr (EPI == EPI_FINAL) {
         if (orow < G.ns) {
           const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -577,7 +594,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
             if (ocol + e < G.ms) store_user(G.user, OTm, orow, ocol + e, xv[e]);
         }
       } else {
-        Elem<T>::store8(OTm + (orow * ldot + ocol) * sizeof(T), x0, x1);
+        Elem<T>::store8(OTm + (static_cast<uint32_t>(orow) * static_cast<uint32_t>(ldot) + ocol) *
+                                  static_cast<uint32_t>(sizeof(T)), x0, x1);
       }
     }
   }
