@@ -45,6 +45,12 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def make_stepper(mx, weights, grads):
+    """The optimizer step this benchmark times: every group of the workload
+    in one MuonStep (grouped Newton-Schulz launches, bf16 MFMA)."""
+    return mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD)
+
+
 def measured_traffic(cfg_index):
     """HBM bytes per step of the Newton-Schulz GEMM launches, from the
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when that
@@ -134,7 +140,7 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
 
-    stepper = mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD)
+    stepper = make_stepper(mx, weights, grads)
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
         dst = torch.empty_like(src)
@@ -173,7 +179,7 @@ def main():
     ns_tflops = algo / (t_ns * 1e-3) / 1e12
     ns_tflops_nominal = nominal / (t_ns * 1e-3) / 1e12
     elems = cfg.elements
-    mom_bytes = elems * (2 + 8 + 2)   # G bf16 read, M fp32 read+write, N bf16 write
+    mom_bytes = elems * (2 + 8 + 4)   # G bf16 read, M fp32 read+write, N fp32 write
     app_bytes = elems * (4 + 2)       # W bf16 read+write, O bf16 read
     mom_gbs = mom_bytes / (t_mom * 1e-3) / 1e9
     app_gbs = app_bytes / (t_app * 1e-3) / 1e9

@@ -141,6 +141,11 @@ size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols,
  * compute: MUON_BF16 = bf16 MFMA operands with fp32 accumulation and an
  *          fp32 copy of X for the a*X term (the fast path);
  *          MUON_F32   = fp32 MFMA throughout (the parity path).
+ *          With MUON_BF16 an F32 `in` is preferred: the fp32 copy of X
+ *          starts from it, while a BF16 `in` starts the iteration from
+ *          bf16-rounded values, an error the iteration amplifies on
+ *          ill-conditioned inputs (about 10x larger output error at
+ *          condition number 1e4).
  * The Gram and polynomial GEMMs compute only upper-triangle tiles and
  * mirror them.  The Newton-Schulz shape padded to the tile size (128 or
  * 256) may hold at most 2^30 elements; larger shapes return

@@ -314,40 +314,20 @@ void ns_gemm_kernel(const GemmLaunch L) {
     for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
   };
 
-  // ---- accumulators.  For the update product the fp32 a*X term is the
-  // starting value (X' = a*X + B*X), loaded here so that its latency overlaps
-  // the operand prologue and the epilogue only stores.
+  // ---- accumulators (fp32, from zero: the update's a*X term is added in
+  // the epilogue, so every rounding of the running sum is at the scale of
+  // the product itself)
   const int frow = lane & 31;
   const int half = lane >> 5;
   const int i_base = ti * BM + wm * WTM + 4 * half;  // acc[fi][fj][4q+e]: row i_base + fi*32 + 8q + e
   const int j_base = tj * BN + wn * WTN + frow;      //                    col j_base + fj*32
   f32x16_t acc[FM][FN];
-  if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
-    const char* Em = G.E0 + mat * G.e0_mat;  // fp32 X; per-matrix byte offsets fit in 32 bits
-    const uint32_t lde = G.lde0;
 #pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          acc[fi][fj][r] = *reinterpret_cast<const float*>(Em + (i * lde + j_base + fj * 32) * 4u);
-        }
-#pragma unroll
-    for (int fi = 0; fi < FM; ++fi)
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[fi][fj][r] *= L.a;
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
   constexpr int kPerTile = IPW + IPWQ;  // DMA instructions per wave per k-tile
   static_assert(SUB % 2 == 0, "fragment double buffer assumes an even substep count");
@@ -476,7 +456,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
   //    needs, so several blocks' loads are in flight at once.
   constexpr int NB = FM * FN;  // 32x32 blocks per wave
   constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
-  constexpr bool kHasE = (EPI == EPI_POLY);  // the update's a*X is already in acc
+  constexpr bool kHasE = (EPI != EPI_GRAM);
   float ebuf[kHasE ? PF + 1 : 1][16];
   auto eload = [&](int blk, float* e) {
     const int fi = blk / FN, fj = blk % FN;
@@ -488,6 +468,14 @@ void ns_gemm_kernel(const GemmLaunch L) {
       for (int r = 0; r < 16; ++r) {
         const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
         e[r] = Elem<T>::load(Em + (i * lde + j) * static_cast<uint32_t>(sizeof(T)));
+      }
+    } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
+      const char* Em = G.E0 + mat * G.e0_mat;  // fp32 X; per-matrix byte offsets fit in 32 bits
+      const uint32_t lde = G.lde0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+        e[r] = *reinterpret_cast<const float*>(Em + (i * lde + j) * 4u);
       }
     }
   };
@@ -502,8 +490,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
     if constexpr (kHasE) {
       if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
       const float* e = ebuf[blk % (PF + 1)];
+      if constexpr (EPI == EPI_POLY) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
+        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
+      }
     }
     if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
       char* Om = G.O0 + mat * G.o0_mat;

@@ -149,7 +149,10 @@ class MuonStep:
         self.lr, self.weight_decay, self.mode, self.coeff = lr, weight_decay, mode, coeff
         self.w, self.g, self.m, self.n, self.o, self.ss, self.mws = [], [], [], [], [], [], []
         dev = None
-        nbuf_dtype = torch.bfloat16 if compute == L.MUON_BF16 else torch.float32
+        # The Newton-Schulz input stays fp32 on both paths: the bf16 path's
+        # fp32 copy of X starts from it, and a bf16-rounded start is the
+        # error that the iteration amplifies most on ill-conditioned inputs.
+        nbuf_dtype = torch.float32
         for weights, grads in groups:
             w, g = batch(weights), batch(grads)
             if (w.count, w.rows, w.cols) != (g.count, g.rows, g.cols):

@@ -180,6 +180,30 @@ def test_ns_bf16(mx, shape):
     assert rel(f64(out[0]), want) <= TOL_BF16
 
 
+ILL_CASES = [("kappa", 128, 4096), ("kappa", 300, 700), ("kappa", 1100, 260), ("power", 1024, 4096),
+             ("power", 520, 1500)]
+
+
+def ill_conditioned(kind, rows, cols):
+    seed = rows * 31 + cols
+    if kind == "kappa":
+        return synth.condition_number(rows, cols, seed)  # singular values 1 .. 1e-4, geometric
+    return synth.power_law(rows, cols, seed)             # singular values 1/k
+
+
+@pytest.mark.parametrize("compute,tol", [(0, TOL_F32), (1, TOL_BF16)])
+@pytest.mark.parametrize("kind,rows,cols", ILL_CASES)
+def test_ns_ill_conditioned(mx, compute, tol, kind, rows, cols):
+    """Ill-conditioned fp32 inputs: the iteration amplifies rounding in the
+    directions of small singular values about a-fold per step, so these
+    cases bound how and where each path rounds (the fp32 input is what the
+    oracle sees; the bf16 path keeps its fp32 copy of X from it)."""
+    N = ill_conditioned(kind, rows, cols).unsqueeze(0).cuda()
+    out = run_ns(mx, N, compute, out_dtype=torch.float32)
+    want = O.newton_schulz(f64(N[0]), 5)
+    assert rel(f64(out[0]), want) <= tol
+
+
 @pytest.mark.parametrize("compute,tol", [(0, TOL_F32), (1, TOL_BF16)])
 @pytest.mark.parametrize("coeffs", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (0.5, -0.25, 0.125)])
 @pytest.mark.parametrize("shape", [(300, 700), (700, 300), (96, 520)])
