@@ -138,10 +138,12 @@ size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols,
  * steps  : K >= 0 (5 in Muon).  a, b, c: finite coefficients, the same at
  *          every step ((3.4445, -4.7750, 2.0315) in Muon).
  * eps    : finite, >= 0 (1e-7 in Muon, [PREPRINT]); added to the norm.
- * compute: MUON_BF16 = bf16 MFMA operands with fp32 accumulation and an
- *          fp32 copy of X for the a*X term (the fast path);
+ * compute: MUON_BF16 = bf16 MFMA operands with fp32 accumulation; X is
+ *          carried between steps as a bf16 high part (the MFMA operand)
+ *          plus a bf16 low part (its rounding residual), about 16
+ *          significant bits, for the a*X term (the fast path);
  *          MUON_F32   = fp32 MFMA throughout (the parity path).
- *          With MUON_BF16 an F32 `in` is preferred: the fp32 copy of X
+ *          With MUON_BF16 an F32 `in` is preferred: the high/low copy of X
  *          starts from it, while a BF16 `in` starts the iteration from
  *          bf16-rounded values, an error the iteration amplifies on
  *          ill-conditioned inputs (about 10x larger output error at

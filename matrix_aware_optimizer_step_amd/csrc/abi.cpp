@@ -110,7 +110,7 @@ struct GroupPlan {
   int32_t Mp, Np;       // padded NS shape
   int32_t Pr, Pc;       // padded stored shape
   // byte offsets into the workspace
-  int64_t x32, xc[2], xt[2], a, b, sumsq, partials;
+  int64_t xlo, xc[2], xt[2], a, b, sumsq, partials;  // xlo: bf16 low part of X (bf16 compute)
   int32_t blocks_per_mat;
 };
 
@@ -151,7 +151,7 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.Pc = p.tall ? p.Mp : p.Np;
     const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
     const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
-    p.x32 = compute == MUON_BF16 ? take(p.count * mn * 4) : -1;
+    p.xlo = compute == MUON_BF16 ? take(p.count * mn * 2) : -1;
     p.xc[0] = take(p.count * mn * es);
     p.xc[1] = take(p.count * mn * es);
     p.xt[0] = take(p.count * mn * es);
@@ -245,6 +245,21 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     ssq[g] = out;
   }
 
+  if (steps == 0) {  // X_0 itself, straight from N
+    for (int g = 0; g < ngroups; ++g) {
+      const GroupPlan& p = plan.g[g];
+      CopyOutArgs ca;
+      ca.N = to_mat(&ins[g]);
+      ca.sumsq = ssq[g];
+      ca.eps = eps;
+      ca.out = to_mat(&outs[g]);
+      ca.rows = p.rows;
+      ca.cols = p.cols;
+      if ((e = launch_copy_out(ca, p.count, stream)) != hipSuccess) return launch_status(e, "copy out");
+    }
+    return ok();
+  }
+
   // 2. X_0 = N / (||N|| + eps) into the padded buffers, both orientations
   for (int g = 0; g < ngroups; ++g) {
     const GroupPlan& p = plan.g[g];
@@ -263,25 +278,9 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     pa.S = ws + (p.tall ? p.xt[0] : p.xc[0]);
     pa.T = ws + (p.tall ? p.xc[0] : p.xt[0]);
     pa.s_mat = pa.t_mat = mn * es;
-    pa.F = compute == MUON_BF16 ? reinterpret_cast<float*>(ws + p.x32) : nullptr;
-    pa.f_mat = mn;
+    pa.Lo = compute == MUON_BF16 ? reinterpret_cast<uint16_t*>(ws + p.xlo) : nullptr;
+    pa.lo_mat = mn;
     if ((e = launch_pack(pa, p.count, stream)) != hipSuccess) return launch_status(e, "pack");
-  }
-
-  if (steps == 0) {
-    for (int g = 0; g < ngroups; ++g) {
-      const GroupPlan& p = plan.g[g];
-      CopyOutArgs ca;
-      ca.X = reinterpret_cast<const float*>(ws + (compute == MUON_BF16 ? p.x32 : p.xc[0]));
-      ca.x_mat = static_cast<int64_t>(p.Mp) * p.Np;
-      ca.ldx = p.Np;
-      ca.out = to_mat(&outs[g]);
-      ca.rows = p.rows;
-      ca.cols = p.cols;
-      ca.tall = p.tall;
-      if ((e = launch_copy_out(ca, p.count, stream)) != hipSuccess) return launch_status(e, "copy out");
-    }
-    return ok();
   }
 
   // 3. the K-step loop: Gram, polynomial, update; one launch per stage and tile class
@@ -335,21 +334,32 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             G.q_mat = mn * es;
             G.ldq = p.Mp;
             G.K = p.Mp;
-            const int64_t xsrc = compute == MUON_BF16 ? p.x32 : p.xc[cur];
-            G.E0 = ws + xsrc;
-            G.e0_mat = mn * 4;
+            // X (fp32), or its bf16 high part (the Gram operand) and low part
+            G.E0 = ws + p.xc[cur];
+            G.e0_mat = mn * es;
             G.lde0 = p.Np;
+            if (compute == MUON_BF16) {
+              G.E1 = ws + p.xlo;
+              G.e1_mat = mn * 2;
+              G.lde1 = p.Np;
+            }
             if (last) {
               G.user = to_mat(&outs[g]);
+            } else if (compute == MUON_BF16) {
+              // the low part is rewritten in place: each element is read
+              // and written by the same lane of the same tile
+              G.O0 = ws + p.xlo;
+              G.o0_mat = mn * 2;
+              G.ldo0 = p.Np;
+              G.O1 = ws + p.xc[nxt];
+              G.o1_mat = mn * 2;
+              G.ldo1 = p.Np;
             } else {
-              G.O0 = ws + (compute == MUON_BF16 ? p.x32 : p.xc[nxt]);
+              G.O0 = ws + p.xc[nxt];
               G.o0_mat = mn * 4;
               G.ldo0 = p.Np;
-              if (compute == MUON_BF16) {
-                G.O1 = ws + p.xc[nxt];
-                G.o1_mat = mn * 2;
-                G.ldo1 = p.Np;
-              }
+            }
+            if (!last) {
               G.OT = ws + p.xt[nxt];
               G.ot_mat = mn * es;
               G.ldot = p.Mp;

@@ -10,9 +10,10 @@
 //                     matrix (deterministic; no float atomics);
 //   apply_kernel      W <- (1 - lr*wd)*W - lr*s*O (section 11.5);
 //   pack_kernel       N / (||N||_F + eps) into the padded Newton-Schulz
-//                     buffers, in both orientations, through an LDS tile
-//                     transpose so that reads and writes stay coalesced;
-//   copy_out_kernel   the zero-step output.
+//                     buffers, in both orientations (and the bf16 low part
+//                     of X), through an LDS tile transpose so that reads
+//                     and writes stay coalesced;
+//   copy_out_kernel   the zero-step output, N / (||N||_F + eps).
 //
 // The streaming kernels move 16 bytes per lane per access (8 bf16 or 4+4
 // fp32 values per thread step), reduce with wave64 shuffles and one LDS
@@ -92,6 +93,11 @@ __device__ __forceinline__ void store8(char* p, int dtype, const float* v) {
 
 __device__ __forceinline__ float load1(const char* p, int dtype) {
   return dtype ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(p)) : *reinterpret_cast<const float*>(p);
+}
+// v - bf16(v) rounded to bf16: the low part that, added to the bf16 high
+// part, carries about 16 significant bits of v (the subtraction is exact).
+__device__ __forceinline__ uint16_t bf16_residual(float v) {
+  return f32_to_bf16(v - bf16_to_f32(f32_to_bf16(v)));
 }
 __device__ __forceinline__ void store1(char* p, int dtype, float v) {
   if (dtype) {
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     if (r < a.rows && c < a.cols) v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
     tile[rr][tx] = v;
     store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
-    if (a.F && !a.tall) a.F[mat * a.f_mat + static_cast<int64_t>(r) * a.Pc + c] = v;
+    if (a.Lo && !a.tall) a.Lo[mat * a.lo_mat + static_cast<int64_t>(r) * a.Pc + c] = bf16_residual(v);
   }
   __syncthreads();
   // write rows of T = columns of the tile
@@ -305,23 +311,25 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     const int r = r0 + tx;
     const float v = tile[tx][cc];
     store1(T + (static_cast<int64_t>(c) * a.Pr + r) * esz, a.compute, v);
-    if (a.F && a.tall) a.F[mat * a.f_mat + static_cast<int64_t>(c) * a.Pr + r] = v;
+    if (a.Lo && a.tall) a.Lo[mat * a.lo_mat + static_cast<int64_t>(c) * a.Pr + r] = bf16_residual(v);
   }
 }
 
 // grid: (ceil(cols/64), ceil(rows/64), count) over the stored output.
 __global__ __launch_bounds__(kThreads) void copy_out_kernel(const CopyOutArgs a) {
   const int64_t mat = blockIdx.z;
+  const char* n = mat_ptr(a.N, mat);
   char* o = mat_ptr(a.out, mat);
+  const int nsz = a.N.dtype ? 2 : 4;
   const int osz = a.out.dtype ? 2 : 4;
-  const float* X = a.X + mat * a.x_mat;
+  const float scale = 1.0f / (sqrtf(a.sumsq[mat]) + a.eps);
   const int tx = threadIdx.x & 63;
   const int ty = threadIdx.x >> 6;
   for (int rr = ty; rr < kTile; rr += 4) {
     const int r = blockIdx.y * kTile + rr;
     const int c = blockIdx.x * kTile + tx;
     if (r < a.rows && c < a.cols) {
-      const float v = a.tall ? X[static_cast<int64_t>(c) * a.ldx + r] : X[static_cast<int64_t>(r) * a.ldx + c];
+      const float v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
       store1(o + (static_cast<int64_t>(r) * a.out.ld + c) * osz, a.out.dtype, v);
     }
   }

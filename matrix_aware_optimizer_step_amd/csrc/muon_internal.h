@@ -44,11 +44,16 @@ struct GemmGroup {
   int32_t tiles_per_mat;
   int32_t tile_begin;            // first linear tile of this group in the launch
   // epilogue operands (row-major, i x j orientation unless noted)
-  const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A (compute type); UPDATE/FINAL: fp32 X
+  // X itself is held as fp32 (fp32 compute) or, with bf16 compute, as a
+  // bf16 high part (the MFMA operand) plus a bf16 low part (the rounding
+  // residual), about 16 significant bits together.
+  const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL: X (fp32) or its high part
   int32_t pad0_;
-  char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: fp32 X (next)
+  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X
+  int32_t pad5_;
+  char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low part
   int32_t pad1_;
-  char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE (bf16 compute): bf16 X (next), else null
+  char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE, bf16 compute: high part of the next X
   int32_t pad2_;
   char* OT; int64_t ot_mat; int32_t ldot;        // UPDATE: X^T (next) in compute type
   int32_t pad3_;
@@ -113,8 +118,9 @@ hipError_t launch_apply(const ApplyArgs& a, int64_t count, bool vec,
 
 // Copy the caller's N (stored m x n) into the padded Newton-Schulz buffers,
 // scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc) and
-// T[c][r] (Pc x Pr), zero outside m x n; F32 copy of X (= S if !tall, T if
-// tall) when F != null.
+// T[c][r] (Pc x Pr), zero outside m x n, in the compute type; with bf16
+// compute and Lo != null also the bf16 residual of X (= S if !tall, T if
+// tall), value - bf16(value), in X's orientation.
 struct PackArgs {
   MatBatch N;
   const float* sumsq;
@@ -125,16 +131,18 @@ struct PackArgs {
   int32_t tall;
   char* S; int64_t s_mat;  // bytes per matrix
   char* T; int64_t t_mat;
-  float* F; int64_t f_mat; // floats per matrix
+  uint16_t* Lo; int64_t lo_mat;  // elements per matrix
 };
 hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream);
 
-// Zero-step output: out (stored orientation) = fp32 X (NS orientation).
+// Zero-step output: out = N / (sqrt(sumsq) + eps), both in the stored
+// orientation.
 struct CopyOutArgs {
-  const float* X; int64_t x_mat; int32_t ldx;
+  MatBatch N;
+  const float* sumsq;
+  float eps;
   MatBatch out;
   int32_t rows, cols;      // stored m, n
-  int32_t tall;
 };
 hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t stream);
 

@@ -451,7 +451,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
   const int gj0 = tj * BN + wn * WTN;  // first column
 
   // 1. finish the values and store them row-major, one 32x32 block at a
-  //    time.  The epilogue operand (fp32 X, or A for the polynomial) of the
+  //    time.  The epilogue operand (X, or A for the polynomial) of the
   //    next PF blocks is loaded ahead, in registers the main loop no longer
   //    needs, so several blocks' loads are in flight at once.
   constexpr int NB = FM * FN;  // 32x32 blocks per wave
@@ -470,12 +470,24 @@ void ns_gemm_kernel(const GemmLaunch L) {
         e[r] = Elem<T>::load(Em + (i * lde + j) * static_cast<uint32_t>(sizeof(T)));
       }
     } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
-      const char* Em = G.E0 + mat * G.e0_mat;  // fp32 X; per-matrix byte offsets fit in 32 bits
+      // X: fp32, or bf16 high part + bf16 low part (per-matrix byte offsets fit in 32 bits)
+      const char* Em = G.E0 + mat * G.e0_mat;
       const uint32_t lde = G.lde0;
+      if constexpr (sizeof(T) == 2) {
+        const char* El = G.E1 + mat * G.e1_mat;
+        const uint32_t ldl = G.lde1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-        e[r] = *reinterpret_cast<const float*>(Em + (i * lde + j) * 4u);
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          e[r] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(Em + (i * lde + j) * 2u)) +
+                 bf16_to_f32(*reinterpret_cast<const uint16_t*>(El + (i * ldl + j) * 2u));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          e[r] = *reinterpret_cast<const float*>(Em + (i * lde + j) * 4u);
+        }
       }
     }
   };
@@ -507,15 +519,24 @@ void ns_gemm_kernel(const GemmLaunch L) {
         Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
       }
     } else if constexpr (EPI == EPI_UPDATE) {
-      char* O0m = G.O0 + mat * G.o0_mat;  // fp32 X'
+      char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
       const uint32_t ldo0 = G.ldo0;
-      char* O1m = G.O1 ? G.O1 + mat * G.o1_mat : nullptr;  // bf16 X'
-      const uint32_t ldo1 = G.ldo1;
+      if constexpr (sizeof(T) == 2) {
+        char* O1m = G.O1 + mat * G.o1_mat;  // bf16 high part of X'
+        const uint32_t ldo1 = G.ldo1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-        *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
-        if (O1m) *reinterpret_cast<uint16_t*>(O1m + (i * ldo1 + j) * 2u) = f32_to_bf16(acc[fi][fj][r]);
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
+          *reinterpret_cast<uint16_t*>(O1m + (i * ldo1 + j) * 2u) = hi;
+          *reinterpret_cast<uint16_t*>(O0m + (i * ldo0 + j) * 2u) = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
+        }
       }
     } else {  // EPI_FINAL: caller output in the Newton-Schulz orientation
       if (!G.tall) {

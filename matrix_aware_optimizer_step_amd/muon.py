@@ -150,7 +150,7 @@ class MuonStep:
         self.w, self.g, self.m, self.n, self.o, self.ss, self.mws = [], [], [], [], [], [], []
         dev = None
         # The Newton-Schulz input stays fp32 on both paths: the bf16 path's
-        # fp32 copy of X starts from it, and a bf16-rounded start is the
+        # high/low copy of X starts from it, and a bf16-rounded start is the
         # error that the iteration amplifies most on ill-conditioned inputs.
         nbuf_dtype = torch.float32
         for weights, grads in groups:
