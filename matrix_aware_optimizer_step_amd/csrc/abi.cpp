@@ -334,14 +334,16 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             G.q_mat = mn * es;
             G.ldq = p.Mp;
             G.K = p.Mp;
-            // X (fp32), or its bf16 high part (the Gram operand) and low part
-            G.E0 = ws + p.xc[cur];
-            G.e0_mat = mn * es;
-            G.lde0 = p.Np;
+            // a*X: X in fp32, or with bf16 compute its low part (the high
+            // part is the Q operand, which the kernel adds from LDS)
             if (compute == MUON_BF16) {
               G.E1 = ws + p.xlo;
               G.e1_mat = mn * 2;
               G.lde1 = p.Np;
+            } else {
+              G.E0 = ws + p.xc[cur];
+              G.e0_mat = mn * 4;
+              G.lde0 = p.Np;
             }
             if (last) {
               G.user = to_mat(&outs[g]);

@@ -47,9 +47,10 @@ struct GemmGroup {
   // X itself is held as fp32 (fp32 compute) or, with bf16 compute, as a
   // bf16 high part (the MFMA operand) plus a bf16 low part (the rounding
   // residual), about 16 significant bits together.
-  const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL: X (fp32) or its high part
+  const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL, fp32 compute: X
   int32_t pad0_;
-  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X
+  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X (the
+                                                 // high part is Q^T, added from the operand tiles)
   int32_t pad5_;
   char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low part
   int32_t pad1_;

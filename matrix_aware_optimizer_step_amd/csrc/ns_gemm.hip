@@ -375,6 +375,15 @@ void ns_gemm_kernel(const GemmLaunch L) {
       b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
   };
   frags(smem, 0, af[0], bfr[0]);
+  // bf16 update: the high part of a*X enters from the operand tiles (below),
+  // the epilogue adds only the low part.  k-tile kt_x0 + hh holds rows
+  // [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e. kFPK of its 32-row blocks.
+  constexpr bool kAddXInLoop = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+  constexpr int kFPK = BK / 32;
+  constexpr int kNH = WTM / BK;
+  static_assert(!kAddXInLoop || (kNH * BK == WTM && kFPK * 32 == BK && RC == 2 * kFPK * 2),
+                "wave rows must split into whole k-tiles of whole 32-row blocks");
+  const int kt_x0 = (ti * BM + wm * WTM) / BK;
   int st = 0;  // stage holding k-tile kt
   for (int kt = 0; kt < nk; ++kt) {
     const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
@@ -389,6 +398,29 @@ void ns_gemm_kernel(const GemmLaunch L) {
     }
     const char* sb = smem + st * STB;
     const int stn = (st + 1 == STAGES) ? 0 : st + 1;
+    if constexpr (kAddXInLoop) {
+      // a * X[i][j] = a * Q[j][k = i]: the k-tiles that cover this wave's
+      // rows hold the bf16 high part of X for its output elements.
+#pragma unroll
+      for (int hh = 0; hh < kNH; ++hh) {
+        if (kt == kt_x0 + hh) {  // uniform over the wave
+#pragma unroll
+          for (int f = 0; f < kFPK; ++f)
+#pragma unroll
+            for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int fi = hh * kFPK + f;
+                const uint2 v = *reinterpret_cast<const uint2*>(
+                    sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
+                acc[fi][fj][4 * q + 0] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x));
+                acc[fi][fj][4 * q + 1] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
+                acc[fi][fj][4 * q + 2] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y));
+                acc[fi][fj][4 * q + 3] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
+              }
+        }
+      }
+    }
     auto mma_range = [&](int cur, int q0, int q1) {
 #pragma unroll
       for (int q = q0; q < q1; ++q) Elem<T>::mma(acc[q / FN][q % FN], af[cur][q / FN], bfr[cur][q % FN]);
@@ -473,14 +505,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
       // X: fp32, or bf16 high part + bf16 low part (per-matrix byte offsets fit in 32 bits)
       const char* Em = G.E0 + mat * G.e0_mat;
       const uint32_t lde = G.lde0;
-      if constexpr (sizeof(T) == 2) {
+      if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
         const char* El = G.E1 + mat * G.e1_mat;
         const uint32_t ldl = G.lde1;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          e[r] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(Em + (i * lde + j) * 2u)) +
-                 bf16_to_f32(*reinterpret_cast<const uint16_t*>(El + (i * ldl + j) * 2u));
+          e[r] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(El + (i * ldl + j) * 2u));
         }
       } else {
 #pragma unroll
