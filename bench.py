@@ -71,6 +71,80 @@ def measured_traffic(cfg_index):
     return rec["ns_gemm_bytes_per_step"]
 
 
+ADAM_LR, ADAM_WD, ADAM_BETAS, ADAM_EPS = 3e-4, 0.1, (0.9, 0.999), 1e-8
+ADAMW_BYTES = 2 + 2 + 2 + 8 + 8  # per element: bf16 theta read+write, bf16 grad, fp32 m and v read+write
+
+
+def make_adamw_step(mx, names, params, grads):
+    """The AdamW leg this benchmark times: the routing helper over the 8B-style
+    model's non-matrix parameters (every one goes to AdamW)."""
+    opt = mx.OptimizerStep(list(zip(names, params, grads)), adam_lr=ADAM_LR, adam_betas=ADAM_BETAS,
+                           adam_eps=ADAM_EPS, adam_weight_decay=ADAM_WD)
+    assert opt.muon is None
+    return opt
+
+
+def bench_adamw(args):
+    """Time the AdamW step over the 8B-style model's embeddings, head and norms;
+    print one JSON line against the HBM roofline."""
+    import numpy as np
+    import torch
+
+    import matrix_aware_optimizer_step_amd as mx
+    from workloads import synth
+
+    mx._lib.load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    shapes = synth.adamw_workload()
+    names = [n for n, _ in shapes]
+    params, grads = synth.adamw_tensors(shapes, step=1, device=dev)
+    opt = make_adamw_step(mx, names, params, grads)
+    elems = sum(g.elements for g in opt.adamw)
+    log(f"[bench] AdamW over {len(shapes)} tensors, {elems / 1e6:.1f} M elements")
+    for _ in range(args.warmup):
+        opt.step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        opt.step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    gbs = elems * ADAMW_BYTES / (ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import adamw as OA
+        n = 1 << 24
+        rng = np.random.default_rng(0)
+        th, g = rng.standard_normal(n) * 0.02, rng.standard_normal(n)
+        m, v = np.zeros(n), np.zeros(n)
+        t1 = time.perf_counter()
+        reps = 0
+        while time.perf_counter() - t1 < 10.0:
+            th, m, v = OA.adamw_step(th, g, m, v, reps + 1, ADAM_LR, *ADAM_BETAS, ADAM_EPS, ADAM_WD)
+            reps += 1
+        sec = (time.perf_counter() - t1) / reps * elems / n
+        cpu = {"value": 1.0 / sec, "unit": "steps/s", "cores": 1, "kind": "oracle",
+               "sample": f"fp64 NumPy AdamW oracle on {n} elements ({reps} steps), scaled by element count",
+               "seconds_per_step": sec}
+    out = {"metric": "AdamW step over the 8B-style model's embeddings, head and norms (HBM GB/s)",
+           "value": gbs, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"AdamW leg: embedding and head {synth.ADAMW_VOCAB}x{synth.ADAMW_HIDDEN} bf16, "
+                                  f"65 RMSNorm weights of {synth.ADAMW_HIDDEN}", "elements": elems,
+                      "bytes_per_element": ADAMW_BYTES, "parallelism": "single GPU"},
+           "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "adamw_kernel"},
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, grads_host, budget_s=20.0):
     """Time the fp64 oracle on a bounded sample of the workload's matrices
     (smallest first until about `budget_s` of work), scaled by NS flops to
@@ -111,6 +185,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--part", default="muon", choices=["muon", "adamw"],
+                    help="muon: the Muon step of --config (default); adamw: the AdamW step over the 8B-style "
+                         "model's embeddings, head and norms")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy before the warmup, so that profiler byte counters "
@@ -120,6 +197,10 @@ def main():
         print(f"bench.py measures one GPU only: the Muon step here runs on a single MI355X with no "
               f"collectives (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
+
+    if args.part == "adamw":
+        bench_adamw(args)
+        return
 
     import numpy as np
     import torch

@@ -25,6 +25,9 @@
  *   [PREPRINT] "SOAP, Muon, and Beyond: Pushing LLM Pretraining Scales"
  *            (epsilon 1e-7 for Muon).
  *
+ * Beside the Muon step, muon_adamw updates the parameters Muon leaves to
+ * AdamW ([GUIDE] sections 5 and 6).
+ *
  * Conventions shared by every entry point:
  *   - All matrix memory and all workspaces are caller-owned DEVICE memory.
  *     The library never allocates, frees or synchronizes; every call only
@@ -188,6 +191,51 @@ muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins,
 muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho,
                          float lr, float weight_decay, int32_t mode,
                          float coeff, void* stream);
+
+/*
+ * AdamW for the parameters Muon does not take (embeddings, output head, norms,
+ * biases), many tensors in one launch ([GUIDE] section 5 "Adam, line by
+ * line" and section 6, decoupled weight decay):
+ *   m <- beta1*m + (1-beta1)*g;   v <- beta2*v + (1-beta2)*g^2
+ *   m_hat = m / (1 - beta1^t);    v_hat = v / (1 - beta2^t)
+ *   theta <- (1 - lr*weight_decay)*theta - lr * m_hat / (sqrt(v_hat) + eps)
+ * Epsilon is added outside the square root.  Arithmetic is fp32 (bias
+ * corrections in double on the host); a BF16 theta is rounded once to
+ * nearest even.
+ *
+ * Every tensor is a contiguous run of numels[i] elements (any shape),
+ * 16-byte aligned.  The tensor list lives in DEVICE memory and is only
+ * read by the kernel: params[i] (theta, in/out, param_dtype), grads[i]
+ * (read, grad_dtype), exp_avg[i] and exp_avg_sq[i] (F32 state, in/out,
+ * zero before step 1), numels[i], and chunk_offsets[0..count] = prefix sums
+ * of ceil(numels[i] / MUON_ADAMW_CHUNK) with chunk_offsets[0] = 0;
+ * total_chunks = chunk_offsets[count] is passed by value (the library does
+ * not read device memory on the host).  Each kernel access is bounded by
+ * its tensor's numel, so an inconsistent chunk table leaves elements
+ * un-updated but never reads or writes outside a tensor.
+ *
+ * step : t >= 1, the number of this update for every tensor in the list
+ *        (one list per parameter group; a tensor whose gradient is absent
+ *        is left out of the call, [GUIDE] 6.2).
+ * beta1, beta2 in [0, 1); eps finite >= 0; lr, weight_decay finite.
+ */
+#define MUON_ADAMW_CHUNK 4096
+
+typedef struct muon_tensor_list {
+  int64_t count;                 /* tensors, >= 1 */
+  int64_t total_chunks;          /* chunk_offsets[count]; 1 .. 2^31-1 */
+  void* const* params;           /* device array [count] */
+  const void* const* grads;      /* device array [count] */
+  float* const* exp_avg;         /* device array [count] */
+  float* const* exp_avg_sq;      /* device array [count] */
+  const int64_t* numels;         /* device array [count] */
+  const int64_t* chunk_offsets;  /* device array [count + 1] */
+  int32_t param_dtype;           /* muon_dtype_t of every theta */
+  int32_t grad_dtype;            /* muon_dtype_t of every gradient */
+} muon_tensor_list_t;
+
+muon_status_t muon_adamw(const muon_tensor_list_t* tensors, int64_t step, float lr, float beta1,
+                         float beta2, float eps, float weight_decay, void* stream);
 
 /* Static text for a status code. */
 const char* muon_status_string(muon_status_t status);

@@ -25,7 +25,9 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
 
 EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
             "muon_momentum", "muon_orthogonalize_workspace", "muon_orthogonalize",
-            "muon_orthogonalize_grouped_workspace", "muon_orthogonalize_grouped", "muon_apply")
+            "muon_orthogonalize_grouped_workspace", "muon_orthogonalize_grouped", "muon_apply", "muon_adamw")
+
+ADAMW_CHUNK = 4096  # MUON_ADAMW_CHUNK
 
 
 class MuonError(RuntimeError):
@@ -38,6 +40,13 @@ class MuonBatch(ctypes.Structure):
     _fields_ = [("ptrs", ctypes.c_void_p), ("base", ctypes.c_void_p), ("stride", ctypes.c_int64),
                 ("count", ctypes.c_int64), ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("ld", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class MuonTensorList(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_int64), ("total_chunks", ctypes.c_int64), ("params", ctypes.c_void_p),
+                ("grads", ctypes.c_void_p), ("exp_avg", ctypes.c_void_p), ("exp_avg_sq", ctypes.c_void_p),
+                ("numels", ctypes.c_void_p), ("chunk_offsets", ctypes.c_void_p), ("param_dtype", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32)]
 
 
 _lib = None
@@ -66,6 +75,7 @@ def load() -> ctypes.CDLL:
         "muon_orthogonalize_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(vp), P, ctypes.c_int,
                                                       f32, f32, f32, f32, i32, vp, sz, vp]),
         "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
+        "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -137,3 +147,9 @@ def muon_apply(weight: MuonBatch, ortho: MuonBatch, lr: float, weight_decay: flo
                stream: int) -> None:
     st = load().muon_apply(_ref(weight), _ref(ortho), lr, weight_decay, mode, coeff, stream)
     _check(st, "muon_apply")
+
+
+def muon_adamw(tensors: MuonTensorList, step: int, lr: float, beta1: float, beta2: float, eps: float,
+               weight_decay: float, stream: int) -> None:
+    st = load().muon_adamw(ctypes.byref(tensors), step, lr, beta1, beta2, eps, weight_decay, stream)
+    _check(st, "muon_adamw")

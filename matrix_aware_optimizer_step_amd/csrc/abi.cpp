@@ -38,6 +38,7 @@ muon_status_t ok() {
 }
 
 constexpr int64_t kAlign = 256;
+static_assert(kAdamWChunk == MUON_ADAMW_CHUNK, "chunk size of the AdamW tensor list");
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
@@ -394,6 +395,45 @@ extern "C" {
 int muon_abi_version(void) { return MUON355_ABI_VERSION; }
 
 const char* muon_last_error(void) { return g_last_error; }
+
+muon_status_t muon_adamw(const muon_tensor_list_t* t, int64_t step, float lr, float beta1, float beta2,
+                         float eps, float weight_decay, void* stream) {
+  if (!t) return fail(MUON_ERR_INVALID_VALUE, "tensor list is NULL");
+  if (t->count < 1) return fail(MUON_ERR_INVALID_VALUE, "count %lld < 1", (long long)t->count);
+  if (t->total_chunks < 1 || t->total_chunks > kMaxElems)
+    return fail(MUON_ERR_INVALID_VALUE, "total_chunks %lld outside [1, 2^31-1]", (long long)t->total_chunks);
+  if (!t->params || !t->grads || !t->exp_avg || !t->exp_avg_sq || !t->numels || !t->chunk_offsets)
+    return fail(MUON_ERR_INVALID_VALUE, "a device array of the tensor list is NULL");
+  if ((t->param_dtype != MUON_F32 && t->param_dtype != MUON_BF16) ||
+      (t->grad_dtype != MUON_F32 && t->grad_dtype != MUON_BF16))
+    return fail(MUON_ERR_INVALID_VALUE, "param_dtype/grad_dtype must be MUON_F32 or MUON_BF16");
+  if (step < 1) return fail(MUON_ERR_INVALID_VALUE, "step %lld < 1", (long long)step);
+  if (!(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f))
+    return fail(MUON_ERR_INVALID_VALUE, "betas must lie in [0, 1)");
+  if (!finite(eps) || eps < 0.0f) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  if (!finite(lr) || !finite(weight_decay)) return fail(MUON_ERR_INVALID_VALUE, "lr and weight_decay must be finite");
+  AdamWArgs a;
+  a.count = t->count;
+  a.params = t->params;
+  a.grads = t->grads;
+  a.exp_avg = t->exp_avg;
+  a.exp_avg_sq = t->exp_avg_sq;
+  a.numels = t->numels;
+  a.chunk_offsets = t->chunk_offsets;
+  a.param_bf16 = t->param_dtype == MUON_BF16;
+  a.grad_bf16 = t->grad_dtype == MUON_BF16;
+  a.beta1 = beta1;
+  a.beta2 = beta2;
+  a.eps = eps;
+  // bias corrections in double: 1 - beta^t loses nothing for small t
+  a.c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
+  a.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+  a.lr = lr;
+  a.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
+  const hipError_t e = launch_adamw(a, t->total_chunks, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return launch_status(e, "adamw");
+  return ok();
+}
 
 const char* muon_status_string(muon_status_t s) {
   switch (s) {

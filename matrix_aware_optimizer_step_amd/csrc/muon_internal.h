@@ -147,4 +147,23 @@ struct CopyOutArgs {
 };
 hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t stream);
 
+// ------------------------------------------------------------ AdamW
+
+constexpr int64_t kAdamWChunk = 4096;  // elements per workgroup; MUON_ADAMW_CHUNK
+
+struct AdamWArgs {
+  int64_t count;                  // tensors
+  void* const* params;            // device arrays of `count` pointers
+  const void* const* grads;
+  float* const* exp_avg;
+  float* const* exp_avg_sq;
+  const int64_t* numels;          // device [count]
+  const int64_t* chunk_offsets;   // device [count + 1]
+  int32_t param_bf16, grad_bf16;
+  float beta1, beta2, eps;
+  float c1, c2;                   // 1/(1-beta1^t), 1/(1-beta2^t)
+  float lr, decay;                // decay = 1 - lr*wd
+};
+hipError_t launch_adamw(const AdamWArgs& a, int64_t total_chunks, hipStream_t stream);
+
 }  // namespace muon

@@ -211,3 +211,114 @@ class MuonStep:
             L.muon_apply(w.desc, o.desc, self.lr, self.weight_decay, self.mode, self.coeff, s)
         if events is not None:
             events[3].record(st)
+
+
+# ---------------------------------------------------------------- AdamW
+
+class AdamW:
+    """AdamW over one parameter group, every tensor in one launch.
+
+    The parameters Muon does not take (embeddings, output head, norms,
+    biases) follow AdamW ("LLM Optimizers: From SGD and AdamW to SOAP, Muon,
+    and Scalable Training", sections 5 and 6).  ``params`` and ``grads`` are
+    lists of contiguous tensors of matching shapes, one dtype per list
+    (bfloat16 or float32); the fp32 moments, the device tables of pointers,
+    sizes and chunk offsets are built here once, so ``step()`` only enqueues
+    ``muon_adamw``.  The gradients are read from the given tensors' storage
+    at every step: copy new gradients into them.
+    """
+
+    def __init__(self, params, grads, *, lr: float = 1e-3, betas=(0.9, 0.999), eps: float = 1e-8,
+                 weight_decay: float = 0.0):
+        params, grads = list(params), list(grads)
+        if not params or len(params) != len(grads):
+            raise ValueError("need matching, non-empty lists of parameters and gradients")
+        dev = params[0].device
+        for p, g in zip(params, grads):
+            if p.shape != g.shape:
+                raise ValueError("parameter and gradient shapes differ")
+            if p.is_sparse or g.is_sparse:
+                raise RuntimeError("AdamW here takes dense gradients only")
+            if not (p.is_contiguous() and g.is_contiguous()):
+                raise ValueError("parameters and gradients must be contiguous")
+            if p.device != dev or g.device != dev:
+                raise ValueError("all tensors must be on one device")
+            if p.dtype != params[0].dtype or g.dtype != grads[0].dtype:
+                raise ValueError("one dtype per list")
+        self.params, self.grads = params, grads
+        self.exp_avg = [torch.zeros(p.shape, dtype=torch.float32, device=dev) for p in params]
+        self.exp_avg_sq = [torch.zeros(p.shape, dtype=torch.float32, device=dev) for p in params]
+        self.lr, self.betas, self.eps, self.weight_decay = lr, tuple(betas), eps, weight_decay
+        self.t = 0
+
+        def table(ts):
+            return torch.tensor([t.data_ptr() for t in ts], dtype=torch.int64, device=dev)
+
+        numels = [p.numel() for p in params]
+        chunks = [0]
+        for n in numels:
+            chunks.append(chunks[-1] + (n + L.ADAMW_CHUNK - 1) // L.ADAMW_CHUNK)
+        self._tables = [table(params), table(grads), table(self.exp_avg), table(self.exp_avg_sq),
+                        torch.tensor(numels, dtype=torch.int64, device=dev),
+                        torch.tensor(chunks, dtype=torch.int64, device=dev)]
+        self.desc = L.MuonTensorList(len(params), chunks[-1], *[t.data_ptr() for t in self._tables],
+                                     dtype_code(params[0]), dtype_code(grads[0]))
+        self.elements = sum(numels)
+
+    def step(self, stream=None) -> None:
+        self.t += 1
+        b1, b2 = self.betas
+        L.muon_adamw(self.desc, self.t, self.lr, b1, b2, self.eps, self.weight_decay, _stream(stream))
+
+
+# ------------------------------------------------------ routing helper
+
+DEFAULT_ADAMW_NAMES = ("embed", "wte", "wpe", "lm_head", "head", "output")
+
+
+def is_muon_param(name: str, p: torch.Tensor, adamw_names=DEFAULT_ADAMW_NAMES) -> bool:
+    """Muon takes the 2-D hidden weight matrices; embeddings, the output head
+    and every tensor that is not 2-D (norms, biases) stay with AdamW."""
+    return p.dim() == 2 and not any(k in name.lower() for k in adamw_names)
+
+
+class OptimizerStep:
+    """One optimizer step for a whole model in one call.
+
+    ``named_params`` is a list of ``(name, parameter, gradient)`` triples.
+    2-D hidden matrices go to Muon (one ``MuonStep``, same-shape matrices
+    batched through pointer arrays); the rest go to AdamW, in a decayed group
+    for tensors of two or more dimensions (embeddings, head) and an undecayed
+    one for norms and biases, each split by dtype.  ``routing`` records the
+    name of every parameter and where it went.
+    """
+
+    def __init__(self, named_params, *, compute: int = L.MUON_BF16, muon_lr: float = 3e-4,
+                 muon_weight_decay: float = 0.1, adam_lr: float = 3e-4, adam_betas=(0.9, 0.999),
+                 adam_eps: float = 1e-8, adam_weight_decay: float = 0.1, is_muon=is_muon_param):
+        shapes = {}
+        adam = {}
+        self.routing = {}
+        for name, p, g in named_params:
+            if g is None:
+                continue  # no gradient: the parameter takes no part in this step
+            if is_muon(name, p):
+                shapes.setdefault((tuple(p.shape), p.dtype, g.dtype), []).append((p, g))
+                self.routing[name] = "muon"
+            else:
+                decay = p.dim() >= 2
+                adam.setdefault((decay, p.dtype, g.dtype), []).append((p, g))
+                self.routing[name] = "adamw" if decay else "adamw_no_decay"
+        self.muon = None
+        if shapes:
+            groups = [([p for p, _ in v], [g for _, g in v]) for v in shapes.values()]
+            self.muon = MuonStep(groups, compute=compute, lr=muon_lr, weight_decay=muon_weight_decay)
+        self.adamw = [AdamW([p for p, _ in v], [g for _, g in v], lr=adam_lr, betas=adam_betas, eps=adam_eps,
+                            weight_decay=adam_weight_decay if decay else 0.0)
+                      for (decay, _, _), v in adam.items()]
+
+    def step(self, stream=None) -> None:
+        if self.muon is not None:
+            self.muon.step(stream=stream)
+        for group in self.adamw:
+            group.step(stream=stream)

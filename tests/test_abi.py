@@ -132,3 +132,30 @@ def test_workspace_queries():
     g = L.muon_orthogonalize_grouped_workspace([2, 1], [4096, 1024], [4096, 4096], L.MUON_BF16)
     assert g >= L.muon_orthogonalize_workspace(2, 4096, 4096, 1) + L.muon_orthogonalize_workspace(1, 1024, 4096, 1) - 4096
     assert L.muon_orthogonalize_workspace(1, 65536, 65536, 1) == 0
+
+
+def adamw_list(**kw):
+    f = dict(count=2, total_chunks=3, params=FAKE, grads=FAKE, exp_avg=FAKE, exp_avg_sq=FAKE, numels=FAKE,
+             chunk_offsets=FAKE, param_dtype=L.MUON_BF16, grad_dtype=L.MUON_BF16)
+    f.update(kw)
+    return L.MuonTensorList(f["count"], f["total_chunks"], f["params"], f["grads"], f["exp_avg"], f["exp_avg_sq"],
+                            f["numels"], f["chunk_offsets"], f["param_dtype"], f["grad_dtype"])
+
+
+@pytest.mark.parametrize("kw", [dict(count=0), dict(total_chunks=0), dict(total_chunks=1 << 31), dict(params=0),
+                                dict(grads=0), dict(exp_avg=0), dict(exp_avg_sq=0), dict(numels=0),
+                                dict(chunk_offsets=0), dict(param_dtype=7), dict(grad_dtype=-1)])
+def test_adamw_rejects_bad_tensor_lists(kw):
+    lib = L.load()
+    assert lib.muon_adamw(ctypes.byref(adamw_list(**kw)), 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 1
+    assert lib.muon_last_error()
+
+
+@pytest.mark.parametrize("step,lr,b1,b2,eps,wd", [(0, 1e-3, 0.9, 0.999, 1e-8, 0.0), (1, 1e-3, 1.0, 0.999, 1e-8, 0.0),
+                                                  (1, 1e-3, 0.9, -0.1, 1e-8, 0.0), (1, 1e-3, 0.9, 0.999, -1e-8, 0.0),
+                                                  (1, float("inf"), 0.9, 0.999, 1e-8, 0.0),
+                                                  (1, 1e-3, 0.9, 0.999, 1e-8, float("nan"))])
+def test_adamw_rejects_bad_hyperparameters(step, lr, b1, b2, eps, wd):
+    lib = L.load()
+    assert lib.muon_adamw(ctypes.byref(adamw_list()), step, lr, b1, b2, eps, wd, None) == 1
+    assert lib.muon_adamw(None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 1

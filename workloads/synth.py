@@ -175,3 +175,36 @@ def initial_weights(config: Config, device="cpu", dtype=None, std: float = 0.02,
     g = _gen(config.index * 10 ** 6 + seed * 100003, device)
     return [(std * torch.randn(grp.count, grp.rows, grp.cols, generator=g, device=device,
                                dtype=torch.float32)).to(dtype) for grp in config.groups]
+
+
+# ---------------------------------------------------------------- AdamW
+
+ADAMW_VOCAB = 128000  # the pages give no vocabulary size for the 8B-style model
+ADAMW_HIDDEN = 4096
+
+
+def adamw_workload(layers: int = 32):
+    """(name, shape) of the 8B-style model's parameters that AdamW takes:
+    token embedding and output head (vocabulary x hidden) and the RMSNorm
+    weights (two per layer and a final one)."""
+    out = [("embed_tokens.weight", (ADAMW_VOCAB, ADAMW_HIDDEN)), ("lm_head.weight", (ADAMW_VOCAB, ADAMW_HIDDEN))]
+    for i in range(layers):
+        out.append((f"layers.{i}.input_norm.weight", (ADAMW_HIDDEN,)))
+        out.append((f"layers.{i}.post_norm.weight", (ADAMW_HIDDEN,)))
+    out.append(("final_norm.weight", (ADAMW_HIDDEN,)))
+    return out
+
+
+def adamw_tensors(shapes, step: int = 1, device="cpu", dtype=torch.bfloat16, std: float = 0.02, seed: int = 9):
+    """Seeded parameters (N(0, std^2); norm weights start at 1) and step-``step``
+    gradients (N(0,1)) for the given (name, shape) list."""
+    params, grads = [], []
+    for i, (name, shape) in enumerate(shapes):
+        g = _gen(seed * 10 ** 6 + i * 10 + step, device)
+        grads.append(torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(dtype))
+        if len(shape) == 1:
+            params.append(torch.ones(*shape, device=device, dtype=dtype))
+        else:
+            gp = _gen(seed * 10 ** 6 + i * 10, device)
+            params.append((std * torch.randn(*shape, generator=gp, device=device, dtype=torch.float32)).to(dtype))
+    return params, grads
