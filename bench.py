@@ -45,10 +45,17 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def make_stepper(mx, weights, grads):
+# Coefficient sets of the pages' Newton-Schulz iterations and their usual step counts: Jordan's quintic
+# (5 steps), the convergent "Track-3" quintic (12 steps) and the classical cubic.
+COEFFS = {"quintic": ((3.4445, -4.7750, 2.0315), 5), "track3": ((2.0, -1.5, 0.5), 12), "cubic": ((1.5, -0.5, 0.0), 5)}
+
+
+def make_stepper(mx, weights, grads, coeffs="quintic", steps=None):
     """The optimizer step this benchmark times: every group of the workload
     in one MuonStep (grouped Newton-Schulz launches, bf16 MFMA)."""
-    return mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD)
+    abc, k = COEFFS[coeffs]
+    return mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD, coeffs=abc,
+                       steps=k if steps is None else steps)
 
 
 def measured_traffic(cfg_index):
@@ -84,6 +91,18 @@ def make_adamw_step(mx, names, params, grads):
     return opt
 
 
+def calibration_copy(dev):
+    """One 1 GiB device-to-device copy, so that profiler byte counters can be
+    scaled against a kernel of known traffic."""
+    import torch
+    src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    log("[bench] 1 GiB calibration copy done")
+
+
 def bench_adamw(args):
     """Time the AdamW step over the 8B-style model's embeddings, head and norms;
     print one JSON line against the HBM roofline."""
@@ -103,6 +122,8 @@ def bench_adamw(args):
     opt = make_adamw_step(mx, names, params, grads)
     elems = sum(g.elements for g in opt.adamw)
     log(f"[bench] AdamW over {len(shapes)} tensors, {elems / 1e6:.1f} M elements")
+    if args.copy_calibration:
+        calibration_copy(dev)
     for _ in range(args.warmup):
         opt.step()
     torch.cuda.synchronize()
@@ -145,7 +166,7 @@ def bench_adamw(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(cfg, grads_host, budget_s=20.0):
+def cpu_baseline(cfg, grads_host, budget_s=20.0, coeffs=COEFFS["quintic"][0], steps=5):
     """Time the fp64 oracle on a bounded sample of the workload's matrices
     (smallest first until about `budget_s` of work), scaled by NS flops to
     the whole workload."""
@@ -156,7 +177,7 @@ def cpu_baseline(cfg, grads_host, budget_s=20.0):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    total_flops = sum(ns_flops(g.count, g.rows, g.cols)[0] for g in cfg.groups)
+    total_flops = sum(ns_flops(g.count, g.rows, g.cols, steps)[0] for g in cfg.groups)
     order = sorted(range(len(cfg.groups)), key=lambda i: cfg.groups[i].rows * cfg.groups[i].cols)
     spent, done_flops, names = 0.0, 0, []
     for gi in order:
@@ -165,10 +186,10 @@ def cpu_baseline(cfg, grads_host, budget_s=20.0):
         W = np.zeros((g.rows, g.cols))
         M = np.zeros((g.rows, g.cols))
         t0 = time.perf_counter()
-        O.muon_step(W, M, G, lr=LR, weight_decay=WD)
+        O.muon_step(W, M, G, lr=LR, weight_decay=WD, coeffs=coeffs, steps=steps)
         dt = time.perf_counter() - t0
         spent += dt
-        done_flops += ns_flops(1, g.rows, g.cols)[0]
+        done_flops += ns_flops(1, g.rows, g.cols, steps)[0]
         names.append(f"{g.name} {g.rows}x{g.cols}")
         if spent > budget_s * 0.5:
             break
@@ -185,6 +206,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--coeffs", default="quintic", choices=sorted(COEFFS),
+                    help="Newton-Schulz coefficient set (quintic: the Muon default)")
+    ap.add_argument("--ns-steps", type=int, default=None, help="Newton-Schulz steps (default: the set's usual count)")
     ap.add_argument("--part", default="muon", choices=["muon", "adamw"],
                     help="muon: the Muon step of --config (default); adamw: the AdamW step over the 8B-style "
                          "model's embeddings, head and norms")
@@ -221,14 +245,10 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
 
-    stepper = make_stepper(mx, weights, grads)
+    stepper = make_stepper(mx, weights, grads, args.coeffs, args.ns_steps)
+    ns_steps = stepper.steps
     if args.copy_calibration:
-        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
-        log("[bench] 1 GiB calibration copy done")
+        calibration_copy(dev)
 
     def one_step(ev=None):
         stepper.step(events=ev)
@@ -254,7 +274,7 @@ def main():
 
     algo, nominal = 0, 0
     for g in cfg.groups:
-        fa, fn = ns_flops(g.count, g.rows, g.cols)
+        fa, fn = ns_flops(g.count, g.rows, g.cols, ns_steps)
         algo += fa
         nominal += fn
     ns_tflops = algo / (t_ns * 1e-3) / 1e12
@@ -269,7 +289,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a bounded sample (host cores)")
         host = [g[0].float().cpu().numpy() for g in grads]
-        cpu = cpu_baseline(cfg, host)
+        cpu = cpu_baseline(cfg, host, coeffs=stepper.coeffs, steps=ns_steps)
         log(f"[bench] oracle: {cpu['seconds_per_step']:.1f} s per step (extrapolated)")
 
     shapes = {g.name: [g.count, g.rows, g.cols] for g in cfg.groups}
@@ -287,7 +307,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"config {cfg.index}: {cfg.name}", "matrices": cfg.matrices,
-                   "shapes": shapes, "gradients": cfg.kind, "ns_steps": 5, "compute": "bf16 MFMA, fp32 accumulate",
+                   "shapes": shapes, "gradients": cfg.kind, "ns_steps": ns_steps, "coefficients": args.coeffs, "compute": "bf16 MFMA, fp32 accumulate",
                    "parallelism": "single GPU"},
         "newton_schulz": {"tflops_algorithmic": ns_tflops, "tflops_nominal_4m2n_2m3": ns_tflops_nominal,
                           "frac_bf16_peak": ns_tflops / PEAK_BF16_TFLOPS, "ms": t_ns,

@@ -205,6 +205,29 @@ def test_ns_ill_conditioned(mx, compute, tol, kind, rows, cols):
 
 
 @pytest.mark.parametrize("compute,tol", [(0, TOL_F32), (1, TOL_BF16)])
+@pytest.mark.parametrize("coeffs,steps", [(O.TRACK3, 12), (O.CUBIC, 5), (O.CUBIC, 10)])
+@pytest.mark.parametrize("kind,rows,cols", [("gauss", 300, 700), ("gauss", 700, 300), ("kappa", 128, 4096)])
+def test_ns_other_coefficient_sets(mx, compute, tol, coeffs, steps, kind, rows, cols):
+    """The pages' other iterations on the same kernels: the convergent
+    'Track-3' quintic run for 12 steps and the classical cubic.
+
+    The fp32 bound is the Muon iteration's 1e-5 scaled by how much more this
+    iteration amplifies rounding: in the directions of small singular values
+    each step multiplies a perturbation by the map's slope at zero, a, so by
+    a^K over K steps, against 3.4445^5 for Muon's five quintic steps
+    (Track-3 x 12: 2^12 / 3.4445^5 = 8.5; the cubic stays at 1e-5)."""
+    if compute == 0:
+        tol = TOL_F32 * max(1.0, coeffs[0] ** steps / O.QUINTIC[0] ** 5)
+    if kind == "gauss":
+        N = randn((1, rows, cols), rows + cols, torch.float32)
+    else:
+        N = ill_conditioned(kind, rows, cols).unsqueeze(0).cuda()
+    out = run_ns(mx, N, compute, steps=steps, coeffs=coeffs, out_dtype=torch.float32)
+    want = O.newton_schulz(f64(N[0]), steps, coeffs)
+    assert rel(f64(out[0]), want) <= tol
+
+
+@pytest.mark.parametrize("compute,tol", [(0, TOL_F32), (1, TOL_BF16)])
 @pytest.mark.parametrize("coeffs", [(1.0, 0.0, 0.0), (0.0, 1.0, 0.0), (0.0, 0.0, 1.0), (0.5, -0.25, 0.125)])
 @pytest.mark.parametrize("shape", [(300, 700), (700, 300), (96, 520)])
 def test_ns_single_stage(mx, compute, tol, coeffs, shape):
