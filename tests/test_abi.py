@@ -159,3 +159,17 @@ def test_adamw_rejects_bad_hyperparameters(step, lr, b1, b2, eps, wd):
     lib = L.load()
     assert lib.muon_adamw(ctypes.byref(adamw_list()), step, lr, b1, b2, eps, wd, None) == 1
     assert lib.muon_adamw(None, 1, 1e-3, 0.9, 0.999, 1e-8, 0.0, None) == 1
+
+
+def test_padded_shape_limit():
+    """The Newton-Schulz shape padded to its tile may hold at most 2^30
+    elements: the workspace query returns 0 above it and the call reports
+    MUON_ERR_UNSUPPORTED before launching anything."""
+    lib = L.load()
+    assert L.muon_orthogonalize_workspace(1, 16384, 65536, L.MUON_BF16) > 0          # exactly 2^30
+    assert L.muon_orthogonalize_workspace(1, 16384, 65537, L.MUON_BF16) == 0         # padded past 2^30
+    assert L.muon_orthogonalize_workspace(1, 65537, 16384, L.MUON_F32) == 0          # tall, same rule
+    d = desc(rows=16384, cols=65537, dtype=L.MUON_BF16)
+    st = lib.muon_orthogonalize(ctypes.byref(d), None, ctypes.byref(d), 5, 3.4445, -4.775, 2.0315, 1e-7,
+                                L.MUON_BF16, FAKE, 1 << 40, None)
+    assert st == 2 and b"2^30" in lib.muon_last_error()
