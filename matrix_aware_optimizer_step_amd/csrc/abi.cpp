@@ -281,6 +281,8 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     pa.s_mat = pa.t_mat = mn * es;
     pa.Lo = compute == MUON_BF16 ? reinterpret_cast<uint16_t*>(ws + p.xlo) : nullptr;
     pa.lo_mat = mn;
+    pa.lo_bm = p.tile;
+    pa.lo_tiles_n = p.Np / p.tile;
     if ((e = launch_pack(pa, p.count, stream)) != hipSuccess) return launch_status(e, "pack");
   }
 

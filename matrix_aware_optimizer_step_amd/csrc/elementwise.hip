@@ -301,9 +301,31 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     if (r < a.rows && c < a.cols) v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
     tile[rr][tx] = v;
     store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
-    if (a.Lo && !a.tall) a.Lo[mat * a.lo_mat + static_cast<int64_t>(r) * a.Pc + c] = bf16_residual(v);
   }
   __syncthreads();
+  if (a.Lo) {
+    // The residual of X in the update kernel's accumulator order: this 64 x 64
+    // tile of X is four consecutive 32x32 blocks of one wave there, one
+    // contiguous run of 4096 values.  Thread t assembles lane (t % 64) of
+    // block (t / 64): its 16 values, rows 8*(r/4) + 4*half + r%4 of the
+    // block, leave as two 16-byte stores.
+    const uint32_t i0 = a.tall ? c0 : r0;  // top-left corner of this tile in X
+    const uint32_t j0 = a.tall ? r0 : c0;
+    uint16_t* run = a.Lo + mat * a.lo_mat + lo_index(i0, j0, a.lo_bm, a.lo_tiles_n);
+    const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int hf = lane >> 5, jl = (b & 1) * 32 + (lane & 31);
+    uint32_t w[8];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int il = (b >> 1) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+      const float v = a.tall ? tile[jl][il] : tile[il][jl];  // X[i][j] = S[j][i] when tall
+      const uint32_t lo = bf16_residual(v);
+      w[r >> 1] = (r & 1) ? (w[r >> 1] | (lo << 16)) : lo;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(run + (b * 64 + lane) * 16);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
   // write rows of T = columns of the tile
   char* T = a.T + mat * a.t_mat;
   for (int cc = ty; cc < kTile; cc += 4) {
@@ -311,7 +333,6 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     const int r = r0 + tx;
     const float v = tile[tx][cc];
     store1(T + (static_cast<int64_t>(c) * a.Pr + r) * esz, a.compute, v);
-    if (a.Lo && a.tall) a.Lo[mat * a.lo_mat + static_cast<int64_t>(c) * a.Pr + r] = bf16_residual(v);
   }
 }
 

@@ -49,10 +49,12 @@ struct GemmGroup {
   // residual), about 16 significant bits together.
   const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL, fp32 compute: X
   int32_t pad0_;
-  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X (the
-                                                 // high part is Q^T, added from the operand tiles)
+  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X in the
+                                                 // lo_index() layout (the high part is Q^T, added
+                                                 // from the operand tiles)
   int32_t pad5_;
-  char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low part
+  char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low
+                                                 // part (lo_index() layout, in place)
   int32_t pad1_;
   char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE, bf16 compute: high part of the next X
   int32_t pad2_;
@@ -64,6 +66,26 @@ struct GemmGroup {
   int32_t ms, ns;                // true (unpadded) Newton-Schulz shape
   int32_t pad4_;
 };
+
+// Layout of the bf16 low part of X (bf16 compute).  Only the update kernel
+// reads and writes it (plus the pack kernel, which writes its first value),
+// so it is kept in the update kernel's accumulator order: a bm x bm output
+// tile is split over 2 x (bm/64) waves of (bm/2) x 64 elements, each wave's
+// sub-tile into 32x32 MFMA blocks, and each block into 64 lanes x 16 values
+// (lane = 32*half + column, value r <-> row 8*(r/4) + 4*half + r%4).  One
+// lane's 16 values of a block are 32 contiguous bytes.  Element (i, j) of
+// the padded Newton-Schulz matrix with `tiles_n` tile columns lives at:
+__host__ __device__ inline uint32_t lo_index(uint32_t i, uint32_t j, uint32_t bm, uint32_t tiles_n) {
+  const uint32_t wgn = bm / 64, wtm = bm / 2, nb = (wtm / 32) * 2;
+  const uint32_t ti = i / bm, tj = j / bm, il = i % bm, jl = j % bm;
+  const uint32_t wave = (il / wtm) * wgn + jl / 64;
+  const uint32_t ii = il % wtm, jj = jl % 64;
+  const uint32_t blk = (ii / 32) * 2 + jj / 32;
+  const uint32_t rb = ii % 32;
+  const uint32_t lane = ((rb % 8) / 4) * 32 + jj % 32;
+  const uint32_t r = 4 * (rb / 8) + rb % 4;
+  return (((ti * tiles_n + tj) * (2 * wgn) + wave) * nb + blk) * 1024u + lane * 16u + r;
+}
 
 struct GemmLaunch {
   int32_t ngroups;
@@ -132,7 +154,8 @@ struct PackArgs {
   int32_t tall;
   char* S; int64_t s_mat;  // bytes per matrix
   char* T; int64_t t_mat;
-  uint16_t* Lo; int64_t lo_mat;  // elements per matrix
+  uint16_t* Lo; int64_t lo_mat;  // elements per matrix, in the lo_index() layout
+  int32_t lo_bm, lo_tiles_n;     // update tile size and tile columns of X
 };
 hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream);
 

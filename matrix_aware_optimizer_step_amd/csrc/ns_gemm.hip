@@ -490,6 +490,24 @@ void ns_gemm_kernel(const GemmLaunch L) {
   constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
   constexpr bool kHasE = (EPI != EPI_GRAM);
   float ebuf[kHasE ? PF + 1 : 1][16];
+  // bf16 update: the low part of X is stored in this kernel's accumulator
+  // order (lo_index()), so each lane's 16 values of a block are 32 contiguous
+  // bytes; all blocks are loaded here in one round of 16-byte loads and the
+  // new low part leaves the same way.
+  constexpr bool kLoNative = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+  static_assert(!kLoNative || (BN == BM && WGM == 2 && WGN == BM / 64 && WTN == 64),
+                "the low part's layout assumes this tile shape (see lo_index)");
+  uint4 lo_pre[kLoNative ? NB : 1][2];
+  const uint32_t lo_off =
+      ((static_cast<uint32_t>(ti * G.tiles_n + tj) * NW + wave) * NB) * 1024u + static_cast<uint32_t>(lane) * 16u;
+  if constexpr (kLoNative) {
+    const char* El = G.E1 + mat * G.e1_mat;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      lo_pre[b][0] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u);
+      lo_pre[b][1] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u + 16u);
+    }
+  }
   auto eload = [&](int blk, float* e) {
     const int fi = blk / FN, fj = blk % FN;
     const int j = j_base + fj * 32;
@@ -506,13 +524,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
       const char* Em = G.E0 + mat * G.e0_mat;
       const uint32_t lde = G.lde0;
       if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
-        const char* El = G.E1 + mat * G.e1_mat;
-        const uint32_t ldl = G.lde1;
+        const uint32_t w[8] = {lo_pre[blk][0].x, lo_pre[blk][0].y, lo_pre[blk][0].z, lo_pre[blk][0].w,
+                               lo_pre[blk][1].x, lo_pre[blk][1].y, lo_pre[blk][1].z, lo_pre[blk][1].w};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          e[r] = bf16_to_f32(*reinterpret_cast<const uint16_t*>(El + (i * ldl + j) * 2u));
-        }
+        for (int r = 0; r < 16; ++r) e[r] = bf16_to_f32(static_cast<uint16_t>(w[r >> 1] >> (16 * (r & 1))));
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -555,13 +570,18 @@ void ns_gemm_kernel(const GemmLaunch L) {
       if constexpr (sizeof(T) == 2) {
         char* O1m = G.O1 + mat * G.o1_mat;  // bf16 high part of X'
         const uint32_t ldo1 = G.ldo1;
+        uint32_t lw[8];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
           const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
           *reinterpret_cast<uint16_t*>(O1m + (i * ldo1 + j) * 2u) = hi;
-          *reinterpret_cast<uint16_t*>(O0m + (i * ldo0 + j) * 2u) = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
+          const uint32_t lo = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
+          lw[r >> 1] = (r & 1) ? (lw[r >> 1] | (lo << 16)) : lo;
         }
+        uint4* Ld = reinterpret_cast<uint4*>(O0m + (lo_off + blk * 1024u) * 2u);
+        Ld[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+        Ld[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
