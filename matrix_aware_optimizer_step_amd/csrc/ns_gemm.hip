@@ -568,14 +568,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
       char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
       const uint32_t ldo0 = G.ldo0;
       if constexpr (sizeof(T) == 2) {
-        char* O1m = G.O1 + mat * G.o1_mat;  // bf16 high part of X'
-        const uint32_t ldo1 = G.ldo1;
+        // the high part leaves from the LDS staging below, as row segments
         uint32_t lw[8];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
           const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
-          *reinterpret_cast<uint16_t*>(O1m + (i * ldo1 + j) * 2u) = hi;
           const uint32_t lo = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
           lw[r >> 1] = (r & 1) ? (lw[r >> 1] | (lo << 16)) : lo;
         }
@@ -642,6 +639,30 @@ void ns_gemm_kernel(const GemmLaunch L) {
           *reinterpret_cast<float4*>(wl + c * ES + r) =
               make_float4(acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
         }
+    if constexpr (EPI == EPI_UPDATE && sizeof(T) == 2) {
+      // the high part of X' row-major: lanes read 4-row x 8-column pieces of
+      // the staged half (16 lanes cover 256 consecutive bytes of LDS) and
+      // store 16-byte row segments
+      char* O1m = G.O1 + mat * G.o1_mat;
+      const uint32_t ldo1 = G.ldo1;
+      const int rg = lane & 15;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int c0 = 8 * (lane >> 4) + 32 * it;
+        float4 x[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const float4*>(wl + (c0 + t) * ES + 4 * rg);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float v[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
+          const uint32_t row = gi0 + h * 64 + 4 * rg + e;
+          Elem<T>::store8(O1m + (row * ldo1 + gj0 + c0) * 2u, make_float4(v[0], v[1], v[2], v[3]),
+                          make_float4(v[4], v[5], v[6], v[7]));
+        }
+      }
+    }
     // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
