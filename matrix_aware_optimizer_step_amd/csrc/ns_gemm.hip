@@ -586,7 +586,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
           *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
         }
       }
-    } else {  // EPI_FINAL: caller output in the Newton-Schulz orientation
+    } else if constexpr (sizeof(T) == 4) {  // EPI_FINAL, fp32 compute: caller output in the NS orientation
       if (!G.tall) {
         char* U = user_ptr(G.user, mat);
 #pragma unroll
@@ -595,7 +595,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
           if (i < G.ms && j < G.ns) store_user(G.user, U, i, j, acc[fi][fj][r]);
         }
       }
-    }
+    }  // EPI_FINAL, bf16 compute: the caller's output leaves from the LDS staging below
   }
 
   // 3. transposed stores through LDS
@@ -603,7 +603,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
   if constexpr (EPI == EPI_UPDATE) {
     transposed = true;
   } else if constexpr (EPI == EPI_FINAL) {
-    transposed = G.tall != 0;
+    transposed = sizeof(T) == 2 || G.tall != 0;  // bf16: staged either way (row or column segments)
   } else {
     transposed = tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
   }
@@ -663,23 +663,67 @@ void ns_gemm_kernel(const GemmLaunch L) {
         }
       }
     }
-    // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int c = (lane >> 3) + 8 * k;
-      const int rc = (lane & 7) * 8;
-      const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
-      const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
-      const int orow = gj0 + c;            // output row = this tile's column
-      const int ocol = gi0 + h * 64 + rc;  // output column = this tile's row
-      if constexpr (EPI == EPI_FINAL) {
-        if (orow < G.ns) {
+    if constexpr (EPI == EPI_FINAL) {
+      // the caller's output: 8-element segments, 16-byte (bf16) or 32-byte
+      // (fp32) stores where a segment is whole and the rows are 16-byte
+      // aligned, element by element at the ragged edges
+      const int es = G.user.dtype ? 2 : 4;
+      const bool vec = ((reinterpret_cast<uintptr_t>(OTm) | static_cast<uintptr_t>(ldot * es)) & 15) == 0;
+      auto put8 = [&](int orow, int ocol, int rows, int cols, const float4& x0, const float4& x1) {
+        if (orow >= rows) return;
+        if (vec && ocol + 8 <= cols) {
+          char* p = OTm + (static_cast<int64_t>(orow) * ldot + ocol) * es;
+          if (G.user.dtype) {
+            Elem<uint16_t>::store8(p, x0, x1);
+          } else {
+            Elem<float>::store8(p, x0, x1);
+          }
+        } else {
           const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (ocol + e < G.ms) store_user(G.user, OTm, orow, ocol + e, xv[e]);
+            if (ocol + e < cols) store_user(G.user, OTm, orow, ocol + e, xv[e]);
+        }
+      };
+      if (!G.tall) {
+        // rows of X are rows of the output: 4-row x 8-column pieces
+        const int rg = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int c0 = 8 * (lane >> 4) + 32 * it;
+          float4 x[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const float4*>(wl + (c0 + t) * ES + 4 * rg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float v[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
+            put8(gi0 + h * 64 + 4 * rg + e, gj0 + c0, G.ms, G.ns, make_float4(v[0], v[1], v[2], v[3]),
+                 make_float4(v[4], v[5], v[6], v[7]));
+          }
         }
       } else {
+        // columns of X are rows of the output: 8 lanes per 64-element row segment
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int c = (lane >> 3) + 8 * k;
+          const int rc = (lane & 7) * 8;
+          const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
+          const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
+          put8(gj0 + c, gi0 + h * 64 + rc, G.ns, G.ms, x0, x1);
+        }
+      }
+    } else {
+      // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = (lane >> 3) + 8 * k;
+        const int rc = (lane & 7) * 8;
+        const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
+        const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
+        const int orow = gj0 + c;            // output row = this tile's column
+        const int ocol = gi0 + h * 64 + rc;  // output column = this tile's row
         Elem<T>::store8(OTm + (static_cast<uint32_t>(orow) * static_cast<uint32_t>(ldot) + ocol) *
                                   static_cast<uint32_t>(sizeof(T)), x0, x1);
       }
