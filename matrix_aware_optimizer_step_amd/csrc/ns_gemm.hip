@@ -198,495 +198,457 @@ void ns_gemm_kernel(const GemmLaunch L) {
   static_assert(SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
 
-  // ---- which tile of which matrix of which group
-  const int t = blockIdx.x;
-  int gi = 0;
-  while (gi + 1 < L.ngroups && t >= L.g[gi + 1].tile_begin) ++gi;
-  const GemmGroup& G = L.g[gi];
-  int lt = t - G.tile_begin;  // position within the group
-  if (XCD) {
-    // Workgroup ids reach the 8 XCDs round-robin.  Inside each group, the
-    // positions that land on one XCD are renumbered to one contiguous range
-    // of the group's tiles: every XCD keeps a proportional share of every
-    // group (groups of unequal tile cost stay balanced across XCDs) and
-    // neighbouring tiles on an XCD share its L2.
-    const int n = G.tiles_per_mat * G.count;
-    const int f = (t - G.tile_begin) & 7;  // first in-group position on this XCD
-    int start = 0;
-    for (int e = 0; e < f; ++e) start += (n - e + 7) >> 3;  // positions on XCDs ranked before
-    lt = start + ((lt - f) >> 3);
-  }
-  const int mat = lt / G.tiles_per_mat;
-  int tt = lt - mat * G.tiles_per_mat;
-  int ti, tj;
-  constexpr int R = BM / BN;  // column tiles per row tile
-  static_assert(R * BN == BM, "BN must divide BM");
-  if (G.sym) {
-    // upper tiles only: row tile ti keeps column tiles tj >= R*ti
-    ti = 0;
-    while (tt >= G.tiles_n - R * ti) {
-      tt -= G.tiles_n - R * ti;
-      ++ti;
+  // Tiles t = blockIdx.x, + gridDim.x, ...: one tile per workgroup when the
+  // grid covers the launch, several in turn when the host chose a persistent
+  // grid (a multiple of 8, so every tile of a workgroup is on its XCD).
+  for (int t = blockIdx.x; t < L.total_tiles; t += gridDim.x) {
+    if (t != static_cast<int>(blockIdx.x)) __syncthreads();  // the previous tile is done with LDS
+    // ---- which tile of which matrix of which group
+    int gi = 0;
+    while (gi + 1 < L.ngroups && t >= L.g[gi + 1].tile_begin) ++gi;
+    const GemmGroup& G = L.g[gi];
+    int lt = t - G.tile_begin;  // position within the group
+    if (XCD) {
+      // Workgroup ids reach the 8 XCDs round-robin.  Inside each group, the
+      // positions that land on one XCD are renumbered to one contiguous range
+      // of the group's tiles: every XCD keeps a proportional share of every
+      // group (groups of unequal tile cost stay balanced across XCDs) and
+      // neighbouring tiles on an XCD share its L2.
+      const int n = G.tiles_per_mat * G.count;
+      const int f = (t - G.tile_begin) & 7;  // first in-group position on this XCD
+      int start = 0;
+      for (int e = 0; e < f; ++e) start += (n - e + 7) >> 3;  // positions on XCDs ranked before
+      lt = start + ((lt - f) >> 3);
     }
-    tj = R * ti + tt;
-  } else if (GM == 1) {
-    ti = tt / G.tiles_n;
-    tj = tt - ti * G.tiles_n;
-  } else {
-    const int span = GM * G.tiles_n;          // tiles in one full group of GM rows
-    const int grp = tt / span;
-    const int in = tt - grp * span;
-    const int rows = min(GM, G.tiles_m - grp * GM);  // the last group may be shorter
-    tj = in / rows;
-    ti = grp * GM + (in - tj * rows);
-  }
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave / WGN;
-  const int wn = wave - wm * WGN;
-
-  const int ldp = G.ldp;
-  const int ldq = G.ldq;
-  const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T);
-  const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * ldq * sizeof(T);
-  const int nk = G.K / BK;
-
-  // ---- operand staging
-  uint32_t dofs_p[DMA ? IPW : 1], dofs_q[DMA ? IPWQ : 1];  // DMA: lane byte offsets within the tile
-  int soff[DMA ? 1 : LOADS];                               // register path: LDS slot offsets
-  Chunk pr[DMA ? 1 : LOADS], qr[DMA ? 1 : LOADSQ];
-  const char* Pl = nullptr;
-  const char* Ql = nullptr;
-  int64_t pstep = 0, qstep = 0;
-  if constexpr (DMA) {
-#pragma unroll
-    for (int r = 0; r < IPW; ++r) {
-      const int row = (wave * IPW + r) * RPI + lane / RC;
-      const int c = swizzle<SWZ, RC>(row, lane % RC);
-      dofs_p[r] = static_cast<uint32_t>((row * ldp + c * CH) * static_cast<int>(sizeof(T)));
-    }
-#pragma unroll
-    for (int r = 0; r < IPWQ; ++r) {
-      const int row = (wave * IPWQ + r) * RPI + lane / RC;
-      const int c = swizzle<SWZ, RC>(row, lane % RC);
-      dofs_q[r] = static_cast<uint32_t>((row * ldq + c * CH) * static_cast<int>(sizeof(T)));
-    }
-  } else {
-    const int lrow = tid / RC;
-    const int lch = tid % RC;
-    Pl = Pt + (static_cast<int64_t>(lrow) * ldp + lch * CH) * sizeof(T);
-    Ql = Qt + (static_cast<int64_t>(lrow) * ldq + lch * CH) * sizeof(T);
-    pstep = static_cast<int64_t>(RPP) * ldp * sizeof(T);
-    qstep = static_cast<int64_t>(RPP) * ldq * sizeof(T);
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int row = lrow + RPP * r;
-      soff[r] = row * ROWB + (swizzle<SWZ, RC>(row, lch) << 4);
-    }
-  }
-
-  // DMA: issue k-tile kt into LDS stage st (lands asynchronously; vmcnt).
-  auto dma_issue = [&](int kt, int st) {
-    const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
-    const char* pk = Pt + kb;
-    const char* qk = Qt + kb;
-    char* lp = smem + st * STB + wave * IPW * 1024;
-    char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
-#pragma unroll
-    for (int r = 0; r < IPW; ++r) lds_dma16(pk + dofs_p[r], lp + r * 1024);
-#pragma unroll
-    for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
-  };
-  auto reg_load = [&](int kt) {
-    const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) pr[r] = *reinterpret_cast<const Chunk*>(Pl + kb + r * pstep);
-#pragma unroll
-    for (int r = 0; r < LOADSQ; ++r) qr[r] = *reinterpret_cast<const Chunk*>(Ql + kb + r * qstep);
-  };
-  auto reg_store = [&](int st) {
-    char* dp = smem + st * STB;
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) *reinterpret_cast<Chunk*>(dp + soff[r]) = pr[r];
-#pragma unroll
-    for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
-  };
-
-  // ---- accumulators (fp32, from zero: the update's a*X term is added in
-  // the epilogue, so every rounding of the running sum is at the scale of
-  // the product itself)
-  const int frow = lane & 31;
-  const int half = lane >> 5;
-  const int i_base = ti * BM + wm * WTM + 4 * half;  // acc[fi][fj][4q+e]: row i_base + fi*32 + 8q + e
-  const int j_base = tj * BN + wn * WTN + frow;      //                    col j_base + fj*32
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  constexpr int kPerTile = IPW + IPWQ;  // DMA instructions per wave per k-tile
-  static_assert(SUB % 2 == 0, "fragment double buffer assumes an even substep count");
-  if constexpr (DMA) {
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) dma_issue(s, s);
-    if (nk >= STAGES - 1) {
-      barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile 0 has landed
+    const int mat = lt / G.tiles_per_mat;
+    int tt = lt - mat * G.tiles_per_mat;
+    int ti, tj;
+    constexpr int R = BM / BN;  // column tiles per row tile
+    static_assert(R * BN == BM, "BN must divide BM");
+    if (G.sym) {
+      // upper tiles only: row tile ti keeps column tiles tj >= R*ti
+      ti = 0;
+      while (tt >= G.tiles_n - R * ti) {
+        tt -= G.tiles_n - R * ti;
+        ++ti;
+      }
+      tj = R * ti + tt;
+    } else if (GM == 1) {
+      ti = tt / G.tiles_n;
+      tj = tt - ti * G.tiles_n;
     } else {
-      barrier_keep_vm<0>();
+      const int span = GM * G.tiles_n;          // tiles in one full group of GM rows
+      const int grp = tt / span;
+      const int in = tt - grp * span;
+      const int rows = min(GM, G.tiles_m - grp * GM);  // the last group may be shorter
+      tj = in / rows;
+      ti = grp * GM + (in - tj * rows);
     }
-  } else {
-    reg_load(0);
-    reg_store(0);
-    __syncthreads();
-  }
 
-  int fa_off[FM], fb_off[FN], fa_row[FM], fb_row[FN];
-#pragma unroll
-  for (int f = 0; f < FM; ++f) {
-    fa_row[f] = wm * WTM + f * 32 + frow;
-    fa_off[f] = fa_row[f] * ROWB;
-  }
-#pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    fb_row[f] = wn * WTN + f * 32 + frow;
-    fb_off[f] = OPB + fb_row[f] * ROWB;
-  }
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WGN;
+    const int wn = wave - wm * WGN;
 
-  // Main loop.  Fragments of substep s+1 are read while the MFMAs of
-  // substep s run; at the last substep of k-tile kt the wave waits for its
-  // own DMA of k-tile kt+1, joins the barrier, and reads k-tile kt+1's first
-  // fragments before issuing kt's last MFMAs, so the barrier and the LDS
-  // latency overlap matrix work.  The barrier also retires every read of
-  // k-tile kt's stage, which the DMA issued next iteration overwrites.
-  Chunk af[2][FM], bfr[2][FN];
-  auto frags = [&](const char* sb, int s, Chunk* a, Chunk* b) {
-    const int ch = 2 * s + half;
+    const int ldp = G.ldp;
+    const int ldq = G.ldq;
+    const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T);
+    const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * ldq * sizeof(T);
+    const int nk = G.K / BK;
+
+    // ---- operand staging
+    uint32_t dofs_p[DMA ? IPW : 1], dofs_q[DMA ? IPWQ : 1];  // DMA: lane byte offsets within the tile
+    int soff[DMA ? 1 : LOADS];                               // register path: LDS slot offsets
+    Chunk pr[DMA ? 1 : LOADS], qr[DMA ? 1 : LOADSQ];
+    const char* Pl = nullptr;
+    const char* Ql = nullptr;
+    int64_t pstep = 0, qstep = 0;
+    if constexpr (DMA) {
 #pragma unroll
-    for (int f = 0; f < FM; ++f)
-      a[f] = *reinterpret_cast<const Chunk*>(sb + fa_off[f] + (swizzle<SWZ, RC>(fa_row[f], ch) << 4));
+      for (int r = 0; r < IPW; ++r) {
+        const int row = (wave * IPW + r) * RPI + lane / RC;
+        const int c = swizzle<SWZ, RC>(row, lane % RC);
+        dofs_p[r] = static_cast<uint32_t>((row * ldp + c * CH) * static_cast<int>(sizeof(T)));
+      }
 #pragma unroll
-    for (int f = 0; f < FN; ++f)
-      b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
-  };
-  frags(smem, 0, af[0], bfr[0]);
-  // bf16 update: the high part of a*X enters from the operand tiles (below),
-  // the epilogue adds only the low part.  k-tile kt_x0 + hh holds rows
-  // [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e. kFPK of its 32-row blocks.
-  constexpr bool kAddXInLoop = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
-  constexpr int kFPK = BK / 32;
-  constexpr int kNH = WTM / BK;
-  static_assert(!kAddXInLoop || (kNH * BK == WTM && kFPK * 32 == BK && RC == 2 * kFPK * 2),
-                "wave rows must split into whole k-tiles of whole 32-row blocks");
-  const int kt_x0 = (ti * BM + wm * WTM) / BK;
-  int st = 0;  // stage holding k-tile kt
-  for (int kt = 0; kt < nk; ++kt) {
-    const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
-    if (issue) {
-      if constexpr (DMA) {
-        int sn = st + STAGES - 1;
-        if (sn >= STAGES) sn -= STAGES;
-        dma_issue(kt + STAGES - 1, sn);
-      } else {
-        reg_load(kt + 1);
+      for (int r = 0; r < IPWQ; ++r) {
+        const int row = (wave * IPWQ + r) * RPI + lane / RC;
+        const int c = swizzle<SWZ, RC>(row, lane % RC);
+        dofs_q[r] = static_cast<uint32_t>((row * ldq + c * CH) * static_cast<int>(sizeof(T)));
+      }
+    } else {
+      const int lrow = tid / RC;
+      const int lch = tid % RC;
+      Pl = Pt + (static_cast<int64_t>(lrow) * ldp + lch * CH) * sizeof(T);
+      Ql = Qt + (static_cast<int64_t>(lrow) * ldq + lch * CH) * sizeof(T);
+      pstep = static_cast<int64_t>(RPP) * ldp * sizeof(T);
+      qstep = static_cast<int64_t>(RPP) * ldq * sizeof(T);
+#pragma unroll
+      for (int r = 0; r < LOADS; ++r) {
+        const int row = lrow + RPP * r;
+        soff[r] = row * ROWB + (swizzle<SWZ, RC>(row, lch) << 4);
       }
     }
-    const char* sb = smem + st * STB;
-    const int stn = (st + 1 == STAGES) ? 0 : st + 1;
-    if constexpr (kAddXInLoop) {
-      // a * X[i][j] = a * Q[j][k = i]: the k-tiles that cover this wave's
-      // rows hold the bf16 high part of X for its output elements.
+
+    // DMA: issue k-tile kt into LDS stage st (lands asynchronously; vmcnt).
+    auto dma_issue = [&](int kt, int st) {
+      const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
+      const char* pk = Pt + kb;
+      const char* qk = Qt + kb;
+      char* lp = smem + st * STB + wave * IPW * 1024;
+      char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
-      for (int hh = 0; hh < kNH; ++hh) {
-        if (kt == kt_x0 + hh) {  // uniform over the wave
+      for (int r = 0; r < IPW; ++r) lds_dma16(pk + dofs_p[r], lp + r * 1024);
 #pragma unroll
-          for (int f = 0; f < kFPK; ++f)
-#pragma unroll
-            for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int fi = hh * kFPK + f;
-                const uint2 v = *reinterpret_cast<const uint2*>(
-                    sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
-                acc[fi][fj][4 * q + 0] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x));
-                acc[fi][fj][4 * q + 1] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
-                acc[fi][fj][4 * q + 2] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y));
-                acc[fi][fj][4 * q + 3] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
-              }
-        }
-      }
-    }
-    auto mma_range = [&](int cur, int q0, int q1) {
-#pragma unroll
-      for (int q = q0; q < q1; ++q) Elem<T>::mma(acc[q / FN][q % FN], af[cur][q / FN], bfr[cur][q % FN]);
+      for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
     };
-    constexpr int NQ = FM * FN;
-    constexpr int kMf = Elem<T>::kMfmaPerChunk;
+    auto reg_load = [&](int kt) {
+      const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
 #pragma unroll
-    for (int s = 0; s < SUB; ++s) {
-      const int cur = s & 1;  // SUB is even: k-tile kt+1 starts in buffer 0 again
-      if (s + 1 < SUB) {
-        frags(sb, s + 1, af[cur ^ 1], bfr[cur ^ 1]);
-        mma_range(cur, 0, NQ);
-        if constexpr (SCHED == 1) {
-          // two MFMAs (their operands' wait comes first), the next substep's
-          // reads, then the remaining MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMf, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, (NQ - 2) * kMf, 0);
-        }
+      for (int r = 0; r < LOADS; ++r) pr[r] = *reinterpret_cast<const Chunk*>(Pl + kb + r * pstep);
+#pragma unroll
+      for (int r = 0; r < LOADSQ; ++r) qr[r] = *reinterpret_cast<const Chunk*>(Ql + kb + r * qstep);
+    };
+    auto reg_store = [&](int st) {
+      char* dp = smem + st * STB;
+#pragma unroll
+      for (int r = 0; r < LOADS; ++r) *reinterpret_cast<Chunk*>(dp + soff[r]) = pr[r];
+#pragma unroll
+      for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
+    };
+
+    // ---- accumulators (fp32, from zero: the update's a*X term is added in
+    // the epilogue, so every rounding of the running sum is at the scale of
+    // the product itself)
+    const int frow = lane & 31;
+    const int half = lane >> 5;
+    const int i_base = ti * BM + wm * WTM + 4 * half;  // acc[fi][fj][4q+e]: row i_base + fi*32 + 8q + e
+    const int j_base = tj * BN + wn * WTN + frow;      //                    col j_base + fj*32
+    f32x16_t acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    constexpr int kPerTile = IPW + IPWQ;  // DMA instructions per wave per k-tile
+    static_assert(SUB % 2 == 0, "fragment double buffer assumes an even substep count");
+    if constexpr (DMA) {
+#pragma unroll
+      for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) dma_issue(s, s);
+      if (nk >= STAGES - 1) {
+        barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile 0 has landed
       } else {
-        // Half of the last substep's MFMAs go before the barrier so the MFMA
-        // pipe stays busy while the wave waits in it.  The barrier and the
-        // next k-tile's first reads are unconditional, also after the last
-        // k-tile (the reads are then unused but in bounds): a branch would
-        // merge two different counts of outstanding LDS reads and force a
-        // full lgkmcnt wait.
-        mma_range(cur, 0, NQ / 2);
+        barrier_keep_vm<0>();
+      }
+    } else {
+      reg_load(0);
+      reg_store(0);
+      __syncthreads();
+    }
+
+    int fa_off[FM], fb_off[FN], fa_row[FM], fb_row[FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+      fa_row[f] = wm * WTM + f * 32 + frow;
+      fa_off[f] = fa_row[f] * ROWB;
+    }
+#pragma unroll
+    for (int f = 0; f < FN; ++f) {
+      fb_row[f] = wn * WTN + f * 32 + frow;
+      fb_off[f] = OPB + fb_row[f] * ROWB;
+    }
+
+    // Main loop.  Fragments of substep s+1 are read while the MFMAs of
+    // substep s run; at the last substep of k-tile kt the wave waits for its
+    // own DMA of k-tile kt+1, joins the barrier, and reads k-tile kt+1's first
+    // fragments before issuing kt's last MFMAs, so the barrier and the LDS
+    // latency overlap matrix work.  The barrier also retires every read of
+    // k-tile kt's stage, which the DMA issued next iteration overwrites.
+    Chunk af[2][FM], bfr[2][FN];
+    auto frags = [&](const char* sb, int s, Chunk* a, Chunk* b) {
+      const int ch = 2 * s + half;
+#pragma unroll
+      for (int f = 0; f < FM; ++f)
+        a[f] = *reinterpret_cast<const Chunk*>(sb + fa_off[f] + (swizzle<SWZ, RC>(fa_row[f], ch) << 4));
+#pragma unroll
+      for (int f = 0; f < FN; ++f)
+        b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
+    };
+    frags(smem, 0, af[0], bfr[0]);
+    // bf16 update: the high part of a*X enters from the operand tiles (below),
+    // the epilogue adds only the low part.  k-tile kt_x0 + hh holds rows
+    // [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e. kFPK of its 32-row blocks.
+    constexpr bool kAddXInLoop = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+    constexpr int kFPK = BK / 32;
+    constexpr int kNH = WTM / BK;
+    static_assert(!kAddXInLoop || (kNH * BK == WTM && kFPK * 32 == BK && RC == 2 * kFPK * 2),
+                  "wave rows must split into whole k-tiles of whole 32-row blocks");
+    const int kt_x0 = (ti * BM + wm * WTM) / BK;
+    int st = 0;  // stage holding k-tile kt
+    for (int kt = 0; kt < nk; ++kt) {
+      const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
+      if (issue) {
         if constexpr (DMA) {
-          if (kt + STAGES - 1 < nk) {
-            barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile kt+1 has landed for this wave
-          } else {
-            barrier_keep_vm<0>();
-          }
+          int sn = st + STAGES - 1;
+          if (sn >= STAGES) sn -= STAGES;
+          dma_issue(kt + STAGES - 1, sn);
         } else {
-          if (issue) reg_store(stn);
-          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS stores done
-          __builtin_amdgcn_s_barrier();
-        }
-        frags(smem + stn * STB, 0, af[cur ^ 1], bfr[cur ^ 1]);
-        mma_range(cur, NQ / 2, NQ);
-        if constexpr (SCHED == 1) {
-          __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, (NQ - NQ / 2) * kMf, 0);
+          reg_load(kt + 1);
         }
       }
-    }
-    st = stn;
-  }
-  // ---- epilogue.  acc[fi][fj][4q+e] holds C[i][j] with
-  //   i = ti*BM + wm*WTM + fi*32 + 8q + 4*half + e
-  //   j = tj*BM + wn*WTN + fj*32 + lane%32
-  // Each value is finished in registers (v replaces acc) and stored
-  // row-major straight from the MFMA layout: 32 lanes cover 32 consecutive
-  // columns of one row.  Transposed outputs (X'^T, the mirror tile of a
-  // symmetric product, a tall caller output) are staged per wave through LDS
-  // in 64-row halves, column-major with a 68-float stride (conflict-free for
-  // the 16-byte writes of 4 rows and the 16-byte reads of 8 rows), and leave
-  // as 128-byte row segments.
-  const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
-  const int gj0 = tj * BN + wn * WTN;  // first column
-
-  // 1. finish the values and store them row-major, one 32x32 block at a
-  //    time.  The epilogue operand (X, or A for the polynomial) of the
-  //    next PF blocks is loaded ahead, in registers the main loop no longer
-  //    needs, so several blocks' loads are in flight at once.
-  constexpr int NB = FM * FN;  // 32x32 blocks per wave
-  constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
-  constexpr bool kHasE = (EPI != EPI_GRAM);
-  float ebuf[kHasE ? PF + 1 : 1][16];
-  // bf16 update: the low part of X is stored in this kernel's accumulator
-  // order (lo_index()), so each lane's 16 values of a block are 32 contiguous
-  // bytes; all blocks are loaded here in one round of 16-byte loads and the
-  // new low part leaves the same way.
-  constexpr bool kLoNative = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
-  static_assert(!kLoNative || (BN == BM && WGM == 2 && WGN == BM / 64 && WTN == 64),
-                "the low part's layout assumes this tile shape (see lo_index)");
-  uint4 lo_pre[kLoNative ? NB : 1][2];
-  const uint32_t lo_off =
-      ((static_cast<uint32_t>(ti * G.tiles_n + tj) * NW + wave) * NB) * 1024u + static_cast<uint32_t>(lane) * 16u;
-  if constexpr (kLoNative) {
-    const char* El = G.E1 + mat * G.e1_mat;
+      const char* sb = smem + st * STB;
+      const int stn = (st + 1 == STAGES) ? 0 : st + 1;
+      if constexpr (kAddXInLoop) {
+        // a * X[i][j] = a * Q[j][k = i]: the k-tiles that cover this wave's
+        // rows hold the bf16 high part of X for its output elements.
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      lo_pre[b][0] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u);
-      lo_pre[b][1] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u + 16u);
-    }
-  }
-  auto eload = [&](int blk, float* e) {
-    const int fi = blk / FN, fj = blk % FN;
-    const int j = j_base + fj * 32;
-    if constexpr (EPI == EPI_POLY) {
-      const char* Em = G.E0 + mat * G.e0_mat;
-      const uint32_t lde = G.lde0;
+        for (int hh = 0; hh < kNH; ++hh) {
+          if (kt == kt_x0 + hh) {  // uniform over the wave
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-        e[r] = Elem<T>::load(Em + (i * lde + j) * static_cast<uint32_t>(sizeof(T)));
-      }
-    } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
-      // X: fp32, or bf16 high part + bf16 low part (per-matrix byte offsets fit in 32 bits)
-      const char* Em = G.E0 + mat * G.e0_mat;
-      const uint32_t lde = G.lde0;
-      if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
-        const uint32_t w[8] = {lo_pre[blk][0].x, lo_pre[blk][0].y, lo_pre[blk][0].z, lo_pre[blk][0].w,
-                               lo_pre[blk][1].x, lo_pre[blk][1].y, lo_pre[blk][1].z, lo_pre[blk][1].w};
+            for (int f = 0; f < kFPK; ++f)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = bf16_to_f32(static_cast<uint16_t>(w[r >> 1] >> (16 * (r & 1))));
-      } else {
+              for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          e[r] = *reinterpret_cast<const float*>(Em + (i * lde + j) * 4u);
-        }
-      }
-    }
-  };
-  if constexpr (kHasE) {
-#pragma unroll
-    for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
-  }
-#pragma unroll
-  for (int blk = 0; blk < NB; ++blk) {
-    const int fi = blk / FN, fj = blk % FN;
-    const int j = j_base + fj * 32;
-    if constexpr (kHasE) {
-      if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
-      const float* e = ebuf[blk % (PF + 1)];
-      if constexpr (EPI == EPI_POLY) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
-      }
-    }
-    if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
-      char* Om = G.O0 + mat * G.o0_mat;
-      const uint32_t ldo = G.ldo0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-        Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
-      }
-    } else if constexpr (EPI == EPI_UPDATE) {
-      char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
-      const uint32_t ldo0 = G.ldo0;
-      if constexpr (sizeof(T) == 2) {
-        // the high part leaves from the LDS staging below, as row segments
-        uint32_t lw[8];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
-          const uint32_t lo = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
-          lw[r >> 1] = (r & 1) ? (lw[r >> 1] | (lo << 16)) : lo;
-        }
-        uint4* Ld = reinterpret_cast<uint4*>(O0m + (lo_off + blk * 1024u) * 2u);
-        Ld[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-        Ld[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
-        }
-      }
-    } else if constexpr (sizeof(T) == 4) {  // EPI_FINAL, fp32 compute: caller output in the NS orientation
-      if (!G.tall) {
-        char* U = user_ptr(G.user, mat);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          if (i < G.ms && j < G.ns) store_user(G.user, U, i, j, acc[fi][fj][r]);
-        }
-      }
-    }  // EPI_FINAL, bf16 compute: the caller's output leaves from the LDS staging below
-  }
-
-  // 3. transposed stores through LDS
-  bool transposed;
-  if constexpr (EPI == EPI_UPDATE) {
-    transposed = true;
-  } else if constexpr (EPI == EPI_FINAL) {
-    transposed = sizeof(T) == 2 || G.tall != 0;  // bf16: staged either way (row or column segments)
-  } else {
-    transposed = tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
-  }
-  if (!transposed) return;  // uniform over the workgroup
-  static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
-  constexpr int ES = 68;  // floats per staged column
-  __syncthreads();        // every wave is done with the operand stages
-  float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
-  char* OTm;
-  int64_t ldot;
-  if constexpr (EPI == EPI_UPDATE) {
-    OTm = G.OT + mat * G.ot_mat;
-    ldot = G.ldot;
-  } else if constexpr (EPI == EPI_FINAL) {
-    OTm = user_ptr(G.user, mat);
-    ldot = G.user.ld;
-  } else {
-    OTm = G.O0 + mat * G.o0_mat;
-    ldot = G.ldo0;
-  }
-#pragma unroll
-  for (int h = 0; h < WTM / 64; ++h) {
-    // registers -> LDS column-major: 4 consecutive rows of one column per write
-#pragma unroll
-    for (int f = 0; f < 2; ++f)
-#pragma unroll
-      for (int fj = 0; fj < FN; ++fj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = f * 32 + 8 * q + 4 * half;
-          const int c = fj * 32 + frow;
-          const int fi = 2 * h + f;
-          *reinterpret_cast<float4*>(wl + c * ES + r) =
-              make_float4(acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
-        }
-    if constexpr (EPI == EPI_UPDATE && sizeof(T) == 2) {
-      // the high part of X' row-major: lanes read 4-row x 8-column pieces of
-      // the staged half (16 lanes cover 256 consecutive bytes of LDS) and
-      // store 16-byte row segments
-      char* O1m = G.O1 + mat * G.o1_mat;
-      const uint32_t ldo1 = G.ldo1;
-      const int rg = lane & 15;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c0 = 8 * (lane >> 4) + 32 * it;
-        float4 x[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const float4*>(wl + (c0 + t) * ES + 4 * rg);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float v[8];
-#pragma unroll
-          for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
-          const uint32_t row = gi0 + h * 64 + 4 * rg + e;
-          Elem<T>::store8(O1m + (row * ldo1 + gj0 + c0) * 2u, make_float4(v[0], v[1], v[2], v[3]),
-                          make_float4(v[4], v[5], v[6], v[7]));
-        }
-      }
-    }
-    if constexpr (EPI == EPI_FINAL) {
-      // the caller's output: 8-element segments, 16-byte (bf16) or 32-byte
-      // (fp32) stores where a segment is whole and the rows are 16-byte
-      // aligned, element by element at the ragged edges
-      const int es = G.user.dtype ? 2 : 4;
-      const bool vec = ((reinterpret_cast<uintptr_t>(OTm) | static_cast<uintptr_t>(ldot * es)) & 15) == 0;
-      auto put8 = [&](int orow, int ocol, int rows, int cols, const float4& x0, const float4& x1) {
-        if (orow >= rows) return;
-        if (vec && ocol + 8 <= cols) {
-          char* p = OTm + (static_cast<int64_t>(orow) * ldot + ocol) * es;
-          if (G.user.dtype) {
-            Elem<uint16_t>::store8(p, x0, x1);
-          } else {
-            Elem<float>::store8(p, x0, x1);
+                for (int q = 0; q < 4; ++q) {
+                  const int fi = hh * kFPK + f;
+                  const uint2 v = *reinterpret_cast<const uint2*>(
+                      sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
+                  acc[fi][fj][4 * q + 0] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x));
+                  acc[fi][fj][4 * q + 1] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
+                  acc[fi][fj][4 * q + 2] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y));
+                  acc[fi][fj][4 * q + 3] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
+                }
           }
-        } else {
-          const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (ocol + e < cols) store_user(G.user, OTm, orow, ocol + e, xv[e]);
         }
+      }
+      auto mma_range = [&](int cur, int q0, int q1) {
+#pragma unroll
+        for (int q = q0; q < q1; ++q) Elem<T>::mma(acc[q / FN][q % FN], af[cur][q / FN], bfr[cur][q % FN]);
       };
-      if (!G.tall) {
-        // rows of X are rows of the output: 4-row x 8-column pieces
+      constexpr int NQ = FM * FN;
+      constexpr int kMf = Elem<T>::kMfmaPerChunk;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        const int cur = s & 1;  // SUB is even: k-tile kt+1 starts in buffer 0 again
+        if (s + 1 < SUB) {
+          frags(sb, s + 1, af[cur ^ 1], bfr[cur ^ 1]);
+          mma_range(cur, 0, NQ);
+          if constexpr (SCHED == 1) {
+            // two MFMAs (their operands' wait comes first), the next substep's
+            // reads, then the remaining MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kMf, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (NQ - 2) * kMf, 0);
+          }
+        } else {
+          // Half of the last substep's MFMAs go before the barrier so the MFMA
+          // pipe stays busy while the wave waits in it.  The barrier and the
+          // next k-tile's first reads are unconditional, also after the last
+          // k-tile (the reads are then unused but in bounds): a branch would
+          // merge two different counts of outstanding LDS reads and force a
+          // full lgkmcnt wait.
+          mma_range(cur, 0, NQ / 2);
+          if constexpr (DMA) {
+            if (kt + STAGES - 1 < nk) {
+              barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile kt+1 has landed for this wave
+            } else {
+              barrier_keep_vm<0>();
+            }
+          } else {
+            if (issue) reg_store(stn);
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): LDS stores done
+            __builtin_amdgcn_s_barrier();
+          }
+          frags(smem + stn * STB, 0, af[cur ^ 1], bfr[cur ^ 1]);
+          mma_range(cur, NQ / 2, NQ);
+          if constexpr (SCHED == 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, FM + FN, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, (NQ - NQ / 2) * kMf, 0);
+          }
+        }
+      }
+      st = stn;
+    }
+    // ---- epilogue.  acc[fi][fj][4q+e] holds C[i][j] with
+    //   i = ti*BM + wm*WTM + fi*32 + 8q + 4*half + e
+    //   j = tj*BM + wn*WTN + fj*32 + lane%32
+    // Each value is finished in registers (v replaces acc) and stored
+    // row-major straight from the MFMA layout: 32 lanes cover 32 consecutive
+    // columns of one row.  Transposed outputs (X'^T, the mirror tile of a
+    // symmetric product, a tall caller output) are staged per wave through LDS
+    // in 64-row halves, column-major with a 68-float stride (conflict-free for
+    // the 16-byte writes of 4 rows and the 16-byte reads of 8 rows), and leave
+    // as 128-byte row segments.
+    const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
+    const int gj0 = tj * BN + wn * WTN;  // first column
+
+    // 1. finish the values and store them row-major, one 32x32 block at a
+    //    time.  The epilogue operand (X, or A for the polynomial) of the
+    //    next PF blocks is loaded ahead, in registers the main loop no longer
+    //    needs, so several blocks' loads are in flight at once.
+    constexpr int NB = FM * FN;  // 32x32 blocks per wave
+    constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
+    constexpr bool kHasE = (EPI != EPI_GRAM);
+    float ebuf[kHasE ? PF + 1 : 1][16];
+    // bf16 update: the low part of X is stored in this kernel's accumulator
+    // order (lo_index()), so each lane's 16 values of a block are 32 contiguous
+    // bytes; all blocks are loaded here in one round of 16-byte loads and the
+    // new low part leaves the same way.
+    constexpr bool kLoNative = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+    static_assert(!kLoNative || (BN == BM && WGM == 2 && WGN == BM / 64 && WTN == 64),
+                  "the low part's layout assumes this tile shape (see lo_index)");
+    uint4 lo_pre[kLoNative ? NB : 1][2];
+    const uint32_t lo_off =
+        ((static_cast<uint32_t>(ti * G.tiles_n + tj) * NW + wave) * NB) * 1024u + static_cast<uint32_t>(lane) * 16u;
+    if constexpr (kLoNative) {
+      const char* El = G.E1 + mat * G.e1_mat;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        lo_pre[b][0] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u);
+        lo_pre[b][1] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u + 16u);
+      }
+    }
+    auto eload = [&](int blk, float* e) {
+      const int fi = blk / FN, fj = blk % FN;
+      const int j = j_base + fj * 32;
+      if constexpr (EPI == EPI_POLY) {
+        const char* Em = G.E0 + mat * G.e0_mat;
+        const uint32_t lde = G.lde0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          e[r] = Elem<T>::load(Em + (i * lde + j) * static_cast<uint32_t>(sizeof(T)));
+        }
+      } else if constexpr (EPI == EPI_UPDATE || EPI == EPI_FINAL) {
+        // X: fp32, or bf16 high part + bf16 low part (per-matrix byte offsets fit in 32 bits)
+        const char* Em = G.E0 + mat * G.e0_mat;
+        const uint32_t lde = G.lde0;
+        if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
+          const uint32_t w[8] = {lo_pre[blk][0].x, lo_pre[blk][0].y, lo_pre[blk][0].z, lo_pre[blk][0].w,
+                                 lo_pre[blk][1].x, lo_pre[blk][1].y, lo_pre[blk][1].z, lo_pre[blk][1].w};
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e[r] = bf16_to_f32(static_cast<uint16_t>(w[r >> 1] >> (16 * (r & 1))));
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+            e[r] = *reinterpret_cast<const float*>(Em + (i * lde + j) * 4u);
+          }
+        }
+      }
+    };
+    if constexpr (kHasE) {
+#pragma unroll
+      for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
+    }
+#pragma unroll
+    for (int blk = 0; blk < NB; ++blk) {
+      const int fi = blk / FN, fj = blk % FN;
+      const int j = j_base + fj * 32;
+      if constexpr (kHasE) {
+        if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
+        const float* e = ebuf[blk % (PF + 1)];
+        if constexpr (EPI == EPI_POLY) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
+        }
+      }
+      if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
+        char* Om = G.O0 + mat * G.o0_mat;
+        const uint32_t ldo = G.ldo0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+          Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
+        }
+      } else if constexpr (EPI == EPI_UPDATE) {
+        char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
+        const uint32_t ldo0 = G.ldo0;
+        if constexpr (sizeof(T) == 2) {
+          // the high part leaves from the LDS staging below, as row segments
+          uint32_t lw[8];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
+            const uint32_t lo = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
+            lw[r >> 1] = (r & 1) ? (lw[r >> 1] | (lo << 16)) : lo;
+          }
+          uint4* Ld = reinterpret_cast<uint4*>(O0m + (lo_off + blk * 1024u) * 2u);
+          Ld[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+          Ld[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+            *reinterpret_cast<float*>(O0m + (i * ldo0 + j) * 4u) = acc[fi][fj][r];
+          }
+        }
+      } else if constexpr (sizeof(T) == 4) {  // EPI_FINAL, fp32 compute: caller output in the NS orientation
+        if (!G.tall) {
+          char* U = user_ptr(G.user, mat);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+            if (i < G.ms && j < G.ns) store_user(G.user, U, i, j, acc[fi][fj][r]);
+          }
+        }
+      }  // EPI_FINAL, bf16 compute: the caller's output leaves from the LDS staging below
+    }
+
+    // 3. transposed stores through LDS
+    bool transposed;
+    if constexpr (EPI == EPI_UPDATE) {
+      transposed = true;
+    } else if constexpr (EPI == EPI_FINAL) {
+      transposed = sizeof(T) == 2 || G.tall != 0;  // bf16: staged either way (row or column segments)
+    } else {
+      transposed = tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
+    }
+    if (!transposed) continue;  // uniform over the workgroup
+    static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
+    constexpr int ES = 68;  // floats per staged column
+    __syncthreads();        // every wave is done with the operand stages
+    float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
+    char* OTm;
+    int64_t ldot;
+    if constexpr (EPI == EPI_UPDATE) {
+      OTm = G.OT + mat * G.ot_mat;
+      ldot = G.ldot;
+    } else if constexpr (EPI == EPI_FINAL) {
+      OTm = user_ptr(G.user, mat);
+      ldot = G.user.ld;
+    } else {
+      OTm = G.O0 + mat * G.o0_mat;
+      ldot = G.ldo0;
+    }
+#pragma unroll
+    for (int h = 0; h < WTM / 64; ++h) {
+      // registers -> LDS column-major: 4 consecutive rows of one column per write
+#pragma unroll
+      for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = f * 32 + 8 * q + 4 * half;
+            const int c = fj * 32 + frow;
+            const int fi = 2 * h + f;
+            *reinterpret_cast<float4*>(wl + c * ES + r) =
+                make_float4(acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
+          }
+      if constexpr (EPI == EPI_UPDATE && sizeof(T) == 2) {
+        // the high part of X' row-major: lanes read 4-row x 8-column pieces of
+        // the staged half (16 lanes cover 256 consecutive bytes of LDS) and
+        // store 16-byte row segments
+        char* O1m = G.O1 + mat * G.o1_mat;
+        const uint32_t ldo1 = G.ldo1;
         const int rg = lane & 15;
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
@@ -699,46 +661,112 @@ void ns_gemm_kernel(const GemmLaunch L) {
             float v[8];
 #pragma unroll
             for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
-            put8(gi0 + h * 64 + 4 * rg + e, gj0 + c0, G.ms, G.ns, make_float4(v[0], v[1], v[2], v[3]),
-                 make_float4(v[4], v[5], v[6], v[7]));
+            const uint32_t row = gi0 + h * 64 + 4 * rg + e;
+            Elem<T>::store8(O1m + (row * ldo1 + gj0 + c0) * 2u, make_float4(v[0], v[1], v[2], v[3]),
+                            make_float4(v[4], v[5], v[6], v[7]));
+          }
+        }
+      }
+      if constexpr (EPI == EPI_FINAL) {
+        // the caller's output: 8-element segments, 16-byte (bf16) or 32-byte
+        // (fp32) stores where a segment is whole and the rows are 16-byte
+        // aligned, element by element at the ragged edges
+        const int es = G.user.dtype ? 2 : 4;
+        const bool vec = ((reinterpret_cast<uintptr_t>(OTm) | static_cast<uintptr_t>(ldot * es)) & 15) == 0;
+        auto put8 = [&](int orow, int ocol, int rows, int cols, const float4& x0, const float4& x1) {
+          if (orow >= rows) return;
+          if (vec && ocol + 8 <= cols) {
+            char* p = OTm + (static_cast<int64_t>(orow) * ldot + ocol) * es;
+            if (G.user.dtype) {
+              Elem<uint16_t>::store8(p, x0, x1);
+            } else {
+              Elem<float>::store8(p, x0, x1);
+            }
+          } else {
+            const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (ocol + e < cols) store_user(G.user, OTm, orow, ocol + e, xv[e]);
+          }
+        };
+        if (!G.tall) {
+          // rows of X are rows of the output: 4-row x 8-column pieces
+          const int rg = lane & 15;
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int c0 = 8 * (lane >> 4) + 32 * it;
+            float4 x[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const float4*>(wl + (c0 + t) * ES + 4 * rg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float v[8];
+#pragma unroll
+              for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
+              put8(gi0 + h * 64 + 4 * rg + e, gj0 + c0, G.ms, G.ns, make_float4(v[0], v[1], v[2], v[3]),
+                   make_float4(v[4], v[5], v[6], v[7]));
+            }
+          }
+        } else {
+          // columns of X are rows of the output: 8 lanes per 64-element row segment
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int c = (lane >> 3) + 8 * k;
+            const int rc = (lane & 7) * 8;
+            const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
+            const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
+            put8(gj0 + c, gi0 + h * 64 + rc, G.ns, G.ms, x0, x1);
           }
         }
       } else {
-        // columns of X are rows of the output: 8 lanes per 64-element row segment
+        // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int c = (lane >> 3) + 8 * k;
           const int rc = (lane & 7) * 8;
           const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
           const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
-          put8(gj0 + c, gi0 + h * 64 + rc, G.ns, G.ms, x0, x1);
+          const int orow = gj0 + c;            // output row = this tile's column
+          const int ocol = gi0 + h * 64 + rc;  // output column = this tile's row
+          Elem<T>::store8(OTm + (static_cast<uint32_t>(orow) * static_cast<uint32_t>(ldot) + ocol) *
+                                    static_cast<uint32_t>(sizeof(T)), x0, x1);
         }
       }
-    } else {
-      // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = (lane >> 3) + 8 * k;
-        const int rc = (lane & 7) * 8;
-        const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
-        const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
-        const int orow = gj0 + c;            // output row = this tile's column
-        const int ocol = gi0 + h * 64 + rc;  // output column = this tile's row
-        Elem<T>::store8(OTm + (static_cast<uint32_t>(orow) * static_cast<uint32_t>(ldot) + ocol) *
-                                  static_cast<uint32_t>(sizeof(T)), x0, x1);
-      }
     }
-  }
+  }  // tiles
 }
 
-// Measured on MI355X (config-2 shapes): 64-element k-tiles moved by LDS DMA
-// through a two-stage ring, the 64-bank swizzle, XCD-contiguous tile ranges
-// and groups of four tile rows for the non-symmetric product.
+// Workgroups of a tile size that are resident on the current device at once
+// (one 256-tile or two 128-tile workgroups per CU: LDS bound), rounded down
+// to a multiple of the 8 XCDs; 0 if the device cannot be queried.
+int resident_workgroups(int tile) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cus[dev] = n;
+  }
+  return (cus[dev] * (tile == 256 ? 1 : 2)) & ~7;
+}
+
+// Launches with many tiles per resident workgroup run on a persistent grid
+// (each workgroup takes tiles t, t + grid, ... of the longest-first order,
+// which keeps the rounds balanced and saves a workgroup launch and retire
+// per tile); short launches keep one workgroup per tile, so the hardware's
+// dynamic dispatch balances tiles of unequal cost.
+// Chosen by measurement on MI355X over the 8B-dense matrix shapes: 64-element
+// k-tiles moved by LDS DMA through a two-stage ring, the 64-bank swizzle,
+// XCD-contiguous tile ranges and groups of four tile rows for the
+// non-symmetric product.
 template <typename T, int BM, int WGM, int WGN, int EPI>
 void launch_one(const GemmLaunch& L, hipStream_t stream) {
   constexpr int RC = 8, STAGES = 2, SWZ = 1, DMA = 1, XCD = 1, SCHED = 0, GM = 4;
-  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM>),
-                     dim3(L.total_tiles), dim3(64 * WGM * WGN), 0, stream, L);
+  const int cap = resident_workgroups(BM);
+  const int grid = (cap >= 8 && L.total_tiles >= 4 * cap) ? cap : L.total_tiles;
+  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM>), dim3(grid),
+                     dim3(64 * WGM * WGN), 0, stream, L);
 }
 
 template <typename T, int BM, int WGM, int WGN>
