@@ -11,7 +11,7 @@ also carries the Newton-Schulz TFLOP/s (algorithmic flops: upper-triangle
 Gram and square, full update product), the roofline of the dominant kernel
 family and the fp64 CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b-dense-layer]
 """
 
 from __future__ import annotations
@@ -58,12 +58,12 @@ def make_stepper(mx, weights, grads, coeffs="quintic", steps=None):
                        steps=k if steps is None else steps)
 
 
-def measured_traffic(cfg_index):
+def measured_traffic(slug):
     """HBM bytes per step of the Newton-Schulz GEMM launches, from the
     rocprofv3 FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when that
     summary was taken on a different version of the kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"ns_gemm_config{cfg_index}_hbm_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"ns_gemm_{slug}_hbm_traffic.md")
     src = os.path.join(ROOT, "matrix_aware_optimizer_step_amd", "csrc", "ns_gemm.hip")
     if not os.path.exists(path):
         return None
@@ -201,16 +201,18 @@ def cpu_baseline(cfg, grads_host, budget_s=20.0, coeffs=COEFFS["quintic"][0], st
 
 
 def main():
+    from workloads.synth import BENCH_WORKLOADS
+
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--workload", default="8b-dense-layer", choices=BENCH_WORKLOADS)
     ap.add_argument("--coeffs", default="quintic", choices=sorted(COEFFS),
                     help="Newton-Schulz coefficient set (quintic: the Muon default)")
     ap.add_argument("--ns-steps", type=int, default=None, help="Newton-Schulz steps (default: the set's usual count)")
     ap.add_argument("--part", default="muon", choices=["muon", "adamw"],
-                    help="muon: the Muon step of --config (default); adamw: the AdamW step over the 8B-style "
+                    help="muon: the Muon step of --workload (default); adamw: the AdamW step over the 8B-style "
                          "model's embeddings, head and norms")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -236,8 +238,8 @@ def main():
     if not torch.cuda.is_available():
         raise RuntimeError("bench.py needs a GPU")
     dev = torch.device("cuda:0")
-    cfg = synth.CONFIGS[args.config]
-    log(f"[bench] config {cfg.index}: {cfg.name}, {cfg.matrices} matrices, {cfg.elements / 1e6:.1f} M elements")
+    cfg = synth.WORKLOADS[args.workload]
+    log(f"[bench] {cfg.slug}: {cfg.name}, {cfg.matrices} matrices, {cfg.elements / 1e6:.1f} M elements")
 
     t0 = time.perf_counter()
     grads = synth.group_gradients(cfg, step=1, device=dev)
@@ -306,7 +308,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"config {cfg.index}: {cfg.name}", "matrices": cfg.matrices,
+        "config": {"workload": f"{cfg.slug}: {cfg.name}", "matrices": cfg.matrices,
                    "shapes": shapes, "gradients": cfg.kind, "ns_steps": ns_steps, "coefficients": args.coeffs, "compute": "bf16 MFMA, fp32 accumulate",
                    "parallelism": "single GPU"},
         "newton_schulz": {"tflops_algorithmic": ns_tflops, "tflops_nominal_4m2n_2m3": ns_tflops_nominal,
@@ -315,7 +317,7 @@ def main():
         "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
                         "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.index),
+                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.slug),
                      "kernel": "ns_gemm_kernel (Gram, polynomial and update launches of muon_orthogonalize_grouped)"},
         "cpu_baseline": cpu,
     }

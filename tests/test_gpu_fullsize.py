@@ -10,7 +10,7 @@ run on the same seeded inputs:
 * the updated bf16 weight: within one bf16 rounding of the oracle's apply
   step evaluated on the GPU's own Newton-Schulz output.
 
-Sampled matrices get their configuration's gradient recipe; the others get a
+Sampled matrices get their workload's gradient recipe; the others get a
 seeded Gaussian of the same shape, which keeps the launch identical while
 sparing the host the cost of generating what is not checked.  Sampled
 indices include the last matrix of large groups, so per-matrix offsets far
@@ -32,12 +32,12 @@ pytestmark = pytest.mark.gpu
 TOL_EW = 1e-6
 TOL_BF16 = 3e-2
 
-# configuration -> {group name: matrix indices within the group to check}
+# workload -> {group name: matrix indices within the group to check}
 SAMPLES = {
-    2: {"wq_wo": [0], "wk_wv": [1], "gate_up": [1], "down": [0]},
-    3: {"wq_wo": [63], "wk_wv": [0], "gate_up": [37], "down": [31]},
-    4: {"gate_up": list(range(0, 256, 16)) + [255], "down": list(range(3, 128, 16)) + [127]},
-    5: {"qkv_heads": list(range(96)), "gate_up": [1], "down": [0]},
+    "8b-dense-layer": {"wq_wo": [0], "wk_wv": [1], "gate_up": [1], "down": [0]},
+    "8b-dense-32-layers": {"wq_wo": [63], "wk_wv": [0], "gate_up": [37], "down": [31]},
+    "moe-30b-a3b-layer": {"gate_up": list(range(0, 256, 16)) + [255], "down": list(range(3, 128, 16)) + [127]},
+    "qkv-heads-kappa1e4": {"qkv_heads": list(range(96)), "gate_up": [1], "down": [0]},
 }
 
 
@@ -67,7 +67,7 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
 def gradients(cfg, dev, picks):
     """Per group a (count, rows, cols) tensor: the recipe for picked matrices,
     a seeded Gaussian filler elsewhere."""
-    counts = synth.moe_token_counts(synth.seed_of(cfg.index, 0, 0), device=dev) if cfg.kind == "moe" else None
+    counts = synth.moe_token_counts(synth.seed_of(cfg.seed_id, 0, 0), device=dev) if cfg.kind == "moe" else None
     out, i = [], 0
     for grp in cfg.groups:
         t = torch.empty(grp.count, grp.rows, grp.cols, dtype=cfg.dtype, device=dev)
@@ -75,25 +75,25 @@ def gradients(cfg, dev, picks):
             if k in picks.get(grp.name, ()):
                 t[k] = synth.gradient(cfg, i, grp.rows, grp.cols, 1, dev, counts).to(cfg.dtype)
             else:
-                t[k] = synth.gaussian(grp.rows, grp.cols, synth.seed_of(cfg.index, i, 1), dev).to(cfg.dtype)
+                t[k] = synth.gaussian(grp.rows, grp.cols, synth.seed_of(cfg.seed_id, i, 1), dev).to(cfg.dtype)
             i += 1
         out.append(t)
     return out
 
 
-@pytest.mark.parametrize("config", [2, 3, 4, 5])
-def test_full_size_step_matches_oracle(mx, config):
-    cfg = synth.CONFIGS[config]
-    picks = SAMPLES[config]
+@pytest.mark.parametrize("workload", list(synth.BENCH_WORKLOADS))
+def test_full_size_step_matches_oracle(mx, workload):
+    cfg = synth.WORKLOADS[workload]
+    picks = SAMPLES[workload]
     dev = torch.device("cuda:0")
-    print(f"[fullsize] config {config}: {cfg.name}", flush=True)
+    print(f"[fullsize] {workload}: {cfg.name}", flush=True)
     grads = gradients(cfg, dev, picks)
     weights = synth.initial_weights(cfg, device=dev)
     w0 = {(gi, k): f64(weights[gi][k]) for gi, grp in enumerate(cfg.groups) for k in picks.get(grp.name, ())}
     stepper = bench.make_stepper(mx, weights, grads)
     stepper.step()
     torch.cuda.synchronize()
-    print(f"[fullsize] config {config}: GPU step done", flush=True)
+    print(f"[fullsize] {workload}: GPU step done", flush=True)
 
     worst = {"mom": 0.0, "sumsq": 0.0, "ortho": 0.0}
     t0 = time.perf_counter()
@@ -106,7 +106,7 @@ def test_full_size_step_matches_oracle(mx, config):
             e_ss = abs(float(stepper.sumsq_buffers[gi][k]) - ss_want) / ss_want
             O_got = f64(stepper.ortho_buffers[gi][k])
             e_o = O.relative_frobenius_error(O_got, O_want)
-            where = f"config {config} {grp.name}[{k}] {grp.rows}x{grp.cols}"
+            where = f"{workload} {grp.name}[{k}] {grp.rows}x{grp.cols}"
             assert e_mom <= TOL_EW, f"{where}: momentum error {e_mom:.3g}"
             assert e_ss <= TOL_EW, f"{where}: sum of squares error {e_ss:.3g}"
             assert e_o <= TOL_BF16, f"{where}: Newton-Schulz error {e_o:.3g}"
@@ -117,7 +117,7 @@ def test_full_size_step_matches_oracle(mx, config):
             assert np.all(np.abs(W_got - bf16_of(W_exact)) <= tol), f"{where}: updated weight"
             worst = {"mom": max(worst["mom"], e_mom), "sumsq": max(worst["sumsq"], e_ss),
                      "ortho": max(worst["ortho"], e_o)}
-    print(f"[fullsize] config {config}: oracle checks {time.perf_counter() - t0:.1f} s, worst errors "
+    print(f"[fullsize] {workload}: oracle checks {time.perf_counter() - t0:.1f} s, worst errors "
           f"momentum {worst['mom']:.2e} sumsq {worst['sumsq']:.2e} Newton-Schulz {worst['ortho']:.2e}", flush=True)
     del stepper, grads, weights
     torch.cuda.empty_cache()

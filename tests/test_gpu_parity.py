@@ -305,7 +305,7 @@ def test_grouped_equals_separate_calls(mx):
 @pytest.mark.parametrize("nesterov", [True, False])
 def test_single_fp32_gradient_three_steps(mx, nesterov):
     """The 256x128 fp32 configuration, three seeded gradients, whole step."""
-    cfg = synth.CONFIGS[1]
+    cfg = synth.WORKLOADS["tiny-256x128-f32"]
     lr, wd = 1.0, 0.5
     W = (0.02 * torch.randn(1, 256, 128, generator=torch.Generator().manual_seed(5))).cuda()
     Wo, Mo = f64(W[0]), np.zeros((256, 128))

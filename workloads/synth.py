@@ -5,26 +5,27 @@ arithmetic.  The GPU tests, the benchmark and the oracle's callers all take
 their inputs from here, so both sides of every parity check see the same
 bits.
 
-Seed rule: matrix ``i`` (counted across the whole configuration, in group
-order) at optimizer step ``t`` (1-based) uses seed ``c*10**6 + i*10 + t``
-for configuration ``c``.
+Seed rule: matrix ``i`` (counted across the whole workload, in group order)
+at optimizer step ``t`` (1-based) uses seed ``c*10**6 + i*10 + t`` for the
+workload's seed id ``c`` (given in brackets below).
 
-Configurations (the model shapes the pages name: an 8B dense GPT and a
+Workloads (the model shapes the pages name: an 8B dense GPT and a
 Qwen3-30B-A3B-style MoE, "SOAP, Muon, and Beyond: Pushing LLM Pretraining
 Scales"; per-head orthogonalization, "Reading notes on SOAP, Muon and
 higher-order optimizers", section 1; MoE effective batch, same notes,
 section 3):
 
-1. one 256x128 fp32 gradient, entries N(0,1), three steps.
-2. one dense 8B-style layer in bf16: Wq, Wo 4096x4096; Wk, Wv 1024x4096;
+tiny-256x128-f32 [1]: one 256x128 fp32 gradient, entries N(0,1), three
+   steps.
+8b-dense-layer [2]: one dense 8B-style layer in bf16: Wq, Wo 4096x4096; Wk, Wv 1024x4096;
    gate, up 14336x4096; down 4096x14336.  G = D X^T with D (m x 4096) and
    X (n x 4096) N(0,1): a sum of 4096 rank-1 outer products.
-3. all 32 layers of those shapes (224 matrices), G = U diag(1/k) V^T with
+8b-dense-32-layers [3]: all 32 layers of those shapes (224 matrices), G = U diag(1/k) V^T with
    Haar-random U, V: a power-law spectrum.
-4. an MoE layer: 128 experts x (gate 768x2048, up 768x2048, down
+moe-30b-a3b-layer [4]: an MoE layer: 128 experts x (gate 768x2048, up 768x2048, down
    2048x768), G_e = c_e * Z_e with Z_e N(0,1) and c_e the expert's token
    count under top-8-of-128 routing of 65536 tokens with N(0,1) logits.
-5. per-head: the 96 row blocks (128x4096) of Wq, Wk, Wv of a 4096-wide,
+qkv-heads-kappa1e4 [5]: per-head: the 96 row blocks (128x4096) of Wq, Wk, Wv of a 4096-wide,
    32-head layer, plus gate, up (14336x4096) and down (4096x14336); every
    matrix G = U diag(sigma) V^T with sigma geometric from 1 to 1e-4
    (condition number 1e4).
@@ -47,7 +48,8 @@ class Group:
 
 @dataclass(frozen=True)
 class Config:
-    index: int
+    slug: str
+    seed_id: int
     name: str
     groups: tuple
     kind: str
@@ -67,20 +69,24 @@ def _layer_groups(layers: int):
             Group("gate_up", 2 * layers, 14336, 4096), Group("down", layers, 4096, 14336))
 
 
-CONFIGS = {
-    1: Config(1, "single 256x128 fp32 gradient", (Group("g", 1, 256, 128),), "gauss", torch.float32),
-    2: Config(2, "one GPT-8B-style dense layer", _layer_groups(1), "rank1_sum", torch.bfloat16),
-    3: Config(3, "32 GPT-8B-style dense layers", _layer_groups(32), "power_law", torch.bfloat16),
-    4: Config(4, "30B-A3B-style MoE layer, 128 experts", (Group("gate_up", 256, 768, 2048),
-                                                        Group("down", 128, 2048, 768)), "moe", torch.bfloat16),
-    5: Config(5, "per-head QKV blocks + MLP, condition number 1e4",
-              (Group("qkv_heads", 96, 128, 4096), Group("gate_up", 2, 14336, 4096), Group("down", 1, 4096, 14336)),
-              "kappa", torch.bfloat16),
-}
+WORKLOADS = {c.slug: c for c in (
+    Config("tiny-256x128-f32", 1, "single 256x128 fp32 gradient", (Group("g", 1, 256, 128),), "gauss",
+           torch.float32),
+    Config("8b-dense-layer", 2, "one GPT-8B-style dense layer", _layer_groups(1), "rank1_sum", torch.bfloat16),
+    Config("8b-dense-32-layers", 3, "32 GPT-8B-style dense layers", _layer_groups(32), "power_law", torch.bfloat16),
+    Config("moe-30b-a3b-layer", 4, "30B-A3B-style MoE layer, 128 experts",
+           (Group("gate_up", 256, 768, 2048), Group("down", 128, 2048, 768)), "moe", torch.bfloat16),
+    Config("qkv-heads-kappa1e4", 5, "per-head QKV blocks + MLP, condition number 1e4",
+           (Group("qkv_heads", 96, 128, 4096), Group("gate_up", 2, 14336, 4096), Group("down", 1, 4096, 14336)),
+           "kappa", torch.bfloat16),
+)}
+
+# the workloads the benchmark times (the tiny one is a parity case only)
+BENCH_WORKLOADS = ("8b-dense-layer", "8b-dense-32-layers", "moe-30b-a3b-layer", "qkv-heads-kappa1e4")
 
 
-def seed_of(config: int, matrix: int, step: int) -> int:
-    return config * 10 ** 6 + matrix * 10 + step
+def seed_of(seed_id: int, matrix: int, step: int) -> int:
+    return seed_id * 10 ** 6 + matrix * 10 + step
 
 
 def _gen(seed: int, device) -> torch.Generator:
@@ -136,7 +142,7 @@ def moe_token_counts(seed: int, tokens: int = 65536, experts: int = 128, topk: i
 def gradient(config: Config, matrix: int, rows: int, cols: int, step: int = 1, device="cpu",
              expert_counts: torch.Tensor | None = None) -> torch.Tensor:
     """fp32 gradient of matrix ``matrix`` of ``config`` at ``step``."""
-    seed = seed_of(config.index, matrix, step)
+    seed = seed_of(config.seed_id, matrix, step)
     if config.kind == "gauss":
         return gaussian(rows, cols, seed, device)
     if config.kind == "rank1_sum":
@@ -147,7 +153,7 @@ def gradient(config: Config, matrix: int, rows: int, cols: int, step: int = 1, d
         return condition_number(rows, cols, seed, device=device)
     if config.kind == "moe":
         if expert_counts is None:
-            expert_counts = moe_token_counts(seed_of(config.index, 0, 0), device=device)
+            expert_counts = moe_token_counts(seed_of(config.seed_id, 0, 0), device=device)
         expert = matrix % 128
         return float(expert_counts[expert]) * gaussian(rows, cols, seed, device)
     raise ValueError(config.kind)
@@ -156,7 +162,7 @@ def gradient(config: Config, matrix: int, rows: int, cols: int, step: int = 1, d
 def group_gradients(config: Config, step: int = 1, device="cpu", dtype=None, groups=None):
     """One tensor (count, rows, cols) per group, in the config's dtype."""
     dtype = dtype or config.dtype
-    counts = moe_token_counts(seed_of(config.index, 0, 0), device=device) if config.kind == "moe" else None
+    counts = moe_token_counts(seed_of(config.seed_id, 0, 0), device=device) if config.kind == "moe" else None
     out = []
     i = 0
     for gi, grp in enumerate(config.groups):
@@ -172,7 +178,7 @@ def group_gradients(config: Config, step: int = 1, device="cpu", dtype=None, gro
 def initial_weights(config: Config, device="cpu", dtype=None, std: float = 0.02, seed: int = 7):
     """W_0 ~ N(0, std^2), one tensor (count, rows, cols) per group."""
     dtype = dtype or config.dtype
-    g = _gen(config.index * 10 ** 6 + seed * 100003, device)
+    g = _gen(config.seed_id * 10 ** 6 + seed * 100003, device)
     return [(std * torch.randn(grp.count, grp.rows, grp.cols, generator=g, device=device,
                                dtype=torch.float32)).to(dtype) for grp in config.groups]
 
