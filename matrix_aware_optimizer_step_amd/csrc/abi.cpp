@@ -40,6 +40,9 @@ muon_status_t ok() {
 constexpr int64_t kAlign = 256;
 static_assert(kAdamWChunk == MUON_ADAMW_CHUNK, "chunk size of the AdamW tensor list");
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+// Longest update reduction (padded short side) that takes the k-major bf16
+// update; longer ones read X^T.
+constexpr int kKMajorMaxK = 2048;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 int esize(int32_t dtype) { return dtype == MUON_BF16 ? 2 : 4; }
@@ -110,6 +113,7 @@ struct GroupPlan {
   int32_t tile;
   int32_t Mp, Np;       // padded NS shape
   int32_t Pr, Pc;       // padded stored shape
+  int32_t kmajor;       // bf16 update reads X itself, k-major (no X^T kept)
   // byte offsets into the workspace
   int64_t xlo, xc[2], xt[2], a, b, sumsq, partials;  // xlo: bf16 low part of X (bf16 compute)
   int32_t blocks_per_mat;
@@ -132,6 +136,20 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     return o;
   };
   plan->g.clear();
+  // With bf16 compute and short update reductions (the padded short side
+  // Mp) the update reads X itself, k-major through LDS transpose reads, and
+  // X^T is never written: the saved X'^T stores outweigh the transpose reads'
+  // slower main loop up to about 2048-deep reductions (MI355X measurements).
+  // The choice is made per tile class, so that every update launch holds all
+  // of its class's groups (a class split in two leaves the smaller launch
+  // unable to fill the GPU).
+  bool kmajor_class[2] = {compute == MUON_BF16, compute == MUON_BF16};  // tile 256, 128
+  for (int i = 0; i < ngroups; ++i) {
+    if (rows[i] < 1 || cols[i] < 1) return false;
+    const int64_t ms = std::min(rows[i], cols[i]);
+    const int tile = ms <= 128 ? 128 : 256;
+    if (align_up(ms, tile) > kKMajorMaxK) kmajor_class[tile == 128] = false;
+  }
   for (int i = 0; i < ngroups; ++i) {
     if (counts[i] < 1 || counts[i] > 65535 || rows[i] < 1 || cols[i] < 1) return false;
     if (rows[i] > kMaxElems / cols[i]) return false;
@@ -145,6 +163,7 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.tile = p.ms <= 128 ? 128 : 256;
     p.Mp = static_cast<int32_t>(align_up(p.ms, p.tile));
     p.Np = static_cast<int32_t>(align_up(p.ns, p.tile));
+    p.kmajor = kmajor_class[p.tile == 128];
     // per-matrix byte offsets inside the GEMM kernels are 32-bit: an fp32
     // padded matrix must stay below 4 GiB
     if (static_cast<int64_t>(p.Mp) * p.Np > (int64_t{1} << 30)) return false;
@@ -155,8 +174,9 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.xlo = compute == MUON_BF16 ? take(p.count * mn * 2) : -1;
     p.xc[0] = take(p.count * mn * es);
     p.xc[1] = take(p.count * mn * es);
-    p.xt[0] = take(p.count * mn * es);
-    p.xt[1] = take(p.count * mn * es);
+    // X^T only where the update reads it
+    p.xt[0] = p.kmajor ? -1 : take(p.count * mn * es);
+    p.xt[1] = p.kmajor ? -1 : take(p.count * mn * es);
     p.a = take(p.count * mm * es);
     p.b = take(p.count * mm * es);
     p.blocks_per_mat = elementwise_blocks_per_matrix(p.rows, p.cols);
@@ -275,9 +295,10 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     pa.Pc = p.Pc;
     pa.compute = compute;
     pa.tall = p.tall;
-    // S is the stored orientation, T its transpose; X = S unless tall.
-    pa.S = ws + (p.tall ? p.xt[0] : p.xc[0]);
-    pa.T = ws + (p.tall ? p.xc[0] : p.xt[0]);
+    // S: the stored orientation, T: its transpose; X is whichever is wide.
+    // A k-major group keeps no X^T.
+    pa.S = p.tall ? (p.kmajor ? nullptr : ws + p.xt[0]) : ws + p.xc[0];
+    pa.T = p.tall ? ws + p.xc[0] : (p.kmajor ? nullptr : ws + p.xt[0]);
     pa.s_mat = pa.t_mat = mn * es;
     pa.Lo = compute == MUON_BF16 ? reinterpret_cast<uint16_t*>(ws + p.xlo) : nullptr;
     pa.lo_mat = mn;
@@ -286,13 +307,15 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     if ((e = launch_pack(pa, p.count, stream)) != hipSuccess) return launch_status(e, "pack");
   }
 
-  // 3. the K-step loop: Gram, polynomial, update; one launch per stage and tile class
+  // 3. the K-step loop: Gram, polynomial, update; one launch per stage and
+  // tile class (the update also per operand layout)
   for (int k = 0; k < steps; ++k) {
     const int cur = k & 1;
     const int nxt = cur ^ 1;
     const bool last = k + 1 == steps;
     for (int stage = 0; stage < 3; ++stage) {
       for (int tile : {256, 128}) {
+      for (int km = 0; km < (stage == 2 ? 2 : 1); ++km) {
         GemmLaunch L;
         std::memset(&L, 0, sizeof(L));
         L.a = a;
@@ -301,7 +324,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
         int total = 0;
         for (int g = 0; g < ngroups; ++g) {
           const GroupPlan& p = plan.g[g];
-          if (p.tile != tile) continue;
+          if (p.tile != tile || (stage == 2 && p.kmajor != km)) continue;  // (a class has one layout)
           const int T = p.Mp / tile;
           const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
           const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
@@ -333,9 +356,10 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             G.P = ws + p.b;
             G.p_mat = mm * es;
             G.ldp = p.Mp;
-            G.Q = ws + p.xt[cur];
+            // second operand: X^T (fp32), or X itself read k-major (bf16)
+            G.Q = ws + (p.kmajor ? p.xc[cur] : p.xt[cur]);
             G.q_mat = mn * es;
-            G.ldq = p.Mp;
+            G.ldq = p.kmajor ? p.Np : p.Mp;
             G.K = p.Mp;
             // a*X: X in fp32, or with bf16 compute its low part (the high
             // part is the Q operand, which the kernel adds from LDS)
@@ -364,7 +388,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
               G.o0_mat = mn * 4;
               G.ldo0 = p.Np;
             }
-            if (!last) {
+            if (!last && !p.kmajor) {
               G.OT = ws + p.xt[nxt];
               G.ot_mat = mn * es;
               G.ldot = p.Mp;
@@ -382,8 +406,9 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
         }
         L.total_tiles = total;
         const int epi = stage == 0 ? EPI_GRAM : stage == 1 ? EPI_POLY : (last ? EPI_FINAL : EPI_UPDATE);
-        if ((e = launch_ns_gemm(compute, tile, epi, L, stream)) != hipSuccess)
+        if ((e = launch_ns_gemm(compute, tile, epi, km != 0, L, stream)) != hipSuccess)
           return launch_status(e, "newton-schulz gemm");
+      }
       }
     }
   }

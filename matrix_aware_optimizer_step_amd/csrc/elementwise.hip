@@ -10,9 +10,10 @@
 //                     matrix (deterministic; no float atomics);
 //   apply_kernel      W <- (1 - lr*wd)*W - lr*s*O (section 11.5);
 //   pack_kernel       N / (||N||_F + eps) into the padded Newton-Schulz
-//                     buffers, in both orientations (and the bf16 low part
-//                     of X), through an LDS tile transpose so that reads
-//                     and writes stay coalesced;
+//                     buffers: X (the wide orientation), X^T for fp32
+//                     compute, the bf16 low part of X for bf16 compute,
+//                     through an LDS tile transpose so that reads and writes
+//                     stay coalesced;
 //   copy_out_kernel   the zero-step output, N / (||N||_F + eps).
 //
 // The streaming kernels move 16 bytes per lane per access (8 bf16 or 4+4
@@ -292,15 +293,15 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
   const int tx = threadIdx.x & 63;
   const int ty = threadIdx.x >> 6;  // 0..3
   const int esz = a.compute ? 2 : 4;
-  // read rows of N (zero outside m x n), write rows of S
-  char* S = a.S + mat * a.s_mat;
+  // read rows of N (zero outside m x n), write rows of S (if wanted)
+  char* S = a.S ? a.S + mat * a.s_mat : nullptr;
   for (int rr = ty; rr < kTile; rr += 4) {
     const int r = r0 + rr;
     const int c = c0 + tx;
     float v = 0.0f;
     if (r < a.rows && c < a.cols) v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
     tile[rr][tx] = v;
-    store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
+    if (S) store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
   }
   __syncthreads();
   if (a.Lo) {
@@ -326,7 +327,8 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
   }
-  // write rows of T = columns of the tile
+  // write rows of T = columns of the tile (if wanted)
+  if (!a.T) return;
   char* T = a.T + mat * a.t_mat;
   for (int cc = ty; cc < kTile; cc += 4) {
     const int c = c0 + cc;

@@ -31,8 +31,10 @@ FastDiv make_fastdiv(uint32_t d);
 
 enum Epi : int { EPI_GRAM = 0, EPI_POLY = 1, EPI_UPDATE = 2, EPI_FINAL = 3 };
 
-// One group of same-shape NT products C = P * Q^T (P: rows i, Q: rows j, both
-// contiguous along the reduction index k), with the stage's epilogue.
+// One group of same-shape products C = P * Q^T with the stage's epilogue.
+// P has rows i contiguous along the reduction index k; Q has rows j
+// contiguous along k, except in the bf16 update and last step, where Q is X
+// itself stored k-major (row k, columns j contiguous; ldq is its row pitch).
 struct GemmGroup {
   const char* P; int64_t p_mat;  // bytes between matrices
   const char* Q; int64_t q_mat;
@@ -50,7 +52,7 @@ struct GemmGroup {
   const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL, fp32 compute: X
   int32_t pad0_;
   const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X in the
-                                                 // lo_index() layout (the high part is Q^T, added
+                                                 // lo_index() layout (the high part is Q = X, added
                                                  // from the operand tiles)
   int32_t pad5_;
   char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low
@@ -58,7 +60,7 @@ struct GemmGroup {
   int32_t pad1_;
   char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE, bf16 compute: high part of the next X
   int32_t pad2_;
-  char* OT; int64_t ot_mat; int32_t ldot;        // UPDATE: X^T (next) in compute type
+  char* OT; int64_t ot_mat; int32_t ldot;        // UPDATE, fp32 compute: X^T (next)
   int32_t pad3_;
   // FINAL: the caller's output in its stored orientation
   MatBatch user;
@@ -96,8 +98,9 @@ struct GemmLaunch {
 };
 
 // Launch one stage for all groups (all with the same tile size `tile`).
-// compute: 0 = f32, 1 = bf16.
-hipError_t launch_ns_gemm(int compute, int tile, int epi, const GemmLaunch& L,
+// compute: 0 = f32, 1 = bf16.  kmajor (bf16 update and last step only): the
+// second operand of every group is X itself, k-major; otherwise X^T.
+hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L,
                           hipStream_t stream);
 
 // ------------------------------------------------------------ elementwise
@@ -152,8 +155,8 @@ struct PackArgs {
   int32_t Pr, Pc;          // padded
   int32_t compute;         // element type of S and T
   int32_t tall;
-  char* S; int64_t s_mat;  // bytes per matrix
-  char* T; int64_t t_mat;
+  char* S; int64_t s_mat;  // stored orientation (bytes per matrix); null: not written
+  char* T; int64_t t_mat;  // its transpose; null: not written
   uint16_t* Lo; int64_t lo_mat;  // elements per matrix, in the lo_index() layout
   int32_t lo_bm, lo_tiles_n;     // update tile size and tile columns of X
 };

@@ -10,6 +10,9 @@
 //   update  X' = a X + B X    P = B, Q = X^T       (X^T kept alongside X)
 //
 // so one kernel template serves all three, with the stage's epilogue fused.
+// With bf16 compute the update instead reads X itself as a k-major second
+// operand (row k of X holds the tile's columns contiguously) through LDS
+// transpose reads, so no X^T is ever written.
 //
 // Tiling: a workgroup computes a BM x BM output tile (BM = 256 with eight
 // wave64s in a 2x4 grid, each owning 128x64; BM = 128 with four wave64s in a
@@ -35,6 +38,19 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 typedef uint32_t Chunk __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  In each group of 16 lanes,
+// lane j names an 8-byte piece P[j] (four 16-bit values); lane i receives
+// P[4e + i/4][i%4] as its value e (checked by an in-bounds probe).  So when
+// lane j points at row k0 + j/4, columns c0 + 4*(j%4) .. +3 of a row-major
+// 16-bit tile, lane i receives column c0 + i of rows k0 .. k0+3.
+__device__ __forceinline__ u32x2_t lds_read_tr(const char* p) {
+  const i16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
@@ -168,8 +184,10 @@ __device__ __forceinline__ void barrier_keep_vm() {
 //           tile rows, column by column inside a group, so that workgroups
 //           running together (one XCD's range under XCD = 1) share GM row
 //           blocks of P and a few column blocks of Q in L2.
+//   QN:     1 = the bf16 update's second operand is X itself, k-major (read
+//           through LDS transpose reads); 0 = it is X^T, n-major.
 template <typename T, int BM, int WGM, int WGN, int EPI, int RC = 4, int STAGES = 4, int SWZ = 1, int DMA = 1,
-          int XCD = 0, int SCHED = 0, int GM = 1, int BN = BM>
+          int XCD = 0, int SCHED = 0, int GM = 1, int BN = BM, int QN = 0>
 __global__ __launch_bounds__(64 * WGM * WGN, 2)  // at least two waves per SIMD
 void ns_gemm_kernel(const GemmLaunch L) {
   constexpr int NW = WGM * WGN;          // waves
@@ -191,6 +209,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
   constexpr int OPB = BM * ROWB;         // bytes of the P tile (the Q tile follows)
   constexpr int STB = (BM + BN) * ROWB;  // bytes of one stage
   static_assert(DMA || STAGES == 2, "the register path is double-buffered");
+  // bf16 update: Q is X, k-major; a k-tile of it is BK rows of QROWB bytes,
+  // 16-byte chunks XOR-swizzled in groups of four by (row % 4), so that the
+  // transpose reads of 4 consecutive rows x 64 bytes hit all 64 banks once.
+  constexpr bool kQN = QN && (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+  constexpr int QROWB = BN * 2;
+  constexpr int QRC = QROWB / 16;
+  static_assert(!kQN || (DMA && QRC >= 16 && BK * QROWB == BN * ROWB), "k-major Q tile: same bytes as n-major");
   static_assert(LOADS * RPP == BM && LOADSQ * RPP == BN, "tile rows must split evenly over the threads");
   static_assert(IPW * RPI * NW == BM && IPWQ * RPI * NW == BN, "tile rows must split evenly over the waves");
   constexpr int EPI_BYTES = NW * 64 * 68 * 4;  // transposed-store staging
@@ -254,7 +279,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
     const int ldp = G.ldp;
     const int ldq = G.ldq;
     const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T);
-    const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * ldq * sizeof(T);
+    // a k-major Q starts at the tile's first column, an n-major one at its first row
+    const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * (kQN ? 1 : ldq) * sizeof(T);
     const int nk = G.K / BK;
 
     // ---- operand staging
@@ -273,9 +299,16 @@ void ns_gemm_kernel(const GemmLaunch L) {
       }
 #pragma unroll
       for (int r = 0; r < IPWQ; ++r) {
-        const int row = (wave * IPWQ + r) * RPI + lane / RC;
-        const int c = swizzle<SWZ, RC>(row, lane % RC);
-        dofs_q[r] = static_cast<uint32_t>((row * ldq + c * CH) * static_cast<int>(sizeof(T)));
+        if constexpr (kQN) {
+          const int slot = (wave * IPWQ + r) * 64 + lane;  // 16-byte slot of the k-tile in LDS
+          const int row = slot / QRC;                      // k
+          const int c = (slot % QRC) ^ ((row & 3) << 2);   // logical chunk: columns 8c .. 8c+7
+          dofs_q[r] = static_cast<uint32_t>(row * ldq * 2 + c * 16);
+        } else {
+          const int row = (wave * IPWQ + r) * RPI + lane / RC;
+          const int c = swizzle<SWZ, RC>(row, lane % RC);
+          dofs_q[r] = static_cast<uint32_t>((row * ldq + c * CH) * static_cast<int>(sizeof(T)));
+        }
       }
     } else {
       const int lrow = tid / RC;
@@ -295,7 +328,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
     auto dma_issue = [&](int kt, int st) {
       const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
       const char* pk = Pt + kb;
-      const char* qk = Qt + kb;
+      const char* qk = Qt + (kQN ? static_cast<int64_t>(kt) * BK * ldq * static_cast<int64_t>(sizeof(T)) : kb);
       char* lp = smem + st * STB + wave * IPW * 1024;
       char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
@@ -361,6 +394,18 @@ void ns_gemm_kernel(const GemmLaunch L) {
       fb_row[f] = wn * WTN + f * 32 + frow;
       fb_off[f] = OPB + fb_row[f] * ROWB;
     }
+    // k-major Q: lane j of a 16-lane group points at row (j/4) of a group of
+    // four and at columns 4*(j%4) .. +3 of its 16-column half of block f;
+    // rows of one read are congruent mod 4 to j/4, which fixes the swizzle
+    int qn_off[kQN ? FN : 1];
+    if constexpr (kQN) {
+      const int j = lane & 15;
+#pragma unroll
+      for (int f = 0; f < FN; ++f) {
+        const int col = wn * WTN + f * 32 + 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+        qn_off[f] = (j >> 2) * QROWB + (((col >> 3) ^ ((j >> 2) << 2)) << 4) + (col & 7) * 2;
+      }
+    }
 
     // Main loop.  Fragments of substep s+1 are read while the MFMAs of
     // substep s run; at the last substep of k-tile kt the wave waits for its
@@ -374,14 +419,26 @@ void ns_gemm_kernel(const GemmLaunch L) {
 #pragma unroll
       for (int f = 0; f < FM; ++f)
         a[f] = *reinterpret_cast<const Chunk*>(sb + fa_off[f] + (swizzle<SWZ, RC>(fa_row[f], ch) << 4));
+      if constexpr (kQN) {
+        // k = 16s + 8*half + 0..7 of column l%32: two transpose reads
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
-        b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
+        for (int f = 0; f < FN; ++f) {
+          const char* q = sb + OPB + qn_off[f] + (8 * half + 16 * s) * QROWB;
+          const u32x2_t lo = lds_read_tr(q);
+          const u32x2_t hi = lds_read_tr(q + 4 * QROWB);
+          b[f] = Chunk{lo.x, lo.y, hi.x, hi.y};
+        }
+      } else {
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+          b[f] = *reinterpret_cast<const Chunk*>(sb + fb_off[f] + (swizzle<SWZ, RC>(fb_row[f], ch) << 4));
+      }
     };
     frags(smem, 0, af[0], bfr[0]);
     // bf16 update: the high part of a*X enters from the operand tiles (below),
-    // the epilogue adds only the low part.  k-tile kt_x0 + hh holds rows
-    // [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e. kFPK of its 32-row blocks.
+    // the epilogue adds only the low part.  k-tile kt_x0 + hh of Q (X k-major,
+    // or X^T) holds rows [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e.
+    // kFPK of its 32-row blocks, at the wave's columns.
     constexpr bool kAddXInLoop = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
     constexpr int kFPK = BK / 32;
     constexpr int kNH = WTM / BK;
@@ -403,8 +460,9 @@ void ns_gemm_kernel(const GemmLaunch L) {
       const char* sb = smem + st * STB;
       const int stn = (st + 1 == STAGES) ? 0 : st + 1;
       if constexpr (kAddXInLoop) {
-        // a * X[i][j] = a * Q[j][k = i]: the k-tiles that cover this wave's
-        // rows hold the bf16 high part of X for its output elements.
+        // a * X[i][j] = a * Q[k = i][j] (k-major) or a * Q[j][k = i] (X^T):
+        // the k-tiles that cover this wave's rows hold the bf16 high part of
+        // X for its output elements.
 #pragma unroll
         for (int hh = 0; hh < kNH; ++hh) {
           if (kt == kt_x0 + hh) {  // uniform over the wave
@@ -414,9 +472,16 @@ void ns_gemm_kernel(const GemmLaunch L) {
               for (int fj = 0; fj < FN; ++fj)
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                  // rows f*32 + 8q + 4*half + 0..3 of the k-tile, column l%32 of block fj
                   const int fi = hh * kFPK + f;
-                  const uint2 v = *reinterpret_cast<const uint2*>(
-                      sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
+                  u32x2_t v;
+                  if constexpr (kQN) {
+                    v = lds_read_tr(sb + OPB + qn_off[fj] + (f * 32 + 8 * q + 4 * half) * QROWB);
+                  } else {  // X^T tile: the four values are consecutive in row l%32
+                    const uint2 u = *reinterpret_cast<const uint2*>(
+                        sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
+                    v = u32x2_t{u.x, u.y};
+                  }
                   acc[fi][fj][4 * q + 0] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x));
                   acc[fi][fj][4 * q + 1] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
                   acc[fi][fj][4 * q + 2] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y));
@@ -718,7 +783,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
             put8(gj0 + c, gi0 + h * 64 + rc, G.ns, G.ms, x0, x1);
           }
         }
-      } else {
+      } else if constexpr (!kQN) {  // the bf16 update writes no X'^T
         // LDS -> global: 8 lanes write one 8 x 8-element row segment of the output
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -760,36 +825,48 @@ int resident_workgroups(int tile) {
 // k-tiles moved by LDS DMA through a two-stage ring, the 64-bank swizzle,
 // XCD-contiguous tile ranges and groups of four tile rows for the
 // non-symmetric product.
-template <typename T, int BM, int WGM, int WGN, int EPI>
+template <typename T, int BM, int WGM, int WGN, int EPI, int QN = 0>
 void launch_one(const GemmLaunch& L, hipStream_t stream) {
   constexpr int RC = 8, STAGES = 2, SWZ = 1, DMA = 1, XCD = 1, SCHED = 0, GM = 4;
   const int cap = resident_workgroups(BM);
   const int grid = (cap >= 8 && L.total_tiles >= 4 * cap) ? cap : L.total_tiles;
-  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM>), dim3(grid),
+  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM, BM, QN>), dim3(grid),
                      dim3(64 * WGM * WGN), 0, stream, L);
 }
 
 template <typename T, int BM, int WGM, int WGN>
-hipError_t launch_t(int epi, const GemmLaunch& L, hipStream_t stream) {
+hipError_t launch_t(int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
   switch (epi) {
     case EPI_GRAM: launch_one<T, BM, WGM, WGN, EPI_GRAM>(L, stream); break;
     case EPI_POLY: launch_one<T, BM, WGM, WGN, EPI_POLY>(L, stream); break;
-    case EPI_UPDATE: launch_one<T, BM, WGM, WGN, EPI_UPDATE>(L, stream); break;
-    default: launch_one<T, BM, WGM, WGN, EPI_FINAL>(L, stream); break;
+    case EPI_UPDATE:
+      if (kmajor && sizeof(T) == 2) {
+        launch_one<T, BM, WGM, WGN, EPI_UPDATE, 1>(L, stream);
+      } else {
+        launch_one<T, BM, WGM, WGN, EPI_UPDATE>(L, stream);
+      }
+      break;
+    default:
+      if (kmajor && sizeof(T) == 2) {
+        launch_one<T, BM, WGM, WGN, EPI_FINAL, 1>(L, stream);
+      } else {
+        launch_one<T, BM, WGM, WGN, EPI_FINAL>(L, stream);
+      }
+      break;
   }
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ns_gemm(int compute, int tile, int epi, const GemmLaunch& L, hipStream_t stream) {
+hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
   if (L.total_tiles <= 0) return hipSuccess;
   if (compute == 1) {
-    return tile == 256 ? launch_t<uint16_t, 256, 2, 4>(epi, L, stream)
-                       : launch_t<uint16_t, 128, 2, 2>(epi, L, stream);
+    return tile == 256 ? launch_t<uint16_t, 256, 2, 4>(epi, kmajor, L, stream)
+                       : launch_t<uint16_t, 128, 2, 2>(epi, kmajor, L, stream);
   }
-  return tile == 256 ? launch_t<float, 256, 2, 4>(epi, L, stream)
-                     : launch_t<float, 128, 2, 2>(epi, L, stream);
+  return tile == 256 ? launch_t<float, 256, 2, 4>(epi, false, L, stream)
+                     : launch_t<float, 128, 2, 2>(epi, false, L, stream);
 }
 
 }  // namespace muon

@@ -300,6 +300,56 @@ def test_grouped_equals_separate_calls(mx):
         assert torch.equal(a, b)
 
 
+def test_grouped_mixed_update_layouts(mx):
+    """With bf16 compute a tile class whose every group pads its short side to
+    at most 2048 updates with X read k-major (no X^T kept); otherwise with X^T.
+    Alone, the first and last shapes here go k-major; grouped with the others
+    they share the X^T layout.  Both layouts give every lane the same k values
+    for every MFMA, so the grouped call must equal the separate calls bit for
+    bit, wide and tall, and match the oracle."""
+    shapes = [(2, 520, 700), (1, 2100, 2200), (1, 2300, 2050), (1, 1900, 2040)]
+    Ns = [randn(s, 70 + k, torch.bfloat16) for k, s in enumerate(shapes)]
+    sep = [run_ns(mx, N, mx.MUON_BF16) for N in Ns]
+    outs = [torch.empty_like(N) for N in Ns]
+    mx.orthogonalize_grouped(Ns, outs, None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    for (n, r, c), N, a, b in zip(shapes, Ns, sep, outs):
+        assert torch.equal(a, b), f"{r}x{c}"
+        for i in range(n):
+            assert rel(f64(b[i]), O.newton_schulz(f64(N[i]), 5)) <= TOL_BF16, f"{r}x{c} matrix {i}"
+
+
+def test_persistent_grid_matches_short_launches(mx):
+    """Launches with at least four tiles per resident workgroup run on a
+    persistent grid (each workgroup walks tiles blockIdx.x, +grid, ...).
+    Three groups sized from the device's CU count so that every stage of both
+    tile sizes takes that path, one of them crossing group boundaries; the
+    result must equal, bit for bit, chunks of at most 100 matrices (one tile
+    per workgroup), and sampled matrices must match the oracle."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    cap256, cap128 = cus & ~7, (2 * cus) & ~7
+    nB = 150                                # 640x384: tall, 3 upper tiles of 256
+    nA = max(4 * cap256 - 3 * nB, 0) + 64   # 256x512: one Gram tile of 256
+    nC = 4 * cap128 + 52                    # 128x256: one Gram tile of 128
+    assert nA + 3 * nB >= 4 * cap256 and nC >= 4 * cap128
+    shapes = [(nA, 256, 512), (nB, 640, 384), (nC, 128, 256)]
+    print(f"[persistent] {cus} CUs, groups {shapes}", flush=True)
+    Ns = [randn(s, 60 + k, torch.bfloat16) for k, s in enumerate(shapes)]
+    outs = [torch.empty_like(N) for N in Ns]
+    mx.orthogonalize_grouped(Ns, outs, None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    short = [torch.empty_like(N) for N in Ns]
+    for N, o in zip(Ns, short):
+        for s in range(0, N.shape[0], 100):
+            mx.orthogonalize(N[s:s + 100], o[s:s + 100], None, 5, O.QUINTIC, O.EPS, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    for (n, r, c), a, b in zip(shapes, outs, short):
+        diff = (a != b).reshape(n, -1).any(dim=1).nonzero().flatten().tolist()
+        assert not diff, f"{r}x{c}: matrices {diff[:8]} differ from the short launches"
+    for (n, r, c), N, out in zip(shapes, Ns, outs):
+        for i in sorted({0, n // 3, n - 1}):
+            assert rel(f64(out[i]), O.newton_schulz(f64(N[i]), 5)) <= TOL_BF16, f"{r}x{c} matrix {i}"
+
+
 # --------------------------------------------------------------- full steps
 
 @pytest.mark.parametrize("nesterov", [True, False])
