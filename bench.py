@@ -58,13 +58,13 @@ def make_stepper(mx, weights, grads, coeffs="quintic", steps=None):
                        steps=k if steps is None else steps)
 
 
-def measured_traffic(slug):
-    """HBM bytes per step of the Newton-Schulz GEMM launches, from the
-    rocprofv3 FETCH_SIZE/WRITE_SIZE summary in profiles/, or None when that
-    summary was taken on a different version of the kernel source."""
+def measured_traffic(profile, source, key):
+    """HBM bytes per step from a rocprofv3 FETCH_SIZE/WRITE_SIZE summary in
+    profiles/ (its traffic-record line), or None when the summary is missing
+    or was taken on a different version of the kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"ns_gemm_{slug}_hbm_traffic.md")
-    src = os.path.join(ROOT, "matrix_aware_optimizer_step_amd", "csrc", "ns_gemm.hip")
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "matrix_aware_optimizer_step_amd", "csrc", source)
     if not os.path.exists(path):
         return None
     rec = None
@@ -75,7 +75,7 @@ def measured_traffic(slug):
         return None
     if rec.get("kernel_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
         return None
-    return rec["ns_gemm_bytes_per_step"]
+    return rec[key]
 
 
 ADAM_LR, ADAM_WD, ADAM_BETAS, ADAM_EPS = 3e-4, 0.1, (0.9, 0.999), 1e-8
@@ -161,7 +161,8 @@ def bench_adamw(args):
                                   f"65 RMSNorm weights of {synth.ADAMW_HIDDEN}", "elements": elems,
                       "bytes_per_element": ADAMW_BYTES, "parallelism": "single GPU"},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                        "frac": gbs / PEAK_HBM_GBS, "traffic": None, "kernel": "adamw_kernel"},
+                        "frac": gbs / PEAK_HBM_GBS, "kernel": "adamw_kernel",
+                        "traffic": measured_traffic("adamw_kernel_8b_nonmatrix_params.md", "adamw.hip", "bytes_per_step")},
            "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
@@ -317,7 +318,8 @@ def main():
         "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
                         "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},
         "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(cfg.slug),
+                     "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"ns_gemm_{cfg.slug}_hbm_traffic.md", "ns_gemm.hip",
+                                                                    "ns_gemm_bytes_per_step"),
                      "kernel": "ns_gemm_kernel (Gram, polynomial and update launches of muon_orthogonalize_grouped)"},
         "cpu_baseline": cpu,
     }
