@@ -120,6 +120,34 @@ muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom,
                             int nesterov, void* workspace, size_t ws_bytes,
                             void* stream);
 
+/* Bytes of device workspace muon_momentum_grouped needs: the sum of
+ * muon_momentum_workspace over the groups; 0 for invalid arguments. */
+size_t muon_momentum_grouped_workspace(int ngroups, const int64_t* counts,
+                                       const int64_t* rows, const int64_t* cols);
+
+/*
+ * muon_momentum for several shape classes in one launch (plus one launch of
+ * the sum-of-squares finalization): group g is the batch grads[g], moms[g],
+ * nouts[g] with its own device float[count] sumsqs[g], all with the meaning,
+ * layout and rules of muon_momentum; beta and nesterov are shared.  The
+ * pages' per-layer and per-expert matrices come in a few shape classes
+ * ([NOTES] section 1 and 3), so one step's momentum is one grid here.
+ *
+ * ngroups: 1..8.  grads, moms: host arrays of ngroups descriptors.  nouts:
+ * host array of ngroups descriptors, or NULL (only without Nesterov: M is
+ * then the Newton-Schulz input of every group).  sumsqs: host array of
+ * ngroups device pointers.  workspace: at least
+ * muon_momentum_grouped_workspace bytes, 16-byte aligned.  Every group is
+ * validated before anything is enqueued; muon_last_error() names the
+ * failing group.  Results equal separate muon_momentum calls bit for bit.
+ */
+muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads,
+                                    const muon_batch_t* moms,
+                                    const muon_batch_t* nouts,
+                                    float* const* sumsqs, float beta,
+                                    int nesterov, void* workspace,
+                                    size_t ws_bytes, void* stream);
+
 /* Bytes of device workspace muon_orthogonalize needs for `count` matrices
  * of stored shape rows x cols computed in `compute` (MUON_BF16 or MUON_F32).
  * Returns 0 for invalid arguments. */
@@ -191,6 +219,19 @@ muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins,
 muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho,
                          float lr, float weight_decay, int32_t mode,
                          float coeff, void* stream);
+
+/*
+ * muon_apply for several shape classes in one launch: group g updates
+ * weights[g] from orthos[g] with the meaning and rules of muon_apply, its
+ * scale s taken from its own (rows, cols); lr, weight_decay, mode and coeff
+ * are shared.  ngroups: 1..8; weights, orthos: host arrays of ngroups
+ * descriptors.  Every group is validated before the launch; results equal
+ * separate muon_apply calls bit for bit.
+ */
+muon_status_t muon_apply_grouped(int ngroups, const muon_batch_t* weights,
+                                 const muon_batch_t* orthos, float lr,
+                                 float weight_decay, int32_t mode, float coeff,
+                                 void* stream);
 
 /*
  * AdamW for the parameters Muon does not take (embeddings, output head, norms,

@@ -10,9 +10,10 @@ tensors into descriptors and holds the buffers of a whole step.
 from . import _lib
 from ._lib import (MUON_BF16, MUON_F32, MUON_SCALE_MATCH_RMS, MUON_SCALE_NONE, MUON_SCALE_ORIGINAL, MuonBatch,
                    MuonError)
-from .muon import (EPS, QUINTIC, AdamW, Batch, MuonStep, OptimizerStep, apply, batch, is_muon_param, momentum,
-                   orthogonalize, orthogonalize_grouped, workspace)
+from .muon import (EPS, QUINTIC, AdamW, Batch, MuonStep, OptimizerStep, apply, apply_grouped, batch, is_muon_param,
+                   momentum, momentum_grouped, orthogonalize, orthogonalize_grouped, workspace)
 
 __all__ = ["_lib", "MUON_BF16", "MUON_F32", "MUON_SCALE_MATCH_RMS", "MUON_SCALE_NONE", "MUON_SCALE_ORIGINAL",
-           "MuonBatch", "MuonError", "EPS", "QUINTIC", "Batch", "MuonStep", "apply", "batch", "momentum",
-           "orthogonalize", "orthogonalize_grouped", "workspace", "AdamW", "OptimizerStep", "is_muon_param"]
+           "MuonBatch", "MuonError", "EPS", "QUINTIC", "Batch", "MuonStep", "apply", "apply_grouped", "batch",
+           "momentum", "momentum_grouped", "orthogonalize", "orthogonalize_grouped", "workspace", "AdamW",
+           "OptimizerStep", "is_muon_param"]

@@ -24,8 +24,9 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
           3: "MUON_ERR_WORKSPACE", 4: "MUON_ERR_LAUNCH"}
 
 EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
-            "muon_momentum", "muon_orthogonalize_workspace", "muon_orthogonalize",
-            "muon_orthogonalize_grouped_workspace", "muon_orthogonalize_grouped", "muon_apply", "muon_adamw")
+            "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped",
+            "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
+            "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw")
 
 ADAMW_CHUNK = 4096  # MUON_ADAMW_CHUNK
 
@@ -68,6 +69,10 @@ def load() -> ctypes.CDLL:
         "muon_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "muon_momentum_workspace": (sz, [i64, i64, i64]),
         "muon_momentum": (ctypes.c_int, [P, P, P, vp, f32, ctypes.c_int, vp, sz, vp]),
+        "muon_momentum_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                 ctypes.POINTER(i64)]),
+        "muon_momentum_grouped": (ctypes.c_int, [ctypes.c_int, P, P, P, ctypes.POINTER(vp), f32, ctypes.c_int, vp,
+                                                 sz, vp]),
         "muon_orthogonalize_workspace": (sz, [i64, i64, i64, i32]),
         "muon_orthogonalize": (ctypes.c_int, [P, vp, P, ctypes.c_int, f32, f32, f32, f32, i32, vp, sz, vp]),
         "muon_orthogonalize_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -75,6 +80,7 @@ def load() -> ctypes.CDLL:
         "muon_orthogonalize_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(vp), P, ctypes.c_int,
                                                       f32, f32, f32, f32, i32, vp, sz, vp]),
         "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
+        "muon_apply_grouped": (ctypes.c_int, [ctypes.c_int, P, P, f32, f32, i32, f32, vp]),
         "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
     }
     for name, (res, args) in sig.items():
@@ -108,6 +114,24 @@ def muon_momentum(grad: MuonBatch, mom: MuonBatch, nout: MuonBatch | None, sumsq
     st = load().muon_momentum(_ref(grad), _ref(mom), _ref(nout), sumsq_ptr, beta, int(bool(nesterov)),
                               workspace_ptr, ws_bytes, stream)
     _check(st, "muon_momentum")
+
+
+def muon_momentum_grouped_workspace(counts, rows, cols) -> int:
+    n = len(counts)
+    arr = ctypes.c_int64 * n
+    return load().muon_momentum_grouped_workspace(n, arr(*counts), arr(*rows), arr(*cols))
+
+
+def muon_momentum_grouped(grads, moms, nouts, sumsq_ptrs, beta: float, nesterov: bool, workspace_ptr: int,
+                          ws_bytes: int, stream: int) -> None:
+    n = len(grads)
+    if len(moms) != n or len(sumsq_ptrs) != n or (nouts is not None and len(nouts) != n):
+        raise ValueError("per-group lists differ in length")
+    no = None if nouts is None else (MuonBatch * n)(*nouts)
+    st = load().muon_momentum_grouped(n, (MuonBatch * n)(*grads), (MuonBatch * n)(*moms), no,
+                                      (ctypes.c_void_p * n)(*sumsq_ptrs), beta, int(bool(nesterov)),
+                                      workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_momentum_grouped")
 
 
 def muon_orthogonalize_workspace(count: int, rows: int, cols: int, compute: int) -> int:
@@ -147,6 +171,16 @@ def muon_apply(weight: MuonBatch, ortho: MuonBatch, lr: float, weight_decay: flo
                stream: int) -> None:
     st = load().muon_apply(_ref(weight), _ref(ortho), lr, weight_decay, mode, coeff, stream)
     _check(st, "muon_apply")
+
+
+def muon_apply_grouped(weights, orthos, lr: float, weight_decay: float, mode: int, coeff: float,
+                       stream: int) -> None:
+    n = len(weights)
+    if len(orthos) != n:
+        raise ValueError("weights and orthos differ in length")
+    st = load().muon_apply_grouped(n, (MuonBatch * n)(*weights), (MuonBatch * n)(*orthos), lr, weight_decay,
+                                   mode, coeff, stream)
+    _check(st, "muon_apply_grouped")
 
 
 def muon_adamw(tensors: MuonTensorList, step: int, lr: float, beta1: float, beta2: float, eps: float,

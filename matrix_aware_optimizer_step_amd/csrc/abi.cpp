@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
+#include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <vector>
@@ -29,6 +30,15 @@ muon_status_t fail(muon_status_t st, const char* fmt, ...) {
   va_start(ap, fmt);
   vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
   va_end(ap);
+  return st;
+}
+
+// Prefix the current error detail with the group it belongs to.
+muon_status_t in_group(muon_status_t st, int g) {
+  if (st == MUON_OK) return st;
+  char tmp[sizeof(g_last_error)];
+  snprintf(tmp, sizeof(tmp), "group %d: %s", g, g_last_error);
+  memcpy(g_last_error, tmp, sizeof(tmp));
   return st;
 }
 
@@ -478,9 +488,14 @@ size_t muon_momentum_workspace(int64_t count, int64_t rows, int64_t cols) {
   return static_cast<size_t>(align_up(count * elementwise_blocks_per_matrix(rows, cols) * 4, kAlign));
 }
 
-muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom, const muon_batch_t* nout,
-                            float* sumsq, float beta, int nesterov, void* workspace, size_t ws_bytes,
-                            void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of one momentum batch; fills the kernel arguments (partials left
+// for the caller) and whether 16-byte accesses apply.
+muon_status_t prepare_momentum(const muon_batch_t* grad, const muon_batch_t* mom, const muon_batch_t* nout,
+                               float* sumsq, float beta, int nesterov, MomentumArgs* a, bool* vec) {
   muon_status_t st;
   if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
   if ((st = check_batch(mom, "mom", false)) != MUON_OK) return st;
@@ -494,30 +509,136 @@ muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom, c
   if (!sumsq) return fail(MUON_ERR_INVALID_VALUE, "sumsq is NULL");
   if (!(beta >= 0.0f && beta < 1.0f)) return fail(MUON_ERR_INVALID_VALUE, "beta must lie in [0, 1)");
   if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_VALUE, "nesterov must be 0 or 1");
-  const size_t need = muon_momentum_workspace(grad->count, grad->rows, grad->cols);
+  std::memset(a, 0, sizeof(*a));
+  a->G = to_mat(grad);
+  a->M = to_mat(mom);
+  if (nout) a->N = to_mat(nout);
+  a->has_n = nout != nullptr;
+  a->blocks_per_mat = elementwise_blocks_per_matrix(grad->rows, grad->cols);
+  a->rows = static_cast<int32_t>(grad->rows);
+  a->cols = static_cast<int32_t>(grad->cols);
+  a->cdiv = make_fastdiv(static_cast<uint32_t>(grad->cols));
+  a->beta = beta;
+  a->nesterov = nesterov;
+  *vec = vec_ok(grad) && vec_ok(mom) && (!nout || vec_ok(nout));
+  return MUON_OK;
+}
+
+muon_status_t check_workspace(void* workspace, size_t ws_bytes, size_t need) {
   if (!workspace || ws_bytes < need)
     return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", ws_bytes, need);
   if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
     return fail(MUON_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  return MUON_OK;
+}
 
+// Checks of one apply batch; fills the kernel arguments.
+muon_status_t prepare_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,
+                            int32_t mode, float coeff, ApplyArgs* a, bool* vec) {
+  muon_status_t st;
+  if ((st = check_batch(weight, "weight", true)) != MUON_OK) return st;
+  if ((st = check_batch(ortho, "ortho", true)) != MUON_OK) return st;
+  if (!same_shape(weight, ortho)) return fail(MUON_ERR_INVALID_VALUE, "weight and ortho shapes differ");
+  if (!finite(lr) || !finite(weight_decay) || !finite(coeff))
+    return fail(MUON_ERR_INVALID_VALUE, "lr, weight_decay and coeff must be finite");
+  const double m = static_cast<double>(weight->rows);
+  const double n = static_cast<double>(weight->cols);
+  double s;
+  switch (mode) {
+    case MUON_SCALE_MATCH_RMS: s = static_cast<double>(coeff) * std::sqrt(m > n ? m : n); break;
+    case MUON_SCALE_ORIGINAL: s = std::sqrt(m / n > 1.0 ? m / n : 1.0); break;
+    case MUON_SCALE_NONE: s = 1.0; break;
+    default: return fail(MUON_ERR_INVALID_VALUE, "unknown scale mode %d", mode);
+  }
+  std::memset(a, 0, sizeof(*a));
+  a->W = to_mat(weight);
+  a->O = to_mat(ortho);
+  a->rows = static_cast<int32_t>(weight->rows);
+  a->cols = static_cast<int32_t>(weight->cols);
+  a->cdiv = make_fastdiv(static_cast<uint32_t>(weight->cols));
+  a->decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
+  a->step = static_cast<float>(static_cast<double>(lr) * s);
+  *vec = vec_ok(weight) && vec_ok(ortho);
+  return MUON_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom, const muon_batch_t* nout,
+                            float* sumsq, float beta, int nesterov, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  muon_status_t st;
   MomentumArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.G = to_mat(grad);
-  a.M = to_mat(mom);
-  if (nout) a.N = to_mat(nout);
-  a.has_n = nout != nullptr;
+  bool vec;
+  if ((st = prepare_momentum(grad, mom, nout, sumsq, beta, nesterov, &a, &vec)) != MUON_OK) return st;
+  if ((st = check_workspace(workspace, ws_bytes, muon_momentum_workspace(grad->count, grad->rows, grad->cols))) !=
+      MUON_OK)
+    return st;
   a.partials = static_cast<float*>(workspace);
-  a.blocks_per_mat = elementwise_blocks_per_matrix(grad->rows, grad->cols);
-  a.rows = static_cast<int32_t>(grad->rows);
-  a.cols = static_cast<int32_t>(grad->cols);
-  a.cdiv = make_fastdiv(static_cast<uint32_t>(grad->cols));
-  a.beta = beta;
-  a.nesterov = nesterov;
-  const bool vec = vec_ok(grad) && vec_ok(mom) && (!nout || vec_ok(nout));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_momentum(a, grad->count, vec, s);
   if (e != hipSuccess) return launch_status(e, "momentum");
   e = launch_sumsq_finalize(a.partials, a.blocks_per_mat, sumsq, grad->count, s);
+  if (e != hipSuccess) return launch_status(e, "sumsq finalize");
+  return ok();
+}
+
+size_t muon_momentum_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
+                                       const int64_t* cols) {
+  if (ngroups < 1 || ngroups > kMaxGroups || !counts || !rows || !cols) return 0;
+  size_t total = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const size_t w = muon_momentum_workspace(counts[g], rows[g], cols[g]);
+    if (w == 0) return 0;
+    total += w;
+  }
+  return total;
+}
+
+muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
+                                    const muon_batch_t* nouts, float* const* sumsqs, float beta, int nesterov,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!grads || !moms || !sumsqs) return fail(MUON_ERR_INVALID_VALUE, "grads, moms and sumsqs must not be NULL");
+  MomentumGroups G;
+  FinalizeGroups F;
+  std::memset(&G, 0, sizeof(G));
+  std::memset(&F, 0, sizeof(F));
+  G.ngroups = F.ngroups = ngroups;
+  int64_t counts[kMaxGroups], rows[kMaxGroups], cols[kMaxGroups];
+  muon_status_t st;
+  for (int g = 0; g < ngroups; ++g) {
+    bool vec;
+    st = prepare_momentum(&grads[g], &moms[g], nouts ? &nouts[g] : nullptr, sumsqs[g], beta, nesterov, &G.g[g],
+                          &vec);
+    if (st != MUON_OK) return in_group(st, g);
+    G.vec[g] = vec;
+    counts[g] = grads[g].count;
+    rows[g] = grads[g].rows;
+    cols[g] = grads[g].cols;
+  }
+  if ((st = check_workspace(workspace, ws_bytes, muon_momentum_grouped_workspace(ngroups, counts, rows, cols))) !=
+      MUON_OK)
+    return st;
+  char* ws = static_cast<char*>(workspace);
+  for (int g = 0; g < ngroups; ++g) {
+    G.g[g].partials = reinterpret_cast<float*>(ws);
+    ws += muon_momentum_workspace(counts[g], rows[g], cols[g]);
+    G.first[g + 1] = G.first[g] + counts[g] * G.g[g].blocks_per_mat;
+    F.first[g + 1] = F.first[g] + counts[g];
+    F.per[g] = G.g[g].blocks_per_mat;
+    F.partials[g] = G.g[g].partials;
+    F.sumsq[g] = sumsqs[g];
+  }
+  if (G.first[ngroups] > INT32_MAX)
+    return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)G.first[ngroups]);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_momentum_grouped(G, s);
+  if (e != hipSuccess) return launch_status(e, "momentum");
+  e = launch_sumsq_finalize_grouped(F, s);
   if (e != hipSuccess) return launch_status(e, "sumsq finalize");
   return ok();
 }
@@ -556,31 +677,33 @@ muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins, c
 muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,
                          int32_t mode, float coeff, void* stream) {
   muon_status_t st;
-  if ((st = check_batch(weight, "weight", true)) != MUON_OK) return st;
-  if ((st = check_batch(ortho, "ortho", true)) != MUON_OK) return st;
-  if (!same_shape(weight, ortho)) return fail(MUON_ERR_INVALID_VALUE, "weight and ortho shapes differ");
-  if (!finite(lr) || !finite(weight_decay) || !finite(coeff))
-    return fail(MUON_ERR_INVALID_VALUE, "lr, weight_decay and coeff must be finite");
-  const double m = static_cast<double>(weight->rows);
-  const double n = static_cast<double>(weight->cols);
-  double s;
-  switch (mode) {
-    case MUON_SCALE_MATCH_RMS: s = static_cast<double>(coeff) * std::sqrt(m > n ? m : n); break;
-    case MUON_SCALE_ORIGINAL: s = std::sqrt(m / n > 1.0 ? m / n : 1.0); break;
-    case MUON_SCALE_NONE: s = 1.0; break;
-    default: return fail(MUON_ERR_INVALID_VALUE, "unknown scale mode %d", mode);
-  }
   ApplyArgs a;
-  std::memset(&a, 0, sizeof(a));
-  a.W = to_mat(weight);
-  a.O = to_mat(ortho);
-  a.rows = static_cast<int32_t>(weight->rows);
-  a.cols = static_cast<int32_t>(weight->cols);
-  a.cdiv = make_fastdiv(static_cast<uint32_t>(weight->cols));
-  a.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
-  a.step = static_cast<float>(static_cast<double>(lr) * s);
-  const bool vec = vec_ok(weight) && vec_ok(ortho);
+  bool vec;
+  if ((st = prepare_apply(weight, ortho, lr, weight_decay, mode, coeff, &a, &vec)) != MUON_OK) return st;
   hipError_t e = launch_apply(a, weight->count, vec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return launch_status(e, "apply");
+  return ok();
+}
+
+muon_status_t muon_apply_grouped(int ngroups, const muon_batch_t* weights, const muon_batch_t* orthos, float lr,
+                                 float weight_decay, int32_t mode, float coeff, void* stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!weights || !orthos) return fail(MUON_ERR_INVALID_VALUE, "weights and orthos must not be NULL");
+  ApplyGroups G;
+  std::memset(&G, 0, sizeof(G));
+  G.ngroups = ngroups;
+  for (int g = 0; g < ngroups; ++g) {
+    bool vec;
+    const muon_status_t st = prepare_apply(&weights[g], &orthos[g], lr, weight_decay, mode, coeff, &G.g[g], &vec);
+    if (st != MUON_OK) return in_group(st, g);
+    G.vec[g] = vec;
+    G.blocks_per_mat[g] = elementwise_blocks_per_matrix(weights[g].rows, weights[g].cols);
+    G.first[g + 1] = G.first[g] + weights[g].count * G.blocks_per_mat[g];
+  }
+  if (G.first[ngroups] > INT32_MAX)
+    return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)G.first[ngroups]);
+  hipError_t e = launch_apply_grouped(G, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return launch_status(e, "apply");
   return ok();
 }

@@ -125,10 +125,10 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
 
 // ------------------------------------------------------------ momentum
 
+// Block `blk` of matrix `mat`: the kernels below differ only in how a
+// workgroup finds its (matrix, block) and its group's arguments.
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumArgs a) {
-  __shared__ float red[kThreads / 64];
-  const int64_t mat = blockIdx.y;
+__device__ __forceinline__ void momentum_block(const MomentumArgs& a, int64_t mat, uint32_t blk, float* red) {
   const char* g = mat_ptr(a.G, mat);
   char* m = mat_ptr(a.M, mat);
   char* n = a.has_n ? mat_ptr(a.N, mat) : nullptr;
@@ -138,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumArgs a
   const float beta = a.beta;
   const float omb = 1.0f - a.beta;
   float ss = 0.0f;
-  const uint32_t base = static_cast<uint32_t>(blockIdx.x) * kElemsPerBlock;
+  const uint32_t base = blk * kElemsPerBlock;
   if (VEC) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -177,7 +177,35 @@ __global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumArgs a
     }
   }
   const float s = block_sum(ss, red);
-  if (threadIdx.x == 0) a.partials[mat * a.blocks_per_mat + blockIdx.x] = s;
+  if (threadIdx.x == 0) a.partials[mat * a.blocks_per_mat + blk] = s;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void momentum_kernel(const MomentumArgs a) {
+  __shared__ float red[kThreads / 64];
+  momentum_block<VEC>(a, blockIdx.y, blockIdx.x, red);
+}
+
+// The group that workgroup b of a flat grouped grid belongs to.
+__device__ __forceinline__ int group_of(const int64_t* first, int ngroups, int64_t b) {
+  int g = 0;
+  while (g + 1 < ngroups && b >= first[g + 1]) ++g;
+  return g;
+}
+
+__global__ __launch_bounds__(kThreads) void momentum_grouped_kernel(const MomentumGroups G) {
+  __shared__ float red[kThreads / 64];
+  const int64_t b = blockIdx.x;
+  const int gi = group_of(G.first, G.ngroups, b);
+  const MomentumArgs& a = G.g[gi];
+  const int64_t local = b - G.first[gi];
+  const int64_t mat = local / a.blocks_per_mat;
+  const uint32_t blk = static_cast<uint32_t>(local - mat * a.blocks_per_mat);
+  if (G.vec[gi]) {
+    momentum_block<true>(a, mat, blk, red);
+  } else {
+    momentum_block<false>(a, mat, blk, red);
+  }
 }
 
 template <bool VEC>
@@ -217,11 +245,8 @@ __global__ __launch_bounds__(kThreads) void sumsq_partials_kernel(const SumsqArg
   if (threadIdx.x == 0) a.partials[mat * a.blocks_per_mat + blockIdx.x] = s;
 }
 
-// One workgroup per matrix: fixed-order fp64 sum of its partials.
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* partials, int per, float* sumsq) {
-  __shared__ double red[kThreads];
-  const int64_t mat = blockIdx.x;
-  const float* p = partials + mat * per;
+// One workgroup per matrix: fixed-order fp64 sum of its `per` partials.
+__device__ __forceinline__ void finalize_one(const float* p, int per, float* out, double* red) {
   double s = 0.0;
   for (int i = threadIdx.x; i < per; i += kThreads) s += static_cast<double>(p[i]);
   red[threadIdx.x] = s;
@@ -231,20 +256,33 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const float* partial
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) sumsq[mat] = static_cast<float>(red[0]);
+  if (threadIdx.x == 0) *out = static_cast<float>(red[0]);
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const float* partials, int per, float* sumsq) {
+  __shared__ double red[kThreads];
+  const int64_t mat = blockIdx.x;
+  finalize_one(partials + mat * per, per, sumsq + mat, red);
+}
+
+__global__ __launch_bounds__(kThreads) void finalize_grouped_kernel(const FinalizeGroups G) {
+  __shared__ double red[kThreads];
+  const int64_t b = blockIdx.x;  // one matrix of one group
+  const int gi = group_of(G.first, G.ngroups, b);
+  const int64_t mat = b - G.first[gi];
+  finalize_one(G.partials[gi] + mat * G.per[gi], G.per[gi], G.sumsq[gi] + mat, red);
 }
 
 // ------------------------------------------------------------ apply
 
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void apply_kernel(const ApplyArgs a) {
-  const int64_t mat = blockIdx.y;
+__device__ __forceinline__ void apply_block(const ApplyArgs& a, int64_t mat, uint32_t blk) {
   char* w = mat_ptr(a.W, mat);
   const char* o = mat_ptr(a.O, mat);
   const int ws = a.W.dtype ? 2 : 4;
   const int os = a.O.dtype ? 2 : 4;
   const uint32_t total = static_cast<uint32_t>(a.rows) * static_cast<uint32_t>(a.cols);
-  const uint32_t base = static_cast<uint32_t>(blockIdx.x) * kElemsPerBlock;
+  const uint32_t base = blk * kElemsPerBlock;
   if (VEC) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -272,6 +310,26 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(const ApplyArgs a) {
         store1(wp, a.W.dtype, v);
       }
     }
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void apply_kernel(const ApplyArgs a) {
+  apply_block<VEC>(a, blockIdx.y, blockIdx.x);
+}
+
+__global__ __launch_bounds__(kThreads) void apply_grouped_kernel(const ApplyGroups G) {
+  const int64_t b = blockIdx.x;
+  const int gi = group_of(G.first, G.ngroups, b);
+  const ApplyArgs& a = G.g[gi];
+  const int64_t per = G.blocks_per_mat[gi];
+  const int64_t local = b - G.first[gi];
+  const int64_t mat = local / per;
+  const uint32_t blk = static_cast<uint32_t>(local - mat * per);
+  if (G.vec[gi]) {
+    apply_block<true>(a, mat, blk);
+  } else {
+    apply_block<false>(a, mat, blk);
   }
 }
 
@@ -399,6 +457,24 @@ hipError_t launch_apply(const ApplyArgs& a, int64_t count, bool vec, hipStream_t
   } else {
     hipLaunchKernelGGL(apply_kernel<false>, grid, dim3(kThreads), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum_grouped(const MomentumGroups& a, hipStream_t stream) {
+  hipLaunchKernelGGL(momentum_grouped_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sumsq_finalize_grouped(const FinalizeGroups& a, hipStream_t stream) {
+  hipLaunchKernelGGL(finalize_grouped_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t stream) {
+  hipLaunchKernelGGL(apply_grouped_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -142,6 +142,40 @@ struct ApplyArgs {
 hipError_t launch_apply(const ApplyArgs& a, int64_t count, bool vec,
                         hipStream_t stream);
 
+// Several groups (shape classes) in one launch over a flat grid: workgroup b
+// belongs to the group g with first[g] <= b < first[g+1]; inside it, the
+// momentum and apply kernels take block (b - first[g]) % blocks_per_mat of
+// matrix (b - first[g]) / blocks_per_mat, and the finalize kernel matrix
+// b - first[g].  vec[g]: the group's rows allow 16-byte accesses.
+struct MomentumGroups {
+  int32_t ngroups;
+  int32_t vec[kMaxGroups];
+  int32_t pad_;
+  int64_t first[kMaxGroups + 1];
+  MomentumArgs g[kMaxGroups];
+};
+hipError_t launch_momentum_grouped(const MomentumGroups& a, hipStream_t stream);
+
+struct FinalizeGroups {
+  int32_t ngroups;
+  int32_t per[kMaxGroups];  // partials per matrix
+  int32_t pad_;
+  int64_t first[kMaxGroups + 1];
+  const float* partials[kMaxGroups];
+  float* sumsq[kMaxGroups];
+};
+hipError_t launch_sumsq_finalize_grouped(const FinalizeGroups& a, hipStream_t stream);
+
+struct ApplyGroups {
+  int32_t ngroups;
+  int32_t vec[kMaxGroups];
+  int32_t blocks_per_mat[kMaxGroups];
+  int32_t pad_;
+  int64_t first[kMaxGroups + 1];
+  ApplyArgs g[kMaxGroups];
+};
+hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t stream);
+
 // Copy the caller's N (stored m x n) into the padded Newton-Schulz buffers,
 // scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc) and
 // T[c][r] (Pc x Pr), zero outside m x n, in the compute type; with bf16

@@ -96,6 +96,20 @@ def momentum(grad, mom, nout, sumsq: torch.Tensor, beta: float = 0.95, nesterov:
                     ws.data_ptr(), ws.numel(), _stream(stream))
 
 
+def momentum_grouped(grads, moms, nouts, sumsqs, beta: float = 0.95, nesterov: bool = True,
+                     ws: torch.Tensor | None = None, stream=None) -> None:
+    """muon_momentum over several shape classes in one launch; ``nouts`` may
+    be None without Nesterov."""
+    bg = [batch(x) for x in grads]
+    bm = [batch(x) for x in moms]
+    bn = None if nouts is None else [batch(x) for x in nouts]
+    if ws is None:
+        need = L.muon_momentum_grouped_workspace([b.count for b in bg], [b.rows for b in bg], [b.cols for b in bg])
+        ws = workspace(need, sumsqs[0].device)
+    L.muon_momentum_grouped([b.desc for b in bg], [b.desc for b in bm], None if bn is None else [b.desc for b in bn],
+                            [s.data_ptr() for s in sumsqs], beta, nesterov, ws.data_ptr(), ws.numel(), _stream(stream))
+
+
 def orthogonalize(inp, out, sumsq: torch.Tensor | None = None, steps: int = 5, coeffs=QUINTIC,
                   eps: float = EPS, compute: int = L.MUON_BF16, ws: torch.Tensor | None = None,
                   stream=None, device=None) -> None:
@@ -127,6 +141,13 @@ def apply(weight, ortho, lr: float, weight_decay: float, mode: int = L.MUON_SCAL
           coeff: float = 0.2, stream=None) -> None:
     w, o = batch(weight), batch(ortho)
     L.muon_apply(w.desc, o.desc, lr, weight_decay, mode, coeff, _stream(stream))
+
+
+def apply_grouped(weights, orthos, lr: float, weight_decay: float, mode: int = L.MUON_SCALE_MATCH_RMS,
+                  coeff: float = 0.2, stream=None) -> None:
+    """muon_apply over several shape classes in one launch."""
+    L.muon_apply_grouped([batch(x).desc for x in weights], [batch(x).desc for x in orthos], lr, weight_decay, mode,
+                         coeff, _stream(stream))
 
 
 class MuonStep:
@@ -165,10 +186,13 @@ class MuonStep:
             self.n.append(batch(torch.empty(shape, dtype=nbuf_dtype, device=dev)))
             self.o.append(batch(torch.empty(shape, dtype=w.keep[-1].dtype, device=dev)))
             self.ss.append(torch.empty(w.count, dtype=torch.float32, device=dev))
-            self.mws.append(workspace(L.muon_momentum_workspace(*shape), dev))
         self.device = dev
-        # groups are orthogonalized together, at most 8 per grouped launch
+        # each stage runs the groups together, at most 8 per grouped launch
         self.chunks = [list(range(i, min(i + 8, len(self.w)))) for i in range(0, len(self.w), 8)]
+        for ch in self.chunks:
+            need = L.muon_momentum_grouped_workspace([self.g[i].count for i in ch], [self.g[i].rows for i in ch],
+                                                     [self.g[i].cols for i in ch])
+            self.mws.append(workspace(need, dev))
         self.ows = []
         for ch in self.chunks:
             need = L.muon_orthogonalize_grouped_workspace([self.n[i].count for i in ch], [self.n[i].rows for i in ch],
@@ -195,9 +219,10 @@ class MuonStep:
         s = _stream(st)
         if events is not None:
             events[0].record(st)
-        for g, m, n, ss, ws in zip(self.g, self.m, self.n, self.ss, self.mws):
-            L.muon_momentum(g.desc, m.desc, n.desc, ss.data_ptr(), self.beta, self.nesterov, ws.data_ptr(),
-                            ws.numel(), s)
+        for ch, ws in zip(self.chunks, self.mws):
+            L.muon_momentum_grouped([self.g[i].desc for i in ch], [self.m[i].desc for i in ch],
+                                    [self.n[i].desc for i in ch], [self.ss[i].data_ptr() for i in ch], self.beta,
+                                    self.nesterov, ws.data_ptr(), ws.numel(), s)
         if events is not None:
             events[1].record(st)
         a, b, c = self.coeffs
@@ -207,8 +232,9 @@ class MuonStep:
                                          self.compute, ws.data_ptr(), ws.numel(), s)
         if events is not None:
             events[2].record(st)
-        for w, o in zip(self.w, self.o):
-            L.muon_apply(w.desc, o.desc, self.lr, self.weight_decay, self.mode, self.coeff, s)
+        for ch in self.chunks:
+            L.muon_apply_grouped([self.w[i].desc for i in ch], [self.o[i].desc for i in ch], self.lr,
+                                 self.weight_decay, self.mode, self.coeff, s)
         if events is not None:
             events[3].record(st)
 

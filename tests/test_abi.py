@@ -109,6 +109,39 @@ def test_grouped_rejects_bad_group_counts():
     assert L.muon_orthogonalize_grouped_workspace([1] * 9, [4] * 9, [4] * 9, 1) == 0
 
 
+def test_momentum_grouped_rejects_bad_arguments():
+    gs, ms, ns = [desc(), desc(rows=32)], [desc(), desc(rows=32)], [desc(), desc(rows=32)]
+    need = L.muon_momentum_grouped_workspace([1, 1], [64, 32], [64, 64])
+    assert need == L.muon_momentum_workspace(1, 64, 64) + L.muon_momentum_workspace(1, 32, 64)
+    call = lambda **kw: L.muon_momentum_grouped(kw.get("g", gs), kw.get("m", ms), kw.get("n", ns),
+                                                kw.get("ss", [FAKE, FAKE]), kw.get("beta", 0.95), kw.get("nest", True),
+                                                kw.get("ws", FAKE), kw.get("wsb", need), 0)
+    assert status_of(lambda: call(beta=1.0)) == INVALID
+    assert status_of(lambda: call(n=None)) == INVALID                    # Nesterov needs outputs
+    assert status_of(lambda: call(m=[desc(), desc(rows=31)])) == INVALID  # group 1 shapes differ
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: call(ss=[FAKE, None])) == INVALID
+    assert status_of(lambda: call(wsb=need - 1)) == WORKSPACE
+    assert status_of(lambda: call(ws=None)) == WORKSPACE
+    assert status_of(lambda: call(g=[desc(), desc(rows=32, dtype=5)])) == INVALID
+    nine = [desc()] * 9
+    assert status_of(lambda: L.muon_momentum_grouped(nine, nine, nine, [FAKE] * 9, 0.9, True, FAKE, 1 << 30, 0)) == INVALID
+    assert L.muon_momentum_grouped_workspace([1] * 9, [4] * 9, [4] * 9) == 0
+    assert L.muon_momentum_grouped_workspace([1, 0], [4, 4], [4, 4]) == 0
+
+
+def test_apply_grouped_rejects_bad_arguments():
+    ws, os_ = [desc(), desc(cols=40)], [desc(), desc(cols=40)]
+    call = lambda **kw: L.muon_apply_grouped(kw.get("w", ws), kw.get("o", os_), kw.get("lr", 1e-3), 0.1,
+                                             kw.get("mode", 0), 0.2, 0)
+    assert status_of(lambda: call(lr=float("nan"))) == INVALID
+    assert status_of(lambda: call(mode=7)) == INVALID
+    assert status_of(lambda: call(o=[desc(), desc(cols=41)])) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    nine = [desc()] * 9
+    assert status_of(lambda: L.muon_apply_grouped(nine, nine, 1e-3, 0.1, 0, 0.2, 0)) == INVALID
+
+
 def test_apply_rejects_bad_arguments():
     w, o = desc(), desc()
     call = lambda **kw: L.muon_apply(kw.get("w", w), kw.get("o", o), kw.get("lr", 1e-3), kw.get("wd", 0.1),

@@ -126,6 +126,57 @@ def test_momentum_nonfinite_propagates(mx):
     assert not math.isfinite(float(ss[0]))
 
 
+GROUPED_EW = [((3, 100, 72), torch.bfloat16), ((2, 33, 50), torch.float32), ((1, 640, 256), torch.bfloat16),
+              ((4, 17, 8), torch.bfloat16)]  # 16-byte and element paths, several blocks, tiny matrices
+
+
+@pytest.mark.parametrize("nesterov", [True, False])
+def test_momentum_grouped_equals_separate_calls(mx, nesterov):
+    """One grouped launch over shape classes (vector and element paths)
+    against separate muon_momentum calls, bit for bit, from a nonzero state;
+    and against the oracle."""
+    beta = 0.9
+    grads = [randn(s, 200 + k, dt, 3.0) for k, (s, dt) in enumerate(GROUPED_EW)]
+    m0 = [randn(s, 300 + k, torch.float32) for k, (s, _) in enumerate(GROUPED_EW)]
+    M1, M2 = [m.clone() for m in m0], [m.clone() for m in m0]
+    N1 = [torch.empty(s, dtype=dt, device="cuda") for s, dt in GROUPED_EW] if nesterov else None
+    N2 = [torch.empty(s, dtype=dt, device="cuda") for s, dt in GROUPED_EW] if nesterov else None
+    ss1 = [torch.empty(s[0], device="cuda") for s, _ in GROUPED_EW]
+    ss2 = [torch.empty(s[0], device="cuda") for s, _ in GROUPED_EW]
+    for k in range(len(GROUPED_EW)):
+        mx.momentum(grads[k], M1[k], N1[k] if nesterov else None, ss1[k], beta, nesterov)
+    mx.momentum_grouped(grads, M2, N2, ss2, beta, nesterov)
+    torch.cuda.synchronize()
+    for k, (s, dt) in enumerate(GROUPED_EW):
+        assert torch.equal(M1[k], M2[k]) and torch.equal(ss1[k], ss2[k]), f"group {k}"
+        if nesterov:
+            assert torch.equal(N1[k], N2[k]), f"group {k}"
+        for i in range(s[0]):
+            Mo, No = O.momentum(f64(m0[k][i]), f64(grads[k][i]), beta, nesterov)
+            assert rel(f64(M2[k][i]), Mo) <= TOL_EW
+            want = O.frobenius_sumsq(No)
+            assert abs(float(ss2[k][i]) - want) <= TOL_EW * want
+
+
+def test_apply_grouped_equals_separate_calls(mx):
+    lr, wd = 1.0, 0.5
+    w0 = [randn(s, 400 + k, dt, 0.02) for k, (s, dt) in enumerate(GROUPED_EW)]
+    Od = [randn(s, 500 + k, dt, 0.05) for k, (s, dt) in enumerate(GROUPED_EW)]
+    W1, W2 = [w.clone() for w in w0], [w.clone() for w in w0]
+    for k in range(len(GROUPED_EW)):
+        mx.apply(W1[k], Od[k], lr, wd, 0, 0.2)
+    mx.apply_grouped(W2, Od, lr, wd, 0, 0.2)
+    torch.cuda.synchronize()
+    for k, (s, dt) in enumerate(GROUPED_EW):
+        assert torch.equal(W1[k], W2[k]), f"group {k}"
+        for i in range(s[0]):
+            want = O.apply_update(f64(w0[k][i]), f64(Od[k][i]), lr, wd, 0, 0.2)
+            if dt == torch.float32:
+                assert rel(f64(W2[k][i]), want) <= TOL_EW
+            else:
+                assert within_one_bf16_rounding(f64(W2[k][i]), want)
+
+
 # --------------------------------------------------------------------- apply
 
 @pytest.mark.parametrize("mode", [mx_mode for mx_mode in (0, 1, 2)])
