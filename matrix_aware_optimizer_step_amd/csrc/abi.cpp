@@ -99,6 +99,15 @@ MatBatch to_mat(const muon_batch_t* b) {
 }
 
 // 16-byte vector path possible: rows of 8 elements start on 16-byte boundaries.
+// Four-element loads (8 bytes of bf16, 16 of f32): every row and matrix
+// starts on a 4-element boundary of a suitably aligned base (the entries of
+// a pointer array are documented 16-byte aligned).
+bool vec4_ok(const muon_batch_t* b) {
+  if (b->ld % 4 != 0) return false;
+  if (b->ptrs) return true;
+  return reinterpret_cast<uintptr_t>(b->base) % (4 * esize(b->dtype)) == 0 && (b->count == 1 || b->stride % 4 == 0);
+}
+
 bool vec_ok(const muon_batch_t* b) {
   if (b->cols % 8 != 0 || b->ld % 8 != 0) return false;
   if (b->ptrs) return true;  // documented: every pointer 16-byte aligned
@@ -305,6 +314,8 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     pa.Pc = p.Pc;
     pa.compute = compute;
     pa.tall = p.tall;
+    pa.nvec = vec4_ok(&ins[g]);
+    pa.pad_ = 0;
     // S: the stored orientation, T: its transpose; X is whichever is wide.
     // A k-major group keeps no X^T.
     pa.S = p.tall ? (p.kmajor ? nullptr : ws + p.xt[0]) : ws + p.xc[0];

@@ -92,6 +92,31 @@ __device__ __forceinline__ void store8(char* p, int dtype, const float* v) {
   }
 }
 
+// Four consecutive values (8 bytes of bf16 or 16 of f32, aligned) as fp32.
+__device__ __forceinline__ void load4(const char* p, int dtype, float* v) {
+  if (dtype) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __builtin_bit_cast(float, u.x << 16);
+    v[1] = __builtin_bit_cast(float, u.x & 0xffff0000u);
+    v[2] = __builtin_bit_cast(float, u.y << 16);
+    v[3] = __builtin_bit_cast(float, u.y & 0xffff0000u);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  }
+}
+
+__device__ __forceinline__ void store4(char* p, int dtype, const float* v) {
+  if (dtype) {
+    uint2 u;
+    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+  } else {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
 __device__ __forceinline__ float load1(const char* p, int dtype) {
   return dtype ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(p)) : *reinterpret_cast<const float*>(p);
 }
@@ -338,7 +363,11 @@ __global__ __launch_bounds__(kThreads) void apply_grouped_kernel(const ApplyGrou
 constexpr int kTile = 64;
 
 // grid: (Pc/64, Pr/64, count).  Each workgroup moves one 64x64 tile of the
-// padded stored-orientation extent.
+// padded stored-orientation extent.  Global accesses are 4-element pieces:
+// 16 threads cover a 64-element row (N rows read, S rows written) or a
+// 64-element column of the tile (T rows written).  With the 65-float LDS
+// row stride both the row writes and the 4-row column reads of a wave hit
+// 64 distinct banks.
 __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
   __shared__ float tile[kTile][kTile + 1];
   const int64_t mat = blockIdx.z;
@@ -348,18 +377,33 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
   const int nsz = a.N.dtype ? 2 : 4;
   const float ssq = a.sumsq[mat];
   const float scale = 1.0f / (sqrtf(ssq) + a.eps);
-  const int tx = threadIdx.x & 63;
-  const int ty = threadIdx.x >> 6;  // 0..3
+  const int q = threadIdx.x & 15;   // 4-element piece of a 64-element row
+  const int rq = threadIdx.x >> 4;  // 0..15
   const int esz = a.compute ? 2 : 4;
   // read rows of N (zero outside m x n), write rows of S (if wanted)
   char* S = a.S ? a.S + mat * a.s_mat : nullptr;
-  for (int rr = ty; rr < kTile; rr += 4) {
+#pragma unroll
+  for (int k = 0; k < kTile / 16; ++k) {
+    const int rr = rq + 16 * k;
     const int r = r0 + rr;
-    const int c = c0 + tx;
-    float v = 0.0f;
-    if (r < a.rows && c < a.cols) v = scale * load1(n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz, a.N.dtype);
-    tile[rr][tx] = v;
-    if (S) store1(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
+    const int c = c0 + 4 * q;
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r < a.rows) {
+      const char* np = n + (static_cast<int64_t>(r) * a.N.ld + c) * nsz;
+      if (a.nvec && c + 3 < a.cols) {
+        load4(np, a.N.dtype, v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < a.cols) v[e] = load1(np + e * nsz, a.N.dtype);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] *= scale;
+      tile[rr][4 * q + e] = v[e];
+    }
+    if (S) store4(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
   }
   __syncthreads();
   if (a.Lo) {
@@ -388,11 +432,13 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
   // write rows of T = columns of the tile (if wanted)
   if (!a.T) return;
   char* T = a.T + mat * a.t_mat;
-  for (int cc = ty; cc < kTile; cc += 4) {
-    const int c = c0 + cc;
-    const int r = r0 + tx;
-    const float v = tile[tx][cc];
-    store1(T + (static_cast<int64_t>(c) * a.Pr + r) * esz, a.compute, v);
+#pragma unroll
+  for (int k = 0; k < kTile / 16; ++k) {
+    const int cc = rq + 16 * k;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][cc];
+    store4(T + (static_cast<int64_t>(c0 + cc) * a.Pr + r0 + 4 * q) * esz, a.compute, v);
   }
 }
 

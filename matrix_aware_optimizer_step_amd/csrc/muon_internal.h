@@ -189,6 +189,8 @@ struct PackArgs {
   int32_t Pr, Pc;          // padded
   int32_t compute;         // element type of S and T
   int32_t tall;
+  int32_t nvec;            // N's rows and matrices start on 4-element boundaries (aligned)
+  int32_t pad_;
   char* S; int64_t s_mat;  // stored orientation (bytes per matrix); null: not written
   char* T; int64_t t_mat;  // its transpose; null: not written
   uint16_t* Lo; int64_t lo_mat;  // elements per matrix, in the lo_index() layout
