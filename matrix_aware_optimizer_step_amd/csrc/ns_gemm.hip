@@ -282,6 +282,14 @@ void ns_gemm_kernel(const GemmLaunch L) {
     // a k-major Q starts at the tile's first column, an n-major one at its first row
     const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * (kQN ? 1 : ldq) * sizeof(T);
     const int nk = G.K / BK;
+    // A diagonal tile of a symmetric product multiplies a block of rows by
+    // itself: its Q tile is the P tile already in LDS, so only P is loaded.
+    // Not on a persistent grid: there the workgroups walk their tiles nearly
+    // in step and share k-tiles in L2, and diagonal tiles finishing early
+    // break that (measured slower on the 32-layer dense set, faster with one
+    // workgroup per tile).
+    const bool same_pq = R == 1 && G.sym && ti == tj && G.P == G.Q && G.p_mat == G.q_mat && ldp == ldq && !kQN &&
+                         static_cast<int>(gridDim.x) == L.total_tiles;
 
     // ---- operand staging
     uint32_t dofs_p[DMA ? IPW : 1], dofs_q[DMA ? IPWQ : 1];  // DMA: lane byte offsets within the tile
@@ -333,8 +341,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
       char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
       for (int r = 0; r < IPW; ++r) lds_dma16(pk + dofs_p[r], lp + r * 1024);
+      if (!same_pq) {
 #pragma unroll
-      for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
+        for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
+      }
     };
     auto reg_load = [&](int kt) {
       const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
@@ -392,7 +402,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
 #pragma unroll
     for (int f = 0; f < FN; ++f) {
       fb_row[f] = wn * WTN + f * 32 + frow;
-      fb_off[f] = OPB + fb_row[f] * ROWB;
+      fb_off[f] = (same_pq ? 0 : OPB) + fb_row[f] * ROWB;
     }
     // k-major Q: lane j of a 16-lane group points at row (j/4) of a group of
     // four and at columns 4*(j%4) .. +3 of its 16-column half of block f;
