@@ -212,3 +212,42 @@ def test_padded_shape_limit():
     st = lib.muon_orthogonalize(ctypes.byref(d), None, ctypes.byref(d), 5, 3.4445, -4.775, 2.0315, 1e-7,
                                 L.MUON_BF16, FAKE, 1 << 40, None)
     assert st == 2 and b"2^30" in lib.muon_last_error()
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include "muon355.h"
+int main(void) {
+  if (muon_abi_version() != 1) return 1;
+  size_t w = muon_orthogonalize_workspace(1, 4096, 14336, MUON_BF16);
+  size_t m = muon_momentum_workspace(2, 768, 2048);
+  int64_t counts[2] = {2, 1}, rows[2] = {768, 4096}, cols[2] = {2048, 14336};
+  size_t g = muon_momentum_grouped_workspace(2, counts, rows, cols);
+  if (w == 0 || m == 0 || g == 0) return 2;
+  /* an invalid descriptor is rejected before anything reaches the GPU */
+  muon_batch_t bad = {NULL, NULL, 0, 1, 64, 64, 64, MUON_F32, 0};
+  muon_status_t st = muon_apply(&bad, &bad, 1e-3f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, NULL);
+  if (st != MUON_ERR_INVALID_VALUE) return 3;
+  printf("%s: %s\n", muon_status_string(st), muon_last_error());
+  return 0;
+}
+"""
+
+
+def test_header_is_c99_and_links(tmp_path):
+    """The header compiles as plain C99 and a C program links and calls the
+    library (queries and argument validation only: no GPU work)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "abi_check.c"
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "abi_check"
+    libdir = os.path.dirname(L.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                    "-L", libdir, "-lmuon355", f"-Wl,-rpath,{libdir}"], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
+    assert out.stdout.startswith("MUON_ERR_INVALID_VALUE: ")
