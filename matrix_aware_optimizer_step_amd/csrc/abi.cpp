@@ -37,7 +37,7 @@ muon_status_t fail(muon_status_t st, const char* fmt, ...) {
 muon_status_t in_group(muon_status_t st, int g) {
   if (st == MUON_OK) return st;
   char tmp[sizeof(g_last_error)];
-  snprintf(tmp, sizeof(tmp), "group %d: %s", g, g_last_error);
+  snprintf(tmp, sizeof(tmp), "group %d: %.480s", g, g_last_error);
   memcpy(g_last_error, tmp, sizeof(tmp));
   return st;
 }

@@ -211,6 +211,27 @@ class MuonStep:
     def sumsq_buffers(self):
         return self.ss
 
+    def state_dict(self) -> dict:
+        """The state a resumed run needs: the fp32 momentum of every group
+        (host copies) and the step's hyperparameters.  Plain tensors and
+        Python values, so torch.save / torch.load(weights_only=True) round-trip
+        it; the weights themselves are the caller's."""
+        return {"momentum": [m.keep[0].detach().to("cpu", copy=True) for m in self.m],
+                "hyper": {"beta": self.beta, "nesterov": bool(self.nesterov), "steps": self.steps,
+                          "coeffs": [float(x) for x in self.coeffs], "eps": self.eps, "lr": self.lr,
+                          "weight_decay": self.weight_decay, "mode": self.mode, "coeff": self.coeff}}
+
+    def load_state_dict(self, state: dict) -> None:
+        mom = state["momentum"]
+        if len(mom) != len(self.m) or any(tuple(t.shape) != tuple(m.keep[0].shape) for m, t in zip(self.m, mom)):
+            raise ValueError("the state was saved for differently shaped groups")
+        for m, t in zip(self.m, mom):
+            m.keep[0].copy_(t)
+        h = state["hyper"]
+        self.beta, self.nesterov, self.steps = h["beta"], h["nesterov"], h["steps"]
+        self.coeffs, self.eps = tuple(h["coeffs"]), h["eps"]
+        self.lr, self.weight_decay, self.mode, self.coeff = h["lr"], h["weight_decay"], h["mode"], h["coeff"]
+
     def step(self, stream=None, events=None) -> None:
         """Enqueue one step.  ``events``, if given, is four torch.cuda.Event
         objects recorded before momentum, before orthogonalization, before
@@ -296,6 +317,25 @@ class AdamW:
         b1, b2 = self.betas
         L.muon_adamw(self.desc, self.t, self.lr, b1, b2, self.eps, self.weight_decay, _stream(stream))
 
+    def state_dict(self) -> dict:
+        """The step count, both moments of every tensor (host copies) and the
+        hyperparameters."""
+        return {"step": self.t, "exp_avg": [m.detach().to("cpu", copy=True) for m in self.exp_avg],
+                "exp_avg_sq": [v.detach().to("cpu", copy=True) for v in self.exp_avg_sq],
+                "hyper": {"lr": self.lr, "betas": list(self.betas), "eps": self.eps, "weight_decay": self.weight_decay}}
+
+    def load_state_dict(self, state: dict) -> None:
+        for key, own in (("exp_avg", self.exp_avg), ("exp_avg_sq", self.exp_avg_sq)):
+            if len(state[key]) != len(own) or any(t.shape != o.shape for t, o in zip(state[key], own)):
+                raise ValueError("the state was saved for differently shaped tensors")
+        # copied into the existing buffers: the device pointer tables stay valid
+        for key, own in (("exp_avg", self.exp_avg), ("exp_avg_sq", self.exp_avg_sq)):
+            for o, t in zip(own, state[key]):
+                o.copy_(t)
+        self.t = int(state["step"])
+        h = state["hyper"]
+        self.lr, self.betas, self.eps, self.weight_decay = h["lr"], tuple(h["betas"]), h["eps"], h["weight_decay"]
+
 
 # ------------------------------------------------------ routing helper
 
@@ -348,3 +388,19 @@ class OptimizerStep:
             self.muon.step(stream=stream)
         for group in self.adamw:
             group.step(stream=stream)
+
+    def state_dict(self) -> dict:
+        """Everything a resumed run needs besides the weights: the Muon
+        momentum, every AdamW group's moments and step count, the
+        hyperparameters and the routing they belong to."""
+        return {"routing": dict(self.routing), "muon": None if self.muon is None else self.muon.state_dict(),
+                "adamw": [g.state_dict() for g in self.adamw]}
+
+    def load_state_dict(self, state: dict) -> None:
+        if state["routing"] != self.routing or len(state["adamw"]) != len(self.adamw) or \
+                (state["muon"] is None) != (self.muon is None):
+            raise ValueError("the state was saved for a different set of parameters")
+        if self.muon is not None:
+            self.muon.load_state_dict(state["muon"])
+        for g, s in zip(self.adamw, state["adamw"]):
+            g.load_state_dict(s)

@@ -1,0 +1,117 @@
+// Drives every entry point of the C-ABI layer through valid and invalid
+// arguments on the CPU (with the stub launchers: nothing reaches a GPU).
+// Device addresses are fake and never dereferenced.  Exits non-zero on the
+// first unexpected status; the sanitizers abort on any memory or UB error.
+#include <cstdint>
+#include <cstdio>
+#include <vector>
+
+#include "muon355.h"
+
+extern "C" void stub_set_workspace(const void* base, size_t bytes);
+extern "C" long stub_launches();
+
+namespace {
+
+int g_fail = 0;
+char* const kDev = reinterpret_cast<char*>(uintptr_t{1} << 40);  // fake, 16-byte aligned, never read
+char* const kWs = reinterpret_cast<char*>(uintptr_t{1} << 44);
+
+void expect(muon_status_t got, muon_status_t want, const char* what) {
+  if (got != want) {
+    std::fprintf(stderr, "%s: status %d, expected %d (%s)\n", what, got, want, muon_last_error());
+    g_fail = 1;
+  }
+}
+
+muon_batch_t batch(int64_t count, int64_t rows, int64_t cols, int32_t dtype, char* base = kDev) {
+  return muon_batch_t{nullptr, base, rows * cols, count, rows, cols, cols, dtype, 0};
+}
+
+void orthogonalize_cases() {
+  struct Case { int64_t count, rows, cols; int32_t compute; int steps; };
+  const Case cases[] = {{1, 256, 128, MUON_F32, 5},   {3, 300, 700, MUON_BF16, 5}, {2, 900, 256, MUON_BF16, 5},
+                        {1, 4096, 14336, MUON_BF16, 5}, {384, 768, 2048, MUON_BF16, 5}, {96, 128, 4096, MUON_BF16, 5},
+                        {1, 1, 64, MUON_BF16, 5},      {1, 64, 1, MUON_F32, 5},      {2, 700, 520, MUON_F32, 12},
+                        {1, 300, 300, MUON_BF16, 0},   {1, 2100, 2200, MUON_BF16, 1}, {1, 129, 900, MUON_F32, 3}};
+  for (const Case& c : cases) {
+    const size_t need = muon_orthogonalize_workspace(c.count, c.rows, c.cols, c.compute);
+    if (need == 0) { std::fprintf(stderr, "workspace query 0\n"); g_fail = 1; continue; }
+    stub_set_workspace(kWs, need);
+    muon_batch_t in = batch(c.count, c.rows, c.cols, c.compute == MUON_BF16 ? MUON_F32 : MUON_F32);
+    muon_batch_t out = batch(c.count, c.rows, c.cols, MUON_BF16);
+    expect(muon_orthogonalize(&in, nullptr, &out, c.steps, 3.4445f, -4.775f, 2.0315f, 1e-7f, c.compute, kWs, need,
+                              nullptr), MUON_OK, "orthogonalize");
+    expect(muon_orthogonalize(&in, nullptr, &out, c.steps, 3.4445f, -4.775f, 2.0315f, 1e-7f, c.compute, kWs, need - 1,
+                              nullptr), MUON_ERR_WORKSPACE, "orthogonalize, short workspace");
+  }
+  // grouped, both tile classes, wide and tall, k-major and X^T classes
+  const int64_t counts[] = {2, 1, 96, 3, 1}, rows[] = {4096, 14336, 128, 520, 2300}, cols[] = {4096, 4096, 4096, 700, 2050};
+  for (int32_t compute : {MUON_BF16, MUON_F32}) {
+    const size_t need = muon_orthogonalize_grouped_workspace(5, counts, rows, cols, compute);
+    stub_set_workspace(kWs, need);
+    std::vector<muon_batch_t> ins, outs;
+    for (int g = 0; g < 5; ++g) {
+      ins.push_back(batch(counts[g], rows[g], cols[g], MUON_F32));
+      outs.push_back(batch(counts[g], rows[g], cols[g], MUON_BF16));
+    }
+    expect(muon_orthogonalize_grouped(5, ins.data(), nullptr, outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
+                                      kWs, need, nullptr), MUON_OK, "orthogonalize_grouped");
+    ins[3].cols = 701;
+    expect(muon_orthogonalize_grouped(5, ins.data(), nullptr, outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
+                                      kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_grouped, shapes");
+  }
+  expect(muon_orthogonalize_workspace(1, 65536, 65536, MUON_F32) == 0 ? MUON_OK : MUON_ERR_LAUNCH, MUON_OK,
+         "padded-size limit");
+  expect(muon_orthogonalize_workspace(int64_t{1} << 40, 64, 64, MUON_BF16) == 0 ? MUON_OK : MUON_ERR_LAUNCH, MUON_OK,
+         "count limit");
+}
+
+void momentum_and_apply_cases() {
+  muon_batch_t g = batch(2, 300, 700, MUON_BF16), m = batch(2, 300, 700, MUON_F32), n = batch(2, 300, 700, MUON_F32);
+  float* sumsq = reinterpret_cast<float*>(kDev);
+  size_t need = muon_momentum_workspace(2, 300, 700);
+  stub_set_workspace(kWs, need);
+  expect(muon_momentum(&g, &m, &n, sumsq, 0.95f, 1, kWs, need, nullptr), MUON_OK, "momentum");
+  expect(muon_momentum(&g, &m, nullptr, sumsq, 0.95f, 0, kWs, need, nullptr), MUON_OK, "momentum without N");
+  expect(muon_momentum(&g, &m, &n, sumsq, 1.0f, 1, kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "momentum beta 1");
+  expect(muon_momentum(&g, &m, &n, sumsq, 0.95f, 1, kWs, need - 4, nullptr), MUON_ERR_WORKSPACE, "momentum workspace");
+  const int64_t counts[] = {2, 1, 96}, rows[] = {4096, 14336, 128}, cols[] = {4096, 4096, 4096};
+  std::vector<muon_batch_t> gs, ms, ns, ws, os;
+  std::vector<float*> sums;
+  for (int i = 0; i < 3; ++i) {
+    gs.push_back(batch(counts[i], rows[i], cols[i], MUON_BF16));
+    ms.push_back(batch(counts[i], rows[i], cols[i], MUON_F32));
+    ns.push_back(batch(counts[i], rows[i], cols[i], MUON_F32));
+    ws.push_back(batch(counts[i], rows[i], cols[i], MUON_BF16));
+    os.push_back(batch(counts[i], rows[i], cols[i], MUON_BF16));
+    sums.push_back(sumsq);
+  }
+  need = muon_momentum_grouped_workspace(3, counts, rows, cols);
+  stub_set_workspace(kWs, need);
+  expect(muon_momentum_grouped(3, gs.data(), ms.data(), ns.data(), sums.data(), 0.95f, 1, kWs, need, nullptr), MUON_OK,
+         "momentum_grouped");
+  expect(muon_momentum_grouped(3, gs.data(), ms.data(), ns.data(), sums.data(), 0.95f, 1, kWs, need - 1, nullptr),
+         MUON_ERR_WORKSPACE, "momentum_grouped workspace");
+  expect(muon_apply(&ws[0], &os[0], 3e-4f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, nullptr), MUON_OK, "apply");
+  expect(muon_apply_grouped(3, ws.data(), os.data(), 3e-4f, 0.1f, MUON_SCALE_ORIGINAL, 0.2f, nullptr), MUON_OK,
+         "apply_grouped");
+  expect(muon_apply_grouped(9, ws.data(), os.data(), 3e-4f, 0.1f, 0, 0.2f, nullptr), MUON_ERR_INVALID_VALUE,
+         "apply_grouped, 9 groups");
+  muon_tensor_list_t t{2, 3, reinterpret_cast<void* const*>(kDev), reinterpret_cast<const void* const*>(kDev),
+                       reinterpret_cast<float* const*>(kDev), reinterpret_cast<float* const*>(kDev),
+                       reinterpret_cast<const int64_t*>(kDev), reinterpret_cast<const int64_t*>(kDev), MUON_BF16,
+                       MUON_BF16};
+  expect(muon_adamw(&t, 1, 1e-3f, 0.9f, 0.999f, 1e-8f, 0.1f, nullptr), MUON_OK, "adamw");
+  expect(muon_adamw(&t, 0, 1e-3f, 0.9f, 0.999f, 1e-8f, 0.1f, nullptr), MUON_ERR_INVALID_VALUE, "adamw step 0");
+}
+
+}  // namespace
+
+int main() {
+  orthogonalize_cases();
+  momentum_and_apply_cases();
+  if (g_fail) return 1;
+  std::printf("ok: %ld launches checked\n", stub_launches());
+  return 0;
+}

@@ -1,0 +1,180 @@
+// Host stand-ins for the kernel launchers of libmuon355, for building the
+// C-ABI layer (abi.cpp) on the CPU under AddressSanitizer and
+// UndefinedBehaviorSanitizer.  Nothing is enqueued and no device address is
+// dereferenced: every launch the C-ABI layer builds is checked instead, each
+// workspace operand against the workspace the caller passed (count x the
+// per-matrix stride plus the operand's full extent for its tile grid).
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+
+#include "muon_internal.h"
+
+namespace {
+
+const char* g_lo = nullptr;
+const char* g_hi = nullptr;
+long g_launches = 0;
+
+[[noreturn]] void die(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::fprintf(stderr, "launch check failed: ");
+  std::vfprintf(stderr, fmt, ap);
+  std::fprintf(stderr, "\n");
+  va_end(ap);
+  std::abort();
+}
+
+// [p, p + (count-1)*mat + extent) inside the workspace
+void in_ws(const void* p, int64_t count, int64_t mat, int64_t extent, const char* what) {
+  if (!p) die("%s is NULL", what);
+  if (count < 1 || mat < 0 || extent <= 0) die("%s: count %lld, stride %lld, extent %lld", what, (long long)count,
+                                                (long long)mat, (long long)extent);
+  const char* c = static_cast<const char*>(p);
+  const int64_t end = (count - 1) * mat + extent;
+  if (c < g_lo || end > g_hi - c) die("%s: [%p, +%lld) outside the workspace [%p, %p)", what, p, (long long)end, g_lo, g_hi);
+}
+
+}  // namespace
+
+extern "C" void stub_set_workspace(const void* base, size_t bytes) {
+  g_lo = static_cast<const char*>(base);
+  g_hi = g_lo + bytes;
+}
+extern "C" long stub_launches() { return g_launches; }
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+
+namespace muon {
+
+FastDiv make_fastdiv(uint32_t d) {
+  if (d == 0) die("division by zero columns");
+  FastDiv f{};
+  f.d = d;
+  return f;
+}
+
+int elementwise_blocks_per_matrix(int64_t rows, int64_t cols) { return static_cast<int>((rows * cols + 8191) / 8192); }
+
+hipError_t launch_momentum(const MomentumArgs& a, int64_t count, bool, hipStream_t) {
+  ++g_launches;
+  in_ws(a.partials, 1, 0, count * a.blocks_per_mat * 4, "momentum partials");
+  return hipSuccess;
+}
+
+hipError_t launch_momentum_grouped(const MomentumGroups& a, hipStream_t) {
+  ++g_launches;
+  if (a.ngroups < 1 || a.ngroups > kMaxGroups || a.first[0] != 0) die("momentum groups: %d", a.ngroups);
+  for (int g = 0; g < a.ngroups; ++g) {
+    const int64_t n = a.first[g + 1] - a.first[g];
+    if (n <= 0 || n % a.g[g].blocks_per_mat) die("momentum group %d: %lld blocks", g, (long long)n);
+    in_ws(a.g[g].partials, 1, 0, n * 4, "grouped momentum partials");
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_sumsq_partials(const SumsqArgs& a, int64_t count, bool, hipStream_t) {
+  ++g_launches;
+  in_ws(a.partials, 1, 0, count * a.blocks_per_mat * 4, "sum-of-squares partials");
+  return hipSuccess;
+}
+
+hipError_t launch_sumsq_finalize(const float* partials, int per, float* sumsq, int64_t count, hipStream_t) {
+  ++g_launches;
+  if (!sumsq || per < 1) die("finalize: sumsq %p, per %d", static_cast<void*>(sumsq), per);
+  in_ws(partials, 1, 0, count * per * 4, "finalize partials");
+  return hipSuccess;
+}
+
+hipError_t launch_sumsq_finalize_grouped(const FinalizeGroups& a, hipStream_t) {
+  ++g_launches;
+  for (int g = 0; g < a.ngroups; ++g)
+    in_ws(a.partials[g], 1, 0, (a.first[g + 1] - a.first[g]) * a.per[g] * 4, "grouped finalize partials");
+  return hipSuccess;
+}
+
+hipError_t launch_apply(const ApplyArgs&, int64_t count, bool, hipStream_t) {
+  ++g_launches;
+  if (count < 1) die("apply count %lld", (long long)count);
+  return hipSuccess;
+}
+
+hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t) {
+  ++g_launches;
+  for (int g = 0; g < a.ngroups; ++g)
+    if (a.first[g + 1] - a.first[g] <= 0) die("apply group %d empty", g);
+  return hipSuccess;
+}
+
+hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t) {
+  ++g_launches;
+  const int es = a.compute ? 2 : 4;
+  const int64_t n = static_cast<int64_t>(a.Pr) * a.Pc;
+  if (a.Pr % 64 || a.Pc % 64) die("pack: padded shape %d x %d", a.Pr, a.Pc);
+  if (!a.S && !a.T) die("pack writes nothing");
+  if (a.S) in_ws(a.S, count, a.s_mat, n * es, "pack S");
+  if (a.T) in_ws(a.T, count, a.t_mat, n * es, "pack T");
+  if (a.Lo) in_ws(a.Lo, count, a.lo_mat * 2, n * 2, "pack low part");
+  return hipSuccess;
+}
+
+hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t) {
+  ++g_launches;
+  if (count < 1 || a.rows < 1 || a.cols < 1) die("copy_out shape");
+  return hipSuccess;
+}
+
+hipError_t launch_adamw(const AdamWArgs& a, int64_t total_chunks, hipStream_t) {
+  ++g_launches;
+  if (total_chunks < 1 || a.count < 1) die("adamw: %lld chunks", (long long)total_chunks);
+  return hipSuccess;
+}
+
+hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L, hipStream_t) {
+  ++g_launches;
+  const int64_t es = compute ? 2 : 4;
+  if (tile != 128 && tile != 256) die("tile %d", tile);
+  if (L.ngroups < 1 || L.ngroups > kMaxGroups) die("ngroups %d", L.ngroups);
+  int64_t begin = 0;
+  for (int g = 0; g < L.ngroups; ++g) {
+    const GemmGroup& G = L.g[g];
+    if (G.tile_begin != begin) die("group %d starts at tile %d, expected %lld", g, G.tile_begin, (long long)begin);
+    const int64_t rows = static_cast<int64_t>(G.tiles_m) * tile, cols = static_cast<int64_t>(G.tiles_n) * tile;
+    const int64_t want = G.sym ? static_cast<int64_t>(G.tiles_m) * (G.tiles_m + 1) / 2 : static_cast<int64_t>(G.tiles_m) * G.tiles_n;
+    if (G.tiles_per_mat != want) die("group %d: %d tiles per matrix, expected %lld", g, G.tiles_per_mat, (long long)want);
+    if (G.K < 64 || G.K % 64) die("group %d: K %d", g, G.K);
+    if (G.ms < 1 || G.ms > rows) die("group %d: short side %d beyond %lld padded rows", g, G.ms, (long long)rows);
+    if (epi >= EPI_UPDATE && (G.ns < G.ms || G.ns > cols)) die("group %d: long side %d, %lld padded columns", g, G.ns, (long long)cols);
+    begin += static_cast<int64_t>(G.tiles_per_mat) * G.count;
+    // operands: P rows i with K contiguous; Q rows j with K contiguous, or k-major (K rows of cols)
+    in_ws(G.P, G.count, G.p_mat, ((rows - 1) * G.ldp + G.K) * es, "P");
+    if (kmajor && epi >= EPI_UPDATE && compute) {
+      in_ws(G.Q, G.count, G.q_mat, ((G.K - 1) * static_cast<int64_t>(G.ldq) + cols) * es, "Q (k-major)");
+    } else {
+      in_ws(G.Q, G.count, G.q_mat, ((cols - 1) * G.ldq + G.K) * es, "Q");
+    }
+    if (epi == EPI_GRAM || epi == EPI_POLY) {
+      if (G.tiles_m != G.tiles_n || !G.sym) die("symmetric stage with a %d x %d grid", G.tiles_m, G.tiles_n);
+      if (epi == EPI_POLY) in_ws(G.E0, G.count, G.e0_mat, ((rows - 1) * G.lde0 + cols) * es, "poly A");
+      in_ws(G.O0, G.count, G.o0_mat, ((rows - 1) * G.ldo0 + cols) * es, "Gram/poly output");
+    } else if (compute) {
+      in_ws(G.E1, G.count, G.e1_mat, rows * cols * 2, "low part in");
+      if (epi == EPI_UPDATE) {
+        in_ws(G.O0, G.count, G.o0_mat, rows * cols * 2, "low part out");
+        in_ws(G.O1, G.count, G.o1_mat, ((rows - 1) * G.ldo1 + cols) * 2, "high part out");
+        if (kmajor != (G.OT == nullptr)) die("X'^T output %p with kmajor %d", static_cast<void*>(G.OT), kmajor);
+        if (G.OT) in_ws(G.OT, G.count, G.ot_mat, ((cols - 1) * G.ldot + rows) * 2, "X'^T out");
+      }
+    } else {
+      in_ws(G.E0, G.count, G.e0_mat, ((rows - 1) * G.lde0 + cols) * 4, "X in");
+      if (epi == EPI_UPDATE) {
+        in_ws(G.O0, G.count, G.o0_mat, ((rows - 1) * G.ldo0 + cols) * 4, "X out");
+        in_ws(G.OT, G.count, G.ot_mat, ((cols - 1) * G.ldot + rows) * 4, "X^T out");
+      }
+    }
+  }
+  if (begin != L.total_tiles) die("%lld tiles in groups, launch says %d", (long long)begin, L.total_tiles);
+  return hipSuccess;
+}
+
+}  // namespace muon

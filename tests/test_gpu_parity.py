@@ -324,6 +324,29 @@ def test_ns_transpose_equivariance(mx):
     assert rel(f64(b[0]).T, f64(a[0])) <= TOL_F32
 
 
+@pytest.mark.parametrize("compute", [0, 1])
+def test_ns_scale_invariance_and_odd_symmetry(mx, compute):
+    """Invariants of the method on the GPU path.  Multiplying N by a power of
+    two scales the sum of squares by its square exactly and the norm exactly,
+    so X_0 is unchanged (eps = 1e-7 is far below the rounding of a norm near
+    40) and so is every later bit, on both paths.  -N gives -O: bit for bit on
+    the fp32 path, whose every rounding is to nearest even; on the bf16 path
+    to within rounding, because the bf16 MFMA's internal summation does not
+    round symmetrically under negation (found by this test: some outputs
+    differ in their last bit)."""
+    for shape in [(2, 300, 700), (1, 900, 256), (3, 128, 512)]:
+        N = randn(shape, sum(shape), torch.float32 if compute == 0 else torch.bfloat16)
+        o = run_ns(mx, N, compute)
+        assert torch.equal(run_ns(mx, 4 * N, compute), o)
+        assert torch.equal(run_ns(mx, N / 8, compute), o)
+        neg = run_ns(mx, -N, compute)
+        if compute == 0:
+            assert torch.equal(neg, -o)
+        else:
+            for i in range(shape[0]):
+                assert rel(-f64(neg[i]), f64(o[i])) <= 1e-2
+
+
 def test_ns_batched_strided_and_pointer_array(mx):
     """A strided batch (per-head row blocks, ld = 4 x cols) and the same
     matrices as a pointer array give the oracle's answer."""
@@ -399,6 +422,29 @@ def test_persistent_grid_matches_short_launches(mx):
     for (n, r, c), N, out in zip(shapes, Ns, outs):
         for i in sorted({0, n // 3, n - 1}):
             assert rel(f64(out[i]), O.newton_schulz(f64(N[i]), 5)) <= TOL_BF16, f"{r}x{c} matrix {i}"
+
+
+def test_muon_step_more_than_eight_groups(mx):
+    """MuonStep runs at most 8 groups per grouped launch; 10 shape groups
+    (two launches per stage) must equal one MuonStep per group, bit for bit,
+    over two steps."""
+    shapes = [(1, 64 + 16 * k, 96 + 8 * k) for k in range(10)]
+    def make():
+        out = []
+        for k, s in enumerate(shapes):
+            out.append((randn(s, 900 + k, torch.bfloat16, 0.02), randn(s, 950 + k, torch.bfloat16)))
+        return out
+    together, apart = make(), make()
+    big = mx.MuonStep(together, lr=0.01, weight_decay=0.1)
+    small = [mx.MuonStep([wg], lr=0.01, weight_decay=0.1) for wg in apart]
+    assert len(big.chunks) == 2
+    for _ in range(2):
+        big.step()
+        for st in small:
+            st.step()
+    torch.cuda.synchronize()
+    for k, ((wa, _), (wb, _)) in enumerate(zip(together, apart)):
+        assert torch.equal(wa, wb), f"group {k}"
 
 
 # --------------------------------------------------------------- full steps
