@@ -159,7 +159,9 @@ def bench_adamw(args):
            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
            "config": {"workload": f"AdamW leg: embedding and head {synth.ADAMW_VOCAB}x{synth.ADAMW_HIDDEN} bf16, "
                                   f"65 RMSNorm weights of {synth.ADAMW_HIDDEN}", "elements": elems,
-                      "bytes_per_element": ADAMW_BYTES, "parallelism": "single GPU"},
+                      "bytes_per_element": ADAMW_BYTES, "parallelism": "single GPU",
+                      "hyperparameters": {"lr": ADAM_LR, "betas": list(ADAM_BETAS), "eps": ADAM_EPS,
+                                          "weight_decay": ADAM_WD}},
            "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": gbs / PEAK_HBM_GBS, "kernel": "adamw_kernel",
                         "traffic": measured_traffic("adamw_kernel_8b_nonmatrix_params.md", "adamw.hip", "bytes_per_step")},
@@ -310,7 +312,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": f"{cfg.slug}: {cfg.name}", "matrices": cfg.matrices,
-                   "shapes": shapes, "gradients": cfg.kind, "ns_steps": ns_steps, "coefficients": args.coeffs, "compute": "bf16 MFMA, fp32 accumulate",
+                   "shapes": shapes, "gradients": cfg.kind, "ns_steps": ns_steps, "coefficients": args.coeffs,
+                   "compute": "bf16 MFMA, fp32 accumulate",
+                   "hyperparameters": {"beta": stepper.beta, "nesterov": bool(stepper.nesterov), "eps": stepper.eps,
+                                       "abc": [float(x) for x in stepper.coeffs], "lr": stepper.lr,
+                                       "weight_decay": stepper.weight_decay,
+                                       "scale": f"{stepper.coeff}*sqrt(max(m,n))", "momentum_dtype": "f32",
+                                       "ns_input_dtype": "f32"},
                    "parallelism": "single GPU"},
         "newton_schulz": {"tflops_algorithmic": ns_tflops, "tflops_nominal_4m2n_2m3": ns_tflops_nominal,
                           "frac_bf16_peak": ns_tflops / PEAK_BF16_TFLOPS, "ms": t_ns,
