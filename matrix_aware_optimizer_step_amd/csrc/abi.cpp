@@ -300,7 +300,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     return ok();
   }
 
-  // 2. X_0 = N / (||N|| + eps) into the padded buffers, both orientations
+  // 2. X_0 = N / (||N|| + eps) into the padded buffers (X, and X^T where the update reads it)
   for (int g = 0; g < ngroups; ++g) {
     const GroupPlan& p = plan.g[g];
     const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;

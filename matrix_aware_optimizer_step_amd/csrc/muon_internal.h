@@ -177,10 +177,11 @@ struct ApplyGroups {
 hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t stream);
 
 // Copy the caller's N (stored m x n) into the padded Newton-Schulz buffers,
-// scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc) and
-// T[c][r] (Pc x Pr), zero outside m x n, in the compute type; with bf16
-// compute and Lo != null also the bf16 residual of X (= S if !tall, T if
-// tall), value - bf16(value), in X's orientation.
+// scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc)
+// and/or T[c][r] (Pc x Pr), each written when non-null, zero outside m x n,
+// in the compute type; with bf16 compute and Lo != null also the bf16
+// residual of X (= S if !tall, T if tall), value - bf16(value), in the
+// update kernel's accumulator order (lo_index()).
 struct PackArgs {
   MatBatch N;
   const float* sumsq;

@@ -10,9 +10,10 @@
 //   update  X' = a X + B X    P = B, Q = X^T       (X^T kept alongside X)
 //
 // so one kernel template serves all three, with the stage's epilogue fused.
-// With bf16 compute the update instead reads X itself as a k-major second
-// operand (row k of X holds the tile's columns contiguously) through LDS
-// transpose reads, so no X^T is ever written.
+// With bf16 compute and short update reductions (a tile class whose padded
+// short side is at most 2048, chosen by the host) the update instead reads X
+// itself as a k-major second operand (row k of X holds the tile's columns
+// contiguously) through LDS transpose reads, and no X^T is written.
 //
 // Tiling: a workgroup computes a BM x BM output tile (BM = 256 with eight
 // wave64s in a 2x4 grid, each owning 128x64; BM = 128 with four wave64s in a
@@ -361,9 +362,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
       for (int r = 0; r < LOADSQ; ++r) *reinterpret_cast<Chunk*>(dp + OPB + soff[r]) = qr[r];
     };
 
-    // ---- accumulators (fp32, from zero: the update's a*X term is added in
-    // the epilogue, so every rounding of the running sum is at the scale of
-    // the product itself)
+    // ---- accumulators (fp32, from zero: the update's a*X term is added later,
+    // its bf16 high part when the main loop reaches the k-tiles that hold it
+    // and the rest in the epilogue, so the running sum's early roundings are
+    // at the scale of the product itself)
     const int frow = lane & 31;
     const int half = lane >> 5;
     const int i_base = ti * BM + wm * WTM + 4 * half;  // acc[fi][fj][4q+e]: row i_base + fi*32 + 8q + e
@@ -551,20 +553,22 @@ void ns_gemm_kernel(const GemmLaunch L) {
     // ---- epilogue.  acc[fi][fj][4q+e] holds C[i][j] with
     //   i = ti*BM + wm*WTM + fi*32 + 8q + 4*half + e
     //   j = tj*BM + wn*WTN + fj*32 + lane%32
-    // Each value is finished in registers (v replaces acc) and stored
-    // row-major straight from the MFMA layout: 32 lanes cover 32 consecutive
-    // columns of one row.  Transposed outputs (X'^T, the mirror tile of a
-    // symmetric product, a tall caller output) are staged per wave through LDS
-    // in 64-row halves, column-major with a 68-float stride (conflict-free for
-    // the 16-byte writes of 4 rows and the 16-byte reads of 8 rows), and leave
-    // as 128-byte row segments.
+    // Each value is finished in registers.  Gram and polynomial tiles, and
+    // the fp32 update, store row-major straight from the MFMA layout (32
+    // lanes cover 32 consecutive columns of one row); the bf16 low part of X'
+    // leaves in its own accumulator-order layout.  Everything else (X'^T, the
+    // mirror tile of a symmetric product, the bf16 high part of X', the last
+    // step's output) is staged per wave through LDS in 64-row halves,
+    // column-major with a 68-float stride (conflict-free for the 16-byte
+    // writes of 4 rows and the 16-byte reads of 8 rows), and leaves as 16-byte
+    // pieces of 128-byte row segments.
     const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
     const int gj0 = tj * BN + wn * WTN;  // first column
 
-    // 1. finish the values and store them row-major, one 32x32 block at a
-    //    time.  The epilogue operand (X, or A for the polynomial) of the
-    //    next PF blocks is loaded ahead, in registers the main loop no longer
-    //    needs, so several blocks' loads are in flight at once.
+    // 1. finish the values, one 32x32 block at a time, and store what leaves
+    //    from registers.  The epilogue operand (X, or A for the polynomial)
+    //    of the next PF blocks can be loaded ahead; PF = 0 measured best (more
+    //    only adds register pressure).
     constexpr int NB = FM * FN;  // 32x32 blocks per wave
     constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
     constexpr bool kHasE = (EPI != EPI_GRAM);
