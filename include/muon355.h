@@ -83,8 +83,8 @@ typedef struct muon_batch {
   void* const* ptrs; /* device array of `count` matrix pointers, or NULL to use base/stride */
   void* base;        /* matrix i at base + i*stride elements when ptrs == NULL */
   int64_t stride;    /* elements between consecutive matrices (strided batch) */
-  int64_t count;     /* number of matrices, >= 1 */
-  int64_t rows;      /* m >= 1 */
+  int64_t count;     /* number of matrices, 1 .. 65535 (split larger batches) */
+  int64_t rows;      /* m >= 1; rows * cols <= 2^31 - 1 */
   int64_t cols;      /* n >= 1 */
   int64_t ld;        /* leading dimension in elements, >= cols */
   int32_t dtype;     /* muon_dtype_t */
