@@ -324,6 +324,22 @@ def test_ns_transpose_equivariance(mx):
     assert rel(f64(b[0]).T, f64(a[0])) <= TOL_F32
 
 
+@pytest.mark.parametrize("shape", [(1, 300, 700), (2, 900, 256), (1, 130, 2000), (3, 128, 512)])
+def test_bf16_carry_of_x_round_trips(mx, shape):
+    """The bf16 path carries X between steps as a bf16 high part plus a
+    residual.  With (a, b, c) = (1, 0, 0) one step gives B = 0 exactly and
+    X_1 = high part + residual, which an fp32 output returns unrounded: it
+    must reproduce X_0 = N/(||N||+eps) to about 16 significant bits.  A
+    bf16-only carry would be off by about 2^-9 relative."""
+    N = randn(shape, 3 * shape[1] + shape[2], torch.float32)
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    mx.orthogonalize(N, out, None, 1, (1.0, 0.0, 0.0), O.EPS, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(shape[0]):
+        x0 = f64(N[i]) / (np.sqrt(np.sum(f64(N[i]) ** 2)) + O.EPS)
+        assert rel(f64(out[i]), x0) <= 3e-5
+
+
 @pytest.mark.parametrize("compute", [0, 1])
 def test_ns_scale_invariance_and_odd_symmetry(mx, compute):
     """Invariants of the method on the GPU path.  Multiplying N by a power of
