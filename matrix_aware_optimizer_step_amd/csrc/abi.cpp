@@ -134,7 +134,8 @@ struct GroupPlan {
   int32_t Pr, Pc;       // padded stored shape
   int32_t kmajor;       // bf16 update reads X itself, k-major (no X^T kept)
   // byte offsets into the workspace
-  int64_t xlo, xc[2], xt[2], a, b, sumsq, partials;  // xlo: bf16 low part of X (bf16 compute)
+  int64_t xlo, xloe, xc[2], xt[2], a, b, sumsq, partials;  // xlo, xloe: low part of X, codes and
+                                                            // exponents (bf16 compute)
   int32_t blocks_per_mat;
 };
 
@@ -190,7 +191,8 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.Pc = p.tall ? p.Mp : p.Np;
     const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
     const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
-    p.xlo = compute == MUON_BF16 ? take(p.count * mn * 2) : -1;
+    p.xlo = compute == MUON_BF16 ? take(p.count * mn) : -1;
+    p.xloe = compute == MUON_BF16 ? take(p.count * mn / kLoExpPerCodes) : -1;
     p.xc[0] = take(p.count * mn * es);
     p.xc[1] = take(p.count * mn * es);
     // X^T only where the update reads it
@@ -321,8 +323,10 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     pa.S = p.tall ? (p.kmajor ? nullptr : ws + p.xt[0]) : ws + p.xc[0];
     pa.T = p.tall ? ws + p.xc[0] : (p.kmajor ? nullptr : ws + p.xt[0]);
     pa.s_mat = pa.t_mat = mn * es;
-    pa.Lo = compute == MUON_BF16 ? reinterpret_cast<uint16_t*>(ws + p.xlo) : nullptr;
+    pa.Lo = compute == MUON_BF16 ? reinterpret_cast<int8_t*>(ws + p.xlo) : nullptr;
     pa.lo_mat = mn;
+    pa.LoE = compute == MUON_BF16 ? reinterpret_cast<uint8_t*>(ws + p.xloe) : nullptr;
+    pa.loe_mat = mn / kLoExpPerCodes;
     pa.lo_bm = p.tile;
     pa.lo_tiles_n = p.Np / p.tile;
     if ((e = launch_pack(pa, p.count, stream)) != hipSuccess) return launch_status(e, "pack");
@@ -377,7 +381,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             G.P = ws + p.b;
             G.p_mat = mm * es;
             G.ldp = p.Mp;
-            // second operand: X^T (fp32), or X itself read k-major (bf16)
+            // second operand: X^T, or X itself read k-major (a k-major bf16 class)
             G.Q = ws + (p.kmajor ? p.xc[cur] : p.xt[cur]);
             G.q_mat = mn * es;
             G.ldq = p.kmajor ? p.Np : p.Mp;
@@ -386,7 +390,9 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             // part is the Q operand, which the kernel adds from LDS)
             if (compute == MUON_BF16) {
               G.E1 = ws + p.xlo;
-              G.e1_mat = mn * 2;
+              G.e1_mat = mn;
+              G.LoE = reinterpret_cast<uint8_t*>(ws + p.xloe);
+              G.loe_mat = mn / kLoExpPerCodes;
               G.lde1 = p.Np;
             } else {
               G.E0 = ws + p.xc[cur];
@@ -399,7 +405,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
               // the low part is rewritten in place: each element is read
               // and written by the same lane of the same tile
               G.O0 = ws + p.xlo;
-              G.o0_mat = mn * 2;
+              G.o0_mat = mn;
               G.ldo0 = p.Np;
               G.O1 = ws + p.xc[nxt];
               G.o1_mat = mn * 2;

@@ -10,8 +10,8 @@
 //                     matrix (deterministic; no float atomics);
 //   apply_kernel      W <- (1 - lr*wd)*W - lr*s*O (section 11.5);
 //   pack_kernel       N / (||N||_F + eps) into the padded Newton-Schulz
-//                     buffers: X (the wide orientation), X^T for fp32
-//                     compute, the bf16 low part of X for bf16 compute,
+//                     buffers: X (the wide orientation), X^T where the
+//                     update reads it, the low part of X for bf16 compute,
 //                     through an LDS tile transpose so that reads and writes
 //                     stay coalesced;
 //   copy_out_kernel   the zero-step output, N / (||N||_F + eps).
@@ -22,6 +22,7 @@
 // so that matrices with ld > cols (row blocks of a larger weight) need no
 // separate path.
 
+#include "lo8.h"
 #include "muon_internal.h"
 
 namespace muon {
@@ -119,11 +120,6 @@ __device__ __forceinline__ void store4(char* p, int dtype, const float* v) {
 
 __device__ __forceinline__ float load1(const char* p, int dtype) {
   return dtype ? bf16_to_f32(*reinterpret_cast<const uint16_t*>(p)) : *reinterpret_cast<const float*>(p);
-}
-// v - bf16(v) rounded to bf16: the low part that, added to the bf16 high
-// part, carries about 16 significant bits of v (the subtraction is exact).
-__device__ __forceinline__ uint16_t bf16_residual(float v) {
-  return f32_to_bf16(v - bf16_to_f32(f32_to_bf16(v)));
 }
 __device__ __forceinline__ void store1(char* p, int dtype, float v) {
   if (dtype) {
@@ -407,27 +403,26 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
   }
   __syncthreads();
   if (a.Lo) {
-    // The residual of X in the update kernel's accumulator order: this 64 x 64
-    // tile of X is four consecutive 32x32 blocks of one wave there, one
-    // contiguous run of 4096 values.  Thread t assembles lane (t % 64) of
-    // block (t / 64): its 16 values, rows 8*(r/4) + 4*half + r%4 of the
-    // block, leave as two 16-byte stores.
+    // The low part of X in the update kernel's accumulator order: this 64 x 64
+    // tile of X is four consecutive 32x32 blocks of one wave there.  Thread t
+    // encodes lane (t % 64) of block (t / 64): its 16 values, rows
+    // 8*(r/4) + 4*half + r%4 of the block, leave as one 16-byte store of
+    // codes and one exponent byte.
     const uint32_t i0 = a.tall ? c0 : r0;  // top-left corner of this tile in X
     const uint32_t j0 = a.tall ? r0 : c0;
-    uint16_t* run = a.Lo + mat * a.lo_mat + lo_index(i0, j0, a.lo_bm, a.lo_tiles_n);
     const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int hf = lane >> 5, jl = (b & 1) * 32 + (lane & 31);
-    uint32_t w[8];
+    float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int il = (b >> 1) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      const float v = a.tall ? tile[jl][il] : tile[il][jl];  // X[i][j] = S[j][i] when tall
-      const uint32_t lo = bf16_residual(v);
-      w[r >> 1] = (r & 1) ? (w[r >> 1] | (lo << 16)) : lo;
+      x[r] = a.tall ? tile[jl][il] : tile[il][jl];  // X[i][j] = S[j][i] when tall
     }
-    uint4* dst = reinterpret_cast<uint4*>(run + (b * 64 + lane) * 16);
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    const Lo8 c = lo8_encode(x);
+    int8_t* run = a.Lo + mat * a.lo_mat + lo_index(i0, j0, a.lo_bm, a.lo_tiles_n);
+    *reinterpret_cast<uint4*>(run + (b * 64 + lane) * 16) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+    a.LoE[mat * a.loe_mat + lo_exp_index(i0 + (b >> 1) * 32 + 4 * hf, j0 + (b & 1) * 32 + (lane & 31), a.lo_bm,
+                                         a.lo_tiles_n)] = static_cast<uint8_t>(c.e);
   }
   // write rows of T = columns of the tile (if wanted)
   if (!a.T) return;

@@ -51,12 +51,14 @@ struct GemmGroup {
   // residual), about 16 significant bits together.
   const char* E0; int64_t e0_mat; int32_t lde0;  // POLY: A; UPDATE/FINAL, fp32 compute: X
   int32_t pad0_;
-  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X in the
-                                                 // lo_index() layout (the high part is Q = X, added
-                                                 // from the operand tiles)
+  const char* E1; int64_t e1_mat; int32_t lde1;  // UPDATE/FINAL, bf16 compute: low part of X, int8
+                                                 // codes in the lo_index() layout (the high part is
+                                                 // Q, added from the operand tiles)
   int32_t pad5_;
+  uint8_t* LoE; int64_t loe_mat;                 // ... and its exponents (lo_exp_index()), read and
+                                                 // rewritten in place by the update
   char* O0; int64_t o0_mat; int32_t ldo0;        // GRAM/POLY: A or B; UPDATE: next X (fp32) or its low
-                                                 // part (lo_index() layout, in place)
+                                                 // part's codes (lo_index() layout, in place)
   int32_t pad1_;
   char* O1; int64_t o1_mat; int32_t ldo1;        // UPDATE, bf16 compute: high part of the next X
   int32_t pad2_;
@@ -69,14 +71,21 @@ struct GemmGroup {
   int32_t pad4_;
 };
 
-// Layout of the bf16 low part of X (bf16 compute).  Only the update kernel
-// reads and writes it (plus the pack kernel, which writes its first value),
-// so it is kept in the update kernel's accumulator order: a bm x bm output
-// tile is split over 2 x (bm/64) waves of (bm/2) x 64 elements, each wave's
-// sub-tile into 32x32 MFMA blocks, and each block into 64 lanes x 16 values
-// (lane = 32*half + column, value r <-> row 8*(r/4) + 4*half + r%4).  One
-// lane's 16 values of a block are 32 contiguous bytes.  Element (i, j) of
-// the padded Newton-Schulz matrix with `tiles_n` tile columns lives at:
+// The low part of X (bf16 compute): the residual X - bf16(X), kept as int8
+// codes in multiples of a step shared by the 16 values one lane holds in one
+// 32x32 MFMA block.  step = 2^(E - 142), with E the biased exponent of the
+// largest |bf16(X)| of those 16: 1/256 of that value's bf16 spacing, so
+// every residual (at most half a spacing) is a code in [-127, 127]; E < 16
+// (values below 2^-111) keeps a zero residual.  With the high part that is
+// about 16 significant bits (device helpers in lo8.h).  Only the update
+// kernel reads and writes it (plus the pack kernel, which writes its first
+// value), so it is kept in the update kernel's accumulator order: a bm x bm
+// output tile is split over 2 x (bm/64) waves of (bm/2) x 64 elements, each
+// wave's sub-tile into 32x32 MFMA blocks, and each block into 64 lanes x 16
+// values (lane = 32*half + column, value r <-> row 8*(r/4) + 4*half + r%4).
+// One lane's 16 codes of a block are 16 contiguous bytes; the code of element
+// (i, j) of the padded Newton-Schulz matrix with `tiles_n` tile columns is
+// at byte:
 __host__ __device__ inline uint32_t lo_index(uint32_t i, uint32_t j, uint32_t bm, uint32_t tiles_n) {
   const uint32_t wgn = bm / 64, wtm = bm / 2, nb = (wtm / 32) * 2;
   const uint32_t ti = i / bm, tj = j / bm, il = i % bm, jl = j % bm;
@@ -88,6 +97,23 @@ __host__ __device__ inline uint32_t lo_index(uint32_t i, uint32_t j, uint32_t bm
   const uint32_t r = 4 * (rb / 8) + rb % 4;
   return (((ti * tiles_n + tj) * (2 * wgn) + wave) * nb + blk) * 1024u + lane * 16u + r;
 }
+
+// One exponent byte per lane and block, a lane's exponents of all its
+// blocks contiguous (one 8- or 4-byte access); the exponent that element
+// (i, j)'s code uses is at byte:
+__host__ __device__ inline uint32_t lo_exp_index(uint32_t i, uint32_t j, uint32_t bm, uint32_t tiles_n) {
+  const uint32_t wgn = bm / 64, wtm = bm / 2, nb = (wtm / 32) * 2;
+  const uint32_t ti = i / bm, tj = j / bm, il = i % bm, jl = j % bm;
+  const uint32_t wave = (il / wtm) * wgn + jl / 64;
+  const uint32_t ii = il % wtm, jj = jl % 64;
+  const uint32_t blk = (ii / 32) * 2 + jj / 32;
+  const uint32_t lane = (((ii % 32) % 8) / 4) * 32 + jj % 32;
+  return (((ti * tiles_n + tj) * (2 * wgn) + wave) * 64u + lane) * nb + blk;
+}
+
+// Bytes of the low part per element of the padded matrix: one code, and one
+// exponent per 16 codes.
+constexpr int kLoExpPerCodes = 16;
 
 struct GemmLaunch {
   int32_t ngroups;
@@ -179,9 +205,8 @@ hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t stream);
 // Copy the caller's N (stored m x n) into the padded Newton-Schulz buffers,
 // scaled by 1/(sqrt(sumsq)+eps):  S[r][c] (stored orientation, Pr x Pc)
 // and/or T[c][r] (Pc x Pr), each written when non-null, zero outside m x n,
-// in the compute type; with bf16 compute and Lo != null also the bf16
-// residual of X (= S if !tall, T if tall), value - bf16(value), in the
-// update kernel's accumulator order (lo_index()).
+// in the compute type; with bf16 compute and Lo != null also the low part of
+// X (= S if !tall, T if tall): codes and exponents of value - bf16(value).
 struct PackArgs {
   MatBatch N;
   const float* sumsq;
@@ -194,8 +219,9 @@ struct PackArgs {
   int32_t pad_;
   char* S; int64_t s_mat;  // stored orientation (bytes per matrix); null: not written
   char* T; int64_t t_mat;  // its transpose; null: not written
-  uint16_t* Lo; int64_t lo_mat;  // elements per matrix, in the lo_index() layout
-  int32_t lo_bm, lo_tiles_n;     // update tile size and tile columns of X
+  int8_t* Lo; int64_t lo_mat;     // low part's codes (lo_index()), bytes per matrix
+  uint8_t* LoE; int64_t loe_mat;  // and exponents (lo_exp_index()), bytes per matrix
+  int32_t lo_bm, lo_tiles_n;      // update tile size and tile columns of X
 };
 hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream);
 

@@ -29,6 +29,7 @@
 // the same lane/element -> k assignment is used for the two operands, so the
 // product does not depend on the hardware's internal k order.
 
+#include "lo8.h"
 #include "muon_internal.h"
 
 namespace muon {
@@ -573,23 +574,26 @@ void ns_gemm_kernel(const GemmLaunch L) {
     constexpr int PF = 0;        // blocks loaded ahead (more only adds register pressure)
     constexpr bool kHasE = (EPI != EPI_GRAM);
     float ebuf[kHasE ? PF + 1 : 1][16];
-    // bf16 update: the low part of X is stored in this kernel's accumulator
-    // order (lo_index()), so each lane's 16 values of a block are 32 contiguous
-    // bytes; all blocks are loaded here in one round of 16-byte loads and the
-    // new low part leaves the same way.
+    // bf16 update: the low part of X is kept in this kernel's accumulator
+    // order (lo_index(), lo_exp_index()): a lane's 16 codes of a block are 16
+    // contiguous bytes and its exponents of all NB blocks NB contiguous bytes,
+    // so everything is loaded here in one round and the new low part leaves
+    // the same way.
     constexpr bool kLoNative = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
-    static_assert(!kLoNative || (BN == BM && WGM == 2 && WGN == BM / 64 && WTN == 64),
+    static_assert(!kLoNative || (BN == BM && WGM == 2 && WGN == BM / 64 && WTN == 64 && NB % 4 == 0),
                   "the low part's layout assumes this tile shape (see lo_index)");
-    uint4 lo_pre[kLoNative ? NB : 1][2];
-    const uint32_t lo_off =
-        ((static_cast<uint32_t>(ti * G.tiles_n + tj) * NW + wave) * NB) * 1024u + static_cast<uint32_t>(lane) * 16u;
+    uint4 lo_pre[kLoNative ? NB : 1];
+    uint32_t lo_exp[kLoNative ? NB / 4 : 1];
+    const uint32_t tile_wave = static_cast<uint32_t>(ti * G.tiles_n + tj) * NW + wave;
+    const uint32_t lo_off = tile_wave * NB * 1024u + static_cast<uint32_t>(lane) * 16u;  // bytes, block 0
+    const uint32_t lo_eoff = (tile_wave * 64u + static_cast<uint32_t>(lane)) * NB;
     if constexpr (kLoNative) {
       const char* El = G.E1 + mat * G.e1_mat;
 #pragma unroll
-      for (int b = 0; b < NB; ++b) {
-        lo_pre[b][0] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u);
-        lo_pre[b][1] = *reinterpret_cast<const uint4*>(El + (lo_off + b * 1024u) * 2u + 16u);
-      }
+      for (int b = 0; b < NB; ++b) lo_pre[b] = *reinterpret_cast<const uint4*>(El + lo_off + b * 1024u);
+      const uint32_t* Ee = reinterpret_cast<const uint32_t*>(G.LoE + mat * G.loe_mat + lo_eoff);
+#pragma unroll
+      for (int k = 0; k < NB / 4; ++k) lo_exp[k] = Ee[k];
     }
     auto eload = [&](int blk, float* e) {
       const int fi = blk / FN, fj = blk % FN;
@@ -607,10 +611,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
         const char* Em = G.E0 + mat * G.e0_mat;
         const uint32_t lde = G.lde0;
         if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
-          const uint32_t w[8] = {lo_pre[blk][0].x, lo_pre[blk][0].y, lo_pre[blk][0].z, lo_pre[blk][0].w,
-                                 lo_pre[blk][1].x, lo_pre[blk][1].y, lo_pre[blk][1].z, lo_pre[blk][1].w};
+          const uint32_t w[4] = {lo_pre[blk].x, lo_pre[blk].y, lo_pre[blk].z, lo_pre[blk].w};
+          const float step = lo8_step((lo_exp[blk >> 2] >> (8 * (blk & 3))) & 0xffu);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = bf16_to_f32(static_cast<uint16_t>(w[r >> 1] >> (16 * (r & 1))));
+          for (int r = 0; r < 16; ++r) e[r] = lo8_decode(w, r, step);
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -624,6 +628,9 @@ void ns_gemm_kernel(const GemmLaunch L) {
 #pragma unroll
       for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
     }
+    uint32_t new_exp[kLoNative ? NB / 4 : 1];
+#pragma unroll
+    for (int k = 0; k < (kLoNative ? NB / 4 : 1); ++k) new_exp[k] = 0;
 #pragma unroll
     for (int blk = 0; blk < NB; ++blk) {
       const int fi = blk / FN, fj = blk % FN;
@@ -651,17 +658,14 @@ void ns_gemm_kernel(const GemmLaunch L) {
         char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
         const uint32_t ldo0 = G.ldo0;
         if constexpr (sizeof(T) == 2) {
-          // the high part leaves from the LDS staging below, as row segments
-          uint32_t lw[8];
+          // the high part leaves from the LDS staging below, as row segments;
+          // the low part's codes here, its exponents after the last block
+          float x[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint16_t hi = f32_to_bf16(acc[fi][fj][r]);
-            const uint32_t lo = f32_to_bf16(acc[fi][fj][r] - bf16_to_f32(hi));
-            lw[r >> 1] = (r & 1) ? (lw[r >> 1] | (lo << 16)) : lo;
-          }
-          uint4* Ld = reinterpret_cast<uint4*>(O0m + (lo_off + blk * 1024u) * 2u);
-          Ld[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-          Ld[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
+          for (int r = 0; r < 16; ++r) x[r] = acc[fi][fj][r];
+          const Lo8 c = lo8_encode(x);
+          *reinterpret_cast<uint4*>(O0m + lo_off + blk * 1024u) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+          new_exp[blk >> 2] |= c.e << (8 * (blk & 3));
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -679,6 +683,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
           }
         }
       }  // EPI_FINAL, bf16 compute: the caller's output leaves from the LDS staging below
+    }
+    if constexpr (kLoNative && EPI == EPI_UPDATE) {
+      uint32_t* Eo = reinterpret_cast<uint32_t*>(G.LoE + mat * G.loe_mat + lo_eoff);  // in place
+#pragma unroll
+      for (int k = 0; k < NB / 4; ++k) Eo[k] = new_exp[k];
     }
 
     // 3. transposed stores through LDS

@@ -114,7 +114,10 @@ hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t) {
   if (!a.S && !a.T) die("pack writes nothing");
   if (a.S) in_ws(a.S, count, a.s_mat, n * es, "pack S");
   if (a.T) in_ws(a.T, count, a.t_mat, n * es, "pack T");
-  if (a.Lo) in_ws(a.Lo, count, a.lo_mat * 2, n * 2, "pack low part");
+  if (a.Lo) {
+    in_ws(a.Lo, count, a.lo_mat, n, "pack low-part codes");
+    in_ws(a.LoE, count, a.loe_mat, n / kLoExpPerCodes, "pack low-part exponents");
+  }
   return hipSuccess;
 }
 
@@ -158,9 +161,10 @@ hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const Gem
       if (epi == EPI_POLY) in_ws(G.E0, G.count, G.e0_mat, ((rows - 1) * G.lde0 + cols) * es, "poly A");
       in_ws(G.O0, G.count, G.o0_mat, ((rows - 1) * G.ldo0 + cols) * es, "Gram/poly output");
     } else if (compute) {
-      in_ws(G.E1, G.count, G.e1_mat, rows * cols * 2, "low part in");
+      in_ws(G.E1, G.count, G.e1_mat, rows * cols, "low-part codes in");
+      in_ws(G.LoE, G.count, G.loe_mat, rows * cols / kLoExpPerCodes, "low-part exponents");
       if (epi == EPI_UPDATE) {
-        in_ws(G.O0, G.count, G.o0_mat, rows * cols * 2, "low part out");
+        in_ws(G.O0, G.count, G.o0_mat, rows * cols, "low-part codes out");
         in_ws(G.O1, G.count, G.o1_mat, ((rows - 1) * G.ldo1 + cols) * 2, "high part out");
         if (kmajor != (G.OT == nullptr)) die("X'^T output %p with kmajor %d", static_cast<void*>(G.OT), kmajor);
         if (G.OT) in_ws(G.OT, G.count, G.ot_mat, ((cols - 1) * G.ldot + rows) * 2, "X'^T out");

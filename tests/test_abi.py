@@ -155,17 +155,20 @@ def test_apply_rejects_bad_arguments():
 def test_workspace_queries():
     assert L.muon_momentum_workspace(0, 4, 4) == 0
     assert L.muon_momentum_workspace(2, 4096, 14336) >= 2 * (4096 * 14336 // 8192) * 4
-    # X and X^T twice each (bf16 compute: plus the bf16 low part of X), and A
-    # and B (4096^2 each).  A bf16 problem whose short side pads to at most
-    # 2048 keeps no X^T: its update reads X itself, k-major.
+    # X and X^T twice each (bf16 compute: plus the low part of X, one int8 code
+    # per element and one exponent byte per 16), and A and B (4096^2 each).  A
+    # bf16 problem whose short side pads to at most 2048 keeps no X^T: its
+    # update reads X itself, k-major.
     b = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_BF16)
     f = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_F32)
     mn, mm = 4096 * 14336, 4096 * 4096
-    assert mn * (2 + 4 * 2) + 2 * mm * 2 <= b < mn * (2 + 4 * 2) + 2 * mm * 2 + (1 << 20)
+    lo = mn + mn // 16
+    assert lo + mn * 4 * 2 + 2 * mm * 2 <= b < lo + mn * 4 * 2 + 2 * mm * 2 + (1 << 20)
     assert mn * 4 * 4 + 2 * mm * 4 <= f < mn * 4 * 4 + 2 * mm * 4 + (1 << 20)
     k = L.muon_orthogonalize_workspace(1, 768, 2048, L.MUON_BF16)
     mn, mm = 768 * 2048, 768 * 768
-    assert mn * (2 + 2 * 2) + 2 * mm * 2 <= k < mn * (2 + 2 * 2) + 2 * mm * 2 + (1 << 20)
+    lo = mn + mn // 16
+    assert lo + mn * 2 * 2 + 2 * mm * 2 <= k < lo + mn * 2 * 2 + 2 * mm * 2 + (1 << 20)
     # tall and wide of one shape pad to the same Newton-Schulz problem
     assert L.muon_orthogonalize_workspace(3, 700, 300, 1) == L.muon_orthogonalize_workspace(3, 300, 700, 1)
     g = L.muon_orthogonalize_grouped_workspace([2, 1], [4096, 1024], [4096, 4096], L.MUON_BF16)
