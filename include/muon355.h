@@ -171,8 +171,9 @@ size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols,
  * eps    : finite, >= 0 (1e-7 in Muon, [PREPRINT]); added to the norm.
  * compute: MUON_BF16 = bf16 MFMA operands with fp32 accumulation; X is
  *          carried between steps as a bf16 high part (the MFMA operand)
- *          plus a bf16 low part (its rounding residual), about 16
- *          significant bits, for the a*X term (the fast path);
+ *          plus its rounding residual as 8-bit codes with an exponent shared
+ *          by 16 values, about 16 significant bits together, for the a*X
+ *          term (the fast path);
  *          MUON_F32   = fp32 MFMA throughout (the parity path).
  *          With MUON_BF16 an F32 `in` is preferred: the high/low copy of X
  *          starts from it, while a BF16 `in` starts the iteration from
