@@ -146,8 +146,11 @@ def apply(weight, ortho, lr: float, weight_decay: float, mode: int = L.MUON_SCAL
 def apply_grouped(weights, orthos, lr: float, weight_decay: float, mode: int = L.MUON_SCALE_MATCH_RMS,
                   coeff: float = 0.2, stream=None) -> None:
     """muon_apply over several shape classes in one launch."""
-    L.muon_apply_grouped([batch(x).desc for x in weights], [batch(x).desc for x in orthos], lr, weight_decay, mode,
-                         coeff, _stream(stream))
+    # the Batch objects own the device pointer arrays of list inputs: keep
+    # them alive across the call
+    bw = [batch(x) for x in weights]
+    bo = [batch(x) for x in orthos]
+    L.muon_apply_grouped([b.desc for b in bw], [b.desc for b in bo], lr, weight_decay, mode, coeff, _stream(stream))
 
 
 class MuonStep:

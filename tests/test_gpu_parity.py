@@ -177,6 +177,20 @@ def test_apply_grouped_equals_separate_calls(mx):
                 assert within_one_bf16_rounding(f64(W2[k][i]), want)
 
 
+def test_apply_grouped_pointer_arrays_equal_strided(mx):
+    # groups passed as lists of 2-D tensors (device pointer arrays owned by
+    # the binding's batches) give the same bits as strided batches
+    lr, wd = 1.0, 0.5
+    w0 = [randn(s, 600 + k, dt, 0.02) for k, (s, dt) in enumerate(GROUPED_EW)]
+    Od = [randn(s, 700 + k, dt, 0.05) for k, (s, dt) in enumerate(GROUPED_EW)]
+    W1, W2 = [w.clone() for w in w0], [w.clone() for w in w0]
+    mx.apply_grouped(W1, Od, lr, wd, 0, 0.2)
+    mx.apply_grouped([list(w.unbind(0)) for w in W2], [list(o.unbind(0)) for o in Od], lr, wd, 0, 0.2)
+    torch.cuda.synchronize()
+    for k in range(len(GROUPED_EW)):
+        assert torch.equal(W1[k], W2[k]), f"group {k}"
+
+
 # --------------------------------------------------------------------- apply
 
 @pytest.mark.parametrize("mode", [mx_mode for mx_mode in (0, 1, 2)])
