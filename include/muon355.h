@@ -24,9 +24,12 @@
  *            (steps 1-4, update size).
  *   [PREPRINT] "SOAP, Muon, and Beyond: Pushing LLM Pretraining Scales"
  *            (epsilon 1e-7 for Muon).
+ *   [ZH]     "初探优化器（一）：从SGD到SOAP-Muon", section 6.2 (the SOAP
+ *            step; one power-iteration step plus QR for the bases).
  *
  * Beside the Muon step, muon_adamw updates the parameters Muon leaves to
- * AdamW ([GUIDE] sections 5 and 6).
+ * AdamW ([GUIDE] sections 5 and 6), and the soap_* calls run SOAP, Adam in
+ * the eigenbasis of Shampoo's statistics ([GUIDE] 11.1-11.2).
  *
  * Conventions shared by every entry point:
  *   - All matrix memory and all workspaces are caller-owned DEVICE memory.
@@ -278,6 +281,71 @@ typedef struct muon_tensor_list {
 
 muon_status_t muon_adamw(const muon_tensor_list_t* tensors, int64_t step, float lr, float beta1,
                          float beta2, float eps, float weight_decay, void* stream);
+
+/*
+ * SOAP: Adam run in the eigenbasis of Shampoo's row and column statistics
+ * ([GUIDE] section 11.1 "SOAP: Adam in Shampoo's eigenbasis" and 11.2;
+ * [ZH] section 6.2), for `count` same-shape
+ * m x n matrices.  All SOAP state is caller-owned F32 device memory, one
+ * muon_batch_t each, with the gradient's count:
+ *   L (m x m), R (n x n)   row and column statistics, zero before step 1;
+ *   QL (m x m), QR (n x n) their bases, the identity before step 1;
+ *   mbar, vbar (m x n)     Adam's moments in the rotated basis, zero before
+ *                          step 1.
+ * A side passed as NULL (statistic and basis together) keeps the identity
+ * basis: an axis too long to precondition ([GUIDE] 11.2).  One update at
+ * step t = 1, 2, ... with refresh interval f:
+ *   soap_statistics(G, L, R, beta_s);
+ *   if ((t - 1) % f == 0) soap_refresh(L, R, QL, QR, mbar, ...);
+ *   soap_precondition(G, QL, QR, mbar, vbar, D, t, beta1, beta2, eps, ...);
+ *   muon_apply(W, D, lr, weight_decay, MUON_SCALE_NONE, 1, stream);
+ * the last line being W <- (1 - lr*wd) W - lr D.  All arithmetic is fp32
+ * (the products on the fp32 matrix cores).  The calls enqueue on `stream`
+ * and never allocate or synchronize; a workspace (16-byte aligned, of the
+ * size its query returns, 0 for arguments out of range) holds temporaries
+ * and is free again when the stream reaches the end of the call.
+ * Errors: as for the Muon calls (NULL or mismatched descriptors, BF16 where
+ * F32 is required, betas outside [0, 1), step < 1, eps not finite or < 0,
+ * a short workspace), checked before anything is enqueued.
+ */
+
+/* L <- beta_s L + (1-beta_s) G G^T and R <- beta_s R + (1-beta_s) G^T G
+ * ([GUIDE] 11.1 first display).  grad: F32 or BF16, m x n.  L or R may be
+ * NULL.  Only the upper triangle of the old statistic is read and both
+ * triangles are written, so a statistic stays exactly symmetric. */
+muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, const muon_batch_t* R,
+                              float beta_s, void* stream);
+
+/* Q factor of a QR factorization, the triangular factor's diagonal made
+ * non-negative (unique for a full-rank input): Householder reflections
+ * in 32-column panels with blocked trailing updates.  a (read only) and q:
+ * F32, n x n, n <= 32768. */
+size_t soap_qr_workspace(int64_t count, int64_t n);
+muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* workspace, size_t ws_bytes,
+                      void* stream);
+
+/* Basis refresh by one power-iteration step plus QR ([GUIDE] 11.2, [ZH]
+ * 6.2 step 2): QL <- qr(L QL), QR <- qr(R QR) as soap_qr, and the first
+ * moment carried exactly into the new bases ([GUIDE] 11.1 third display):
+ * mbar <- QL_new^T QL_old mbar QR_old^T QR_new.  mbar (m x n) gives the
+ * shape; a NULL side is left out. */
+size_t soap_refresh_workspace(int64_t count, int64_t rows, int64_t cols, int with_l, int with_r);
+muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const muon_batch_t* QL,
+                           const muon_batch_t* QR, const muon_batch_t* mbar, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* [GUIDE] 11.1 between refreshes:
+ *   Gbar = QL^T G QR;  mbar <- beta1 mbar + (1-beta1) Gbar;
+ *   vbar <- beta2 vbar + (1-beta2) Gbar^2;
+ *   D = QL [ (mbar / (1-beta1^t)) / (sqrt(vbar / (1-beta2^t)) + eps) ] QR^T
+ * with epsilon after the square root.  grad: F32 or BF16, m x n; QL, QR
+ * as above or NULL (identity); mbar, vbar in/out; dir (D, out): F32 m x n,
+ * not aliasing the others. */
+size_t soap_precondition_workspace(int64_t count, int64_t rows, int64_t cols);
+muon_status_t soap_precondition(const muon_batch_t* grad, const muon_batch_t* QL, const muon_batch_t* QR,
+                                const muon_batch_t* mbar, const muon_batch_t* vbar, const muon_batch_t* dir,
+                                int64_t step, float beta1, float beta2, float eps, void* workspace,
+                                size_t ws_bytes, void* stream);
 
 /* Static text for a status code. */
 const char* muon_status_string(muon_status_t status);

@@ -26,7 +26,9 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
 EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
             "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped",
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
-            "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw")
+            "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
+            "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
+            "soap_precondition_workspace", "soap_precondition")
 
 ADAMW_CHUNK = 4096  # MUON_ADAMW_CHUNK
 
@@ -82,6 +84,13 @@ def load() -> ctypes.CDLL:
         "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
         "muon_apply_grouped": (ctypes.c_int, [ctypes.c_int, P, P, f32, f32, i32, f32, vp]),
         "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
+        "soap_statistics": (ctypes.c_int, [P, P, P, f32, vp]),
+        "soap_qr_workspace": (sz, [i64, i64]),
+        "soap_qr": (ctypes.c_int, [P, P, vp, sz, vp]),
+        "soap_refresh_workspace": (sz, [i64, i64, i64, ctypes.c_int, ctypes.c_int]),
+        "soap_refresh": (ctypes.c_int, [P, P, P, P, P, vp, sz, vp]),
+        "soap_precondition_workspace": (sz, [i64, i64, i64]),
+        "soap_precondition": (ctypes.c_int, [P, P, P, P, P, P, i64, f32, f32, f32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -187,3 +196,37 @@ def muon_adamw(tensors: MuonTensorList, step: int, lr: float, beta1: float, beta
                weight_decay: float, stream: int) -> None:
     st = load().muon_adamw(ctypes.byref(tensors), step, lr, beta1, beta2, eps, weight_decay, stream)
     _check(st, "muon_adamw")
+
+
+def soap_statistics(grad: MuonBatch, L: MuonBatch | None, R: MuonBatch | None, beta_s: float, stream: int) -> None:
+    _check(load().soap_statistics(_ref(grad), _ref(L), _ref(R), beta_s, stream), "soap_statistics")
+
+
+def soap_qr_workspace(count: int, n: int) -> int:
+    return load().soap_qr_workspace(count, n)
+
+
+def soap_qr(a: MuonBatch, q: MuonBatch, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load().soap_qr(_ref(a), _ref(q), workspace_ptr, ws_bytes, stream), "soap_qr")
+
+
+def soap_refresh_workspace(count: int, rows: int, cols: int, with_l: bool, with_r: bool) -> int:
+    return load().soap_refresh_workspace(count, rows, cols, int(bool(with_l)), int(bool(with_r)))
+
+
+def soap_refresh(L: MuonBatch | None, R: MuonBatch | None, QL: MuonBatch | None, QR: MuonBatch | None,
+                 mbar: MuonBatch, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    st = load().soap_refresh(_ref(L), _ref(R), _ref(QL), _ref(QR), _ref(mbar), workspace_ptr, ws_bytes, stream)
+    _check(st, "soap_refresh")
+
+
+def soap_precondition_workspace(count: int, rows: int, cols: int) -> int:
+    return load().soap_precondition_workspace(count, rows, cols)
+
+
+def soap_precondition(grad: MuonBatch, QL: MuonBatch | None, QR: MuonBatch | None, mbar: MuonBatch,
+                      vbar: MuonBatch, direction: MuonBatch, step: int, beta1: float, beta2: float, eps: float,
+                      workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    st = load().soap_precondition(_ref(grad), _ref(QL), _ref(QR), _ref(mbar), _ref(vbar), _ref(direction), step,
+                                  beta1, beta2, eps, workspace_ptr, ws_bytes, stream)
+    _check(st, "soap_precondition")

@@ -15,7 +15,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmuon355.so")
-SOURCES = ["abi.cpp", "elementwise.hip", "ns_gemm.hip", "adamw.hip"]
+SOURCES = ["abi.cpp", "elementwise.hip", "ns_gemm.hip", "adamw.hip", "soap.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 ALU ops are disabled in all device code.

@@ -726,3 +726,383 @@ muon_status_t muon_apply_grouped(int ngroups, const muon_batch_t* weights, const
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ SOAP
+//
+// Adam in the eigenbasis of Shampoo's statistics ("LLM Optimizers: From SGD
+// and AdamW to SOAP, Muon, and Scalable Training", sections 11.1-11.2;
+// "初探优化器（一）：从SGD到SOAP-Muon", section 6.2), on the fp32 products,
+// the blocked Householder QR and the rotated-Adam kernel of soap.hip.
+
+namespace {
+
+constexpr int64_t kQrMaxDim = 32768;
+constexpr int kMaxSplits = 16;
+
+int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
+
+// Per-matrix float offsets of the QR scratch for an n x n factorization.
+struct QrLayout {
+  int64_t V, Q, W, W2, TT, TQ, sgn, total;
+};
+
+QrLayout qr_layout(int64_t n) {
+  const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
+  QrLayout L;
+  int64_t o = 0;
+  L.V = o;   o += round64(n * n);
+  L.Q = o;   o += round64(n * n);
+  L.W = o;   o += round64(int64_t{kMaxSplits} * kQrPanel * n);
+  L.W2 = o;  o += round64(int64_t{kQrPanel} * n);
+  L.TT = o;  o += round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
+  L.TQ = o;  o += panels * round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
+  L.sgn = o; o += round64(n);
+  L.total = o;
+  return L;
+}
+
+// Split-K plan for a reduction of length K over `tiles` output tiles of
+// `count` matrices: enough splits for about 512 workgroups, each split at
+// least 64 deep, a multiple of the 16-deep k-slice.
+int plan_splits(int64_t K, int64_t tiles, int64_t count, int* ksplit) {
+  int64_t want = (512 + tiles * count - 1) / (tiles * count);
+  want = std::min<int64_t>(want, kMaxSplits);
+  want = std::min<int64_t>(want, std::max<int64_t>(1, K / 64));
+  want = std::min<int64_t>(want, std::max<int64_t>(1, 65535 / count));
+  want = std::max<int64_t>(want, 1);
+  int64_t ks = (K + want - 1) / want;
+  ks = (ks + kSgemmBK - 1) / kSgemmBK * kSgemmBK;
+  *ksplit = static_cast<int>(std::max<int64_t>(ks, 1));
+  return static_cast<int>(std::max<int64_t>(1, (K + *ksplit - 1) / *ksplit));
+}
+
+SgemmOperand op_batch(const muon_batch_t* b, bool kcontig) {
+  SgemmOperand o;
+  std::memset(&o, 0, sizeof(o));
+  o.base = static_cast<const char*>(b->base);
+  o.stride = b->stride * esize(b->dtype);
+  o.ptrs = b->ptrs;
+  o.ld = b->ld;
+  o.dtype = b->dtype == MUON_BF16 ? 1 : 0;
+  o.kcontig = kcontig;
+  o.vec = vec4_ok(b);
+  return o;
+}
+
+SgemmOperand op_ws(const float* base, int64_t mat, int64_t ld, bool kcontig, int64_t off = 0) {
+  SgemmOperand o;
+  std::memset(&o, 0, sizeof(o));
+  o.base = reinterpret_cast<const char*>(base);
+  o.stride = mat * 4;
+  o.off = off * 4;
+  o.ld = ld;
+  o.kcontig = kcontig;
+  o.vec = ld % 4 == 0 && off % 4 == 0 && mat % 4 == 0;
+  return o;
+}
+
+struct COut {
+  char* c;
+  int64_t stride;
+  void* const* ptrs;
+  int64_t off;
+  int64_t ld;
+};
+
+COut out_batch(const muon_batch_t* b) {
+  return COut{static_cast<char*>(b->base), b->stride * 4, b->ptrs, 0, b->ld};
+}
+
+COut out_ws(float* base, int64_t mat, int64_t ld, int64_t off = 0) {
+  return COut{reinterpret_cast<char*>(base), mat * 4, nullptr, off * 4, ld};
+}
+
+hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int64_t M, int64_t N, int64_t K,
+                int64_t count, float alpha, float beta, bool sym, hipStream_t s, int splits = 1, int ksplit = 0,
+                int64_t c_split_floats = 0) {
+  if (M == 0 || N == 0) return hipSuccess;
+  SgemmArgs g;
+  std::memset(&g, 0, sizeof(g));
+  g.a = A;
+  g.b = B;
+  g.c = C.c;
+  g.c_stride = C.stride;
+  g.c_ptrs = C.ptrs;
+  g.c_off = C.off;
+  g.ldc = C.ld;
+  g.c_split = c_split_floats * 4;
+  g.M = static_cast<int32_t>(M);
+  g.N = static_cast<int32_t>(N);
+  g.K = static_cast<int32_t>(K);
+  g.splits = splits;
+  g.ksplit = splits > 1 ? ksplit : static_cast<int32_t>(std::max<int64_t>(K, 1));
+  g.count = static_cast<int32_t>(count);
+  g.alpha = alpha;
+  g.beta = beta;
+  g.sym = sym;
+  return launch_sgemm(g, s);
+}
+
+#define SOAP_TRY(expr, what)                                  \
+  do {                                                        \
+    const hipError_t e_ = (expr);                             \
+    if (e_ != hipSuccess) return launch_status(e_, what);     \
+  } while (0)
+
+// Q factor (R's diagonal made non-negative) of the n x n matrices in P
+// (contiguous, p_mat floats apart; overwritten), written to `q`.
+// Factorization: per 32-column panel, the panel kernel, then the trailing
+// columns  A_t <- (I - V T^T V^T) A_t  as  W = V^T A_t (split over the
+// reduction), W2 = [T^T ... T^T] [W_0; ...; W_s-1], A_t -= V W2.
+// Formation, last panel first:  Q_t <- (I - V T V^T) Q_t  from Q = I.
+muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, float* ws, const muon_batch_t* q,
+                         hipStream_t s) {
+  const QrLayout L = qr_layout(n);
+  const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
+  const int64_t tslot = round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
+  auto ntiles = [](int64_t x) { return (x + kSgemmTile - 1) / kSgemmTile; };
+  for (int64_t p = 0; p < panels; ++p) {
+    const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0, nt = h - nb;
+    int ks_f = 0, ks_q = 0;
+    const int sf = nt > 0 ? plan_splits(h, ntiles(nt), count, &ks_f) : 1;
+    const int sq = plan_splits(h, ntiles(h), count, &ks_q);
+    QrPanelArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.A = P;
+    a.a_mat = p_mat;
+    a.V = ws + L.V;
+    a.v_mat = L.total;
+    a.TrepT = ws + L.TT;
+    a.tT_mat = L.total;
+    a.TrepQ = ws + L.TQ + p * tslot;
+    a.tQ_mat = L.total;
+    a.sgn = ws + L.sgn;
+    a.s_mat = L.total;
+    a.n = static_cast<int32_t>(n);
+    a.c0 = static_cast<int32_t>(c0);
+    a.reps_t = sf;
+    a.reps_q = sq;
+    a.vec = n % 4 == 0;
+    SOAP_TRY(launch_qr_panel(a, count, s), "qr panel");
+    if (nt > 0) {
+      const int64_t vo = c0 * n + c0;
+      SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, false, vo), op_ws(P, p_mat, n, false, vo + nb),
+                    out_ws(ws + L.W, L.total, nt), nb, nt, h, count, 1.f, 0.f, false, s, sf, ks_f, nb * nt),
+               "qr trailing product");
+      SOAP_TRY(gemm(op_ws(ws + L.TT, L.total, nb * sf, true), op_ws(ws + L.W, L.total, nt, false),
+                    out_ws(ws + L.W2, L.total, nt), nb, nt, nb * sf, count, 1.f, 0.f, false, s),
+               "qr block factor");
+      SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, true, vo), op_ws(ws + L.W2, L.total, nt, false),
+                    out_ws(P, p_mat, n, vo + nb), h, nt, nb, count, -1.f, 1.f, false, s),
+               "qr trailing update");
+    }
+  }
+  SOAP_TRY(launch_eye(ws + L.Q, L.total, static_cast<int32_t>(n), count, s), "qr identity");
+  for (int64_t p = panels - 1; p >= 0; --p) {
+    const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0;
+    int ks_q = 0;
+    const int sq = plan_splits(h, ntiles(h), count, &ks_q);
+    const int64_t vo = c0 * n + c0;
+    SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, false, vo), op_ws(ws + L.Q, L.total, n, false, vo),
+                  out_ws(ws + L.W, L.total, h), nb, h, h, count, 1.f, 0.f, false, s, sq, ks_q, nb * h),
+             "qr formation product");
+    SOAP_TRY(gemm(op_ws(ws + L.TQ + p * tslot, L.total, nb * sq, true), op_ws(ws + L.W, L.total, h, false),
+                  out_ws(ws + L.W2, L.total, h), nb, h, nb * sq, count, 1.f, 0.f, false, s),
+             "qr formation factor");
+    SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, true, vo), op_ws(ws + L.W2, L.total, h, false),
+                  out_ws(ws + L.Q, L.total, n, vo), h, h, nb, count, -1.f, 1.f, false, s),
+             "qr formation update");
+  }
+  SOAP_TRY(launch_sign_copy(ws + L.Q, L.total, ws + L.sgn, L.total, to_mat(q), static_cast<int32_t>(n), count, s),
+           "qr signs");
+  return MUON_OK;
+}
+
+muon_status_t check_f32(const muon_batch_t* b, const char* name, int64_t count, int64_t rows, int64_t cols) {
+  muon_status_t st;
+  if ((st = check_batch(b, name, false)) != MUON_OK) return st;
+  if (b->count != count || b->rows != rows || b->cols != cols)
+    return fail(MUON_ERR_INVALID_VALUE, "%s: %lld x (%lld x %lld) given, %lld x (%lld x %lld) expected", name,
+                (long long)b->count, (long long)b->rows, (long long)b->cols, (long long)count, (long long)rows,
+                (long long)cols);
+  return MUON_OK;
+}
+
+size_t qr_bytes(int64_t count, int64_t n) {
+  return static_cast<size_t>(count * (round64(n * n) + qr_layout(n).total) * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t soap_qr_workspace(int64_t count, int64_t n) {
+  if (count < 1 || count > 65535 || n < 1 || n > kQrMaxDim) return 0;
+  return qr_bytes(count, n);
+}
+
+muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* workspace, size_t ws_bytes,
+                      void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(a, "a", false)) != MUON_OK) return st;
+  if (a->rows != a->cols) return fail(MUON_ERR_INVALID_VALUE, "a: must be square");
+  if (a->rows > kQrMaxDim) return fail(MUON_ERR_UNSUPPORTED, "a: order above %lld", (long long)kQrMaxDim);
+  if ((st = check_f32(q, "q", a->count, a->rows, a->cols)) != MUON_OK) return st;
+  const int64_t n = a->rows;
+  if ((st = check_workspace(workspace, ws_bytes, soap_qr_workspace(a->count, n))) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* P = static_cast<float*>(workspace);
+  float* ws = P + a->count * round64(n * n);
+  SOAP_TRY(launch_gather(to_mat(a), P, round64(n * n), static_cast<int32_t>(n), static_cast<int32_t>(n), a->count,
+                         s),
+           "qr input");
+  if ((st = qr_enqueue(P, round64(n * n), n, a->count, ws, q, s)) != MUON_OK) return st;
+  return ok();
+}
+
+muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, const muon_batch_t* R, float beta_s,
+                              void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
+  if (!(beta_s >= 0.f && beta_s < 1.f)) return fail(MUON_ERR_INVALID_VALUE, "beta_s %g outside [0, 1)", beta_s);
+  const int64_t c = grad->count, m = grad->rows, n = grad->cols;
+  if (L && (st = check_f32(L, "L", c, m, m)) != MUON_OK) return st;
+  if (R && (st = check_f32(R, "R", c, n, n)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // L <- b L + (1-b) G G^T, R <- b R + (1-b) G^T G, upper tiles mirrored
+  if (L)
+    SOAP_TRY(gemm(op_batch(grad, true), op_batch(grad, true), out_batch(L), m, m, n, c, 1.f - beta_s, beta_s, true, s),
+             "statistics L");
+  if (R)
+    SOAP_TRY(gemm(op_batch(grad, false), op_batch(grad, false), out_batch(R), n, n, m, c, 1.f - beta_s, beta_s, true,
+                  s),
+             "statistics R");
+  return ok();
+}
+
+size_t soap_refresh_workspace(int64_t count, int64_t rows, int64_t cols, int with_l, int with_r) {
+  if (count < 1 || count > 65535 || rows < 1 || cols < 1 || rows > kMaxElems / cols) return 0;
+  if ((with_l && rows > kQrMaxDim) || (with_r && cols > kQrMaxDim)) return 0;
+  size_t side = 0;
+  if (with_l) side = std::max(side, qr_bytes(count, rows));
+  if (with_r) side = std::max(side, qr_bytes(count, cols));
+  return side + static_cast<size_t>(count * round64(rows * cols) * 4);
+}
+
+muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const muon_batch_t* QL,
+                           const muon_batch_t* QR, const muon_batch_t* mbar, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(mbar, "mbar", false)) != MUON_OK) return st;
+  const int64_t c = mbar->count, m = mbar->rows, n = mbar->cols;
+  if (!L != !QL || !R != !QR) return fail(MUON_ERR_INVALID_VALUE, "a statistic and its basis come together");
+  if (L && ((st = check_f32(L, "L", c, m, m)) != MUON_OK || (st = check_f32(QL, "QL", c, m, m)) != MUON_OK))
+    return st;
+  if (R && ((st = check_f32(R, "R", c, n, n)) != MUON_OK || (st = check_f32(QR, "QR", c, n, n)) != MUON_OK))
+    return st;
+  if ((st = check_workspace(workspace, ws_bytes, soap_refresh_workspace(c, m, n, L != nullptr, R != nullptr))) !=
+      MUON_OK)
+    return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* tmp = static_cast<float*>(workspace);
+  const int64_t tmat = round64(m * n);
+  float* P = tmp + c * tmat;
+  if (L) {
+    // P = L QL; tmp = QL_old Mbar; QL = qr(P); Mbar = QL_new^T tmp
+    const int64_t pm = round64(m * m);
+    float* ws = P + c * pm;
+    SOAP_TRY(gemm(op_batch(L, true), op_batch(QL, false), out_ws(P, pm, m), m, m, m, c, 1.f, 0.f, false, s),
+             "refresh power step L");
+    SOAP_TRY(gemm(op_batch(QL, true), op_batch(mbar, false), out_ws(tmp, tmat, n), m, n, m, c, 1.f, 0.f, false, s),
+             "refresh moment L");
+    if ((st = qr_enqueue(P, pm, m, c, ws, QL, s)) != MUON_OK) return st;
+    SOAP_TRY(gemm(op_batch(QL, false), op_ws(tmp, tmat, n, false), out_batch(mbar), m, n, m, c, 1.f, 0.f, false, s),
+             "refresh moment L'");
+  }
+  if (R) {
+    // P = R QR; tmp = Mbar QR_old^T; QR = qr(P); Mbar = tmp QR_new
+    const int64_t pm = round64(n * n);
+    float* ws = P + c * pm;
+    SOAP_TRY(gemm(op_batch(R, true), op_batch(QR, false), out_ws(P, pm, n), n, n, n, c, 1.f, 0.f, false, s),
+             "refresh power step R");
+    SOAP_TRY(gemm(op_batch(mbar, true), op_batch(QR, true), out_ws(tmp, tmat, n), m, n, n, c, 1.f, 0.f, false, s),
+             "refresh moment R");
+    if ((st = qr_enqueue(P, pm, n, c, ws, QR, s)) != MUON_OK) return st;
+    SOAP_TRY(gemm(op_ws(tmp, tmat, n, true), op_batch(QR, false), out_batch(mbar), m, n, n, c, 1.f, 0.f, false, s),
+             "refresh moment R'");
+  }
+  return ok();
+}
+
+size_t soap_precondition_workspace(int64_t count, int64_t rows, int64_t cols) {
+  if (count < 1 || count > 65535 || rows < 1 || cols < 1 || rows > kMaxElems / cols) return 0;
+  return static_cast<size_t>(2 * count * round64(rows * cols) * 4);
+}
+
+muon_status_t soap_precondition(const muon_batch_t* grad, const muon_batch_t* QL, const muon_batch_t* QR,
+                                const muon_batch_t* mbar, const muon_batch_t* vbar, const muon_batch_t* dir,
+                                int64_t step, float beta1, float beta2, float eps, void* workspace,
+                                size_t ws_bytes, void* stream) {
+  muon_status_t st;
+  if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
+  const int64_t c = grad->count, m = grad->rows, n = grad->cols;
+  if (QL && (st = check_f32(QL, "QL", c, m, m)) != MUON_OK) return st;
+  if (QR && (st = check_f32(QR, "QR", c, n, n)) != MUON_OK) return st;
+  if ((st = check_f32(mbar, "mbar", c, m, n)) != MUON_OK) return st;
+  if ((st = check_f32(vbar, "vbar", c, m, n)) != MUON_OK) return st;
+  if ((st = check_f32(dir, "dir", c, m, n)) != MUON_OK) return st;
+  if (step < 1) return fail(MUON_ERR_INVALID_VALUE, "step %lld < 1", (long long)step);
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f))
+    return fail(MUON_ERR_INVALID_VALUE, "betas must lie in [0, 1)");
+  if (!(finite(eps) && eps >= 0.f)) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  if ((st = check_workspace(workspace, ws_bytes, soap_precondition_workspace(c, m, n))) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t wm = round64(m * n);
+  float* w1 = static_cast<float*>(workspace);
+  float* w2 = w1 + c * wm;
+  // Gbar = QL^T G QR (sides without a basis skipped)
+  MatBatch gbar = to_mat(grad);
+  if (QL) {
+    float* dst = QR ? w1 : w2;
+    SOAP_TRY(gemm(op_batch(QL, false), op_batch(grad, false), out_ws(dst, wm, n), m, n, m, c, 1.f, 0.f, false, s),
+             "rotate left");
+    gbar = MatBatch{reinterpret_cast<char*>(dst), wm * 4, nullptr, n, MUON_F32, 0};
+  }
+  if (QR) {
+    const SgemmOperand src = QL ? op_ws(w1, wm, n, true) : op_batch(grad, true);
+    SOAP_TRY(gemm(src, op_batch(QR, false), out_ws(w2, wm, n), m, n, n, c, 1.f, 0.f, false, s), "rotate right");
+    gbar = MatBatch{reinterpret_cast<char*>(w2), wm * 4, nullptr, n, MUON_F32, 0};
+  }
+  // Adam in the rotated basis: Dbar into w2 (in place over Gbar), or into
+  // dir when both bases are the identity
+  RotAdamArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  ra.G = gbar;
+  ra.M = to_mat(mbar);
+  ra.V = to_mat(vbar);
+  ra.out = (QL || QR) ? MatBatch{reinterpret_cast<char*>(w2), wm * 4, nullptr, n, MUON_F32, 0} : to_mat(dir);
+  ra.rows = static_cast<int32_t>(m);
+  ra.cols = static_cast<int32_t>(n);
+  ra.beta1 = beta1;
+  ra.beta2 = beta2;
+  ra.eps = eps;
+  ra.c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
+  ra.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+  SOAP_TRY(launch_rot_adam(ra, c, s), "rotated adam");
+  // D = QL Dbar QR^T
+  if (QL && QR) {
+    SOAP_TRY(gemm(op_batch(QL, true), op_ws(w2, wm, n, false), out_ws(w1, wm, n), m, n, m, c, 1.f, 0.f, false, s),
+             "rotate back left");
+    SOAP_TRY(gemm(op_ws(w1, wm, n, true), op_batch(QR, true), out_batch(dir), m, n, n, c, 1.f, 0.f, false, s),
+             "rotate back right");
+  } else if (QL) {
+    SOAP_TRY(gemm(op_batch(QL, true), op_ws(w2, wm, n, false), out_batch(dir), m, n, m, c, 1.f, 0.f, false, s),
+             "rotate back left");
+  } else if (QR) {
+    SOAP_TRY(gemm(op_ws(w2, wm, n, true), op_batch(QR, true), out_batch(dir), m, n, n, c, 1.f, 0.f, false, s),
+             "rotate back right");
+  }
+  return ok();
+}
+
+}  // extern "C"

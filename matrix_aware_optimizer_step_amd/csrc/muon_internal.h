@@ -255,4 +255,93 @@ struct AdamWArgs {
 };
 hipError_t launch_adamw(const AdamWArgs& a, int64_t total_chunks, hipStream_t stream);
 
+// ------------------------------------------------------------ SOAP
+
+// One operand of the fp32 product C = alpha*op(A)*op(B) + beta*C, as the
+// kernel reads it: batch entry b starts at (ptrs ? ptrs[b] : base + b*stride)
+// + off.  kcontig: the reduction index is the contiguous one in memory (A
+// stored M x K, or B stored N x K); otherwise the outer index is (A stored
+// K x M, B stored K x N).  vec: every 4-element run along the contiguous
+// index that starts on a multiple of 4 is aligned for one vector load.
+struct SgemmOperand {
+  const char* base;
+  int64_t stride;          // bytes between batch entries
+  const void* const* ptrs;
+  int64_t off;             // bytes
+  int64_t ld;              // elements
+  int32_t dtype;           // 0 = f32, 1 = bf16
+  int32_t kcontig;
+  int32_t vec;
+  int32_t pad_;
+};
+
+// C is fp32.  With splits > 1, split s of batch entry b sums the reduction
+// range [s*ksplit, min(K, (s+1)*ksplit)) into C_b + s*c_split (beta = 0).
+// sym: op(A)*op(B) is symmetric (M == N); only tiles ti <= tj are computed
+// and each value is stored at (i, j) and (j, i), so C stays exactly
+// symmetric (and beta*C reads only the upper triangle).
+struct SgemmArgs {
+  SgemmOperand a, b;
+  char* c;
+  int64_t c_stride;
+  void* const* c_ptrs;
+  int64_t c_off;
+  int64_t ldc;
+  int64_t c_split;
+  int32_t M, N, K, ksplit;
+  int32_t splits, count;
+  float alpha, beta;
+  int32_t sym;
+  int32_t pad_;
+};
+constexpr int kSgemmTile = 128;
+constexpr int kSgemmBK = 16;
+hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream);
+
+// Householder QR, one 32-column panel of `count` n x n matrices (row-major,
+// ld n): columns c0 .. c0+nb-1 (nb = min(32, n - c0)) are reduced to upper
+// triangular form in A (reflector entries below the diagonal), the
+// reflectors are written explicitly to V (unit diagonal, zeros above it;
+// rows c0 .. n-1 of those columns), and the sign of each R diagonal entry
+// (+1 for zero) to sgn.  The block factor T of H_c0 ... H_(c0+nb-1) =
+// I - V T V^T (nb x nb, upper triangular) is written repeated side by side
+// for the split-K products: TrepT (nb x nb*reps_t, row-major) holds
+// [T^T ... T^T], TrepQ (nb x nb*reps_q) holds [T ... T].
+constexpr int kQrPanel = 32;
+struct QrPanelArgs {
+  float* A; int64_t a_mat;       // floats per matrix
+  float* V; int64_t v_mat;
+  float* TrepT; int64_t tT_mat;
+  float* TrepQ; int64_t tQ_mat;
+  float* sgn; int64_t s_mat;
+  int32_t n, c0, reps_t, reps_q;
+  int32_t vec;                   // n % 4 == 0 (16-byte rows of the panel)
+  int32_t pad_;
+};
+hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream);
+
+// dst[b][i][j] = src(b)[i][j] for `count` rows x cols f32 matrices (dst
+// contiguous, d_mat floats per matrix).
+hipError_t launch_gather(const MatBatch& src, float* dst, int64_t d_mat, int32_t rows, int32_t cols,
+                         int64_t count, hipStream_t stream);
+
+// Q[i][j] = (i == j) for `count` n x n matrices (ld n).
+hipError_t launch_eye(float* Q, int64_t q_mat, int32_t n, int64_t count, hipStream_t stream);
+
+// dst[i][j] = src[i][j] * sgn[j] (src ld n, dst a caller batch, f32).
+hipError_t launch_sign_copy(const float* src, int64_t src_mat, const float* sgn, int64_t s_mat,
+                            const MatBatch& dst, int32_t n, int64_t count, hipStream_t stream);
+
+// Adam in the rotated basis, elementwise over `count` rows x cols matrices:
+//   M <- b1 M + (1-b1) g,  V <- b2 V + (1-b2) g^2,
+//   out = (c1 M) / (sqrt(c2 V) + eps),
+// g read from G (f32 or bf16), M, V in place (f32), out f32.
+struct RotAdamArgs {
+  MatBatch G, M, V, out;
+  int32_t rows, cols;
+  float beta1, beta2, eps, c1, c2;
+  int32_t pad_;
+};
+hipError_t launch_rot_adam(const RotAdamArgs& a, int64_t count, hipStream_t stream);
+
 }  // namespace muon

@@ -1,0 +1,441 @@
+// SOAP kernels of libmuon355: Adam run in the eigenbasis of Shampoo's row
+// and column statistics ("LLM Optimizers: From SGD and AdamW to SOAP, Muon,
+// and Scalable Training", sections 11.1-11.2; "初探优化器（一）：从SGD到
+// SOAP-Muon", section 6.2).
+//
+//   sgemm_kernel      C = alpha*op(A)*op(B) + beta*C in fp32 on the fp32 MFMA
+//                     (v_mfma_f32_32x32x2_f32): the statistics G G^T and
+//                     G^T G, the rotations Q_L^T G Q_R and Q_L D Q_R^T, the
+//                     power-iteration product S Q and the QR's block updates.
+//   qr_panel_kernel   one 32-column panel of a Householder QR (the basis
+//                     refresh): reflectors, their block factor T, and the
+//                     signs that make R's diagonal non-negative.
+//   rot_adam_kernel   Adam's moments and direction in the rotated basis.
+//
+// Everything here computes in fp32.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+#include "muon_internal.h"
+
+namespace muon {
+namespace {
+
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kT = kSgemmTile;      // 128 x 128 output tile
+constexpr int kBK = kSgemmBK;       // 16-deep k-slices
+constexpr int kPitch = kT + 4;      // LDS row pitch in floats
+constexpr int kThreads = 256;       // 4 waves, 2 x 2, each 64 x 64
+
+__device__ __forceinline__ float bf16f(uint32_t h) { return __uint_as_float(h << 16); }
+
+__device__ __forceinline__ float load1(const char* p, int32_t dtype, int64_t idx) {
+  return dtype ? bf16f(reinterpret_cast<const uint16_t*>(p)[idx]) : reinterpret_cast<const float*>(p)[idx];
+}
+
+// Four consecutive elements of memory row `row` (of `rows`), columns
+// col .. col+3 (of `cols`), zero outside.
+__device__ __forceinline__ void load_run(const char* p, const SgemmOperand& o, int row, int col, int rows,
+                                         int cols, float* v) {
+  if (row >= rows) {
+    v[0] = v[1] = v[2] = v[3] = 0.f;
+    return;
+  }
+  const int64_t idx = static_cast<int64_t>(row) * o.ld + col;
+  if (o.vec && col + 3 < cols) {
+    if (o.dtype) {
+      const uint2 u = *reinterpret_cast<const uint2*>(p + idx * 2);
+      v[0] = bf16f(u.x & 0xffffu);
+      v[1] = bf16f(u.x >> 16);
+      v[2] = bf16f(u.y & 0xffffu);
+      v[3] = bf16f(u.y >> 16);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(p + idx * 4);
+      v[0] = f.x;
+      v[1] = f.y;
+      v[2] = f.z;
+      v[3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (col + e < cols) ? load1(p, o.dtype, idx + e) : 0.f;
+  }
+}
+
+// One 128 (outer) x 16 (reduction) slice of an operand into registers,
+// eight values per thread: outer rows o0.. (of `outer`), reduction k0..
+// (below klim).
+__device__ __forceinline__ void load_slice(const char* p, const SgemmOperand& o, int outer, int klim, int o0,
+                                           int k0, float* r) {
+  const int t = threadIdx.x;
+  if (o.kcontig) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) load_run(p, o, o0 + t / 4 + 64 * g, k0 + 4 * (t % 4), outer, klim, r + 4 * g);
+  } else {
+#pragma unroll
+    for (int g = 0; g < 2; ++g) load_run(p, o, k0 + t / 32 + 8 * g, o0 + 4 * (t % 32), klim, outer, r + 4 * g);
+  }
+}
+
+// The slice into LDS as S[k][outer] (pitch kPitch).  The scattered form
+// (kcontig) writes 64 distinct banks per wave: address mod 64 is
+// 16*(t%4) + 4e + t/4 for lanes t of one wave.
+__device__ __forceinline__ void store_slice(float* S, const SgemmOperand& o, const float* r) {
+  const int t = threadIdx.x;
+  if (o.kcontig) {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kPitch + t / 4 + 64 * g] = r[4 * g + e];
+  } else {
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+      *reinterpret_cast<float4*>(S + (t / 32 + 8 * g) * kPitch + 4 * (t % 32)) =
+          make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
+  }
+}
+
+__device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
+  const char* p = o.ptrs ? static_cast<const char*>(o.ptrs[b]) : o.base + static_cast<int64_t>(b) * o.stride;
+  return p + o.off;
+}
+
+__global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
+  const int tj = blockIdx.x, ti = blockIdx.y;
+  if (a.sym && ti > tj) return;
+  const int bi = blockIdx.z / a.splits, sp = blockIdx.z % a.splits;
+  const int kbeg = sp * a.ksplit;
+  const int kend = min(a.K, kbeg + a.ksplit);
+  const char* pa = entry(a.a, bi);
+  const char* pb = entry(a.b, bi);
+  char* pc = (a.c_ptrs ? static_cast<char*>(a.c_ptrs[bi]) : a.c + static_cast<int64_t>(bi) * a.c_stride) + a.c_off +
+             static_cast<int64_t>(sp) * a.c_split;
+
+  __shared__ float As[kBK * kPitch];
+  __shared__ float Bs[kBK * kPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int i0 = ti * kT, j0 = tj * kT;
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int y = 0; y < 2; ++y)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
+
+  float ra[8], rb[8];
+  if (kbeg < kend) {
+    load_slice(pa, a.a, a.M, kend, i0, kbeg, ra);
+    load_slice(pb, a.b, a.N, kend, j0, kbeg, rb);
+  }
+  for (int k0 = kbeg; k0 < kend; k0 += kBK) {
+    store_slice(As, a.a, ra);
+    store_slice(Bs, a.b, rb);
+    __syncthreads();
+    if (k0 + kBK < kend) {  // next slice in flight during the products
+      load_slice(pa, a.a, a.M, kend, i0, k0 + kBK, ra);
+      load_slice(pb, a.b, a.N, kend, j0, k0 + kBK, rb);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kBK / 2; ++kk) {
+      // lane: A[i = l32][k = half] and B[k = half][j = l32] of each 32 x 2 step
+      const float* ar = As + (2 * kk + half) * kPitch + wm * 64 + l32;
+      const float* br = Bs + (2 * kk + half) * kPitch + wn * 64 + l32;
+      const float a0 = ar[0], a1 = ar[32], b0 = br[0], b1 = br[32];
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // accumulator r of lane: row 8*(r/4) + 4*half + r%4, column l32 of its block
+  float* C = reinterpret_cast<float*>(pc);
+  const bool diag = a.sym && ti == tj;
+#pragma unroll
+  for (int fi = 0; fi < 2; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < 2; ++fj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + wm * 64 + fi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int j = j0 + wn * 64 + fj * 32 + l32;
+        if (i >= a.M || j >= a.N || (diag && i > j)) continue;
+        float* cij = C + static_cast<int64_t>(i) * a.ldc + j;
+        float v = a.alpha * acc[fi][fj][r];
+        if (a.beta != 0.f) v += a.beta * *cij;
+        *cij = v;
+        if (a.sym && i != j) C[static_cast<int64_t>(j) * a.ldc + i] = v;
+      }
+}
+
+// --------------------------------------------------------------- QR panel
+
+constexpr int kQrThreads = 512;
+constexpr int kQrWaves = kQrThreads / 64;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Workgroup sums of 32 per-thread values, left in tot[0..31].  Inside each
+// wave a reduce-scatter halves the values at every exchange (xor 32, 16, 8,
+// 4, 2), so lane l ends with value l >> 1, completed by the xor-1 exchange.
+__device__ __forceinline__ void block_sum32(float* w, float* part, float* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int h = 16; h >= 1; h >>= 1) {
+    const bool up = (lane & (2 * h)) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = up ? w[i] : w[i + h];
+      const float keep = up ? w[i + h] : w[i];
+      w[i] = keep + __shfl_xor(send, 2 * h);
+    }
+  }
+  w[0] += __shfl_xor(w[0], 1);
+  if ((lane & 1) == 0) part[wave * 32 + (lane >> 1)] = w[0];
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    float s = 0.f;
+    for (int q = 0; q < kQrWaves; ++q) s += part[q * 32 + threadIdx.x];
+    tot[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+// Columns c0 .. c0+nb-1 of A (rows c0 .. n-1), one column at a time
+// (LAPACK's dlarfg / dlarft conventions):
+//   x = A[c:, c], alpha = x_0, s = |x_1:|^2; s = 0: no reflection (tau 0,
+//   beta = alpha); else beta = -sign(alpha) |x|, tau = (beta - alpha)/beta,
+//   v = x / (alpha - beta) with v_0 = 1, so (I - tau v v^T) x = beta e_0;
+//   every later panel column y <- y - tau v (v^T y);
+//   T[0:j, j] = -tau_j T[0:j, 0:j] (V[:, 0:j]^T v_j), T[j][j] = tau_j.
+// Row r of a column step belongs to thread (r - c) mod 512 in every phase
+// that writes it; the barrier ending each column orders the next column's
+// reads, which start one row lower.
+template <bool VEC>
+__global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
+  const int64_t b = blockIdx.x;
+  float* A = a.A + b * a.a_mat;
+  float* V = a.V + b * a.v_mat;
+  float* TrT = a.TrepT + b * a.tT_mat;
+  float* TrQ = a.TrepQ + b * a.tQ_mat;
+  float* sg = a.sgn + b * a.s_mat;
+  const int n = a.n, c0 = a.c0;
+  const int nb = min(kQrPanel, n - c0);
+  const int tid = threadIdx.x;
+
+  __shared__ float part[kQrWaves * 32];
+  __shared__ float tot[32];
+  __shared__ float Ts[kQrPanel][kQrPanel + 1];
+  __shared__ float par[3];
+
+  for (int j = 0; j < nb; ++j) {
+    const int c = c0 + j;
+    float s = 0.f;
+    for (int r = c + 1 + tid; r < n; r += kQrThreads) {
+      const float x = A[static_cast<int64_t>(r) * n + c];
+      s += x * x;
+    }
+    s = wave_sum(s);
+    if ((tid & 63) == 0) part[tid >> 6] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+      for (int q = 0; q < kQrWaves; ++q) t += part[q];
+      const float alpha = A[static_cast<int64_t>(c) * n + c];
+      float beta = alpha, tau = 0.f, scale = 0.f;
+      if (t > 0.f) {
+        const float nrm = sqrtf(alpha * alpha + t);
+        beta = alpha >= 0.f ? -nrm : nrm;
+        tau = (beta - alpha) / beta;
+        scale = 1.f / (alpha - beta);
+      }
+      par[0] = beta;
+      par[1] = tau;
+      par[2] = scale;
+      sg[c] = beta < 0.f ? -1.f : 1.f;
+      Ts[j][j] = tau;
+      A[static_cast<int64_t>(c) * n + c] = beta;  // row c belongs to thread 0 below
+    }
+    __syncthreads();
+    const float tau = par[1], scale = par[2];
+
+    // v below the diagonal, in place; dot products of v with the panel's
+    // columns: the earlier reflectors (q < j) and the columns still to be
+    // reduced (q > j)
+    float w[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) w[q] = 0.f;
+    for (int r = c + tid; r < n; r += kQrThreads) {
+      float* row = A + static_cast<int64_t>(r) * n + c0;
+      float vr = 1.f;
+      if (r > c) {
+        vr = row[j] * scale;
+        row[j] = vr;
+      }
+      float x[32];
+      if (VEC && nb == 32) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float4 f = reinterpret_cast<const float4*>(row)[q];
+          x[4 * q] = f.x;
+          x[4 * q + 1] = f.y;
+          x[4 * q + 2] = f.z;
+          x[4 * q + 3] = f.w;
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 32; ++q) x[q] = q < nb ? row[q] : 0.f;
+      }
+#pragma unroll
+      for (int q = 0; q < 32; ++q) w[q] += q == j ? 0.f : vr * x[q];
+    }
+    block_sum32(w, part, tot);
+
+    if (tid < j) {
+      float t = 0.f;
+      for (int k = tid; k < j; ++k) t += Ts[tid][k] * tot[k];
+      Ts[tid][j] = -tau * t;
+    }
+    if (j + 1 < nb) {
+      for (int r = c + tid; r < n; r += kQrThreads) {
+        float* row = A + static_cast<int64_t>(r) * n + c0;
+        const float vr = r > c ? row[j] : 1.f;
+        for (int q = j + 1; q < nb; ++q) row[q] -= tau * tot[q] * vr;
+      }
+    }
+    __syncthreads();
+  }
+
+  // explicit reflectors (rows c0 .. n-1 of the panel's columns)
+  for (int r = c0 + tid; r < n; r += kQrThreads) {
+    const float* row = A + static_cast<int64_t>(r) * n + c0;
+    float* vrow = V + static_cast<int64_t>(r) * n + c0;
+    for (int q = 0; q < nb; ++q) vrow[q] = r > c0 + q ? row[q] : (r == c0 + q ? 1.f : 0.f);
+  }
+  // T below its diagonal is zero; repeated copies for the split products
+  for (int e = tid; e < nb * nb; e += kQrThreads) {
+    const int i = e / nb, k = e % nb;
+    const float t = k >= i ? Ts[i][k] : 0.f;     // T[i][k]
+    const float tt = i >= k ? Ts[k][i] : 0.f;    // T^T[i][k]
+    for (int s = 0; s < a.reps_t; ++s) TrT[static_cast<int64_t>(i) * nb * a.reps_t + s * nb + k] = tt;
+    for (int s = 0; s < a.reps_q; ++s) TrQ[static_cast<int64_t>(i) * nb * a.reps_q + s * nb + k] = t;
+  }
+}
+
+// ----------------------------------------------------------- elementwise
+
+__global__ void eye_kernel(float* Q, int64_t q_mat, int32_t n) {
+  const int64_t b = blockIdx.y;
+  const int64_t nn = static_cast<int64_t>(n) * n;
+  for (int64_t e = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; e < nn;
+       e += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    Q[b * q_mat + e] = (e / n == e % n) ? 1.f : 0.f;
+}
+
+__device__ __forceinline__ char* mat_entry(const MatBatch& m, int64_t b) {
+  return m.ptrs ? static_cast<char*>(m.ptrs[b]) : m.base + b * m.stride_bytes;
+}
+
+constexpr int kRowChunk = 1024;  // columns per workgroup in the row-wise kernels
+
+__global__ __launch_bounds__(256) void sign_copy_kernel(const float* src, int64_t src_mat, const float* sgn,
+                                                        int64_t s_mat, MatBatch dst, int32_t n) {
+  const int64_t b = blockIdx.y;
+  const int chunks = (n + kRowChunk - 1) / kRowChunk;
+  const int r = blockIdx.x / chunks, cc = blockIdx.x % chunks;
+  const float* srow = src + b * src_mat + static_cast<int64_t>(r) * n;
+  const float* sg = sgn + b * s_mat;
+  float* drow = reinterpret_cast<float*>(mat_entry(dst, b)) + static_cast<int64_t>(r) * dst.ld;
+  for (int j = cc * kRowChunk + threadIdx.x; j < min(n, (cc + 1) * kRowChunk); j += blockDim.x)
+    drow[j] = srow[j] * sg[j];
+}
+
+__global__ __launch_bounds__(256) void gather_kernel(MatBatch src, float* dst, int64_t d_mat, int32_t rows,
+                                                     int32_t cols) {
+  const int64_t b = blockIdx.y;
+  const int chunks = (cols + kRowChunk - 1) / kRowChunk;
+  const int r = blockIdx.x / chunks, cc = blockIdx.x % chunks;
+  const float* srow = reinterpret_cast<const float*>(mat_entry(src, b)) + static_cast<int64_t>(r) * src.ld;
+  float* drow = dst + b * d_mat + static_cast<int64_t>(r) * cols;
+  for (int j = cc * kRowChunk + threadIdx.x; j < min(cols, (cc + 1) * kRowChunk); j += blockDim.x)
+    drow[j] = srow[j];
+}
+
+// [GUIDE] 11.1 in the rotated basis; epsilon after the square root.
+__global__ __launch_bounds__(256) void rot_adam_kernel(RotAdamArgs a) {
+  const int64_t b = blockIdx.y;
+  const int chunks = (a.cols + kRowChunk - 1) / kRowChunk;
+  const int r = blockIdx.x / chunks, cc = blockIdx.x % chunks;
+  const char* grow = mat_entry(a.G, b) + static_cast<int64_t>(r) * a.G.ld * (a.G.dtype ? 2 : 4);
+  float* mrow = reinterpret_cast<float*>(mat_entry(a.M, b)) + static_cast<int64_t>(r) * a.M.ld;
+  float* vrow = reinterpret_cast<float*>(mat_entry(a.V, b)) + static_cast<int64_t>(r) * a.V.ld;
+  float* orow = reinterpret_cast<float*>(mat_entry(a.out, b)) + static_cast<int64_t>(r) * a.out.ld;
+  for (int j = cc * kRowChunk + threadIdx.x; j < min(a.cols, (cc + 1) * kRowChunk); j += blockDim.x) {
+    const float g = load1(grow, a.G.dtype, j);
+    const float m = a.beta1 * mrow[j] + (1.f - a.beta1) * g;
+    const float v = a.beta2 * vrow[j] + (1.f - a.beta2) * g * g;
+    mrow[j] = m;
+    vrow[j] = v;
+    orow[j] = (a.c1 * m) / (sqrtf(a.c2 * v) + a.eps);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream) {
+  const dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT, a.count * a.splits);
+  hipLaunchKernelGGL(sgemm_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream) {
+  if (a.vec)
+    hipLaunchKernelGGL(qr_panel_kernel<true>, dim3(count), dim3(kQrThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(qr_panel_kernel<false>, dim3(count), dim3(kQrThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_eye(float* Q, int64_t q_mat, int32_t n, int64_t count, hipStream_t stream) {
+  const int64_t nn = static_cast<int64_t>(n) * n;
+  const int blocks = static_cast<int>(std::min<int64_t>((nn + 255) / 256, 4096));
+  hipLaunchKernelGGL(eye_kernel, dim3(blocks, count), dim3(256), 0, stream, Q, q_mat, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_sign_copy(const float* src, int64_t src_mat, const float* sgn, int64_t s_mat,
+                            const MatBatch& dst, int32_t n, int64_t count, hipStream_t stream) {
+  const int chunks = (n + kRowChunk - 1) / kRowChunk;
+  hipLaunchKernelGGL(sign_copy_kernel, dim3(n * chunks, count), dim3(256), 0, stream, src, src_mat, sgn, s_mat,
+                     dst, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const MatBatch& src, float* dst, int64_t d_mat, int32_t rows, int32_t cols,
+                         int64_t count, hipStream_t stream) {
+  const int chunks = (cols + kRowChunk - 1) / kRowChunk;
+  hipLaunchKernelGGL(gather_kernel, dim3(rows * chunks, count), dim3(256), 0, stream, src, dst, d_mat, rows,
+                     cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_rot_adam(const RotAdamArgs& a, int64_t count, hipStream_t stream) {
+  const int chunks = (a.cols + kRowChunk - 1) / kRowChunk;
+  hipLaunchKernelGGL(rot_adam_kernel, dim3(a.rows * chunks, count), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace muon

@@ -106,11 +106,53 @@ void momentum_and_apply_cases() {
   expect(muon_adamw(&t, 0, 1e-3f, 0.9f, 0.999f, 1e-8f, 0.1f, nullptr), MUON_ERR_INVALID_VALUE, "adamw step 0");
 }
 
+
+void soap_cases() {
+  struct Case { int64_t count, m, n; bool l, r; };
+  const Case cases[] = {{2, 4096, 4096, true, true},   {2, 1024, 4096, true, true}, {2, 14336, 4096, false, true},
+                        {1, 4096, 14336, true, false}, {3, 130, 70, true, true},    {1, 1, 33, true, true},
+                        {4, 33, 200, true, true},      {2, 40, 50, false, false}};
+  for (const Case& c : cases) {
+    muon_batch_t g = batch(c.count, c.m, c.n, MUON_BF16);
+    muon_batch_t Ls = batch(c.count, c.m, c.m, MUON_F32), QL = batch(c.count, c.m, c.m, MUON_F32);
+    muon_batch_t Rs = batch(c.count, c.n, c.n, MUON_F32), QR = batch(c.count, c.n, c.n, MUON_F32);
+    muon_batch_t mb = batch(c.count, c.m, c.n, MUON_F32), vb = batch(c.count, c.m, c.n, MUON_F32);
+    muon_batch_t d = batch(c.count, c.m, c.n, MUON_F32);
+    const muon_batch_t* pL = c.l ? &Ls : nullptr;
+    const muon_batch_t* pR = c.r ? &Rs : nullptr;
+    const muon_batch_t* pQL = c.l ? &QL : nullptr;
+    const muon_batch_t* pQR = c.r ? &QR : nullptr;
+    expect(soap_statistics(&g, pL, pR, 0.9f, nullptr), MUON_OK, "soap_statistics");
+    size_t need = soap_refresh_workspace(c.count, c.m, c.n, c.l, c.r);
+    stub_set_workspace(kWs, need);
+    if (c.l || c.r) {
+      expect(soap_refresh(pL, pR, pQL, pQR, &mb, kWs, need, nullptr), MUON_OK, "soap_refresh");
+      expect(soap_refresh(pL, pR, pQL, pQR, &mb, kWs, need - 1, nullptr), MUON_ERR_WORKSPACE,
+             "soap_refresh, short workspace");
+    }
+    need = soap_precondition_workspace(c.count, c.m, c.n);
+    stub_set_workspace(kWs, need);
+    expect(soap_precondition(&g, pQL, pQR, &mb, &vb, &d, 3, 0.9f, 0.999f, 1e-8f, kWs, need, nullptr), MUON_OK,
+           "soap_precondition");
+    expect(soap_precondition(&g, pQL, pQR, &mb, &vb, &d, 0, 0.9f, 0.999f, 1e-8f, kWs, need, nullptr),
+           MUON_ERR_INVALID_VALUE, "soap_precondition, step 0");
+  }
+  for (int64_t n : {1, 5, 32, 33, 100, 257, 300, 1024, 4096}) {
+    for (int64_t count : {1, 3}) {
+      const size_t need = soap_qr_workspace(count, n);
+      stub_set_workspace(kWs, need);
+      muon_batch_t a = batch(count, n, n, MUON_F32), q = batch(count, n, n, MUON_F32);
+      expect(soap_qr(&a, &q, kWs, need, nullptr), MUON_OK, "soap_qr");
+    }
+  }
+}
+
 }  // namespace
 
 int main() {
   orthogonalize_cases();
   momentum_and_apply_cases();
+  soap_cases();
   if (g_fail) return 1;
   std::printf("ok: %ld launches checked\n", stub_launches());
   return 0;

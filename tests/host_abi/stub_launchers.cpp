@@ -8,6 +8,8 @@
 #include <cstdio>
 #include <cstdlib>
 
+#include <algorithm>
+
 #include "muon_internal.h"
 
 namespace {
@@ -178,6 +180,114 @@ hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const Gem
     }
   }
   if (begin != L.total_tiles) die("%lld tiles in groups, launch says %d", (long long)begin, L.total_tiles);
+  return hipSuccess;
+}
+
+}  // namespace muon
+
+// ------------------------------------------------------------------ SOAP
+
+namespace {
+
+using muon::MatBatch;
+using muon::SgemmOperand;
+
+bool in_workspace(const void* p) {
+  const char* c = static_cast<const char*>(p);
+  return c >= g_lo && c < g_hi;
+}
+
+// A product operand that lives in the workspace: every batch entry's rows x
+// cols (memory orientation) inside it.  Caller memory is not checked.
+void check_operand(const SgemmOperand& o, int64_t outer, int64_t K, int64_t count, const char* what) {
+  if (o.ptrs || !in_workspace(o.base)) return;
+  const int64_t es = o.dtype ? 2 : 4;
+  const int64_t rows = o.kcontig ? outer : K, cols = o.kcontig ? K : outer;
+  if (o.ld < cols) die("%s: ld %lld < %lld columns", what, (long long)o.ld, (long long)cols);
+  if (o.vec && (o.ld % 4 || (reinterpret_cast<uintptr_t>(o.base) + o.off) % (4 * es) || o.stride % (4 * es)))
+    die("%s: vector loads on a misaligned operand", what);
+  in_ws(o.base + o.off, count, o.stride, ((rows - 1) * o.ld + cols) * es, what);
+}
+
+void check_batch_ws(const MatBatch& m, int64_t rows, int64_t cols, int64_t count, const char* what) {
+  if (m.ptrs || !in_workspace(m.base)) return;
+  if (m.ld < cols) die("%s: ld %lld < %lld", what, (long long)m.ld, (long long)cols);
+  in_ws(m.base, count, m.stride_bytes, ((rows - 1) * m.ld + cols) * (m.dtype ? 2 : 4), what);
+}
+
+}  // namespace
+
+namespace muon {
+
+hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t) {
+  ++g_launches;
+  if (a.M < 1 || a.N < 1 || a.K < 1 || a.count < 1 || a.splits < 1) die("sgemm %d x %d x %d", a.M, a.N, a.K);
+  if (int64_t{a.count} * a.splits > 65535) die("sgemm: %d x %d batch entries", a.count, a.splits);
+  if (a.splits > 1) {
+    if (a.ksplit % kSgemmBK || int64_t{a.splits - 1} * a.ksplit >= a.K || int64_t{a.splits} * a.ksplit < a.K)
+      die("sgemm: %d splits of %d do not tile K = %d", a.splits, a.ksplit, a.K);
+    if (a.beta != 0.f) die("sgemm: split partials with beta != 0");
+    if (a.sym) die("sgemm: symmetric split");
+  } else if (a.ksplit < a.K) {
+    die("sgemm: ksplit %d < K %d", a.ksplit, a.K);
+  }
+  if (a.sym && a.M != a.N) die("sgemm: symmetric %d x %d", a.M, a.N);
+  check_operand(a.a, a.M, a.K, a.count, "sgemm A");
+  check_operand(a.b, a.N, a.K, a.count, "sgemm B");
+  if (!a.c_ptrs && in_workspace(a.c)) {
+    if (a.ldc < a.N) die("sgemm C: ldc %lld < %d", (long long)a.ldc, a.N);
+    const int64_t extent = ((int64_t{a.M} - 1) * a.ldc + a.N) * 4;
+    if (a.splits > 1 && a.c_split < extent) die("sgemm C: split partials overlap");
+    in_ws(a.c + a.c_off, a.count, a.c_stride, (int64_t{a.splits} - 1) * a.c_split + extent, "sgemm C");
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t) {
+  ++g_launches;
+  if (a.n < 1 || a.c0 < 0 || a.c0 >= a.n || a.c0 % kQrPanel) die("qr panel: n %d, c0 %d", a.n, a.c0);
+  if (a.reps_t < 1 || a.reps_t > 16 || a.reps_q < 1 || a.reps_q > 16) die("qr panel reps %d %d", a.reps_t, a.reps_q);
+  if (a.vec != (a.n % 4 == 0)) die("qr panel vec flag");
+  const int64_t n = a.n, nb = std::min<int64_t>(kQrPanel, n - a.c0);
+  in_ws(a.A, count, a.a_mat * 4, n * n * 4, "qr A");
+  in_ws(a.V, count, a.v_mat * 4, n * n * 4, "qr V");
+  in_ws(a.TrepT, count, a.tT_mat * 4, nb * nb * a.reps_t * 4, "qr T^T copies");
+  in_ws(a.TrepQ, count, a.tQ_mat * 4, nb * nb * a.reps_q * 4, "qr T copies");
+  in_ws(a.sgn, count, a.s_mat * 4, n * 4, "qr signs");
+  return hipSuccess;
+}
+
+hipError_t launch_eye(float* Q, int64_t q_mat, int32_t n, int64_t count, hipStream_t) {
+  ++g_launches;
+  in_ws(Q, count, q_mat * 4, int64_t{n} * n * 4, "identity");
+  return hipSuccess;
+}
+
+hipError_t launch_sign_copy(const float* src, int64_t src_mat, const float* sgn, int64_t s_mat, const MatBatch& dst,
+                            int32_t n, int64_t count, hipStream_t) {
+  ++g_launches;
+  in_ws(src, count, src_mat * 4, int64_t{n} * n * 4, "sign copy source");
+  in_ws(sgn, count, s_mat * 4, int64_t{n} * 4, "sign copy signs");
+  if (dst.dtype != 0 || dst.ld < n) die("sign copy destination");
+  return hipSuccess;
+}
+
+hipError_t launch_gather(const MatBatch& src, float* dst, int64_t d_mat, int32_t rows, int32_t cols, int64_t count,
+                         hipStream_t) {
+  ++g_launches;
+  if (src.dtype != 0 || src.ld < cols) die("gather source");
+  in_ws(dst, count, d_mat * 4, int64_t{rows} * cols * 4, "gather destination");
+  return hipSuccess;
+}
+
+hipError_t launch_rot_adam(const RotAdamArgs& a, int64_t count, hipStream_t) {
+  ++g_launches;
+  if (a.rows < 1 || a.cols < 1) die("rotated adam %d x %d", a.rows, a.cols);
+  check_batch_ws(a.G, a.rows, a.cols, count, "rotated adam G");
+  check_batch_ws(a.M, a.rows, a.cols, count, "rotated adam M");
+  check_batch_ws(a.V, a.rows, a.cols, count, "rotated adam V");
+  check_batch_ws(a.out, a.rows, a.cols, count, "rotated adam out");
+  if (a.out.dtype != 0 || a.M.dtype != 0 || a.V.dtype != 0) die("rotated adam state dtypes");
   return hipSuccess;
 }
 

@@ -18,7 +18,7 @@ FAKE = 0x10000  # non-NULL, 16-byte aligned; never dereferenced: validation fail
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:muon|soap)_[a-z_]+)\s*\(", text)))
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -226,7 +226,8 @@ int main(void) {
   size_t m = muon_momentum_workspace(2, 768, 2048);
   int64_t counts[2] = {2, 1}, rows[2] = {768, 4096}, cols[2] = {2048, 14336};
   size_t g = muon_momentum_grouped_workspace(2, counts, rows, cols);
-  if (w == 0 || m == 0 || g == 0) return 2;
+  size_t q = soap_qr_workspace(2, 4096), r = soap_refresh_workspace(1, 1024, 4096, 1, 1);
+  if (w == 0 || m == 0 || g == 0 || q == 0 || r == 0) return 2;
   /* an invalid descriptor is rejected before anything reaches the GPU */
   muon_batch_t bad = {NULL, NULL, 0, 1, 64, 64, 64, MUON_F32, 0};
   muon_status_t st = muon_apply(&bad, &bad, 1e-3f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, NULL);
@@ -254,3 +255,79 @@ def test_header_is_c99_and_links(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert out.returncode == 0, (out.returncode, out.stdout, out.stderr)
     assert out.stdout.startswith("MUON_ERR_INVALID_VALUE: ")
+
+
+# ----------------------------------------------------------------- SOAP
+
+def test_soap_workspace_queries():
+    assert L.soap_qr_workspace(0, 64) == 0
+    assert L.soap_qr_workspace(1, 0) == 0
+    assert L.soap_qr_workspace(1, 40000) == 0
+    assert L.soap_qr_workspace(2, 100) >= 2 * 3 * 100 * 100 * 4
+    assert L.soap_qr_workspace(2, 100) == 2 * L.soap_qr_workspace(1, 100)
+    assert L.soap_precondition_workspace(3, 64, 96) == 2 * 3 * 64 * 96 * 4
+    assert L.soap_precondition_workspace(1, 0, 5) == 0
+    # the refresh holds the moment's temporary plus the larger side's QR
+    assert L.soap_refresh_workspace(1, 64, 128, 1, 1) == 64 * 128 * 4 + L.soap_qr_workspace(1, 128)
+    assert L.soap_refresh_workspace(1, 64, 128, 1, 0) == 64 * 128 * 4 + L.soap_qr_workspace(1, 64)
+    assert L.soap_refresh_workspace(1, 64, 40000, 1, 1) == 0
+    assert L.soap_refresh_workspace(1, 64, 40000, 1, 0) > 0
+
+
+def test_soap_statistics_rejects_bad_arguments():
+    g = desc(count=2, rows=64, cols=96)
+    Ls, Rs = desc(count=2, rows=64, cols=64), desc(count=2, rows=96, cols=96)
+    assert status_of(lambda: L.soap_statistics(g, Ls, Rs, 1.0, 0)) == INVALID
+    assert status_of(lambda: L.soap_statistics(g, Ls, Rs, -0.1, 0)) == INVALID
+    assert status_of(lambda: L.soap_statistics(g, Rs, None, 0.9, 0)) == INVALID
+    assert status_of(lambda: L.soap_statistics(g, None, desc(count=1, rows=96, cols=96), 0.9, 0)) == INVALID
+    assert status_of(lambda: L.soap_statistics(g, desc(count=2, rows=64, cols=64, dtype=L.MUON_BF16), None, 0.9,
+                                               0)) == UNSUPPORTED
+    assert status_of(lambda: L.soap_statistics(desc(count=0), None, None, 0.9, 0)) == INVALID
+
+
+def test_soap_qr_rejects_bad_arguments():
+    a = desc(count=2, rows=64, cols=64)
+    assert status_of(lambda: L.soap_qr(desc(count=2, rows=64, cols=32), a, FAKE, 1 << 30, 0)) == INVALID
+    assert status_of(lambda: L.soap_qr(a, desc(count=1, rows=64, cols=64), FAKE, 1 << 30, 0)) == INVALID
+    assert status_of(lambda: L.soap_qr(a, desc(count=2, rows=64, cols=64, dtype=L.MUON_BF16), FAKE, 1 << 30,
+                                       0)) == UNSUPPORTED
+    assert status_of(lambda: L.soap_qr(desc(rows=40000, cols=40000), desc(rows=40000, cols=40000), FAKE, 1 << 40,
+                                       0)) == UNSUPPORTED
+    need = L.soap_qr_workspace(2, 64)
+    assert status_of(lambda: L.soap_qr(a, a, FAKE, need - 1, 0)) == WORKSPACE
+    assert status_of(lambda: L.soap_qr(a, a, None, need, 0)) == WORKSPACE
+    assert status_of(lambda: L.soap_qr(a, a, FAKE + 4, need, 0)) == WORKSPACE
+
+
+def test_soap_refresh_rejects_bad_arguments():
+    m, n = 64, 96
+    mb = desc(count=2, rows=m, cols=n)
+    Ls, QL = desc(count=2, rows=m, cols=m), desc(count=2, rows=m, cols=m)
+    Rs, QR = desc(count=2, rows=n, cols=n), desc(count=2, rows=n, cols=n)
+    need = L.soap_refresh_workspace(2, m, n, 1, 1)
+    assert status_of(lambda: L.soap_refresh(Ls, Rs, None, QR, mb, FAKE, need, 0)) == INVALID
+    assert status_of(lambda: L.soap_refresh(None, Rs, QL, QR, mb, FAKE, need, 0)) == INVALID
+    assert status_of(lambda: L.soap_refresh(Ls, Rs, QL, Rs, desc(count=2, rows=m, cols=m), FAKE, need, 0)) == INVALID
+    assert status_of(lambda: L.soap_refresh(Ls, Rs, QL, QR, mb, FAKE, need - 1, 0)) == WORKSPACE
+    assert status_of(lambda: L.soap_refresh(Ls, Rs, QL, QR, desc(count=2, rows=m, cols=n, dtype=L.MUON_BF16), FAKE,
+                                            need, 0)) == UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(step=0), INVALID), (dict(beta1=1.0), INVALID), (dict(beta2=-0.5), INVALID), (dict(eps=-1.0), INVALID),
+    (dict(eps=float("nan")), INVALID), (dict(eps=float("inf")), INVALID), (dict(ws=-1), WORKSPACE),
+    (dict(dir_dtype=L.MUON_BF16), UNSUPPORTED), (dict(dir_rows=32), INVALID), (dict(ql_rows=96), INVALID),
+])
+def test_soap_precondition_rejects_bad_arguments(kw, code):
+    m, n, c = 64, 96, 2
+    a = dict(step=1, beta1=0.9, beta2=0.999, eps=1e-8, ws=0, dir_dtype=L.MUON_F32, dir_rows=m, ql_rows=m)
+    a.update(kw)
+    g = desc(count=c, rows=m, cols=n, dtype=L.MUON_BF16)
+    ql = desc(count=c, rows=a["ql_rows"], cols=a["ql_rows"])
+    qr = desc(count=c, rows=n, cols=n)
+    st = desc(count=c, rows=m, cols=n)
+    d = desc(count=c, rows=a["dir_rows"], cols=n, dtype=a["dir_dtype"])
+    need = L.soap_precondition_workspace(c, m, n) + a["ws"]
+    assert status_of(lambda: L.soap_precondition(g, ql, qr, st, st, d, a["step"], a["beta1"], a["beta2"], a["eps"],
+                                                 FAKE, need, 0)) == code

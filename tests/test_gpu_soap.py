@@ -1,0 +1,224 @@
+"""GPU parity of the SOAP entry points (soap_statistics, soap_qr,
+soap_refresh, soap_precondition, and a whole step with muon_apply) against
+the fp64 oracle in oracle/soap.py.
+
+The library computes in fp32 (the products on the fp32 matrix cores, the QR
+by Householder reflections), the oracle in fp64.  Tolerances, relative
+Frobenius error per matrix, from the fp32 arithmetic:
+
+* statistics (sums of up to a few hundred products): 1e-6;
+* QR of a well-conditioned matrix (condition number ~10): 1e-5, with
+  Q^T Q = I to 1e-5;
+* the direction D and the updated weight: 1e-3.  A refresh takes the QR of
+  L Q; the forward error of an fp32 Householder QR is of order n u kappa(L)
+  (n <= 200, u = 6e-8, kappa(L) <= ~50 here: up to ~6e-4 per basis), and the
+  direction carries both bases.  The errors measured are printed.
+
+The multi-step runs start from statistics L_0 = I, R_0 = I (a damping prior,
+as Shampoo's eps*I).  From zero statistics one side of a non-square gradient
+is rank deficient at the first refresh, and the QR then completes its basis
+with directions fixed only by round-off; from step 2 on SOAP's result depends
+on that completion (Adam's elementwise steps are not rotation invariant), so
+it is not unique.  With the prior every refresh sees a full-rank statistic.
+
+At step 1 Adam's direction in the rotated basis is g / (|g| + eps): a sign
+for entries far above eps.  An entry of the rotated gradient within fp32
+round-off of zero could take either sign, so the step-by-step comparisons
+use eps = 1e-2 (entries ~1), which bounds the direction's sensitivity; the
+default eps = 1e-8 is checked after three steps, where the direction is a
+ratio of averages over three independent gradients.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import adamw as OA
+from oracle import oracle as O
+from oracle import soap as S
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    import matrix_aware_optimizer_step_amd as m
+    m._lib.load()
+    return m
+
+
+def f64(t):
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def rel(a, b):
+    return O.relative_frobenius_error(a, b)
+
+
+def f32(x):
+    return float(np.float32(x))
+
+
+@pytest.mark.parametrize("n", [1, 5, 32, 33, 100, 257, 300])
+def test_qr_matches_oracle(mx, n):
+    from matrix_aware_optimizer_step_amd import soap
+    print(f"soap_qr n={n}", flush=True)
+    count = 2
+    A = torch.stack([synth.gaussian(n, n, seed=100 + n + b) for b in range(count)]).float()
+    A += 3.0 * float(np.sqrt(n)) * torch.eye(n)
+    Ad = A.cuda()
+    Q = torch.full_like(Ad, float("nan"))
+    soap.qr(Ad, Q)
+    torch.cuda.synchronize()
+    for b in range(count):
+        want, _ = S.qr_nonneg(f64(A[b]))
+        got = f64(Q[b])
+        assert rel(got, want) <= 1e-5, (n, b, rel(got, want))
+        assert np.max(np.abs(got.T @ got - np.eye(n))) <= 1e-5
+    assert torch.equal(Ad.cpu(), A), "soap_qr must not modify its input"
+
+
+def test_qr_rank_deficient_is_orthogonal(mx):
+    # zero columns and a repeated column: Q stays orthogonal and Q R = A
+    from matrix_aware_optimizer_step_amd import soap
+    n = 70
+    A = synth.gaussian(n, n, seed=7).float()
+    A[:, 10] = 0.0
+    A[:, 40] = A[:, 3]
+    A[:, 69] = 0.0
+    Q = torch.empty(n, n, device="cuda")
+    soap.qr(A.cuda(), Q)
+    torch.cuda.synchronize()
+    q = f64(Q)
+    assert np.max(np.abs(q.T @ q - np.eye(n))) <= 1e-5
+    R = q.T @ f64(A)
+    assert np.max(np.abs(np.tril(R, -1))) <= 1e-4 * np.max(np.abs(R))
+    assert np.all(np.diag(R) >= -1e-4 * np.max(np.abs(R)))
+
+
+@pytest.mark.parametrize("m,n,gdtype", [(64, 96, torch.float32), (130, 70, torch.bfloat16), (1, 33, torch.float32)])
+def test_statistics_match_oracle(mx, m, n, gdtype):
+    from matrix_aware_optimizer_step_amd import soap
+    print(f"soap_statistics {m}x{n} {gdtype}", flush=True)
+    count, b = 3, 0.8
+    Ld = torch.zeros(count, m, m, device="cuda")
+    Rd = torch.zeros(count, n, n, device="cuda")
+    Lo = [np.zeros((m, m)) for _ in range(count)]
+    Ro = [np.zeros((n, n)) for _ in range(count)]
+    for t in range(3):
+        G = torch.stack([synth.gaussian(m, n, seed=1000 * t + i) for i in range(count)]).to(gdtype)
+        soap.statistics(G.cuda(), Ld, Rd, b)
+        for i in range(count):
+            Lo[i], Ro[i] = S.statistics(Lo[i], Ro[i], f64(G[i]), f32(b))
+    torch.cuda.synchronize()
+    for i in range(count):
+        assert rel(f64(Ld[i]), Lo[i]) <= 1e-6
+        assert rel(f64(Rd[i]), Ro[i]) <= 1e-6
+        assert torch.equal(Ld[i], Ld[i].T) and torch.equal(Rd[i], Rd[i].T)
+
+
+def run_steps(mx, m, n, steps, *, count=2, max_dim=4096, freq=2, eps=1e-2, wdtype=torch.float32,
+              gdtype=torch.float32, lr=0.5, wd=0.2, check_each=True, tol=1e-3, seed=0, prior=1.0):
+    """Run SoapStep and the oracle side by side from statistics prior*I;
+    compare D and W; return the worst D error and the worst basis error."""
+    from matrix_aware_optimizer_step_amd import soap
+    b1, b2, bs = 0.9, 0.95, 0.8
+    W0 = torch.stack([synth.gaussian(m, n, seed=seed + 50 + i) for i in range(count)]).to(wdtype)
+    W = W0.cuda()
+    G = torch.empty(count, m, n, dtype=gdtype, device="cuda")
+    step = soap.SoapStep([(W, G)], lr=lr, weight_decay=wd, betas=(b1, b2), eps=eps, beta_s=bs, freq=freq,
+                         max_dim=max_dim)
+    states = [S.init_state(m, n, max_dim) for _ in range(count)]
+    grp = step.groups[0]
+    for st in states:
+        if st.L is not None:
+            st.L = prior * np.eye(m)
+        if st.R is not None:
+            st.R = prior * np.eye(n)
+    for k in ("L", "R"):
+        if grp[k] is not None:
+            grp[k].copy_(prior * torch.eye(grp[k].shape[-1], device="cuda"))
+    Wo = [f64(W0[i]) for i in range(count)]
+    worst = worst_q = 0.0
+    for t in range(1, steps + 1):
+        Gh = torch.stack([synth.gaussian(m, n, seed=seed + 7919 * t + i) for i in range(count)]).to(gdtype)
+        G.copy_(Gh)
+        Wprev = [f64(W[i]) for i in range(count)]
+        step.step()
+        torch.cuda.synchronize()
+        for i in range(count):
+            # the oracle steps from the weight the GPU held (bf16 rounding of W does not accumulate)
+            Wi, D = S.soap_step(Wprev[i], f64(Gh[i]), states[i], lr=f32(lr), weight_decay=f32(wd), beta1=f32(b1),
+                                beta2=f32(b2), eps=f32(eps), beta_s=f32(bs), freq=freq)
+            Wo[i] = Wi
+            for k, q in (("QL", states[i].QL), ("QR", states[i].QR)):
+                if grp[k] is not None:
+                    worst_q = max(worst_q, rel(f64(grp[k][i]), q))
+            if check_each or t == steps:
+                e = rel(f64(grp["D"][i]), D)
+                worst = max(worst, e)
+                assert e <= tol, (t, i, e)
+                if wdtype == torch.float32:
+                    assert rel(f64(W[i]), Wi) <= tol
+                else:
+                    ulp = np.abs(Wi) * 2.0 ** -8 + tol * np.max(np.abs(Wi))
+                    assert np.all(np.abs(f64(W[i]) - Wi) <= ulp)
+    print(f"  {m}x{n}: worst D error {worst:.2e}, worst basis error {worst_q:.2e}")
+    return worst, worst_q
+
+
+@pytest.mark.parametrize("m,n", [(64, 96), (96, 64), (130, 70), (33, 200)])
+def test_soap_steps_match_oracle(mx, m, n):
+    print(f"soap steps {m}x{n}", flush=True)
+    run_steps(mx, m, n, steps=4, freq=2)
+
+
+def test_soap_one_sided(mx):
+    # rows over max_dim: identity basis on the left, the column side only
+    print("soap one-sided", flush=True)
+    run_steps(mx, 150, 40, steps=3, max_dim=100, freq=1)
+    run_steps(mx, 40, 150, steps=3, max_dim=100, freq=1)
+
+
+def test_soap_identity_bases_is_adamw(mx):
+    # both axes over max_dim: the layer is AdamW ([GUIDE] 11.2); the oracle
+    # of SOAP then equals the AdamW oracle (pinned on the CPU)
+    print("soap identity", flush=True)
+    run_steps(mx, 40, 50, steps=3, max_dim=0, tol=1e-6)
+
+
+def test_soap_default_eps_after_three_steps(mx):
+    print("soap default eps", flush=True)
+    run_steps(mx, 96, 128, steps=3, freq=2, eps=1e-8, check_each=False, tol=1e-3)
+
+
+def test_soap_bf16_weight_and_gradient(mx):
+    print("soap bf16", flush=True)
+    run_steps(mx, 80, 112, steps=3, wdtype=torch.bfloat16, gdtype=torch.bfloat16)
+
+
+def test_soap_pointer_array_state_matches_strided(mx):
+    # the entry points take pointer-array batches as well: one refresh and
+    # one precondition with every state tensor passed as a list
+    from matrix_aware_optimizer_step_amd import soap
+    m, n, c = 48, 80, 3
+    G = torch.stack([synth.gaussian(m, n, seed=300 + i) for i in range(c)]).cuda()
+    outs = []
+    for as_list in (False, True):
+        Ls = torch.zeros(c, m, m, device="cuda")
+        Rs = torch.zeros(c, n, n, device="cuda")
+        QL = torch.eye(m, device="cuda").expand(c, m, m).contiguous()
+        QR = torch.eye(n, device="cuda").expand(c, n, n).contiguous()
+        Mb = torch.zeros(c, m, n, device="cuda")
+        Vb = torch.zeros(c, m, n, device="cuda")
+        D = torch.empty(c, m, n, device="cuda")
+        lst = (lambda x: list(x.unbind(0))) if as_list else (lambda x: x)
+        soap.statistics(lst(G), lst(Ls), lst(Rs), 0.5)
+        soap.refresh(lst(Mb), lst(Ls), lst(Rs), lst(QL), lst(QR))
+        soap.precondition(lst(G), lst(Mb), lst(Vb), lst(D), 1, lst(QL), lst(QR))
+        torch.cuda.synchronize()
+        outs.append(D.clone())
+    assert torch.equal(outs[0], outs[1])
