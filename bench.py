@@ -169,6 +169,125 @@ def bench_adamw(args):
     print(json.dumps(out), flush=True)
 
 
+PEAK_FP32_MFMA_TFLOPS = 157.3   # MI355X dense fp32 matrix
+SOAP_LR, SOAP_WD, SOAP_MAX_DIM, SOAP_FREQ = 3e-4, 0.1, 8192, 10
+
+
+def soap_flops(m, n, with_l, with_r, refresh=False):
+    """Algorithmic flops of one SOAP update of an m x n matrix: the
+    statistics (upper triangles), the rotations of G into the basis and of
+    the direction back; with ``refresh`` the power-iteration product, the
+    Householder QR (4/3 d^3 to factor, 4/3 d^3 to form Q) and the two
+    products that carry the first moment into the new basis, per side."""
+    f = 0
+    if with_l:
+        f += m * (m + 1) * n + 2 * (2 * m * m * n)
+        if refresh:
+            f += 2 * m ** 3 + (8 * m ** 3) // 3 + 2 * (2 * m * m * n)
+    if with_r:
+        f += n * (n + 1) * m + 2 * (2 * m * n * n)
+        if refresh:
+            f += 2 * n ** 3 + (8 * n ** 3) // 3 + 2 * (2 * m * n * n)
+    return f
+
+
+def bench_soap(args):
+    """Time SOAP steps (statistics, basis refresh every SOAP_FREQ steps,
+    rotated Adam, update) over the layer's matrices; print one JSON line
+    against the fp32 MFMA roofline."""
+    import numpy as np
+    import torch
+
+    import matrix_aware_optimizer_step_amd as mx
+    from matrix_aware_optimizer_step_amd import soap
+    from workloads import synth
+
+    mx._lib.load()
+    if not torch.cuda.is_available():
+        raise RuntimeError("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    cfg = synth.WORKLOADS[args.workload]
+    grads = synth.group_gradients(cfg, step=1, device=dev)
+    weights = synth.initial_weights(cfg, device=dev)
+    step = soap.SoapStep(list(zip(weights, grads)), lr=SOAP_LR, weight_decay=SOAP_WD, freq=SOAP_FREQ,
+                         max_dim=SOAP_MAX_DIM)
+    torch.cuda.synchronize()
+    log(f"[bench] SOAP over {cfg.slug}: {cfg.matrices} matrices, workspace {step.ws.numel() / 2**30:.2f} GiB")
+    if args.copy_calibration:
+        calibration_copy(dev)
+    for _ in range(args.warmup):
+        step.step()
+    torch.cuda.synchronize()
+    log(f"[bench] {args.warmup} warmup steps done")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    refreshes = 0
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        refreshes += (step.t % step.freq) == 0      # the coming step refreshes
+        step.step(events=events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"[bench] {args.steps} timed steps done in {wall:.3f} s ({refreshes} refreshes)")
+    ph = [sum(e[i].elapsed_time(e[i + 1]) for e in events) / args.steps for i in range(4)]
+    sides = [(g.count, g.rows, g.cols, g.rows <= SOAP_MAX_DIM, g.cols <= SOAP_MAX_DIM) for g in cfg.groups]
+    base = sum(c * soap_flops(m, n, wl, wr) for c, m, n, wl, wr in sides)
+    extra = sum(c * (soap_flops(m, n, wl, wr, True) - soap_flops(m, n, wl, wr)) for c, m, n, wl, wr in sides)
+    flops = base + extra * refreshes / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+    # the products outside the refresh: statistics and the rotations (the
+    # precondition phase also runs the elementwise rotated-Adam kernel)
+    gemm_ms = ph[0] + ph[2]
+    gemm_tflops = base / (gemm_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import soap as OS
+        g0 = next(g for g in cfg.groups if g.name == "wk_wv")
+        G = grads[[g.name for g in cfg.groups].index("wk_wv")][0].double().cpu().numpy()
+        W = np.zeros((g0.rows, g0.cols))
+        st = OS.init_state(g0.rows, g0.cols, SOAP_MAX_DIM)
+        t1 = time.perf_counter()
+        OS.soap_step(W, G, st, lr=SOAP_LR, weight_decay=SOAP_WD, freq=SOAP_FREQ)
+        t_ref = time.perf_counter() - t1
+        t1 = time.perf_counter()
+        OS.soap_step(W, G, st, lr=SOAP_LR, weight_decay=SOAP_WD, freq=SOAP_FREQ)
+        t_plain = time.perf_counter() - t1
+        fs_plain = soap_flops(g0.rows, g0.cols, True, True)
+        fs_ref = soap_flops(g0.rows, g0.cols, True, True, True)
+        rate_plain, rate_ref = fs_plain / t_plain, (fs_ref - fs_plain) / max(t_ref - t_plain, 1e-9)
+        sec = base / rate_plain + extra / SOAP_FREQ / rate_ref
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        except Exception:
+            threads = os.cpu_count() or 1
+        cpu = {"value": 1.0 / sec, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+               "sample": f"fp64 NumPy SOAP oracle: one {g0.rows}x{g0.cols} matrix, a step with refresh "
+                         f"({t_ref:.1f} s) and one without ({t_plain:.1f} s); scaled by flops to the workload "
+                         f"with one refresh per {SOAP_FREQ} steps",
+               "seconds_per_step": sec}
+    out = {"metric": "SOAP steps/sec + fp32 MFMA TFLOP/s of its products per layer set",
+           "value": 1e3 / ms_per_step, "unit": "steps/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"{cfg.slug} (SOAP): {cfg.name}", "matrices": cfg.matrices,
+                      "shapes": {g.name: [g.count, g.rows, g.cols] for g in cfg.groups},
+                      "preconditioned_sides": {g.name: [g.rows <= SOAP_MAX_DIM, g.cols <= SOAP_MAX_DIM]
+                                               for g in cfg.groups},
+                      "refresh_every": SOAP_FREQ, "refreshes_timed": refreshes,
+                      "hyperparameters": {"lr": SOAP_LR, "weight_decay": SOAP_WD, "betas": [step.beta1, step.beta2],
+                                          "eps": step.eps, "beta_s": step.beta_s, "max_dim": SOAP_MAX_DIM},
+                      "parallelism": "single GPU"},
+           "phases_ms": {"statistics": ph[0], "refresh": ph[1], "precondition": ph[2], "apply": ph[3]},
+           "soap": {"flops_per_step": flops, "tflops": flops / (ms_per_step * 1e-3) / 1e12,
+                    "flops_statistics_and_rotations": base, "flops_refresh": extra},
+           "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
+                        "frac": gemm_tflops / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                        "kernel": "sgemm_kernel (statistics and rotation products; timed with the rotated-Adam "
+                                  "kernel of the precondition phase)"},
+           "cpu_baseline": cpu}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline(cfg, grads_host, budget_s=20.0, coeffs=COEFFS["quintic"][0], steps=5):
     """Time the fp64 oracle on a bounded sample of the workload's matrices
     (smallest first until about `budget_s` of work), scaled by NS flops to
@@ -214,9 +333,9 @@ def main():
     ap.add_argument("--coeffs", default="quintic", choices=sorted(COEFFS),
                     help="Newton-Schulz coefficient set (quintic: the Muon default)")
     ap.add_argument("--ns-steps", type=int, default=None, help="Newton-Schulz steps (default: the set's usual count)")
-    ap.add_argument("--part", default="muon", choices=["muon", "adamw"],
+    ap.add_argument("--part", default="muon", choices=["muon", "adamw", "soap"],
                     help="muon: the Muon step of --workload (default); adamw: the AdamW step over the 8B-style "
-                         "model's embeddings, head and norms")
+                         "model's embeddings, head and norms; soap: SOAP steps over --workload's matrices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy before the warmup, so that profiler byte counters "
@@ -229,6 +348,9 @@ def main():
 
     if args.part == "adamw":
         bench_adamw(args)
+        return
+    if args.part == "soap":
+        bench_soap(args)
         return
 
     import numpy as np

@@ -318,7 +318,7 @@ muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, c
 
 /* Q factor of a QR factorization, the triangular factor's diagonal made
  * non-negative (unique for a full-rank input): Householder reflections
- * in 32-column panels with blocked trailing updates.  a (read only) and q:
+ * in 16-column panels with blocked trailing updates.  a (read only) and q:
  * F32, n x n, n <= 32768. */
 size_t soap_qr_workspace(int64_t count, int64_t n);
 muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* workspace, size_t ws_bytes,

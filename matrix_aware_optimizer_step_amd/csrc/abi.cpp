@@ -741,6 +741,10 @@ constexpr int kMaxSplits = 16;
 
 int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 
+// Floats of one panel's reflector slot: kQrPanel columns of up to n rows,
+// column-major with column pitch n.
+int64_t qr_vslot(int64_t n) { return round64(int64_t{kQrPanel} * n); }
+
 // Per-matrix float offsets of the QR scratch for an n x n factorization.
 struct QrLayout {
   int64_t V, Q, W, W2, TT, TQ, sgn, total;
@@ -750,7 +754,7 @@ QrLayout qr_layout(int64_t n) {
   const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
   QrLayout L;
   int64_t o = 0;
-  L.V = o;   o += round64(n * n);
+  L.V = o;   o += panels * qr_vslot(n);
   L.Q = o;   o += round64(n * n);
   L.W = o;   o += round64(int64_t{kMaxSplits} * kQrPanel * n);
   L.W2 = o;  o += round64(int64_t{kQrPanel} * n);
@@ -851,7 +855,7 @@ hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int
 
 // Q factor (R's diagonal made non-negative) of the n x n matrices in P
 // (contiguous, p_mat floats apart; overwritten), written to `q`.
-// Factorization: per 32-column panel, the panel kernel, then the trailing
+// Factorization: per 16-column panel, the panel kernel, then the trailing
 // columns  A_t <- (I - V T^T V^T) A_t  as  W = V^T A_t (split over the
 // reduction), W2 = [T^T ... T^T] [W_0; ...; W_s-1], A_t -= V W2.
 // Formation, last panel first:  Q_t <- (I - V T V^T) Q_t  from Q = I.
@@ -861,16 +865,18 @@ muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, floa
   const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
   const int64_t tslot = round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
   auto ntiles = [](int64_t x) { return (x + kSgemmTile - 1) / kSgemmTile; };
+  const int64_t vslot = qr_vslot(n);
   for (int64_t p = 0; p < panels; ++p) {
     const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0, nt = h - nb;
     int ks_f = 0, ks_q = 0;
     const int sf = nt > 0 ? plan_splits(h, ntiles(nt), count, &ks_f) : 1;
     const int sq = plan_splits(h, ntiles(h), count, &ks_q);
+    float* V = ws + L.V + p * vslot;  // the panel's reflectors, column-major (pitch n)
     QrPanelArgs a;
     std::memset(&a, 0, sizeof(a));
     a.A = P;
     a.a_mat = p_mat;
-    a.V = ws + L.V;
+    a.V = V;
     a.v_mat = L.total;
     a.TrepT = ws + L.TT;
     a.tT_mat = L.total;
@@ -882,18 +888,18 @@ muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, floa
     a.c0 = static_cast<int32_t>(c0);
     a.reps_t = sf;
     a.reps_q = sq;
-    a.vec = n % 4 == 0;
     SOAP_TRY(launch_qr_panel(a, count, s), "qr panel");
     if (nt > 0) {
-      const int64_t vo = c0 * n + c0;
-      SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, false, vo), op_ws(P, p_mat, n, false, vo + nb),
-                    out_ws(ws + L.W, L.total, nt), nb, nt, h, count, 1.f, 0.f, false, s, sf, ks_f, nb * nt),
+      const int64_t ao = c0 * n + c0;
+      // V^T as an M x K operand is the slot's rows (kcontig); V as h x nb is its transpose
+      SOAP_TRY(gemm(op_ws(V, L.total, n, true), op_ws(P, p_mat, n, false, ao + nb), out_ws(ws + L.W, L.total, nt),
+                    nb, nt, h, count, 1.f, 0.f, false, s, sf, ks_f, nb * nt),
                "qr trailing product");
       SOAP_TRY(gemm(op_ws(ws + L.TT, L.total, nb * sf, true), op_ws(ws + L.W, L.total, nt, false),
                     out_ws(ws + L.W2, L.total, nt), nb, nt, nb * sf, count, 1.f, 0.f, false, s),
                "qr block factor");
-      SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, true, vo), op_ws(ws + L.W2, L.total, nt, false),
-                    out_ws(P, p_mat, n, vo + nb), h, nt, nb, count, -1.f, 1.f, false, s),
+      SOAP_TRY(gemm(op_ws(V, L.total, n, false), op_ws(ws + L.W2, L.total, nt, false),
+                    out_ws(P, p_mat, n, ao + nb), h, nt, nb, count, -1.f, 1.f, false, s),
                "qr trailing update");
     }
   }
@@ -902,15 +908,16 @@ muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, floa
     const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0;
     int ks_q = 0;
     const int sq = plan_splits(h, ntiles(h), count, &ks_q);
-    const int64_t vo = c0 * n + c0;
-    SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, false, vo), op_ws(ws + L.Q, L.total, n, false, vo),
-                  out_ws(ws + L.W, L.total, h), nb, h, h, count, 1.f, 0.f, false, s, sq, ks_q, nb * h),
+    const int64_t qo = c0 * n + c0;
+    float* V = ws + L.V + p * vslot;
+    SOAP_TRY(gemm(op_ws(V, L.total, n, true), op_ws(ws + L.Q, L.total, n, false, qo), out_ws(ws + L.W, L.total, h),
+                  nb, h, h, count, 1.f, 0.f, false, s, sq, ks_q, nb * h),
              "qr formation product");
     SOAP_TRY(gemm(op_ws(ws + L.TQ + p * tslot, L.total, nb * sq, true), op_ws(ws + L.W, L.total, h, false),
                   out_ws(ws + L.W2, L.total, h), nb, h, nb * sq, count, 1.f, 0.f, false, s),
              "qr formation factor");
-    SOAP_TRY(gemm(op_ws(ws + L.V, L.total, n, true, vo), op_ws(ws + L.W2, L.total, h, false),
-                  out_ws(ws + L.Q, L.total, n, vo), h, h, nb, count, -1.f, 1.f, false, s),
+    SOAP_TRY(gemm(op_ws(V, L.total, n, false), op_ws(ws + L.W2, L.total, h, false), out_ws(ws + L.Q, L.total, n, qo),
+                  h, h, nb, count, -1.f, 1.f, false, s),
              "qr formation update");
   }
   SOAP_TRY(launch_sign_copy(ws + L.Q, L.total, ws + L.sgn, L.total, to_mat(q), static_cast<int32_t>(n), count, s),

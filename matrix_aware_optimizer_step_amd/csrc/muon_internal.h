@@ -298,25 +298,24 @@ constexpr int kSgemmTile = 128;
 constexpr int kSgemmBK = 16;
 hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream);
 
-// Householder QR, one 32-column panel of `count` n x n matrices (row-major,
-// ld n): columns c0 .. c0+nb-1 (nb = min(32, n - c0)) are reduced to upper
-// triangular form in A (reflector entries below the diagonal), the
-// reflectors are written explicitly to V (unit diagonal, zeros above it;
-// rows c0 .. n-1 of those columns), and the sign of each R diagonal entry
-// (+1 for zero) to sgn.  The block factor T of H_c0 ... H_(c0+nb-1) =
-// I - V T V^T (nb x nb, upper triangular) is written repeated side by side
-// for the split-K products: TrepT (nb x nb*reps_t, row-major) holds
-// [T^T ... T^T], TrepQ (nb x nb*reps_q) holds [T ... T].
-constexpr int kQrPanel = 32;
+// Householder QR, one 16-column panel of `count` n x n matrices (row-major,
+// ld n): columns c0 .. c0+nb-1 (nb = min(16, n - c0)), rows c0 .. n-1, of A
+// (read only) are reduced in this panel's slot V of the reflector buffer,
+// column-major: column q of the panel at V + q*n, row r - c0 at offset
+// r - c0.  The slot ends holding the explicit reflectors (unit diagonal,
+// zeros above it); sgn gets the sign of each R diagonal entry (+1 for
+// zero).  The block factor T of H_c0 ... H_(c0+nb-1) = I - V T V^T (nb x nb,
+// upper triangular) is written repeated side by side for the split-K
+// products: TrepT (nb x nb*reps_t, row-major) holds [T^T ... T^T], TrepQ
+// (nb x nb*reps_q) holds [T ... T].
+constexpr int kQrPanel = 16;
 struct QrPanelArgs {
-  float* A; int64_t a_mat;       // floats per matrix
+  const float* A; int64_t a_mat;  // floats per matrix
   float* V; int64_t v_mat;
   float* TrepT; int64_t tT_mat;
   float* TrepQ; int64_t tQ_mat;
   float* sgn; int64_t s_mat;
   int32_t n, c0, reps_t, reps_q;
-  int32_t vec;                   // n % 4 == 0 (16-byte rows of the panel)
-  int32_t pad_;
 };
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream);
 

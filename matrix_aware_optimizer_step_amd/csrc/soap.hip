@@ -7,9 +7,10 @@
 //                     (v_mfma_f32_32x32x2_f32): the statistics G G^T and
 //                     G^T G, the rotations Q_L^T G Q_R and Q_L D Q_R^T, the
 //                     power-iteration product S Q and the QR's block updates.
-//   qr_panel_kernel   one 32-column panel of a Householder QR (the basis
+//   qr_panel_*        one 16-column panel of a Householder QR (the basis
 //                     refresh): reflectors, their block factor T, and the
-//                     signs that make R's diagonal non-negative.
+//                     signs that make R's diagonal non-negative; held in
+//                     registers up to 4096 rows, else worked in memory.
 //   rot_adam_kernel   Adam's moments and direction in the rotated basis.
 //
 // Everything here computes in fp32.
@@ -66,36 +67,44 @@ __device__ __forceinline__ void load_run(const char* p, const SgemmOperand& o, i
   }
 }
 
-// One 128 (outer) x 16 (reduction) slice of an operand into registers,
-// eight values per thread: outer rows o0.. (of `outer`), reduction k0..
-// (below klim).
+// One OUT (outer) x 16 (reduction) slice of an operand into registers,
+// OUT/64 runs of four per thread (threads beyond OUT*4 runs idle): outer
+// rows o0.. (of `outer`), reduction k0.. (below klim).
+template <int OUT>
 __device__ __forceinline__ void load_slice(const char* p, const SgemmOperand& o, int outer, int klim, int o0,
                                            int k0, float* r) {
-  const int t = threadIdx.x;
-  if (o.kcontig) {
+  constexpr int kRuns = OUT * kBK / 4;
+  constexpr int kG = (kRuns + kThreads - 1) / kThreads;
 #pragma unroll
-    for (int g = 0; g < 2; ++g) load_run(p, o, o0 + t / 4 + 64 * g, k0 + 4 * (t % 4), outer, klim, r + 4 * g);
-  } else {
-#pragma unroll
-    for (int g = 0; g < 2; ++g) load_run(p, o, k0 + t / 32 + 8 * g, o0 + 4 * (t % 32), klim, outer, r + 4 * g);
+  for (int g = 0; g < kG; ++g) {
+    const int t = threadIdx.x + kThreads * g;
+    if (kRuns % kThreads != 0 && t >= kRuns) continue;
+    if (o.kcontig)
+      load_run(p, o, o0 + t / 4, k0 + 4 * (t % 4), outer, klim, r + 4 * g);
+    else
+      load_run(p, o, k0 + t / (OUT / 4), o0 + 4 * (t % (OUT / 4)), klim, outer, r + 4 * g);
   }
 }
 
-// The slice into LDS as S[k][outer] (pitch kPitch).  The scattered form
-// (kcontig) writes 64 distinct banks per wave: address mod 64 is
-// 16*(t%4) + 4e + t/4 for lanes t of one wave.
+// The slice into LDS as S[k][outer] (pitch OUT + 4).  For OUT = 128 the
+// scattered form (kcontig) writes 64 distinct banks per wave: address mod
+// 64 is 16*(t%4) + 4e + t/4 for lanes t of one wave.
+template <int OUT>
 __device__ __forceinline__ void store_slice(float* S, const SgemmOperand& o, const float* r) {
-  const int t = threadIdx.x;
-  if (o.kcontig) {
+  constexpr int kRuns = OUT * kBK / 4;
+  constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kP = OUT + 4;
 #pragma unroll
-    for (int g = 0; g < 2; ++g)
+  for (int g = 0; g < kG; ++g) {
+    const int t = threadIdx.x + kThreads * g;
+    if (kRuns % kThreads != 0 && t >= kRuns) continue;
+    if (o.kcontig) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kPitch + t / 4 + 64 * g] = r[4 * g + e];
-  } else {
-#pragma unroll
-    for (int g = 0; g < 2; ++g)
-      *reinterpret_cast<float4*>(S + (t / 32 + 8 * g) * kPitch + 4 * (t % 32)) =
+      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kP + t / 4] = r[4 * g + e];
+    } else {
+      *reinterpret_cast<float4*>(S + (t / (OUT / 4)) * kP + 4 * (t % (OUT / 4))) =
           make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
+    }
   }
 }
 
@@ -104,7 +113,13 @@ __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
   return p + o.off;
 }
 
+// TM x 128 output tile, four waves: TM = 128 as 2 x 2 waves of 64 x 64,
+// TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.
+template <int TM>
 __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
+  constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
+  constexpr int FI = TM / WM / 32, FJ = kT / WN / 32;
+  constexpr int kPA = TM + 4;
   const int tj = blockIdx.x, ti = blockIdx.y;
   if (a.sym && ti > tj) return;
   const int bi = blockIdx.z / a.splits, sp = blockIdx.z % a.splits;
@@ -115,44 +130,46 @@ __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
   char* pc = (a.c_ptrs ? static_cast<char*>(a.c_ptrs[bi]) : a.c + static_cast<int64_t>(bi) * a.c_stride) + a.c_off +
              static_cast<int64_t>(sp) * a.c_split;
 
-  __shared__ float As[kBK * kPitch];
+  __shared__ float As[kBK * kPA];
   __shared__ float Bs[kBK * kPitch];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
-  const int i0 = ti * kT, j0 = tj * kT;
+  const int i0 = ti * TM, j0 = tj * kT;
 
-  f32x16_t acc[2][2];
+  f32x16_t acc[FI][FJ];
 #pragma unroll
-  for (int x = 0; x < 2; ++x)
+  for (int x = 0; x < FI; ++x)
 #pragma unroll
-    for (int y = 0; y < 2; ++y)
+    for (int y = 0; y < FJ; ++y)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  float ra[8], rb[8];
+  float ra[(TM * kBK / 4 + kThreads - 1) / kThreads * 4], rb[8];
   if (kbeg < kend) {
-    load_slice(pa, a.a, a.M, kend, i0, kbeg, ra);
-    load_slice(pb, a.b, a.N, kend, j0, kbeg, rb);
+    load_slice<TM>(pa, a.a, a.M, kend, i0, kbeg, ra);
+    load_slice<kT>(pb, a.b, a.N, kend, j0, kbeg, rb);
   }
   for (int k0 = kbeg; k0 < kend; k0 += kBK) {
-    store_slice(As, a.a, ra);
-    store_slice(Bs, a.b, rb);
+    store_slice<TM>(As, a.a, ra);
+    store_slice<kT>(Bs, a.b, rb);
     __syncthreads();
     if (k0 + kBK < kend) {  // next slice in flight during the products
-      load_slice(pa, a.a, a.M, kend, i0, k0 + kBK, ra);
-      load_slice(pb, a.b, a.N, kend, j0, k0 + kBK, rb);
+      load_slice<TM>(pa, a.a, a.M, kend, i0, k0 + kBK, ra);
+      load_slice<kT>(pb, a.b, a.N, kend, j0, k0 + kBK, rb);
     }
 #pragma unroll
     for (int kk = 0; kk < kBK / 2; ++kk) {
       // lane: A[i = l32][k = half] and B[k = half][j = l32] of each 32 x 2 step
-      const float* ar = As + (2 * kk + half) * kPitch + wm * 64 + l32;
-      const float* br = Bs + (2 * kk + half) * kPitch + wn * 64 + l32;
-      const float a0 = ar[0], a1 = ar[32], b0 = br[0], b1 = br[32];
-      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b0, acc[0][0], 0, 0, 0);
-      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b1, acc[0][1], 0, 0, 0);
-      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b0, acc[1][0], 0, 0, 0);
-      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b1, acc[1][1], 0, 0, 0);
+      float av[FI], bv[FJ];
+#pragma unroll
+      for (int x = 0; x < FI; ++x) av[x] = As[(2 * kk + half) * kPA + wm * (TM / WM) + x * 32 + l32];
+#pragma unroll
+      for (int y = 0; y < FJ; ++y) bv[y] = Bs[(2 * kk + half) * kPitch + wn * (kT / WN) + y * 32 + l32];
+#pragma unroll
+      for (int x = 0; x < FI; ++x)
+#pragma unroll
+        for (int y = 0; y < FJ; ++y) acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[x], bv[y], acc[x][y], 0, 0, 0);
     }
     __syncthreads();
   }
@@ -161,13 +178,13 @@ __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
   float* C = reinterpret_cast<float*>(pc);
   const bool diag = a.sym && ti == tj;
 #pragma unroll
-  for (int fi = 0; fi < 2; ++fi)
+  for (int fi = 0; fi < FI; ++fi)
 #pragma unroll
-    for (int fj = 0; fj < 2; ++fj)
+    for (int fj = 0; fj < FJ; ++fj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = i0 + wm * 64 + fi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int j = j0 + wn * 64 + fj * 32 + l32;
+        const int i = i0 + wm * (TM / WM) + fi * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const int j = j0 + wn * (kT / WN) + fj * 32 + l32;
         if (i >= a.M || j >= a.N || (diag && i > j)) continue;
         float* cij = C + static_cast<int64_t>(i) * a.ldc + j;
         float v = a.alpha * acc[fi][fj][r];
@@ -221,40 +238,61 @@ __device__ __forceinline__ void block_sum32(float* w, float* part, float* tot) {
 //   v = x / (alpha - beta) with v_0 = 1, so (I - tau v v^T) x = beta e_0;
 //   every later panel column y <- y - tau v (v^T y);
 //   T[0:j, j] = -tau_j T[0:j, 0:j] (V[:, 0:j]^T v_j), T[j][j] = tau_j.
-// Row r of a column step belongs to thread (r - c) mod 512 in every phase
-// that writes it; the barrier ending each column orders the next column's
-// reads, which start one row lower.
-template <bool VEC>
+// The panel is first copied, column-major, into its slot of the reflector
+// buffer, P[q][r] = A[c0 + r][c0 + q] at V + q*n + r, and reduced there:
+// lanes take consecutive rows, so every column access of a wave is one
+// contiguous run.  Column j of the slot ends as the explicit reflector
+// (zeros above its unit diagonal).  Row r of a column step belongs to
+// thread (r - j) mod kQrThreads in every phase that writes it; the barrier
+// ending each column orders the next column's reads.  A is only read: R is
+// not needed, only the signs of its diagonal.
 __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
   const int64_t b = blockIdx.x;
-  float* A = a.A + b * a.a_mat;
-  float* V = a.V + b * a.v_mat;
+  const float* A = a.A + b * a.a_mat;
+  float* P = a.V + b * a.v_mat;
   float* TrT = a.TrepT + b * a.tT_mat;
   float* TrQ = a.TrepQ + b * a.tQ_mat;
   float* sg = a.sgn + b * a.s_mat;
-  const int n = a.n, c0 = a.c0;
-  const int nb = min(kQrPanel, n - c0);
-  const int tid = threadIdx.x;
+  const int n = a.n, c0 = a.c0, h = n - c0;
+  const int nb = min(kQrPanel, h);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  __shared__ float tile[kQrWaves][32][33];
   __shared__ float part[kQrWaves * 32];
   __shared__ float tot[32];
   __shared__ float Ts[kQrPanel][kQrPanel + 1];
   __shared__ float par[3];
 
+  // copy in: each wave moves 32 rows at a time through its own LDS tile
+  // (row reads of 128 bytes, column writes of 128 bytes)
+  for (int r0 = 32 * wave; r0 < h; r0 += 32 * kQrWaves) {
+    for (int i = 0; i < 16; ++i) {
+      const int rr = 2 * i + (lane >> 5), q = lane & 31, r = r0 + rr;
+      tile[wave][rr][q] = (r < h && q < nb) ? A[static_cast<int64_t>(c0 + r) * n + c0 + q] : 0.f;
+    }
+    __builtin_amdgcn_wave_barrier();
+    for (int q2 = 0; q2 < 32; q2 += 2) {
+      const int q = q2 + (lane >> 5), rr = lane & 31, r = r0 + rr;
+      if (r < h && q < nb) P[static_cast<int64_t>(q) * n + r] = tile[wave][rr][q];
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
   for (int j = 0; j < nb; ++j) {
-    const int c = c0 + j;
+    float* pj = P + static_cast<int64_t>(j) * n;
     float s = 0.f;
-    for (int r = c + 1 + tid; r < n; r += kQrThreads) {
-      const float x = A[static_cast<int64_t>(r) * n + c];
+    for (int r = j + 1 + tid; r < h; r += kQrThreads) {
+      const float x = pj[r];
       s += x * x;
     }
     s = wave_sum(s);
-    if ((tid & 63) == 0) part[tid >> 6] = s;
+    if (lane == 0) part[wave] = s;
     __syncthreads();
     if (tid == 0) {
       float t = 0.f;
       for (int q = 0; q < kQrWaves; ++q) t += part[q];
-      const float alpha = A[static_cast<int64_t>(c) * n + c];
+      const float alpha = pj[j];
       float beta = alpha, tau = 0.f, scale = 0.f;
       if (t > 0.f) {
         const float nrm = sqrtf(alpha * alpha + t);
@@ -262,12 +300,10 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
         tau = (beta - alpha) / beta;
         scale = 1.f / (alpha - beta);
       }
-      par[0] = beta;
       par[1] = tau;
       par[2] = scale;
-      sg[c] = beta < 0.f ? -1.f : 1.f;
+      sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
       Ts[j][j] = tau;
-      A[static_cast<int64_t>(c) * n + c] = beta;  // row c belongs to thread 0 below
     }
     __syncthreads();
     const float tau = par[1], scale = par[2];
@@ -278,29 +314,15 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
     float w[32];
 #pragma unroll
     for (int q = 0; q < 32; ++q) w[q] = 0.f;
-    for (int r = c + tid; r < n; r += kQrThreads) {
-      float* row = A + static_cast<int64_t>(r) * n + c0;
+    for (int r = j + tid; r < h; r += kQrThreads) {
       float vr = 1.f;
-      if (r > c) {
-        vr = row[j] * scale;
-        row[j] = vr;
-      }
-      float x[32];
-      if (VEC && nb == 32) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float4 f = reinterpret_cast<const float4*>(row)[q];
-          x[4 * q] = f.x;
-          x[4 * q + 1] = f.y;
-          x[4 * q + 2] = f.z;
-          x[4 * q + 3] = f.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 32; ++q) x[q] = q < nb ? row[q] : 0.f;
+      if (r > j) {
+        vr = pj[r] * scale;
+        pj[r] = vr;
       }
 #pragma unroll
-      for (int q = 0; q < 32; ++q) w[q] += q == j ? 0.f : vr * x[q];
+      for (int q = 0; q < 32; ++q)
+        if (q < nb && q != j) w[q] += vr * P[static_cast<int64_t>(q) * n + r];
     }
     block_sum32(w, part, tot);
 
@@ -310,28 +332,174 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
       Ts[tid][j] = -tau * t;
     }
     if (j + 1 < nb) {
-      for (int r = c + tid; r < n; r += kQrThreads) {
-        float* row = A + static_cast<int64_t>(r) * n + c0;
-        const float vr = r > c ? row[j] : 1.f;
-        for (int q = j + 1; q < nb; ++q) row[q] -= tau * tot[q] * vr;
+      for (int r = j + tid; r < h; r += kQrThreads) {
+        const float vr = r > j ? pj[r] : 1.f;
+        for (int q = j + 1; q < nb; ++q) P[static_cast<int64_t>(q) * n + r] -= tau * tot[q] * vr;
       }
     }
+    // explicit reflector: unit diagonal, zeros above it (R is not kept)
+    for (int r = tid; r <= j; r += kQrThreads) pj[r] = r == j ? 1.f : 0.f;
     __syncthreads();
   }
 
-  // explicit reflectors (rows c0 .. n-1 of the panel's columns)
-  for (int r = c0 + tid; r < n; r += kQrThreads) {
-    const float* row = A + static_cast<int64_t>(r) * n + c0;
-    float* vrow = V + static_cast<int64_t>(r) * n + c0;
-    for (int q = 0; q < nb; ++q) vrow[q] = r > c0 + q ? row[q] : (r == c0 + q ? 1.f : 0.f);
-  }
   // T below its diagonal is zero; repeated copies for the split products
   for (int e = tid; e < nb * nb; e += kQrThreads) {
     const int i = e / nb, k = e % nb;
     const float t = k >= i ? Ts[i][k] : 0.f;     // T[i][k]
     const float tt = i >= k ? Ts[k][i] : 0.f;    // T^T[i][k]
-    for (int s = 0; s < a.reps_t; ++s) TrT[static_cast<int64_t>(i) * nb * a.reps_t + s * nb + k] = tt;
-    for (int s = 0; s < a.reps_q; ++s) TrQ[static_cast<int64_t>(i) * nb * a.reps_q + s * nb + k] = t;
+    for (int s2 = 0; s2 < a.reps_t; ++s2) TrT[static_cast<int64_t>(i) * nb * a.reps_t + s2 * nb + k] = tt;
+    for (int s2 = 0; s2 < a.reps_q; ++s2) TrQ[static_cast<int64_t>(i) * nb * a.reps_q + s2 * nb + k] = t;
+  }
+}
+
+// The same panel step with the panel held in registers: 512 threads, row
+// r = tid + 512 k (k < 8) in x[k][0..15], so a panel of up to 4096 rows
+// costs no memory traffic between its load and the store of the
+// reflectors; a column step is two workgroup reductions.
+constexpr int kRegThreads = 512;
+constexpr int kRegRows = 8;
+constexpr int kRegWaves = kRegThreads / 64;
+
+// Workgroup sums of 16 per-thread values into tot[0..15]: reduce-scatter
+// inside each wave (xor 32, 16, 8, 4 leave value lane >> 2 in each group of
+// four lanes, completed by xor 2 and 1).
+__device__ __forceinline__ void block_sum16(float* w, float* part, float* tot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int h = 8; h >= 1; h >>= 1) {
+    const bool up = (lane & (4 * h)) != 0;
+#pragma unroll
+    for (int i = 0; i < h; ++i) {
+      const float send = up ? w[i] : w[i + h];
+      const float keep = up ? w[i + h] : w[i];
+      w[i] = keep + __shfl_xor(send, 4 * h);
+    }
+  }
+  w[0] += __shfl_xor(w[0], 2);
+  w[0] += __shfl_xor(w[0], 1);
+  if ((lane & 3) == 0) part[wave * 16 + (lane >> 2)] = w[0];
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float s = 0.f;
+    for (int q = 0; q < kRegWaves; ++q) s += part[q * 16 + threadIdx.x];
+    tot[threadIdx.x] = s;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a) {
+  const int64_t b = blockIdx.x;
+  const float* A = a.A + b * a.a_mat;
+  float* P = a.V + b * a.v_mat;
+  float* TrT = a.TrepT + b * a.tT_mat;
+  float* TrQ = a.TrepQ + b * a.tQ_mat;
+  float* sg = a.sgn + b * a.s_mat;
+  const int n = a.n, c0 = a.c0, h = n - c0;
+  const int nb = min(kQrPanel, h);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  __shared__ float part[kRegWaves * 16];
+  __shared__ float tot[16];
+  __shared__ float Ts[kQrPanel][kQrPanel + 1];
+  __shared__ float par[3];
+
+  float x[kRegRows][kQrPanel];
+#pragma unroll
+  for (int k = 0; k < kRegRows; ++k) {
+    const int r = tid + kRegThreads * k;
+    const float* row = A + static_cast<int64_t>(c0 + (r < h ? r : 0)) * n + c0;
+#pragma unroll
+    for (int q = 0; q < kQrPanel; ++q) x[k][q] = (r < h && q < nb) ? row[q < nb ? q : 0] : 0.f;
+  }
+
+  // x is only indexed by constants (column j is picked out with selects),
+  // so it stays in registers; v is recomputed from x where needed rather
+  // than held across the reductions
+  auto column = [&](int k, int j) {
+    float c = 0.f;
+#pragma unroll
+    for (int q = 0; q < kQrPanel; ++q) c = q == j ? x[k][q] : c;
+    return c;
+  };
+  for (int j = 0; j < nb; ++j) {
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      const int r = tid + kRegThreads * k;
+      const float c = column(k, j);
+      s += (r > j && r < h) ? c * c : 0.f;
+      if (k == 0 && tid == j) par[0] = c;  // alpha: row j is thread j's first row (j < 16)
+    }
+    s = wave_sum(s);
+    if (lane == 0) part[wave] = s;
+    __syncthreads();
+    if (tid == 0) {
+      float t = 0.f;
+      for (int q = 0; q < kRegWaves; ++q) t += part[q];
+      const float alpha = par[0];
+      float beta = alpha, tau = 0.f, scale = 0.f;
+      if (t > 0.f) {
+        const float nrm = sqrtf(alpha * alpha + t);
+        beta = alpha >= 0.f ? -nrm : nrm;
+        tau = (beta - alpha) / beta;
+        scale = 1.f / (alpha - beta);
+      }
+      par[1] = tau;
+      par[2] = scale;
+      sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
+      Ts[j][j] = tau;
+    }
+    __syncthreads();
+    const float tau = par[1], scale = par[2];
+
+    float w[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) w[q] = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      const int r = tid + kRegThreads * k;
+      const bool below = r > j && r < h;
+      const float vk = below ? column(k, j) * scale : (r == j ? 1.f : 0.f);
+#pragma unroll
+      for (int q = 0; q < kQrPanel; ++q) {
+        if (q == j && below) x[k][q] = vk;
+        w[q] += q == j ? 0.f : vk * x[k][q];
+      }
+    }
+    block_sum16(w, part, tot);
+
+    if (tid < j) {
+      float t = 0.f;
+      for (int k = tid; k < j; ++k) t += Ts[tid][k] * tot[k];
+      Ts[tid][j] = -tau * t;
+    }
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      const int r = tid + kRegThreads * k;
+      const float vk = (r > j && r < h) ? column(k, j) : (r == j ? 1.f : 0.f);
+#pragma unroll
+      for (int q = 0; q < kQrPanel; ++q)
+        if (q > j) x[k][q] -= tau * tot[q] * vk;
+    }
+    __syncthreads();
+  }
+
+  // explicit reflectors, column-major in the slot (coalesced across lanes)
+#pragma unroll
+  for (int k = 0; k < kRegRows; ++k) {
+    const int r = tid + kRegThreads * k;
+    if (r < h) {
+#pragma unroll
+      for (int q = 0; q < kQrPanel; ++q)
+        if (q < nb) P[static_cast<int64_t>(q) * n + r] = r > q ? x[k][q] : (r == q ? 1.f : 0.f);
+    }
+  }
+  for (int e = tid; e < nb * nb; e += kRegThreads) {
+    const int i = e / nb, k = e % nb;
+    const float t = k >= i ? Ts[i][k] : 0.f;
+    const float tt = i >= k ? Ts[k][i] : 0.f;
+    for (int s2 = 0; s2 < a.reps_t; ++s2) TrT[static_cast<int64_t>(i) * nb * a.reps_t + s2 * nb + k] = tt;
+    for (int s2 = 0; s2 < a.reps_q; ++s2) TrQ[static_cast<int64_t>(i) * nb * a.reps_q + s2 * nb + k] = t;
   }
 }
 
@@ -396,16 +564,21 @@ __global__ __launch_bounds__(256) void rot_adam_kernel(RotAdamArgs a) {
 }  // namespace
 
 hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream) {
-  const dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT, a.count * a.splits);
-  hipLaunchKernelGGL(sgemm_kernel, grid, dim3(kThreads), 0, stream, a);
+  if (a.M <= 32 && !a.sym) {
+    const dim3 grid((a.N + kT - 1) / kT, (a.M + 31) / 32, a.count * a.splits);
+    hipLaunchKernelGGL(sgemm_kernel<32>, grid, dim3(kThreads), 0, stream, a);
+  } else {
+    const dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT, a.count * a.splits);
+    hipLaunchKernelGGL(sgemm_kernel<kT>, grid, dim3(kThreads), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream) {
-  if (a.vec)
-    hipLaunchKernelGGL(qr_panel_kernel<true>, dim3(count), dim3(kQrThreads), 0, stream, a);
+  if (a.n - a.c0 <= kRegThreads * kRegRows)
+    hipLaunchKernelGGL(qr_panel_reg_kernel, dim3(count), dim3(kRegThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL(qr_panel_kernel<false>, dim3(count), dim3(kQrThreads), 0, stream, a);
+    hipLaunchKernelGGL(qr_panel_kernel, dim3(count), dim3(kQrThreads), 0, stream, a);
   return hipGetLastError();
 }
 

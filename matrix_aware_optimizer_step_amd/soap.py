@@ -135,14 +135,33 @@ class SoapStep:
                     g[k].copy_(s[k])
         self.t = int(state["t"])
 
-    def step(self, stream=None) -> None:
+    def step(self, stream=None, events=None) -> None:
+        """One SOAP update of every group.  ``events``: five torch.cuda
+        Events recorded on the stream before the statistics, after them,
+        after the refreshes, after the rotated Adam directions and after the
+        weight updates (the phases run group after group)."""
         self.t += 1
-        s = _stream(stream)
+        st = stream if stream is not None else torch.cuda.current_stream()
+        s = _stream(st)
+
+        def rec(i):
+            if events is not None:
+                events[i].record(st)
+
+        rec(0)
         for g in self.groups:
             statistics(g["G"], g["L"], g["R"], self.beta_s, stream=s)
-            if (self.t - 1) % self.freq == 0 and (g["L"] is not None or g["R"] is not None):
-                refresh(g["mbar"], g["L"], g["R"], g["QL"], g["QR"], ws=self.ws, stream=s)
+        rec(1)
+        if (self.t - 1) % self.freq == 0:
+            for g in self.groups:
+                if g["L"] is not None or g["R"] is not None:
+                    refresh(g["mbar"], g["L"], g["R"], g["QL"], g["QR"], ws=self.ws, stream=s)
+        rec(2)
+        for g in self.groups:
             precondition(g["G"], g["mbar"], g["vbar"], g["D"], self.t, g["QL"], g["QR"], self.beta1, self.beta2,
                          self.eps, ws=self.ws, stream=s)
+        rec(3)
+        for g in self.groups:
             bw, bd = batch(g["W"]), batch(g["D"])
             L.muon_apply(bw.desc, bd.desc, self.lr, self.weight_decay, L.MUON_SCALE_NONE, 1.0, s)
+        rec(4)

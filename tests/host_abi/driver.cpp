@@ -137,7 +137,7 @@ void soap_cases() {
     expect(soap_precondition(&g, pQL, pQR, &mb, &vb, &d, 0, 0.9f, 0.999f, 1e-8f, kWs, need, nullptr),
            MUON_ERR_INVALID_VALUE, "soap_precondition, step 0");
   }
-  for (int64_t n : {1, 5, 32, 33, 100, 257, 300, 1024, 4096}) {
+  for (int64_t n : {1, 5, 16, 17, 33, 100, 257, 300, 1024, 4096, 4200}) {
     for (int64_t count : {1, 3}) {
       const size_t need = soap_qr_workspace(count, n);
       stub_set_workspace(kWs, need);

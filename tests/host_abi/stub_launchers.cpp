@@ -247,10 +247,9 @@ hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t) {
   ++g_launches;
   if (a.n < 1 || a.c0 < 0 || a.c0 >= a.n || a.c0 % kQrPanel) die("qr panel: n %d, c0 %d", a.n, a.c0);
   if (a.reps_t < 1 || a.reps_t > 16 || a.reps_q < 1 || a.reps_q > 16) die("qr panel reps %d %d", a.reps_t, a.reps_q);
-  if (a.vec != (a.n % 4 == 0)) die("qr panel vec flag");
-  const int64_t n = a.n, nb = std::min<int64_t>(kQrPanel, n - a.c0);
+  const int64_t n = a.n, h = n - a.c0, nb = std::min<int64_t>(kQrPanel, h);
   in_ws(a.A, count, a.a_mat * 4, n * n * 4, "qr A");
-  in_ws(a.V, count, a.v_mat * 4, n * n * 4, "qr V");
+  in_ws(a.V, count, a.v_mat * 4, ((nb - 1) * n + h) * 4, "qr reflector slot");
   in_ws(a.TrepT, count, a.tT_mat * 4, nb * nb * a.reps_t * 4, "qr T^T copies");
   in_ws(a.TrepQ, count, a.tQ_mat * 4, nb * nb * a.reps_q * 4, "qr T copies");
   in_ws(a.sgn, count, a.s_mat * 4, n * 4, "qr signs");

@@ -62,7 +62,7 @@ def f32(x):
     return float(np.float32(x))
 
 
-@pytest.mark.parametrize("n", [1, 5, 32, 33, 100, 257, 300])
+@pytest.mark.parametrize("n", [1, 5, 16, 17, 33, 100, 257, 300, 4200])
 def test_qr_matches_oracle(mx, n):
     from matrix_aware_optimizer_step_amd import soap
     print(f"soap_qr n={n}", flush=True)
@@ -222,3 +222,19 @@ def test_soap_pointer_array_state_matches_strided(mx):
         torch.cuda.synchronize()
         outs.append(D.clone())
     assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("m,n,count,max_dim", [(1024, 4096, 2, 8192), (4096, 14336, 1, 8192)])
+def test_soap_full_size_layer_matrices(mx, m, n, count, max_dim):
+    """The 8B-style layer's Wk/Wv pair (both sides preconditioned, refresh by
+    4096-wide QRs) and its down projection (rows only: the 14336 axis keeps
+    the identity), at full size through SoapStep as the benchmark runs it.
+    The statistics start from a prior comparable to the gradient's largest
+    squared singular value, so that each refresh's QR is well conditioned
+    (kappa ~2) and the comparison checks the wiring at full size rather
+    than fp32 conditioning (covered above)."""
+    print(f"soap full size {count}x{m}x{n}", flush=True)
+    sig2 = (np.sqrt(m) + np.sqrt(n)) ** 2
+    worst, worst_q = run_steps(mx, m, n, steps=2, count=count, max_dim=max_dim, freq=1, eps=1e-2, tol=1e-4,
+                               prior=float(sig2), seed=31)
+    assert worst_q <= 1e-4
