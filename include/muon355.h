@@ -334,6 +334,16 @@ muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const m
                            const muon_batch_t* QR, const muon_batch_t* mbar, void* workspace, size_t ws_bytes,
                            void* stream);
 
+/* soap_refresh for up to 8 groups (shape classes) at once: Ls[g], Rs[g],
+ * QLs[g], QRs[g] point to group g's descriptors or are NULL for a side
+ * without statistic; mbars[g] is group g's first moment.  All QRs of one
+ * order, over every group and side, run as one batched factorization. */
+size_t soap_refresh_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
+                                      const int64_t* cols, const int* with_l, const int* with_r);
+muon_status_t soap_refresh_grouped(int ngroups, const muon_batch_t* const* Ls, const muon_batch_t* const* Rs,
+                                   const muon_batch_t* const* QLs, const muon_batch_t* const* QRs,
+                                   const muon_batch_t* mbars, void* workspace, size_t ws_bytes, void* stream);
+
 /* [GUIDE] 11.1 between refreshes:
  *   Gbar = QL^T G QR;  mbar <- beta1 mbar + (1-beta1) Gbar;
  *   vbar <- beta2 vbar + (1-beta2) Gbar^2;

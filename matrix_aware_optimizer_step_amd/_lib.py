@@ -28,6 +28,7 @@ EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_m
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
             "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
             "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
+            "soap_refresh_grouped_workspace", "soap_refresh_grouped",
             "soap_precondition_workspace", "soap_precondition")
 
 ADAMW_CHUNK = 4096  # MUON_ADAMW_CHUNK
@@ -89,6 +90,11 @@ def load() -> ctypes.CDLL:
         "soap_qr": (ctypes.c_int, [P, P, vp, sz, vp]),
         "soap_refresh_workspace": (sz, [i64, i64, i64, ctypes.c_int, ctypes.c_int]),
         "soap_refresh": (ctypes.c_int, [P, P, P, P, P, vp, sz, vp]),
+        "soap_refresh_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                ctypes.POINTER(i64), ctypes.POINTER(ctypes.c_int),
+                                                ctypes.POINTER(ctypes.c_int)]),
+        "soap_refresh_grouped": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P),
+                                                ctypes.POINTER(P), ctypes.POINTER(P), P, vp, sz, vp]),
         "soap_precondition_workspace": (sz, [i64, i64, i64]),
         "soap_precondition": (ctypes.c_int, [P, P, P, P, P, P, i64, f32, f32, f32, vp, sz, vp]),
     }
@@ -218,6 +224,26 @@ def soap_refresh(L: MuonBatch | None, R: MuonBatch | None, QL: MuonBatch | None,
                  mbar: MuonBatch, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
     st = load().soap_refresh(_ref(L), _ref(R), _ref(QL), _ref(QR), _ref(mbar), workspace_ptr, ws_bytes, stream)
     _check(st, "soap_refresh")
+
+
+def soap_refresh_grouped_workspace(counts, rows, cols, with_l, with_r) -> int:
+    n = len(counts)
+    i64, ci = ctypes.c_int64 * n, ctypes.c_int * n
+    return load().soap_refresh_grouped_workspace(n, i64(*counts), i64(*rows), i64(*cols),
+                                                 ci(*[int(bool(x)) for x in with_l]),
+                                                 ci(*[int(bool(x)) for x in with_r]))
+
+
+def soap_refresh_grouped(Ls, Rs, QLs, QRs, mbars, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    """Ls, Rs, QLs, QRs: per-group MuonBatch or None; mbars: per-group MuonBatch."""
+    n = len(mbars)
+    if not (len(Ls) == len(Rs) == len(QLs) == len(QRs) == n):
+        raise ValueError("per-group lists differ in length")
+    PB = ctypes.POINTER(MuonBatch)
+    arr = lambda xs: (PB * n)(*[PB() if x is None else ctypes.pointer(x) for x in xs])
+    st = load().soap_refresh_grouped(n, arr(Ls), arr(Rs), arr(QLs), arr(QRs), (MuonBatch * n)(*mbars), workspace_ptr,
+                                     ws_bytes, stream)
+    _check(st, "soap_refresh_grouped")
 
 
 def soap_precondition_workspace(count: int, rows: int, cols: int) -> int:

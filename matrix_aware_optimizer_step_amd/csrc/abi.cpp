@@ -859,7 +859,14 @@ hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int
 // columns  A_t <- (I - V T^T V^T) A_t  as  W = V^T A_t (split over the
 // reduction), W2 = [T^T ... T^T] [W_0; ...; W_s-1], A_t -= V W2.
 // Formation, last panel first:  Q_t <- (I - V T V^T) Q_t  from Q = I.
-muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, float* ws, const muon_batch_t* q,
+// Where a batched QR's Q factors go: matrices first .. first+count-1 of the
+// batch into the caller's batch q.
+struct QrOut {
+  const muon_batch_t* q;
+  int64_t first, count;
+};
+
+muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, float* ws, const QrOut* outs, int nouts,
                          hipStream_t s) {
   const QrLayout L = qr_layout(n);
   const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
@@ -920,8 +927,10 @@ muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, floa
                   h, h, nb, count, -1.f, 1.f, false, s),
              "qr formation update");
   }
-  SOAP_TRY(launch_sign_copy(ws + L.Q, L.total, ws + L.sgn, L.total, to_mat(q), static_cast<int32_t>(n), count, s),
-           "qr signs");
+  for (int o = 0; o < nouts; ++o)
+    SOAP_TRY(launch_sign_copy(ws + L.Q + outs[o].first * L.total, L.total, ws + L.sgn + outs[o].first * L.total,
+                              L.total, to_mat(outs[o].q), static_cast<int32_t>(n), outs[o].count, s),
+             "qr signs");
   return MUON_OK;
 }
 
@@ -963,7 +972,8 @@ muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* worksp
   SOAP_TRY(launch_gather(to_mat(a), P, round64(n * n), static_cast<int32_t>(n), static_cast<int32_t>(n), a->count,
                          s),
            "qr input");
-  if ((st = qr_enqueue(P, round64(n * n), n, a->count, ws, q, s)) != MUON_OK) return st;
+  const QrOut out{q, 0, a->count};
+  if ((st = qr_enqueue(P, round64(n * n), n, a->count, ws, &out, 1, s)) != MUON_OK) return st;
   return ok();
 }
 
@@ -987,58 +997,149 @@ muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, c
   return ok();
 }
 
-size_t soap_refresh_workspace(int64_t count, int64_t rows, int64_t cols, int with_l, int with_r) {
-  if (count < 1 || count > 65535 || rows < 1 || cols < 1 || rows > kMaxElems / cols) return 0;
-  if ((with_l && rows > kQrMaxDim) || (with_r && cols > kQrMaxDim)) return 0;
+size_t soap_refresh_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,
+                                      const int* with_l, const int* with_r) {
+  if (ngroups < 1 || ngroups > kMaxGroups || !counts || !rows || !cols || !with_l || !with_r) return 0;
+  int64_t tmp = 0;
+  std::vector<std::pair<int64_t, int64_t>> dims;  // (order, matrices of that order)
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t c = counts[g], m = rows[g], n = cols[g];
+    if (c < 1 || c > 65535 || m < 1 || n < 1 || m > kMaxElems / n) return 0;
+    if ((with_l[g] && m > kQrMaxDim) || (with_r[g] && n > kQrMaxDim)) return 0;
+    tmp += 2 * c * round64(m * n);
+    for (int side = 0; side < 2; ++side) {
+      if (!(side ? with_r[g] : with_l[g])) continue;
+      const int64_t d = side ? n : m;
+      auto it = std::find_if(dims.begin(), dims.end(), [d](const std::pair<int64_t, int64_t>& x) { return x.first == d; });
+      if (it == dims.end()) dims.emplace_back(d, c); else it->second += c;
+    }
+  }
   size_t side = 0;
-  if (with_l) side = std::max(side, qr_bytes(count, rows));
-  if (with_r) side = std::max(side, qr_bytes(count, cols));
-  return side + static_cast<size_t>(count * round64(rows * cols) * 4);
+  for (const auto& d : dims) {
+    if (d.second > 65535) return 0;
+    side = std::max(side, qr_bytes(d.second, d.first));
+  }
+  return side + static_cast<size_t>(tmp * 4);
+}
+
+size_t soap_refresh_workspace(int64_t count, int64_t rows, int64_t cols, int with_l, int with_r) {
+  return soap_refresh_grouped_workspace(1, &count, &rows, &cols, &with_l, &with_r);
+}
+
+muon_status_t soap_refresh_grouped(int ngroups, const muon_batch_t* const* Ls, const muon_batch_t* const* Rs,
+                                   const muon_batch_t* const* QLs, const muon_batch_t* const* QRs,
+                                   const muon_batch_t* mbars, void* workspace, size_t ws_bytes, void* stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!Ls || !Rs || !QLs || !QRs || !mbars)
+    return fail(MUON_ERR_INVALID_VALUE, "the per-group arrays must not be NULL");
+  muon_status_t st;
+  int64_t counts[kMaxGroups], rows[kMaxGroups], cols[kMaxGroups];
+  int wl[kMaxGroups], wr[kMaxGroups];
+  for (int g = 0; g < ngroups; ++g) {
+    const muon_batch_t* mb = &mbars[g];
+    if ((st = check_batch(mb, "mbar", false)) != MUON_OK) return in_group(st, g);
+    const int64_t c = mb->count, m = mb->rows, n = mb->cols;
+    if (!Ls[g] != !QLs[g] || !Rs[g] != !QRs[g])
+      return in_group(fail(MUON_ERR_INVALID_VALUE, "a statistic and its basis come together"), g);
+    if (Ls[g] && ((st = check_f32(Ls[g], "L", c, m, m)) != MUON_OK || (st = check_f32(QLs[g], "QL", c, m, m)) != MUON_OK))
+      return in_group(st, g);
+    if (Rs[g] && ((st = check_f32(Rs[g], "R", c, n, n)) != MUON_OK || (st = check_f32(QRs[g], "QR", c, n, n)) != MUON_OK))
+      return in_group(st, g);
+    counts[g] = c;
+    rows[g] = m;
+    cols[g] = n;
+    wl[g] = Ls[g] != nullptr;
+    wr[g] = Rs[g] != nullptr;
+  }
+  const size_t need = soap_refresh_grouped_workspace(ngroups, counts, rows, cols, wl, wr);
+  if (need == 0) return fail(MUON_ERR_UNSUPPORTED, "refresh sizes outside the supported range");
+  if ((st = check_workspace(workspace, ws_bytes, need)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  // two m x n temporaries per group for the first moment, then the region
+  // of the QR batch of each distinct order, reused order after order
+  float* t1[kMaxGroups];
+  float* t2[kMaxGroups];
+  float* cur = static_cast<float*>(workspace);
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t tm = round64(rows[g] * cols[g]);
+    t1[g] = cur;
+    t2[g] = cur + counts[g] * tm;
+    cur += 2 * counts[g] * tm;
+  }
+  float* region = cur;
+  std::vector<int64_t> orders;
+  for (int g = 0; g < ngroups; ++g) {
+    if (wl[g] && std::find(orders.begin(), orders.end(), rows[g]) == orders.end()) orders.push_back(rows[g]);
+    if (wr[g] && std::find(orders.begin(), orders.end(), cols[g]) == orders.end()) orders.push_back(cols[g]);
+  }
+  for (const int64_t d : orders) {
+    const int64_t pm = round64(d * d);
+    int64_t total = 0;
+    for (int g = 0; g < ngroups; ++g) total += counts[g] * ((wl[g] && rows[g] == d) + (wr[g] && cols[g] == d));
+    float* P = region;
+    float* qws = P + total * pm;
+    QrOut outs[2 * kMaxGroups];
+    int nouts = 0;
+    int64_t first = 0;
+    // power-iteration products and the first moment in the old bases:
+    // t1 = QL_old mbar, or mbar QR_old^T, or (both sides of this order) t2 = QL_old mbar QR_old^T
+    for (int g = 0; g < ngroups; ++g) {
+      const int64_t c = counts[g], m = rows[g], n = cols[g], tm = round64(m * n);
+      const bool l = wl[g] && m == d, r = wr[g] && n == d;
+      if (l) {
+        SOAP_TRY(gemm(op_batch(Ls[g], true), op_batch(QLs[g], false), out_ws(P + first * pm, pm, m), m, m, m, c, 1.f,
+                      0.f, false, s),
+                 "refresh power step L");
+        outs[nouts++] = QrOut{QLs[g], first, c};
+        first += c;
+        SOAP_TRY(gemm(op_batch(QLs[g], true), op_batch(&mbars[g], false), out_ws(t1[g], tm, n), m, n, m, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment L");
+      }
+      if (r) {
+        SOAP_TRY(gemm(op_batch(Rs[g], true), op_batch(QRs[g], false), out_ws(P + first * pm, pm, n), n, n, n, c, 1.f,
+                      0.f, false, s),
+                 "refresh power step R");
+        outs[nouts++] = QrOut{QRs[g], first, c};
+        first += c;
+        const SgemmOperand src = l ? op_ws(t1[g], tm, n, true) : op_batch(&mbars[g], true);
+        SOAP_TRY(gemm(src, op_batch(QRs[g], true), out_ws(l ? t2[g] : t1[g], tm, n), m, n, n, c, 1.f, 0.f, false, s),
+                 "refresh moment R");
+      }
+    }
+    if ((st = qr_enqueue(P, pm, d, total, qws, outs, nouts, s)) != MUON_OK) return st;
+    // the first moment into the new bases
+    for (int g = 0; g < ngroups; ++g) {
+      const int64_t c = counts[g], m = rows[g], n = cols[g], tm = round64(m * n);
+      const bool l = wl[g] && m == d, r = wr[g] && n == d;
+      if (l && r) {
+        SOAP_TRY(gemm(op_batch(QLs[g], false), op_ws(t2[g], tm, n, false), out_ws(t1[g], tm, n), m, n, m, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment L'");
+        SOAP_TRY(gemm(op_ws(t1[g], tm, n, true), op_batch(QRs[g], false), out_batch(&mbars[g]), m, n, n, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment R'");
+      } else if (l) {
+        SOAP_TRY(gemm(op_batch(QLs[g], false), op_ws(t1[g], tm, n, false), out_batch(&mbars[g]), m, n, m, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment L'");
+      } else if (r) {
+        SOAP_TRY(gemm(op_ws(t1[g], tm, n, true), op_batch(QRs[g], false), out_batch(&mbars[g]), m, n, n, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment R'");
+      }
+    }
+  }
+  return ok();
 }
 
 muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const muon_batch_t* QL,
                            const muon_batch_t* QR, const muon_batch_t* mbar, void* workspace, size_t ws_bytes,
                            void* stream) {
-  muon_status_t st;
-  if ((st = check_batch(mbar, "mbar", false)) != MUON_OK) return st;
-  const int64_t c = mbar->count, m = mbar->rows, n = mbar->cols;
-  if (!L != !QL || !R != !QR) return fail(MUON_ERR_INVALID_VALUE, "a statistic and its basis come together");
-  if (L && ((st = check_f32(L, "L", c, m, m)) != MUON_OK || (st = check_f32(QL, "QL", c, m, m)) != MUON_OK))
-    return st;
-  if (R && ((st = check_f32(R, "R", c, n, n)) != MUON_OK || (st = check_f32(QR, "QR", c, n, n)) != MUON_OK))
-    return st;
-  if ((st = check_workspace(workspace, ws_bytes, soap_refresh_workspace(c, m, n, L != nullptr, R != nullptr))) !=
-      MUON_OK)
-    return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  float* tmp = static_cast<float*>(workspace);
-  const int64_t tmat = round64(m * n);
-  float* P = tmp + c * tmat;
-  if (L) {
-    // P = L QL; tmp = QL_old Mbar; QL = qr(P); Mbar = QL_new^T tmp
-    const int64_t pm = round64(m * m);
-    float* ws = P + c * pm;
-    SOAP_TRY(gemm(op_batch(L, true), op_batch(QL, false), out_ws(P, pm, m), m, m, m, c, 1.f, 0.f, false, s),
-             "refresh power step L");
-    SOAP_TRY(gemm(op_batch(QL, true), op_batch(mbar, false), out_ws(tmp, tmat, n), m, n, m, c, 1.f, 0.f, false, s),
-             "refresh moment L");
-    if ((st = qr_enqueue(P, pm, m, c, ws, QL, s)) != MUON_OK) return st;
-    SOAP_TRY(gemm(op_batch(QL, false), op_ws(tmp, tmat, n, false), out_batch(mbar), m, n, m, c, 1.f, 0.f, false, s),
-             "refresh moment L'");
-  }
-  if (R) {
-    // P = R QR; tmp = Mbar QR_old^T; QR = qr(P); Mbar = tmp QR_new
-    const int64_t pm = round64(n * n);
-    float* ws = P + c * pm;
-    SOAP_TRY(gemm(op_batch(R, true), op_batch(QR, false), out_ws(P, pm, n), n, n, n, c, 1.f, 0.f, false, s),
-             "refresh power step R");
-    SOAP_TRY(gemm(op_batch(mbar, true), op_batch(QR, true), out_ws(tmp, tmat, n), m, n, n, c, 1.f, 0.f, false, s),
-             "refresh moment R");
-    if ((st = qr_enqueue(P, pm, n, c, ws, QR, s)) != MUON_OK) return st;
-    SOAP_TRY(gemm(op_ws(tmp, tmat, n, true), op_batch(QR, false), out_batch(mbar), m, n, n, c, 1.f, 0.f, false, s),
-             "refresh moment R'");
-  }
-  return ok();
+  if (!mbar) return fail(MUON_ERR_INVALID_VALUE, "mbar: descriptor is NULL");
+  return soap_refresh_grouped(1, &L, &R, &QL, &QR, mbar, workspace, ws_bytes, stream);
 }
 
 size_t soap_precondition_workspace(int64_t count, int64_t rows, int64_t cols) {

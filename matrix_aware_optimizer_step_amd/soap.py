@@ -64,6 +64,19 @@ def refresh(mbar, Lstat=None, Rstat=None, QL=None, QR=None, ws: torch.Tensor | N
     L.soap_refresh(*map(_desc, bs), ws.data_ptr(), ws.numel(), _stream(stream))
 
 
+def refresh_grouped(mbars, Lstats, Rstats, QLs, QRs, ws: torch.Tensor | None = None, stream=None) -> None:
+    """refresh() for up to 8 groups in one call: every QR of one order over
+    all groups and sides runs as one batched factorization."""
+    bm = [batch(x) for x in mbars]
+    bl, br, bql, bqr = ([None if x is None else batch(x) for x in xs] for xs in (Lstats, Rstats, QLs, QRs))
+    if ws is None:
+        need = L.soap_refresh_grouped_workspace([b.count for b in bm], [b.rows for b in bm], [b.cols for b in bm],
+                                                [x is not None for x in Lstats], [x is not None for x in Rstats])
+        ws = workspace(need, bm[0].keep[-1].device)
+    L.soap_refresh_grouped([_desc(b) for b in bl], [_desc(b) for b in br], [_desc(b) for b in bql],
+                           [_desc(b) for b in bqr], [b.desc for b in bm], ws.data_ptr(), ws.numel(), _stream(stream))
+
+
 def precondition(grad, mbar, vbar, out, step: int, QL=None, QR=None, beta1: float = BETA1, beta2: float = BETA2,
                  eps: float = EPS, ws: torch.Tensor | None = None, stream=None) -> None:
     """out = QL [Adam's direction of QL^T G QR in the rotated basis] QR^T."""
@@ -113,10 +126,20 @@ class SoapStep:
                   "QR": eye(n) if n <= max_dim else None,
                   "mbar": torch.zeros(c, m, n, **f), "vbar": torch.zeros(c, m, n, **f),
                   "D": torch.empty(c, m, n, **f)}
-            need = max(need, L.soap_precondition_workspace(c, m, n),
-                       L.soap_refresh_workspace(c, m, n, st["L"] is not None, st["R"] is not None))
+            need = max(need, L.soap_precondition_workspace(c, m, n))
             self.groups.append(st)
+        self.chunks = [[i for i in range(k, min(k + 8, len(self.groups))) if self._preconditioned(i)]
+                       for k in range(0, len(self.groups), 8)]
+        self.chunks = [ch for ch in self.chunks if ch]
+        for ch in self.chunks:
+            gs = [self.groups[i] for i in ch]
+            need = max(need, L.soap_refresh_grouped_workspace(
+                [g["D"].shape[0] for g in gs], [g["D"].shape[1] for g in gs], [g["D"].shape[2] for g in gs],
+                [g["L"] is not None for g in gs], [g["R"] is not None for g in gs]))
         self.ws = workspace(need, dev)
+
+    def _preconditioned(self, i) -> bool:
+        return self.groups[i]["L"] is not None or self.groups[i]["R"] is not None
 
     STATE = ("L", "R", "QL", "QR", "mbar", "vbar")
 
@@ -153,9 +176,10 @@ class SoapStep:
             statistics(g["G"], g["L"], g["R"], self.beta_s, stream=s)
         rec(1)
         if (self.t - 1) % self.freq == 0:
-            for g in self.groups:
-                if g["L"] is not None or g["R"] is not None:
-                    refresh(g["mbar"], g["L"], g["R"], g["QL"], g["QR"], ws=self.ws, stream=s)
+            for ch in self.chunks:
+                gs = [self.groups[i] for i in ch]
+                refresh_grouped([g["mbar"] for g in gs], [g["L"] for g in gs], [g["R"] for g in gs],
+                                [g["QL"] for g in gs], [g["QR"] for g in gs], ws=self.ws, stream=s)
         rec(2)
         for g in self.groups:
             precondition(g["G"], g["mbar"], g["vbar"], g["D"], self.t, g["QL"], g["QR"], self.beta1, self.beta2,

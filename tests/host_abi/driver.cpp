@@ -137,6 +137,33 @@ void soap_cases() {
     expect(soap_precondition(&g, pQL, pQR, &mb, &vb, &d, 0, 0.9f, 0.999f, 1e-8f, kWs, need, nullptr),
            MUON_ERR_INVALID_VALUE, "soap_precondition, step 0");
   }
+  {  // the 8B-style layer's groups in one grouped refresh, as the benchmark runs it
+    const int64_t counts[] = {2, 2, 2, 1}, rows[] = {4096, 1024, 14336, 4096}, cols[] = {4096, 4096, 4096, 14336};
+    const int wl[] = {1, 1, 0, 1}, wr[] = {1, 1, 1, 0};
+    std::vector<muon_batch_t> L, R, QL, QR, mb;
+    for (int g = 0; g < 4; ++g) {
+      L.push_back(batch(counts[g], rows[g], rows[g], MUON_F32));
+      QL.push_back(batch(counts[g], rows[g], rows[g], MUON_F32));
+      R.push_back(batch(counts[g], cols[g], cols[g], MUON_F32));
+      QR.push_back(batch(counts[g], cols[g], cols[g], MUON_F32));
+      mb.push_back(batch(counts[g], rows[g], cols[g], MUON_F32));
+    }
+    const muon_batch_t* pl[4];
+    const muon_batch_t* pr[4];
+    const muon_batch_t* pql[4];
+    const muon_batch_t* pqr[4];
+    for (int g = 0; g < 4; ++g) {
+      pl[g] = wl[g] ? &L[g] : nullptr;
+      pql[g] = wl[g] ? &QL[g] : nullptr;
+      pr[g] = wr[g] ? &R[g] : nullptr;
+      pqr[g] = wr[g] ? &QR[g] : nullptr;
+    }
+    const size_t need = soap_refresh_grouped_workspace(4, counts, rows, cols, wl, wr);
+    stub_set_workspace(kWs, need);
+    expect(soap_refresh_grouped(4, pl, pr, pql, pqr, mb.data(), kWs, need, nullptr), MUON_OK, "soap_refresh_grouped");
+    expect(soap_refresh_grouped(4, pl, pr, pql, pqr, mb.data(), kWs, need - 1, nullptr), MUON_ERR_WORKSPACE,
+           "soap_refresh_grouped, short workspace");
+  }
   for (int64_t n : {1, 5, 16, 17, 33, 100, 257, 300, 1024, 4096, 4200}) {
     for (int64_t count : {1, 3}) {
       const size_t need = soap_qr_workspace(count, n);

@@ -267,9 +267,15 @@ def test_soap_workspace_queries():
     assert L.soap_qr_workspace(2, 100) == 2 * L.soap_qr_workspace(1, 100)
     assert L.soap_precondition_workspace(3, 64, 96) == 2 * 3 * 64 * 96 * 4
     assert L.soap_precondition_workspace(1, 0, 5) == 0
-    # the refresh holds the moment's temporary plus the larger side's QR
-    assert L.soap_refresh_workspace(1, 64, 128, 1, 1) == 64 * 128 * 4 + L.soap_qr_workspace(1, 128)
-    assert L.soap_refresh_workspace(1, 64, 128, 1, 0) == 64 * 128 * 4 + L.soap_qr_workspace(1, 64)
+    # the refresh holds two moment temporaries plus the largest batched QR
+    # (both sides of one order factor together)
+    assert L.soap_refresh_workspace(1, 64, 128, 1, 1) == 2 * 64 * 128 * 4 + L.soap_qr_workspace(1, 128)
+    assert L.soap_refresh_workspace(1, 64, 128, 1, 0) == 2 * 64 * 128 * 4 + L.soap_qr_workspace(1, 64)
+    assert L.soap_refresh_workspace(2, 96, 96, 1, 1) == 2 * 2 * 96 * 96 * 4 + L.soap_qr_workspace(4, 96)
+    g = L.soap_refresh_grouped_workspace([2, 2, 1], [4096, 1024, 4096], [4096, 4096, 14336], [1, 1, 1], [1, 1, 0])
+    tmp = 2 * 4 * (2 * 4096 * 4096 + 2 * 1024 * 4096 + 4096 * 14336)
+    assert g == tmp + L.soap_qr_workspace(2 + 2 + 2 + 1, 4096)
+    assert L.soap_refresh_grouped_workspace([1] * 9, [64] * 9, [64] * 9, [1] * 9, [1] * 9) == 0
     assert L.soap_refresh_workspace(1, 64, 40000, 1, 1) == 0
     assert L.soap_refresh_workspace(1, 64, 40000, 1, 0) > 0
 
@@ -331,3 +337,19 @@ def test_soap_precondition_rejects_bad_arguments(kw, code):
     need = L.soap_precondition_workspace(c, m, n) + a["ws"]
     assert status_of(lambda: L.soap_precondition(g, ql, qr, st, st, d, a["step"], a["beta1"], a["beta2"], a["eps"],
                                                  FAKE, need, 0)) == code
+
+
+def test_soap_refresh_grouped_rejects_bad_arguments():
+    m, n = 64, 96
+    mb = [desc(count=2, rows=m, cols=n), desc(count=1, rows=n, cols=n)]
+    Ls = [desc(count=2, rows=m, cols=m), desc(count=1, rows=n, cols=n)]
+    Rs = [desc(count=2, rows=n, cols=n), None]
+    QLs = [desc(count=2, rows=m, cols=m), desc(count=1, rows=n, cols=n)]
+    QRs = [desc(count=2, rows=n, cols=n), None]
+    need = L.soap_refresh_grouped_workspace([2, 1], [m, n], [n, n], [1, 1], [1, 0])
+    assert status_of(lambda: L.soap_refresh_grouped(Ls, Rs, QLs, QRs, mb, FAKE, need - 1, 0)) == WORKSPACE
+    assert status_of(lambda: L.soap_refresh_grouped(Ls, Rs, [QLs[0], None], QRs, mb, FAKE, need, 0)) == INVALID
+    bad = [desc(count=2, rows=m, cols=n), desc(count=2, rows=n, cols=n)]
+    with pytest.raises(L.MuonError) as e:
+        L.soap_refresh_grouped(Ls, Rs, QLs, QRs, bad, FAKE, need, 0)
+    assert e.value.status == INVALID and "group 1" in str(e.value)

@@ -238,3 +238,43 @@ def test_soap_full_size_layer_matrices(mx, m, n, count, max_dim):
     worst, worst_q = run_steps(mx, m, n, steps=2, count=count, max_dim=max_dim, freq=1, eps=1e-2, tol=1e-4,
                                prior=float(sig2), seed=31)
     assert worst_q <= 1e-4
+
+
+def test_grouped_refresh_matches_per_group(mx):
+    """soap_refresh_grouped batches every QR of one order over groups and
+    sides (here order 96 is group 0's column side and group 1's row side);
+    it matches one refresh per group to fp32 round-off (the batched QR may
+    split its reductions differently) and the oracle to the step tolerance."""
+    from matrix_aware_optimizer_step_amd import soap
+    shapes = [(2, 64, 96), (1, 96, 40)]
+    rng = np.random.default_rng(5)
+
+    def spd(c, d):
+        G = rng.standard_normal((c, d, 2 * d))
+        return np.eye(d) + np.einsum("bij,bkj->bik", G, G) / (2 * d)
+
+    def orth(c, d):
+        return np.stack([np.linalg.qr(rng.standard_normal((d, d)))[0] for _ in range(c)])
+
+    host = [dict(L=spd(c, m), R=spd(c, n), QL=orth(c, m), QR=orth(c, n), M=rng.standard_normal((c, m, n)))
+            for c, m, n in shapes]
+    cu = lambda a: torch.from_numpy(a).float().cuda()
+    runs = []
+    for grouped in (False, True):
+        st = [{k: cu(v) for k, v in h.items()} for h in host]
+        if grouped:
+            soap.refresh_grouped([x["M"] for x in st], [x["L"] for x in st], [x["R"] for x in st],
+                                 [x["QL"] for x in st], [x["QR"] for x in st])
+        else:
+            for x in st:
+                soap.refresh(x["M"], x["L"], x["R"], x["QL"], x["QR"])
+        torch.cuda.synchronize()
+        runs.append(st)
+    for g, (c, m, n) in enumerate(shapes):
+        for i in range(c):
+            QLn, QRn, Mn = S.refresh(host[g]["L"][i], host[g]["R"][i], host[g]["QL"][i], host[g]["QR"][i],
+                                     host[g]["M"][i])
+            for k, want in (("QL", QLn), ("QR", QRn), ("M", Mn)):
+                a, b = f64(runs[0][g][k][i]), f64(runs[1][g][k][i])
+                assert rel(b, a) <= 1e-5, (g, i, k, rel(b, a))
+                assert rel(b, want) <= 1e-4, (g, i, k, rel(b, want))
