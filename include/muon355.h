@@ -35,7 +35,9 @@
  *   - All matrix memory and all workspaces are caller-owned DEVICE memory.
  *     The library never allocates, frees or synchronizes; every call only
  *     enqueues kernels on `stream` (a hipStream_t; NULL = the null stream)
- *     and returns.
+ *     and returns.  Debugging aid: with MUON355_DEBUG_SYNC=1 in
+ *     the environment every call waits for the work it enqueued and reports
+ *     a failed kernel as MUON_ERR_LAUNCH naming the call.
  *   - Matrices are row-major with a leading dimension `ld` (elements between
  *     consecutive rows, ld >= cols).  A batch holds `count` matrices of one
  *     shape and dtype: matrix i lives at ptrs[i] when `ptrs` is non-NULL (a

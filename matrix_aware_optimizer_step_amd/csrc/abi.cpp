@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -120,6 +121,19 @@ bool finite(float x) { return std::isfinite(x); }
 muon_status_t launch_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(MUON_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
   return MUON_OK;
+}
+
+// With MUON355_DEBUG_SYNC=1 in the environment every entry point waits for
+// the work it enqueued and reports a failed kernel as MUON_ERR_LAUNCH naming
+// the call.  A debugging aid only: otherwise the library never synchronizes.
+muon_status_t done(hipStream_t s, const char* what) {
+  const char* v = std::getenv("MUON355_DEBUG_SYNC");
+  if (v && v[0] == '1' && v[1] == '\0') {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(MUON_ERR_LAUNCH, "%s (debug sync): %s", what, hipGetErrorString(e));
+  }
+  return ok();
 }
 
 // ------------------------------------------------------------ NS workspace plan
@@ -299,7 +313,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
       ca.cols = p.cols;
       if ((e = launch_copy_out(ca, p.count, stream)) != hipSuccess) return launch_status(e, "copy out");
     }
-    return ok();
+    return done(stream, "run_orthogonalize");
   }
 
   // 2. X_0 = N / (||N|| + eps) into the padded buffers (X, and X^T where the update reads it)
@@ -439,7 +453,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
       }
     }
   }
-  return ok();
+  return done(stream, "run_orthogonalize");
 }
 
 }  // namespace
@@ -486,7 +500,7 @@ muon_status_t muon_adamw(const muon_tensor_list_t* t, int64_t step, float lr, fl
   a.decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
   const hipError_t e = launch_adamw(a, t->total_chunks, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return launch_status(e, "adamw");
-  return ok();
+  return done(static_cast<hipStream_t>(stream), "muon_adamw");
 }
 
 const char* muon_status_string(muon_status_t s) {
@@ -599,7 +613,7 @@ muon_status_t muon_momentum(const muon_batch_t* grad, const muon_batch_t* mom, c
   if (e != hipSuccess) return launch_status(e, "momentum");
   e = launch_sumsq_finalize(a.partials, a.blocks_per_mat, sumsq, grad->count, s);
   if (e != hipSuccess) return launch_status(e, "sumsq finalize");
-  return ok();
+  return done(s, "muon_momentum");
 }
 
 size_t muon_momentum_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
@@ -657,7 +671,7 @@ muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads, cons
   if (e != hipSuccess) return launch_status(e, "momentum");
   e = launch_sumsq_finalize_grouped(F, s);
   if (e != hipSuccess) return launch_status(e, "sumsq finalize");
-  return ok();
+  return done(s, "muon_momentum_grouped");
 }
 
 size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols, int32_t compute) {
@@ -699,7 +713,7 @@ muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho, 
   if ((st = prepare_apply(weight, ortho, lr, weight_decay, mode, coeff, &a, &vec)) != MUON_OK) return st;
   hipError_t e = launch_apply(a, weight->count, vec, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return launch_status(e, "apply");
-  return ok();
+  return done(static_cast<hipStream_t>(stream), "muon_apply");
 }
 
 muon_status_t muon_apply_grouped(int ngroups, const muon_batch_t* weights, const muon_batch_t* orthos, float lr,
@@ -722,7 +736,7 @@ muon_status_t muon_apply_grouped(int ngroups, const muon_batch_t* weights, const
     return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)G.first[ngroups]);
   hipError_t e = launch_apply_grouped(G, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return launch_status(e, "apply");
-  return ok();
+  return done(static_cast<hipStream_t>(stream), "muon_apply_grouped");
 }
 
 }  // extern "C"
@@ -974,7 +988,7 @@ muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* worksp
            "qr input");
   const QrOut out{q, 0, a->count};
   if ((st = qr_enqueue(P, round64(n * n), n, a->count, ws, &out, 1, s)) != MUON_OK) return st;
-  return ok();
+  return done(s, "soap_qr");
 }
 
 muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, const muon_batch_t* R, float beta_s,
@@ -994,7 +1008,7 @@ muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, c
     SOAP_TRY(gemm(op_batch(grad, false), op_batch(grad, false), out_batch(R), n, n, m, c, 1.f - beta_s, beta_s, true,
                   s),
              "statistics R");
-  return ok();
+  return done(s, "soap_statistics");
 }
 
 size_t soap_refresh_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,
@@ -1132,7 +1146,7 @@ muon_status_t soap_refresh_grouped(int ngroups, const muon_batch_t* const* Ls, c
       }
     }
   }
-  return ok();
+  return done(s, "soap_refresh_grouped");
 }
 
 muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const muon_batch_t* QL,
@@ -1210,7 +1224,7 @@ muon_status_t soap_precondition(const muon_batch_t* grad, const muon_batch_t* QL
     SOAP_TRY(gemm(op_ws(w2, wm, n, true), op_batch(QR, true), out_batch(dir), m, n, n, c, 1.f, 0.f, false, s),
              "rotate back right");
   }
-  return ok();
+  return done(s, "soap_precondition");
 }
 
 }  // extern "C"

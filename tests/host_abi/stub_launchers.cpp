@@ -46,6 +46,8 @@ extern "C" void stub_set_workspace(const void* base, size_t bytes) {
 }
 extern "C" long stub_launches() { return g_launches; }
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub"; }
+extern "C" hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+extern "C" hipError_t hipGetLastError() { return hipSuccess; }
 
 namespace muon {
 

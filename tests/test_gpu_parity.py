@@ -511,3 +511,60 @@ def test_zero_gradient_step_is_pure_decay(mx):
     assert torch.count_nonzero(step.ortho_buffers[0]).item() == 0
     want = f64(W0) * (1 - 0.01 * 0.5) ** 3
     assert rel(f64(W), want) <= TOL_EW
+
+
+# ------------------------------------------------ hyperparameter groups, debug sync
+
+def f32(x):
+    return float(np.float32(x))
+
+
+def test_groups_with_different_hyperparameters(mx):
+    """Two optimizer groups with different momentum, Nesterov, step count,
+    coefficients, shape factor, learning rate and decay, stepped in turn on
+    one stream for two steps: each matches the oracle run with its own
+    hyperparameters (the library holds no state between calls)."""
+    hp = [dict(beta=0.9, nesterov=False, steps=4, coeffs=(3.4445, -4.7750, 2.0315), lr=0.5, weight_decay=0.2,
+               mode=mx.MUON_SCALE_ORIGINAL, coeff=0.2),
+          dict(beta=0.95, nesterov=True, steps=6, coeffs=(2.0, -1.5, 0.5), lr=1.0, weight_decay=0.0,
+               mode=mx.MUON_SCALE_MATCH_RMS, coeff=0.16)]
+    shapes = [(2, 96, 160), (1, 200, 72)]
+    gen = torch.Generator().manual_seed(11)
+    W0 = [0.02 * torch.randn(*s, generator=gen) for s in shapes]
+    Gs = [[torch.randn(*s, generator=gen) for s in shapes] for _ in range(2)]
+    Wd = [w.clone().cuda() for w in W0]
+    Gd = [torch.empty(*s, device="cuda") for s in shapes]
+    steps = [mx.MuonStep([(Wd[k], Gd[k])], compute=mx.MUON_F32, **hp[k]) for k in range(2)]
+    Wo = [[f64(W0[k][i]) for i in range(shapes[k][0])] for k in range(2)]
+    Mo = [[np.zeros(shapes[k][1:]) for _ in range(shapes[k][0])] for k in range(2)]
+    for t in range(2):
+        for k in range(2):
+            Gd[k].copy_(Gs[t][k])
+            steps[k].step()
+        torch.cuda.synchronize()
+        for k in range(2):
+            h = {key: (f32(v) if isinstance(v, float) else v) for key, v in hp[k].items()}
+            for i in range(shapes[k][0]):
+                Wo[k][i], Mo[k][i], _, _ = O.muon_step(Wo[k][i], Mo[k][i], f64(Gs[t][k][i]), **h)
+                assert rel(f64(Wd[k][i]), Wo[k][i]) <= 1e-5, (t, k, i)
+
+
+def test_debug_sync_gives_the_same_results(mx, monkeypatch):
+    """With MUON355_DEBUG_SYNC=1 every entry point waits for its kernels and
+    checks them; the results are bit-identical to the asynchronous run."""
+    outs = []
+    for flag in (None, "1"):
+        if flag is None:
+            monkeypatch.delenv("MUON355_DEBUG_SYNC", raising=False)
+        else:
+            monkeypatch.setenv("MUON355_DEBUG_SYNC", flag)
+        gen = torch.Generator().manual_seed(5)
+        W = (0.02 * torch.randn(2, 130, 300, generator=gen)).to(torch.bfloat16).cuda()
+        G = torch.randn(2, 130, 300, generator=gen).to(torch.bfloat16).cuda()
+        st = mx.MuonStep([(W, G)], compute=mx.MUON_BF16, lr=0.01, weight_decay=0.1)
+        st.step()
+        st.step()
+        torch.cuda.synchronize()
+        outs.append(W.clone())
+    monkeypatch.delenv("MUON355_DEBUG_SYNC", raising=False)
+    assert torch.equal(outs[0], outs[1])
