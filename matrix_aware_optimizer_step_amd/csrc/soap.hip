@@ -108,6 +108,77 @@ __device__ __forceinline__ void store_slice(float* S, const SgemmOperand& o, con
   }
 }
 
+// Fast path, for operands whose every 4-element run along the contiguous
+// index is aligned and inside the row (leading dimension and both extents
+// multiples of 4): element type and orientation are template arguments and
+// each run is one vector load from clamped indices, zeroed by a select when
+// out of range.  No branch separates a load from its use, so the loads of
+// the next slice stay in flight during the products.
+template <bool BF16>
+__device__ __forceinline__ void load4_fast(const char* p, int64_t idx, float* v) {
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p + idx * 2);
+    v[0] = bf16f(u.x & 0xffffu);
+    v[1] = bf16f(u.x >> 16);
+    v[2] = bf16f(u.y & 0xffffu);
+    v[3] = bf16f(u.y >> 16);
+  } else {
+    const float4 f = *reinterpret_cast<const float4*>(p + idx * 4);
+    v[0] = f.x;
+    v[1] = f.y;
+    v[2] = f.z;
+    v[3] = f.w;
+  }
+}
+
+template <int OUT, bool BF16, bool KC>
+__device__ __forceinline__ void load_slice_fast(const char* p, int64_t ld, int outer, int klim, int o0, int k0,
+                                                float* r) {
+  constexpr int kRuns = OUT * kBK / 4;
+  constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int t = threadIdx.x + kThreads * g;
+    if (kRuns % kThreads != 0 && t >= kRuns) continue;
+    const int row = KC ? o0 + t / 4 : k0 + t / (OUT / 4);
+    const int col = KC ? k0 + 4 * (t % 4) : o0 + 4 * (t % (OUT / 4));
+    const int rows = KC ? outer : klim, cols = KC ? klim : outer;
+    const bool in = row < rows && col < cols;
+    float v[4];
+    load4_fast<BF16>(p, static_cast<int64_t>(min(row, rows - 1)) * ld + min(col, cols - 4), v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[4 * g + e] = in ? v[e] : 0.f;
+  }
+}
+
+template <int OUT, bool KC>
+__device__ __forceinline__ void store_slice_fast(float* S, const float* r) {
+  constexpr int kRuns = OUT * kBK / 4;
+  constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kP = OUT + 4;
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int t = threadIdx.x + kThreads * g;
+    if (kRuns % kThreads != 0 && t >= kRuns) continue;
+    if constexpr (KC) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kP + t / 4] = r[4 * g + e];
+    } else {
+      *reinterpret_cast<float4*>(S + (t / (OUT / 4)) * kP + 4 * (t % (OUT / 4))) =
+          make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
+    }
+  }
+}
+
+// Operand configuration of the fast path: bit 0 A bf16, bit 1 A kcontig,
+// bit 2 B bf16, bit 3 B kcontig; -1 = the generic path.
+template <int CFG>
+struct FastCfg {
+  static constexpr bool kOn = CFG >= 0;
+  static constexpr bool kAB = CFG >= 0 && (CFG & 1), kAK = CFG >= 0 && (CFG & 2);
+  static constexpr bool kBB = CFG >= 0 && (CFG & 4), kBK = CFG >= 0 && (CFG & 8);
+};
+
 __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
   const char* p = o.ptrs ? static_cast<const char*>(o.ptrs[b]) : o.base + static_cast<int64_t>(b) * o.stride;
   return p + o.off;
@@ -115,8 +186,9 @@ __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
 
 // TM x 128 output tile, four waves: TM = 128 as 2 x 2 waves of 64 x 64,
 // TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.
-template <int TM>
+template <int TM, int CFG>
 __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
+  using F = FastCfg<CFG>;
   constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
   constexpr int FI = TM / WM / 32, FJ = kT / WN / 32;
   constexpr int kPA = TM + 4;
@@ -146,18 +218,26 @@ __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
   float ra[(TM * kBK / 4 + kThreads - 1) / kThreads * 4], rb[8];
-  if (kbeg < kend) {
-    load_slice<TM>(pa, a.a, a.M, kend, i0, kbeg, ra);
-    load_slice<kT>(pb, a.b, a.N, kend, j0, kbeg, rb);
-  }
-  for (int k0 = kbeg; k0 < kend; k0 += kBK) {
-    store_slice<TM>(As, a.a, ra);
-    store_slice<kT>(Bs, a.b, rb);
-    __syncthreads();
-    if (k0 + kBK < kend) {  // next slice in flight during the products
-      load_slice<TM>(pa, a.a, a.M, kend, i0, k0 + kBK, ra);
-      load_slice<kT>(pb, a.b, a.N, kend, j0, k0 + kBK, rb);
+  auto load = [&](int k0) {
+    if constexpr (F::kOn) {
+      load_slice_fast<TM, F::kAB, F::kAK>(pa, a.a.ld, a.M, kend, i0, k0, ra);
+      load_slice_fast<kT, F::kBB, F::kBK>(pb, a.b.ld, a.N, kend, j0, k0, rb);
+    } else {
+      load_slice<TM>(pa, a.a, a.M, kend, i0, k0, ra);
+      load_slice<kT>(pb, a.b, a.N, kend, j0, k0, rb);
     }
+  };
+  if (kbeg < kend) load(kbeg);
+  for (int k0 = kbeg; k0 < kend; k0 += kBK) {
+    if constexpr (F::kOn) {
+      store_slice_fast<TM, F::kAK>(As, ra);
+      store_slice_fast<kT, F::kBK>(Bs, rb);
+    } else {
+      store_slice<TM>(As, a.a, ra);
+      store_slice<kT>(Bs, a.b, rb);
+    }
+    __syncthreads();
+    if (k0 + kBK < kend) load(k0 + kBK);  // next slice in flight during the products
 #pragma unroll
     for (int kk = 0; kk < kBK / 2; ++kk) {
       // lane: A[i = l32][k = half] and B[k = half][j = l32] of each 32 x 2 step
@@ -563,13 +643,49 @@ __global__ __launch_bounds__(256) void rot_adam_kernel(RotAdamArgs a) {
 
 }  // namespace
 
+namespace {
+
+template <int TM, int CFG>
+void launch_cfg(const SgemmArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((sgemm_kernel<TM, CFG>), grid, dim3(kThreads), 0, stream, a);
+}
+
+template <int TM, int CFG = 0>
+void launch_fast(int cfg, const SgemmArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (CFG < 16) {
+    if (cfg == CFG)
+      launch_cfg<TM, CFG>(a, grid, stream);
+    else
+      launch_fast<TM, CFG + 1>(cfg, a, grid, stream);
+  }
+}
+
+// The fast path needs every 4-element run aligned and inside its row: both
+// operands' vector flag, and K plus each operand's outer extent along its
+// contiguous index a multiple of 4.
+int fast_cfg(const SgemmArgs& a) {
+  const bool ok = a.a.vec && a.b.vec && a.K % 4 == 0 && (a.a.kcontig || a.M % 4 == 0) &&
+                  (a.b.kcontig || a.N % 4 == 0) && !a.a.ptrs && !a.b.ptrs;
+  if (!ok) return -1;
+  return (a.a.dtype ? 1 : 0) | (a.a.kcontig ? 2 : 0) | (a.b.dtype ? 4 : 0) | (a.b.kcontig ? 8 : 0);
+}
+
+}  // namespace
+
 hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream) {
+  const int cfg = fast_cfg(a);
   if (a.M <= 32 && !a.sym) {
     const dim3 grid((a.N + kT - 1) / kT, (a.M + 31) / 32, a.count * a.splits);
-    hipLaunchKernelGGL(sgemm_kernel<32>, grid, dim3(kThreads), 0, stream, a);
+    if (cfg >= 0)
+      launch_fast<32>(cfg, a, grid, stream);
+    else
+      launch_cfg<32, -1>(a, grid, stream);
   } else {
     const dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT, a.count * a.splits);
-    hipLaunchKernelGGL(sgemm_kernel<kT>, grid, dim3(kThreads), 0, stream, a);
+    if (cfg >= 0)
+      launch_fast<kT>(cfg, a, grid, stream);
+    else
+      launch_cfg<kT, -1>(a, grid, stream);
   }
   return hipGetLastError();
 }
