@@ -781,7 +781,7 @@ QrLayout qr_layout(int64_t n) {
 
 // Split-K plan for a reduction of length K over `tiles` output tiles of
 // `count` matrices: enough splits for about 512 workgroups, each split at
-// least 64 deep, a multiple of the 16-deep k-slice.
+// least 64 deep, a multiple of the k-slice depth.
 int plan_splits(int64_t K, int64_t tiles, int64_t count, int* ksplit) {
   int64_t want = (512 + tiles * count - 1) / (tiles * count);
   want = std::min<int64_t>(want, kMaxSplits);

@@ -295,7 +295,7 @@ struct SgemmArgs {
   int32_t pad_;
 };
 constexpr int kSgemmTile = 128;
-constexpr int kSgemmBK = 16;
+constexpr int kSgemmBK = 32;
 hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream);
 
 // Householder QR, one 16-column panel of `count` n x n matrices (row-major,

@@ -28,7 +28,7 @@ namespace {
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kT = kSgemmTile;      // 128 x 128 output tile
-constexpr int kBK = kSgemmBK;       // 16-deep k-slices
+constexpr int kBK = kSgemmBK;       // 32-deep k-slices
 constexpr int kPitch = kT + 4;      // LDS row pitch in floats
 constexpr int kThreads = 256;       // 4 waves, 2 x 2, each 64 x 64
 
@@ -67,32 +67,34 @@ __device__ __forceinline__ void load_run(const char* p, const SgemmOperand& o, i
   }
 }
 
-// One OUT (outer) x 16 (reduction) slice of an operand into registers,
-// OUT/64 runs of four per thread (threads beyond OUT*4 runs idle): outer
+// One OUT (outer) x kBK (reduction) slice of an operand into registers,
+// OUT*kBK/1024 runs of four per thread (threads beyond the runs idle): outer
 // rows o0.. (of `outer`), reduction k0.. (below klim).
 template <int OUT>
 __device__ __forceinline__ void load_slice(const char* p, const SgemmOperand& o, int outer, int klim, int o0,
                                            int k0, float* r) {
   constexpr int kRuns = OUT * kBK / 4;
   constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kRPR = kBK / 4;  // runs per row of a k-contiguous operand
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     const int t = threadIdx.x + kThreads * g;
     if (kRuns % kThreads != 0 && t >= kRuns) continue;
     if (o.kcontig)
-      load_run(p, o, o0 + t / 4, k0 + 4 * (t % 4), outer, klim, r + 4 * g);
+      load_run(p, o, o0 + t / kRPR, k0 + 4 * (t % kRPR), outer, klim, r + 4 * g);
     else
       load_run(p, o, k0 + t / (OUT / 4), o0 + 4 * (t % (OUT / 4)), klim, outer, r + 4 * g);
   }
 }
 
 // The slice into LDS as S[k][outer] (pitch OUT + 4).  For OUT = 128 the
-// scattered form (kcontig) writes 64 distinct banks per wave: address mod
-// 64 is 16*(t%4) + 4e + t/4 for lanes t of one wave.
+// scattered form (kcontig, eight runs per row) touches each bank at most
+// twice per wave: address mod 64 is 16*(t%8) + 4e + t/8 for lanes t.
 template <int OUT>
 __device__ __forceinline__ void store_slice(float* S, const SgemmOperand& o, const float* r) {
   constexpr int kRuns = OUT * kBK / 4;
   constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kRPR = kBK / 4;  // runs per row of a k-contiguous operand
   constexpr int kP = OUT + 4;
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
@@ -100,7 +102,7 @@ __device__ __forceinline__ void store_slice(float* S, const SgemmOperand& o, con
     if (kRuns % kThreads != 0 && t >= kRuns) continue;
     if (o.kcontig) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kP + t / 4] = r[4 * g + e];
+      for (int e = 0; e < 4; ++e) S[(4 * (t % kRPR) + e) * kP + t / kRPR] = r[4 * g + e];
     } else {
       *reinterpret_cast<float4*>(S + (t / (OUT / 4)) * kP + 4 * (t % (OUT / 4))) =
           make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
@@ -136,12 +138,13 @@ __device__ __forceinline__ void load_slice_fast(const char* p, int64_t ld, int o
                                                 float* r) {
   constexpr int kRuns = OUT * kBK / 4;
   constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kRPR = kBK / 4;  // runs per row of a k-contiguous operand
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
     const int t = threadIdx.x + kThreads * g;
     if (kRuns % kThreads != 0 && t >= kRuns) continue;
-    const int row = KC ? o0 + t / 4 : k0 + t / (OUT / 4);
-    const int col = KC ? k0 + 4 * (t % 4) : o0 + 4 * (t % (OUT / 4));
+    const int row = KC ? o0 + t / kRPR : k0 + t / (OUT / 4);
+    const int col = KC ? k0 + 4 * (t % kRPR) : o0 + 4 * (t % (OUT / 4));
     const int rows = KC ? outer : klim, cols = KC ? klim : outer;
     const bool in = row < rows && col < cols;
     float v[4];
@@ -155,6 +158,7 @@ template <int OUT, bool KC>
 __device__ __forceinline__ void store_slice_fast(float* S, const float* r) {
   constexpr int kRuns = OUT * kBK / 4;
   constexpr int kG = (kRuns + kThreads - 1) / kThreads;
+  constexpr int kRPR = kBK / 4;  // runs per row of a k-contiguous operand
   constexpr int kP = OUT + 4;
 #pragma unroll
   for (int g = 0; g < kG; ++g) {
@@ -162,7 +166,7 @@ __device__ __forceinline__ void store_slice_fast(float* S, const float* r) {
     if (kRuns % kThreads != 0 && t >= kRuns) continue;
     if constexpr (KC) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) S[(4 * (t % 4) + e) * kP + t / 4] = r[4 * g + e];
+      for (int e = 0; e < 4; ++e) S[(4 * (t % kRPR) + e) * kP + t / kRPR] = r[4 * g + e];
     } else {
       *reinterpret_cast<float4*>(S + (t / (OUT / 4)) * kP + 4 * (t % (OUT / 4))) =
           make_float4(r[4 * g], r[4 * g + 1], r[4 * g + 2], r[4 * g + 3]);
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
-  float ra[(TM * kBK / 4 + kThreads - 1) / kThreads * 4], rb[8];
+  float ra[(TM * kBK / 4 + kThreads - 1) / kThreads * 4], rb[(kT * kBK / 4 + kThreads - 1) / kThreads * 4];
   auto load = [&](int k0) {
     if constexpr (F::kOn) {
       load_slice_fast<TM, F::kAB, F::kAK>(pa, a.a.ld, a.M, kend, i0, k0, ra);
