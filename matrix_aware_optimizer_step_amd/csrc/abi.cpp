@@ -755,26 +755,31 @@ constexpr int kMaxSplits = 16;
 
 int64_t round64(int64_t x) { return (x + 63) / 64 * 64; }
 
-// Floats of one panel's reflector slot: kQrPanel columns of up to n rows,
-// column-major with column pitch n.
-int64_t qr_vslot(int64_t n) { return round64(int64_t{kQrPanel} * n); }
+// Floats of one panel's reflector slot: kQrPanel columns of n rows,
+// column-major with column pitch n and absolute row indices.  The slots of
+// one matrix are contiguous, so the reflectors of an outer block form one
+// (block width) x n matrix with leading dimension n.
+int64_t qr_vslot(int64_t n) { return int64_t{kQrPanel} * n; }
 
 // Per-matrix float offsets of the QR scratch for an n x n factorization.
 struct QrLayout {
-  int64_t V, Q, W, W2, TT, TQ, sgn, total;
+  int64_t V, Q, W, W2, TT, TQ, Y, sgn, tau, total;
 };
 
 QrLayout qr_layout(int64_t n) {
   const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
+  const int64_t blocks = (n + kQrOuter - 1) / kQrOuter;
   QrLayout L;
   int64_t o = 0;
-  L.V = o;   o += panels * qr_vslot(n);
+  L.V = o;   o += round64(panels * qr_vslot(n));
   L.Q = o;   o += round64(n * n);
-  L.W = o;   o += round64(int64_t{kMaxSplits} * kQrPanel * n);
-  L.W2 = o;  o += round64(int64_t{kQrPanel} * n);
-  L.TT = o;  o += round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
-  L.TQ = o;  o += panels * round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
+  L.W = o;   o += round64(int64_t{kMaxSplits} * kQrOuter * n);
+  L.W2 = o;  o += round64(int64_t{kQrOuter} * n);
+  L.TT = o;  o += round64(int64_t{kQrOuter} * kQrOuter * kMaxSplits);
+  L.TQ = o;  o += blocks * round64(int64_t{kQrOuter} * kQrOuter * kMaxSplits);
+  L.Y = o;   o += round64(int64_t{kQrOuter} * kQrOuter);
   L.sgn = o; o += round64(n);
+  L.tau = o; o += round64(n);
   L.total = o;
   return L;
 }
@@ -867,12 +872,6 @@ hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int
     if (e_ != hipSuccess) return launch_status(e_, what);     \
   } while (0)
 
-// Q factor (R's diagonal made non-negative) of the n x n matrices in P
-// (contiguous, p_mat floats apart; overwritten), written to `q`.
-// Factorization: per 16-column panel, the panel kernel, then the trailing
-// columns  A_t <- (I - V T^T V^T) A_t  as  W = V^T A_t (split over the
-// reduction), W2 = [T^T ... T^T] [W_0; ...; W_s-1], A_t -= V W2.
-// Formation, last panel first:  Q_t <- (I - V T V^T) Q_t  from Q = I.
 // Where a batched QR's Q factors go: matrices first .. first+count-1 of the
 // batch into the caller's batch q.
 struct QrOut {
@@ -880,65 +879,113 @@ struct QrOut {
   int64_t first, count;
 };
 
+// Q factor (R's diagonal made non-negative) of the n x n matrices in P
+// (contiguous, p_mat floats apart; overwritten), written to the outputs.
+// Two-level blocked Householder QR in the compact WY form I - V T V^T:
+//  - each 128-column outer block is reduced 16 columns at a time by the
+//    panel kernel, each panel's reflectors applied at once to the rest of
+//    the block (W = V^T A_blk, W2 = T^T W, A_blk -= V W2);
+//  - the block's factor T comes from the Gram matrix of its reflectors, and
+//    the trailing matrix is updated once per block: W = V^T A_t (split over
+//    the reduction), W2 = [T^T ... T^T] [W_0; ...], A_t -= V W2;
+//  - Q is formed from the identity, last block first: Q_t -= V (T (V^T Q_t)).
+// V is kept transposed (rows are reflectors), so V^T X is the product of the
+// k-contiguous operand V with X.
 muon_status_t qr_enqueue(float* P, int64_t p_mat, int64_t n, int64_t count, float* ws, const QrOut* outs, int nouts,
                          hipStream_t s) {
   const QrLayout L = qr_layout(n);
-  const int64_t panels = (n + kQrPanel - 1) / kQrPanel;
-  const int64_t tslot = round64(int64_t{kQrPanel} * kQrPanel * kMaxSplits);
-  auto ntiles = [](int64_t x) { return (x + kSgemmTile - 1) / kSgemmTile; };
   const int64_t vslot = qr_vslot(n);
-  for (int64_t p = 0; p < panels; ++p) {
-    const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0, nt = h - nb;
-    int ks_f = 0, ks_q = 0;
-    const int sf = nt > 0 ? plan_splits(h, ntiles(nt), count, &ks_f) : 1;
-    const int sq = plan_splits(h, ntiles(h), count, &ks_q);
-    float* V = ws + L.V + p * vslot;  // the panel's reflectors, column-major (pitch n)
-    QrPanelArgs a;
-    std::memset(&a, 0, sizeof(a));
-    a.A = P;
-    a.a_mat = p_mat;
-    a.V = V;
-    a.v_mat = L.total;
-    a.TrepT = ws + L.TT;
-    a.tT_mat = L.total;
-    a.TrepQ = ws + L.TQ + p * tslot;
-    a.tQ_mat = L.total;
-    a.sgn = ws + L.sgn;
-    a.s_mat = L.total;
-    a.n = static_cast<int32_t>(n);
-    a.c0 = static_cast<int32_t>(c0);
-    a.reps_t = sf;
-    a.reps_q = sq;
-    SOAP_TRY(launch_qr_panel(a, count, s), "qr panel");
-    if (nt > 0) {
-      const int64_t ao = c0 * n + c0;
-      // V^T as an M x K operand is the slot's rows (kcontig); V as h x nb is its transpose
-      SOAP_TRY(gemm(op_ws(V, L.total, n, true), op_ws(P, p_mat, n, false, ao + nb), out_ws(ws + L.W, L.total, nt),
-                    nb, nt, h, count, 1.f, 0.f, false, s, sf, ks_f, nb * nt),
+  const int64_t tslot = round64(int64_t{kQrOuter} * kQrOuter * kMaxSplits);
+  auto ntiles = [](int64_t x) { return (x + kSgemmTile - 1) / kSgemmTile; };
+  for (int64_t c0o = 0; c0o < n; c0o += kQrOuter) {
+    const int64_t bw = std::min<int64_t>(kQrOuter, n - c0o), ho = n - c0o, nto = ho - bw;
+    float* Vo = ws + L.V + (c0o / kQrPanel) * vslot;  // the block's reflectors, bw x n
+    for (int64_t c1 = c0o; c1 < c0o + bw; c1 += kQrPanel) {
+      const int64_t nb = std::min<int64_t>(kQrPanel, n - c1), h = n - c1, w = c0o + bw - c1 - nb;
+      int ks = 0;
+      const int si = w > 0 ? plan_splits(h, ntiles(w), count, &ks) : 1;
+      float* Vp = ws + L.V + (c1 / kQrPanel) * vslot;
+      QrPanelArgs a;
+      std::memset(&a, 0, sizeof(a));
+      a.A = P;
+      a.a_mat = p_mat;
+      a.V = Vp + c1;
+      a.v_mat = L.total;
+      a.TrepT = ws + L.TT;
+      a.tT_mat = L.total;
+      a.TrepQ = ws + L.TT;  // not written: reps_q = 0
+      a.tQ_mat = L.total;
+      a.sgn = ws + L.sgn;
+      a.tau = ws + L.tau;
+      a.s_mat = L.total;
+      a.n = static_cast<int32_t>(n);
+      a.c0 = static_cast<int32_t>(c1);
+      a.reps_t = si;
+      a.reps_q = 0;
+      a.zpre = static_cast<int32_t>(c1 - c0o);
+      SOAP_TRY(launch_qr_panel(a, count, s), "qr panel");
+      if (w > 0) {
+        const int64_t ao = c1 * n + c1 + nb;
+        SOAP_TRY(gemm(op_ws(Vp, L.total, n, true, c1), op_ws(P, p_mat, n, false, ao), out_ws(ws + L.W, L.total, w), nb,
+                      w, h, count, 1.f, 0.f, false, s, si, ks, nb * w),
+                 "qr panel update product");
+        SOAP_TRY(gemm(op_ws(ws + L.TT, L.total, nb * si, true), op_ws(ws + L.W, L.total, w, false),
+                      out_ws(ws + L.W2, L.total, w), nb, w, nb * si, count, 1.f, 0.f, false, s),
+                 "qr panel update factor");
+        SOAP_TRY(gemm(op_ws(Vp, L.total, n, false, c1), op_ws(ws + L.W2, L.total, w, false),
+                      out_ws(P, p_mat, n, ao), h, w, nb, count, -1.f, 1.f, false, s),
+                 "qr panel update");
+      }
+    }
+    int ks_o = 0, ks_q = 0;
+    const int so = nto > 0 ? plan_splits(ho, ntiles(nto), count, &ks_o) : 1;
+    const int sq = plan_splits(ho, ntiles(ho), count, &ks_q);
+    SOAP_TRY(gemm(op_ws(Vo, L.total, n, true, c0o), op_ws(Vo, L.total, n, true, c0o), out_ws(ws + L.Y, L.total, bw),
+                  bw, bw, ho, count, 1.f, 0.f, true, s),
+             "qr block gram");
+    QrTArgs t;
+    std::memset(&t, 0, sizeof(t));
+    t.Y = ws + L.Y;
+    t.y_mat = L.total;
+    t.tau = ws + L.tau + c0o;
+    t.s_mat = L.total;
+    t.TrepT = ws + L.TT;
+    t.tT_mat = L.total;
+    t.TrepQ = ws + L.TQ + (c0o / kQrOuter) * tslot;
+    t.tQ_mat = L.total;
+    t.bw = static_cast<int32_t>(bw);
+    t.reps_t = so;
+    t.reps_q = sq;
+    SOAP_TRY(launch_qr_tfactor(t, count, s), "qr block factor");
+    if (nto > 0) {
+      const int64_t ao = c0o * n + c0o + bw;
+      SOAP_TRY(gemm(op_ws(Vo, L.total, n, true, c0o), op_ws(P, p_mat, n, false, ao), out_ws(ws + L.W, L.total, nto),
+                    bw, nto, ho, count, 1.f, 0.f, false, s, so, ks_o, bw * nto),
                "qr trailing product");
-      SOAP_TRY(gemm(op_ws(ws + L.TT, L.total, nb * sf, true), op_ws(ws + L.W, L.total, nt, false),
-                    out_ws(ws + L.W2, L.total, nt), nb, nt, nb * sf, count, 1.f, 0.f, false, s),
-               "qr block factor");
-      SOAP_TRY(gemm(op_ws(V, L.total, n, false), op_ws(ws + L.W2, L.total, nt, false),
-                    out_ws(P, p_mat, n, ao + nb), h, nt, nb, count, -1.f, 1.f, false, s),
+      SOAP_TRY(gemm(op_ws(ws + L.TT, L.total, bw * so, true), op_ws(ws + L.W, L.total, nto, false),
+                    out_ws(ws + L.W2, L.total, nto), bw, nto, bw * so, count, 1.f, 0.f, false, s),
+               "qr trailing factor");
+      SOAP_TRY(gemm(op_ws(Vo, L.total, n, false, c0o), op_ws(ws + L.W2, L.total, nto, false),
+                    out_ws(P, p_mat, n, ao), ho, nto, bw, count, -1.f, 1.f, false, s),
                "qr trailing update");
     }
   }
   SOAP_TRY(launch_eye(ws + L.Q, L.total, static_cast<int32_t>(n), count, s), "qr identity");
-  for (int64_t p = panels - 1; p >= 0; --p) {
-    const int64_t c0 = p * kQrPanel, nb = std::min<int64_t>(kQrPanel, n - c0), h = n - c0;
+  for (int64_t c0o = (n - 1) / kQrOuter * kQrOuter; c0o >= 0; c0o -= kQrOuter) {
+    const int64_t bw = std::min<int64_t>(kQrOuter, n - c0o), ho = n - c0o;
     int ks_q = 0;
-    const int sq = plan_splits(h, ntiles(h), count, &ks_q);
-    const int64_t qo = c0 * n + c0;
-    float* V = ws + L.V + p * vslot;
-    SOAP_TRY(gemm(op_ws(V, L.total, n, true), op_ws(ws + L.Q, L.total, n, false, qo), out_ws(ws + L.W, L.total, h),
-                  nb, h, h, count, 1.f, 0.f, false, s, sq, ks_q, nb * h),
+    const int sq = plan_splits(ho, ntiles(ho), count, &ks_q);
+    const int64_t qo = c0o * n + c0o;
+    float* Vo = ws + L.V + (c0o / kQrPanel) * vslot;
+    SOAP_TRY(gemm(op_ws(Vo, L.total, n, true, c0o), op_ws(ws + L.Q, L.total, n, false, qo),
+                  out_ws(ws + L.W, L.total, ho), bw, ho, ho, count, 1.f, 0.f, false, s, sq, ks_q, bw * ho),
              "qr formation product");
-    SOAP_TRY(gemm(op_ws(ws + L.TQ + p * tslot, L.total, nb * sq, true), op_ws(ws + L.W, L.total, h, false),
-                  out_ws(ws + L.W2, L.total, h), nb, h, nb * sq, count, 1.f, 0.f, false, s),
+    SOAP_TRY(gemm(op_ws(ws + L.TQ + (c0o / kQrOuter) * tslot, L.total, bw * sq, true),
+                  op_ws(ws + L.W, L.total, ho, false), out_ws(ws + L.W2, L.total, ho), bw, ho, bw * sq, count, 1.f,
+                  0.f, false, s),
              "qr formation factor");
-    SOAP_TRY(gemm(op_ws(V, L.total, n, false), op_ws(ws + L.W2, L.total, h, false), out_ws(ws + L.Q, L.total, n, qo),
-                  h, h, nb, count, -1.f, 1.f, false, s),
+    SOAP_TRY(gemm(op_ws(Vo, L.total, n, false, c0o), op_ws(ws + L.W2, L.total, ho, false),
+                  out_ws(ws + L.Q, L.total, n, qo), ho, ho, bw, count, -1.f, 1.f, false, s),
              "qr formation update");
   }
   for (int o = 0; o < nouts; ++o)

@@ -300,24 +300,44 @@ hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream);
 
 // Householder QR, one 16-column panel of `count` n x n matrices (row-major,
 // ld n): columns c0 .. c0+nb-1 (nb = min(16, n - c0)), rows c0 .. n-1, of A
-// (read only) are reduced in this panel's slot V of the reflector buffer,
-// column-major: column q of the panel at V + q*n, row r - c0 at offset
-// r - c0.  The slot ends holding the explicit reflectors (unit diagonal,
-// zeros above it); sgn gets the sign of each R diagonal entry (+1 for
-// zero).  The block factor T of H_c0 ... H_(c0+nb-1) = I - V T V^T (nb x nb,
-// upper triangular) is written repeated side by side for the split-K
-// products: TrepT (nb x nb*reps_t, row-major) holds [T^T ... T^T], TrepQ
-// (nb x nb*reps_q) holds [T ... T].
+// (read only) are reduced in the panel's slot of the reflector buffer,
+// column-major with absolute rows: V points at row c0 of the slot's first
+// column (column q at V + q*n, row c0 + r at offset r), and the zpre rows
+// above it (up to the enclosing outer block's first row) are zeroed.  The
+// slot ends holding the explicit reflectors (unit diagonal, zeros above
+// it); tau[c0 + j] gets each reflector's factor and sgn[c0 + j] the sign of
+// R's diagonal entry (+1 for zero).  The block factor T of
+// H_c0 ... H_(c0+nb-1) = I - V T V^T (nb x nb, upper triangular) is written
+// repeated side by side for the split-K products: TrepT (nb x nb*reps_t,
+// row-major) holds [T^T ... T^T], TrepQ (nb x nb*reps_q) holds [T ... T]
+// (reps_q may be 0).
 constexpr int kQrPanel = 16;
+constexpr int kQrOuter = 128;   // outer block: the trailing matrix is updated once per 128 columns
 struct QrPanelArgs {
   const float* A; int64_t a_mat;  // floats per matrix
   float* V; int64_t v_mat;
   float* TrepT; int64_t tT_mat;
   float* TrepQ; int64_t tQ_mat;
-  float* sgn; int64_t s_mat;
+  float* sgn; float* tau; int64_t s_mat;
   int32_t n, c0, reps_t, reps_q;
+  int32_t zpre;
+  int32_t pad_;
 };
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream);
+
+// Block factor of an outer block of bw (<= 128) reflectors from their Gram
+// matrix Y = V^T V (bw x bw, ld bw) and factors tau: T[j][j] = tau_j,
+// T[0:j, j] = -tau_j T[0:j, 0:j] Y[0:j, j]; written as TrepT / TrepQ like
+// the panel's (bw x bw*reps).
+struct QrTArgs {
+  const float* Y; int64_t y_mat;
+  const float* tau; int64_t s_mat;
+  float* TrepT; int64_t tT_mat;
+  float* TrepQ; int64_t tQ_mat;
+  int32_t bw, reps_t, reps_q;
+  int32_t pad_;
+};
+hipError_t launch_qr_tfactor(const QrTArgs& a, int64_t count, hipStream_t stream);
 
 // dst[b][i][j] = src(b)[i][j] for `count` rows x cols f32 matrices (dst
 // contiguous, d_mat floats per matrix).

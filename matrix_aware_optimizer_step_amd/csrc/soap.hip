@@ -337,6 +337,7 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
   float* TrT = a.TrepT + b * a.tT_mat;
   float* TrQ = a.TrepQ + b * a.tQ_mat;
   float* sg = a.sgn + b * a.s_mat;
+  float* tg = a.tau + b * a.s_mat;
   const int n = a.n, c0 = a.c0, h = n - c0;
   const int nb = min(kQrPanel, h);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -387,6 +388,7 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
       par[1] = tau;
       par[2] = scale;
       sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
+      tg[c0 + j] = tau;
       Ts[j][j] = tau;
     }
     __syncthreads();
@@ -426,6 +428,9 @@ __global__ __launch_bounds__(kQrThreads) void qr_panel_kernel(QrPanelArgs a) {
     __syncthreads();
   }
 
+  // rows of the outer block above the panel: zero in these columns
+  for (int r = tid; r < a.zpre; r += blockDim.x)
+    for (int q = 0; q < nb; ++q) P[static_cast<int64_t>(q) * n - a.zpre + r] = 0.f;
   // T below its diagonal is zero; repeated copies for the split products
   for (int e = tid; e < nb * nb; e += kQrThreads) {
     const int i = e / nb, k = e % nb;
@@ -478,6 +483,7 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
   float* TrT = a.TrepT + b * a.tT_mat;
   float* TrQ = a.TrepQ + b * a.tQ_mat;
   float* sg = a.sgn + b * a.s_mat;
+  float* tg = a.tau + b * a.s_mat;
   const int n = a.n, c0 = a.c0, h = n - c0;
   const int nb = min(kQrPanel, h);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -531,6 +537,7 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
       par[1] = tau;
       par[2] = scale;
       sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
+      tg[c0 + j] = tau;
       Ts[j][j] = tau;
     }
     __syncthreads();
@@ -578,12 +585,50 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
         if (q < nb) P[static_cast<int64_t>(q) * n + r] = r > q ? x[k][q] : (r == q ? 1.f : 0.f);
     }
   }
+  // rows of the outer block above the panel: zero in these columns
+  for (int r = tid; r < a.zpre; r += blockDim.x)
+    for (int q = 0; q < nb; ++q) P[static_cast<int64_t>(q) * n - a.zpre + r] = 0.f;
   for (int e = tid; e < nb * nb; e += kRegThreads) {
     const int i = e / nb, k = e % nb;
     const float t = k >= i ? Ts[i][k] : 0.f;
     const float tt = i >= k ? Ts[k][i] : 0.f;
     for (int s2 = 0; s2 < a.reps_t; ++s2) TrT[static_cast<int64_t>(i) * nb * a.reps_t + s2 * nb + k] = tt;
     for (int s2 = 0; s2 < a.reps_q; ++s2) TrQ[static_cast<int64_t>(i) * nb * a.reps_q + s2 * nb + k] = t;
+  }
+}
+
+// Block factor of an outer block from the Gram matrix of its reflectors
+// (LAPACK's dlarft recurrence, column by column): one workgroup per matrix,
+// Y and T in LDS, thread i computes T[i][j] for i < j.
+constexpr int kTfThreads = kQrOuter;
+__global__ __launch_bounds__(kTfThreads) void qr_tfactor_kernel(QrTArgs a) {
+  const int64_t b = blockIdx.x;
+  const float* Y = a.Y + b * a.y_mat;
+  const float* tau = a.tau + b * a.s_mat;
+  float* TrT = a.TrepT + b * a.tT_mat;
+  float* TrQ = a.TrepQ + b * a.tQ_mat;
+  const int bw = a.bw, tid = threadIdx.x;
+  __shared__ float Ys[kQrOuter][kQrOuter + 1];
+  __shared__ float T[kQrOuter][kQrOuter + 1];
+  for (int e = tid; e < bw * bw; e += kTfThreads) Ys[e / bw][e % bw] = Y[e];
+  __syncthreads();
+  for (int j = 0; j < bw; ++j) {
+    const float tj = tau[j];
+    if (tid < j) {
+      float t = 0.f;
+      for (int k = tid; k < j; ++k) t += T[tid][k] * Ys[k][j];
+      T[tid][j] = -tj * t;
+    } else if (tid == j) {
+      T[j][j] = tj;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < bw * bw; e += kTfThreads) {
+    const int i = e / bw, k = e % bw;
+    const float t = k >= i ? T[i][k] : 0.f;
+    const float tt = i >= k ? T[k][i] : 0.f;
+    for (int s2 = 0; s2 < a.reps_t; ++s2) TrT[static_cast<int64_t>(i) * bw * a.reps_t + s2 * bw + k] = tt;
+    for (int s2 = 0; s2 < a.reps_q; ++s2) TrQ[static_cast<int64_t>(i) * bw * a.reps_q + s2 * bw + k] = t;
   }
 }
 
@@ -699,6 +744,11 @@ hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stre
     hipLaunchKernelGGL(qr_panel_reg_kernel, dim3(count), dim3(kRegThreads), 0, stream, a);
   else
     hipLaunchKernelGGL(qr_panel_kernel, dim3(count), dim3(kQrThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_qr_tfactor(const QrTArgs& a, int64_t count, hipStream_t stream) {
+  hipLaunchKernelGGL(qr_tfactor_kernel, dim3(count), dim3(kTfThreads), 0, stream, a);
   return hipGetLastError();
 }
 

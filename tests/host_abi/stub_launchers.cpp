@@ -248,13 +248,27 @@ hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t) {
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t) {
   ++g_launches;
   if (a.n < 1 || a.c0 < 0 || a.c0 >= a.n || a.c0 % kQrPanel) die("qr panel: n %d, c0 %d", a.n, a.c0);
-  if (a.reps_t < 1 || a.reps_t > 16 || a.reps_q < 1 || a.reps_q > 16) die("qr panel reps %d %d", a.reps_t, a.reps_q);
+  if (a.reps_t < 1 || a.reps_t > 16 || a.reps_q < 0 || a.reps_q > 16) die("qr panel reps %d %d", a.reps_t, a.reps_q);
+  if (a.zpre < 0 || a.zpre > a.c0 || a.zpre >= kQrOuter) die("qr panel: %d rows above", a.zpre);
   const int64_t n = a.n, h = n - a.c0, nb = std::min<int64_t>(kQrPanel, h);
   in_ws(a.A, count, a.a_mat * 4, n * n * 4, "qr A");
-  in_ws(a.V, count, a.v_mat * 4, ((nb - 1) * n + h) * 4, "qr reflector slot");
+  in_ws(a.V - a.zpre, count, a.v_mat * 4, ((nb - 1) * n + a.zpre + h) * 4, "qr reflector slot");
   in_ws(a.TrepT, count, a.tT_mat * 4, nb * nb * a.reps_t * 4, "qr T^T copies");
-  in_ws(a.TrepQ, count, a.tQ_mat * 4, nb * nb * a.reps_q * 4, "qr T copies");
+  if (a.reps_q > 0) in_ws(a.TrepQ, count, a.tQ_mat * 4, nb * nb * a.reps_q * 4, "qr T copies");
   in_ws(a.sgn, count, a.s_mat * 4, n * 4, "qr signs");
+  in_ws(a.tau, count, a.s_mat * 4, n * 4, "qr factors");
+  return hipSuccess;
+}
+
+hipError_t launch_qr_tfactor(const QrTArgs& a, int64_t count, hipStream_t) {
+  ++g_launches;
+  if (a.bw < 1 || a.bw > kQrOuter || a.reps_t < 1 || a.reps_t > 16 || a.reps_q < 1 || a.reps_q > 16)
+    die("qr block factor: width %d, reps %d %d", a.bw, a.reps_t, a.reps_q);
+  const int64_t bw = a.bw;
+  in_ws(a.Y, count, a.y_mat * 4, bw * bw * 4, "qr block gram");
+  in_ws(a.tau, count, a.s_mat * 4, bw * 4, "qr block factors");
+  in_ws(a.TrepT, count, a.tT_mat * 4, bw * bw * a.reps_t * 4, "qr block T^T copies");
+  in_ws(a.TrepQ, count, a.tQ_mat * 4, bw * bw * a.reps_q * 4, "qr block T copies");
   return hipSuccess;
 }
 
