@@ -189,9 +189,11 @@ __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
 }
 
 // TM x 128 output tile, four waves: TM = 128 as 2 x 2 waves of 64 x 64,
-// TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.
+// TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.  At
+// least three workgroups per CU (accumulators in VGPRs, no AGPRs): a third
+// wave per SIMD covers the LDS reads before each step's products.
 template <int TM, int CFG>
-__global__ __launch_bounds__(kThreads) void sgemm_kernel(SgemmArgs a) {
+__global__ __launch_bounds__(kThreads, 3) void sgemm_kernel(SgemmArgs a) {
   using F = FastCfg<CFG>;
   constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
   constexpr int FI = TM / WM / 32, FJ = kT / WN / 32;
