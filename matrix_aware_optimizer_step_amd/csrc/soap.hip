@@ -600,9 +600,14 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
 }
 
 // Block factor of an outer block from the Gram matrix of its reflectors
-// (LAPACK's dlarft recurrence, column by column): one workgroup per matrix,
-// Y and T in LDS, thread i computes T[i][j] for i < j.
-constexpr int kTfThreads = kQrOuter;
+// (LAPACK's dlarft recurrence T[0:j, j] = -tau_j T[0:j, 0:j] Y[0:j, j],
+// taken 16 columns at a time).  First every 16 x 16 diagonal block by the
+// scalar recurrence, all blocks at once; then block column J from the
+// finished columns to its left: T[0:16J, J] = -(T[0:16J, 0:16J] Y[0:16J, J]) T_JJ,
+// two small products spread over the workgroup.  Y, T and the intermediate
+// product live in LDS; one workgroup per matrix.
+constexpr int kTfThreads = 256;
+constexpr int kTfB = 16;
 __global__ __launch_bounds__(kTfThreads) void qr_tfactor_kernel(QrTArgs a) {
   const int64_t b = blockIdx.x;
   const float* Y = a.Y + b * a.y_mat;
@@ -610,18 +615,49 @@ __global__ __launch_bounds__(kTfThreads) void qr_tfactor_kernel(QrTArgs a) {
   float* TrT = a.TrepT + b * a.tT_mat;
   float* TrQ = a.TrepQ + b * a.tQ_mat;
   const int bw = a.bw, tid = threadIdx.x;
+  const int nblk = (bw + kTfB - 1) / kTfB;
   __shared__ float Ys[kQrOuter][kQrOuter + 1];
   __shared__ float T[kQrOuter][kQrOuter + 1];
-  for (int e = tid; e < bw * bw; e += kTfThreads) Ys[e / bw][e % bw] = Y[e];
+  __shared__ float X[kQrOuter - kTfB][kTfB + 1];
+  for (int e = tid; e < bw * bw; e += kTfThreads) {
+    Ys[e / bw][e % bw] = Y[e];
+    T[e / bw][e % bw] = 0.f;
+  }
   __syncthreads();
-  for (int j = 0; j < bw; ++j) {
-    const float tj = tau[j];
-    if (tid < j) {
+  // diagonal blocks: thread (J, i) owns row 16J + i of block J
+  {
+    const int J = tid / kTfB, i = tid % kTfB, r = kTfB * J + i;
+    const bool own = J < nblk && r < bw;
+    const int jb = J < nblk ? min(kTfB, bw - kTfB * J) : 0;
+    for (int j = 0; j < kTfB; ++j) {
+      if (own && j < jb) {
+        const int c = kTfB * J + j;
+        if (i < j) {
+          float t = 0.f;
+          for (int k = i; k < j; ++k) t += T[r][kTfB * J + k] * Ys[kTfB * J + k][c];
+          T[r][c] = -tau[c] * t;
+        } else if (i == j) {
+          T[r][c] = tau[c];
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // off-diagonal block columns, left to right
+  for (int J = 1; J < nblk; ++J) {
+    const int c0 = kTfB * J, jb = min(kTfB, bw - c0);
+    for (int e = tid; e < c0 * jb; e += kTfThreads) {
+      const int i = e / jb, c = e % jb;
       float t = 0.f;
-      for (int k = tid; k < j; ++k) t += T[tid][k] * Ys[k][j];
-      T[tid][j] = -tj * t;
-    } else if (tid == j) {
-      T[j][j] = tj;
+      for (int k = i; k < c0; ++k) t += T[i][k] * Ys[k][c0 + c];
+      X[i][c] = t;
+    }
+    __syncthreads();
+    for (int e = tid; e < c0 * jb; e += kTfThreads) {
+      const int i = e / jb, c = e % jb;
+      float t = 0.f;
+      for (int k = 0; k <= c; ++k) t += X[i][k] * T[c0 + k][c0 + c];
+      T[i][c0 + c] = -t;
     }
     __syncthreads();
   }
