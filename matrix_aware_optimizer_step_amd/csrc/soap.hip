@@ -491,9 +491,10 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   __shared__ float part[kRegWaves * 16];
+  __shared__ float partn[kRegWaves];  // norm partials: apart from part, which the dot products reuse
   __shared__ float tot[16];
   __shared__ float Ts[kQrPanel][kQrPanel + 1];
-  __shared__ float par[3];
+  __shared__ float par[1];
 
   float x[kRegRows][kQrPanel];
 #pragma unroll
@@ -513,6 +514,9 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
     for (int q = 0; q < kQrPanel; ++q) c = q == j ? x[k][q] : c;
     return c;
   };
+  // three barriers per column: every thread forms the reflector's factors
+  // from the wave partials itself, and the next column's writes go to LDS
+  // words that this column has finished reading before its last barrier
   for (int j = 0; j < nb; ++j) {
     float s = 0.f;
 #pragma unroll
@@ -523,27 +527,24 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
       if (k == 0 && tid == j) par[0] = c;  // alpha: row j is thread j's first row (j < 16)
     }
     s = wave_sum(s);
-    if (lane == 0) part[wave] = s;
+    if (lane == 0) partn[wave] = s;
     __syncthreads();
+    float t2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < kRegWaves; ++q) t2 += partn[q];
+    const float alpha = par[0];
+    float beta = alpha, tau = 0.f, scale = 0.f;
+    if (t2 > 0.f) {
+      const float nrm = sqrtf(alpha * alpha + t2);
+      beta = alpha >= 0.f ? -nrm : nrm;
+      tau = (beta - alpha) / beta;
+      scale = 1.f / (alpha - beta);
+    }
     if (tid == 0) {
-      float t = 0.f;
-      for (int q = 0; q < kRegWaves; ++q) t += part[q];
-      const float alpha = par[0];
-      float beta = alpha, tau = 0.f, scale = 0.f;
-      if (t > 0.f) {
-        const float nrm = sqrtf(alpha * alpha + t);
-        beta = alpha >= 0.f ? -nrm : nrm;
-        tau = (beta - alpha) / beta;
-        scale = 1.f / (alpha - beta);
-      }
-      par[1] = tau;
-      par[2] = scale;
       sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
       tg[c0 + j] = tau;
       Ts[j][j] = tau;
     }
-    __syncthreads();
-    const float tau = par[1], scale = par[2];
 
     float w[16];
 #pragma unroll
@@ -574,8 +575,8 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
       for (int q = 0; q < kQrPanel; ++q)
         if (q > j) x[k][q] -= tau * tot[q] * vk;
     }
-    __syncthreads();
   }
+  __syncthreads();
 
   // explicit reflectors, column-major in the slot (coalesced across lanes)
 #pragma unroll
