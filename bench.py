@@ -281,7 +281,10 @@ def bench_soap(args):
            "soap": {"flops_per_step": flops, "tflops": flops / (ms_per_step * 1e-3) / 1e12,
                     "flops_statistics_and_rotations": base, "flops_refresh": extra},
            "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP32_MFMA_TFLOPS, "unit": "TFLOP/s",
-                        "frac": gemm_tflops / PEAK_FP32_MFMA_TFLOPS, "traffic": None,
+                        "frac": gemm_tflops / PEAK_FP32_MFMA_TFLOPS,
+                        "traffic": measured_traffic("soap_sgemm_8b-dense-layer_hbm_traffic.md", "soap.hip",
+                                                    "soap_products_bytes_per_step")
+                        if cfg.slug == "8b-dense-layer" else None,
                         "kernel": "sgemm_kernel (statistics and rotation products; timed with the rotated-Adam "
                                   "kernel of the precondition phase)"},
            "cpu_baseline": cpu}
