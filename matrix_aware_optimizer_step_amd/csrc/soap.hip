@@ -198,8 +198,20 @@ __global__ __launch_bounds__(kThreads, 3) void sgemm_kernel(SgemmArgs a) {
   constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
   constexpr int FI = TM / WM / 32, FJ = kT / WN / 32;
   constexpr int kPA = TM + 4;
-  const int tj = blockIdx.x, ti = blockIdx.y;
-  if (a.sym && ti > tj) return;
+  int tj = blockIdx.x, ti = blockIdx.y;
+  if (a.sym) {
+    // A symmetric product launches only its upper-triangle tiles: blockIdx.x
+    // enumerates them row by row.  (A full grid whose lower half returns at
+    // once ran the remaining tiles at half their rate.)
+    const int T = (a.N + kT - 1) / kT;
+    int p = blockIdx.x;
+    ti = 0;
+    while (p >= T - ti) {
+      p -= T - ti;
+      ++ti;
+    }
+    tj = ti + p;
+  }
   const int bi = blockIdx.z / a.splits, sp = blockIdx.z % a.splits;
   const int kbeg = sp * a.ksplit;
   const int kend = min(a.K, kbeg + a.ksplit);
@@ -769,7 +781,8 @@ hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream) {
     else
       launch_cfg<32, -1>(a, grid, stream);
   } else {
-    const dim3 grid((a.N + kT - 1) / kT, (a.M + kT - 1) / kT, a.count * a.splits);
+    const int T = (a.N + kT - 1) / kT;  // a symmetric product has M = N
+    const dim3 grid(a.sym ? T * (T + 1) / 2 : T, a.sym ? 1 : (a.M + kT - 1) / kT, a.count * a.splits);
     if (cfg >= 0)
       launch_fast<kT>(cfg, a, grid, stream);
     else
