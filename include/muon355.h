@@ -318,6 +318,17 @@ muon_status_t muon_adamw(const muon_tensor_list_t* tensors, int64_t step, float 
 muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, const muon_batch_t* R,
                               float beta_s, void* stream);
 
+/* soap_statistics for up to 8 groups (shape classes) at once: grads[g] is
+ * group g's gradient descriptor and Ls[g], Rs[g] point to its statistics or
+ * are NULL.  The products
+ * of all groups share launches (one per operand layout, longest reduction
+ * first), so small groups fill the chip beside large ones; every statistic
+ * is bit-identical to soap_statistics on its group.  The three arrays are
+ * host arrays of ngroups entries.  Errors name the group; nothing is
+ * enqueued unless every group is valid. */
+muon_status_t soap_statistics_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* Ls,
+                                      const muon_batch_t* const* Rs, float beta_s, void* stream);
+
 /* Q factor of a QR factorization, the triangular factor's diagonal made
  * non-negative (unique for a full-rank input): Householder reflections
  * in 16-column panels with blocked trailing updates.  a (read only) and q:

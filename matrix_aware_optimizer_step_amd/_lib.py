@@ -27,7 +27,7 @@ EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_m
             "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped",
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
             "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
-            "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
+            "soap_statistics_grouped", "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
             "soap_refresh_grouped_workspace", "soap_refresh_grouped",
             "soap_precondition_workspace", "soap_precondition")
 
@@ -86,6 +86,7 @@ def load() -> ctypes.CDLL:
         "muon_apply_grouped": (ctypes.c_int, [ctypes.c_int, P, P, f32, f32, i32, f32, vp]),
         "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
         "soap_statistics": (ctypes.c_int, [P, P, P, f32, vp]),
+        "soap_statistics_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(P), ctypes.POINTER(P), f32, vp]),
         "soap_qr_workspace": (sz, [i64, i64]),
         "soap_qr": (ctypes.c_int, [P, P, vp, sz, vp]),
         "soap_refresh_workspace": (sz, [i64, i64, i64, ctypes.c_int, ctypes.c_int]),
@@ -224,6 +225,17 @@ def soap_refresh(L: MuonBatch | None, R: MuonBatch | None, QL: MuonBatch | None,
                  mbar: MuonBatch, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
     st = load().soap_refresh(_ref(L), _ref(R), _ref(QL), _ref(QR), _ref(mbar), workspace_ptr, ws_bytes, stream)
     _check(st, "soap_refresh")
+
+
+def soap_statistics_grouped(grads, Ls, Rs, beta_s: float, stream: int) -> None:
+    """grads: per-group MuonBatch; Ls, Rs: per-group MuonBatch or None."""
+    n = len(grads)
+    if not (len(Ls) == len(Rs) == n):
+        raise ValueError("per-group lists differ in length")
+    PB = ctypes.POINTER(MuonBatch)
+    arr = lambda xs: (PB * n)(*[PB() if x is None else ctypes.pointer(x) for x in xs])
+    st = load().soap_statistics_grouped(n, (MuonBatch * n)(*grads), arr(Ls), arr(Rs), beta_s, stream)
+    _check(st, "soap_statistics_grouped")
 
 
 def soap_refresh_grouped_workspace(counts, rows, cols, with_l, with_r) -> int:

@@ -840,10 +840,9 @@ COut out_ws(float* base, int64_t mat, int64_t ld, int64_t off = 0) {
   return COut{reinterpret_cast<char*>(base), mat * 4, nullptr, off * 4, ld};
 }
 
-hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int64_t M, int64_t N, int64_t K,
-                int64_t count, float alpha, float beta, bool sym, hipStream_t s, int splits = 1, int ksplit = 0,
-                int64_t c_split_floats = 0) {
-  if (M == 0 || N == 0) return hipSuccess;
+SgemmArgs gemm_args(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int64_t M, int64_t N, int64_t K,
+                    int64_t count, float alpha, float beta, bool sym, int splits = 1, int ksplit = 0,
+                    int64_t c_split_floats = 0) {
   SgemmArgs g;
   std::memset(&g, 0, sizeof(g));
   g.a = A;
@@ -863,7 +862,14 @@ hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int
   g.alpha = alpha;
   g.beta = beta;
   g.sym = sym;
-  return launch_sgemm(g, s);
+  return g;
+}
+
+hipError_t gemm(const SgemmOperand& A, const SgemmOperand& B, const COut& C, int64_t M, int64_t N, int64_t K,
+                int64_t count, float alpha, float beta, bool sym, hipStream_t s, int splits = 1, int ksplit = 0,
+                int64_t c_split_floats = 0) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return launch_sgemm(gemm_args(A, B, C, M, N, K, count, alpha, beta, sym, splits, ksplit, c_split_floats), s);
 }
 
 #define SOAP_TRY(expr, what)                                  \
@@ -1009,6 +1015,42 @@ size_t qr_bytes(int64_t count, int64_t n) {
   return static_cast<size_t>(count * (round64(n * n) + qr_layout(n).total) * 4);
 }
 
+// soap_statistics and soap_statistics_grouped: every group is checked before
+// anything is enqueued; `grouped` names the group in error messages.
+muon_status_t statistics(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* Ls,
+                         const muon_batch_t* const* Rs, float beta_s, void* stream, bool grouped) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!grads || !Ls || !Rs) return fail(MUON_ERR_INVALID_VALUE, "the per-group arrays must not be NULL");
+  if (!(beta_s >= 0.f && beta_s < 1.f)) return fail(MUON_ERR_INVALID_VALUE, "beta_s %g outside [0, 1)", beta_s);
+  auto tag = [&](muon_status_t st, int g) { return grouped ? in_group(st, g) : st; };
+  muon_status_t st;
+  for (int g = 0; g < ngroups; ++g) {
+    const muon_batch_t* grad = &grads[g];
+    if ((st = check_batch(grad, "grad", true)) != MUON_OK) return tag(st, g);
+    const int64_t c = grad->count, m = grad->rows, n = grad->cols;
+    if (Ls[g] && (st = check_f32(Ls[g], "L", c, m, m)) != MUON_OK) return tag(st, g);
+    if (Rs[g] && (st = check_f32(Rs[g], "R", c, n, n)) != MUON_OK) return tag(st, g);
+  }
+  // L <- b L + (1-b) G G^T, R <- b R + (1-b) G^T G, upper tiles mirrored;
+  // all of them in as few launches as their operand layouts allow
+  SgemmArgs gs[2 * kMaxGroups];
+  int np = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const muon_batch_t* grad = &grads[g];
+    const int64_t c = grad->count, m = grad->rows, n = grad->cols;
+    if (Ls[g])
+      gs[np++] = gemm_args(op_batch(grad, true), op_batch(grad, true), out_batch(Ls[g]), m, m, n, c, 1.f - beta_s,
+                           beta_s, true);
+    if (Rs[g])
+      gs[np++] = gemm_args(op_batch(grad, false), op_batch(grad, false), out_batch(Rs[g]), n, n, m, c, 1.f - beta_s,
+                           beta_s, true);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (np > 0) SOAP_TRY(launch_sgemm_list(gs, np, s), "statistics");
+  return done(s, grouped ? "soap_statistics_grouped" : "soap_statistics");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1040,22 +1082,13 @@ muon_status_t soap_qr(const muon_batch_t* a, const muon_batch_t* q, void* worksp
 
 muon_status_t soap_statistics(const muon_batch_t* grad, const muon_batch_t* L, const muon_batch_t* R, float beta_s,
                               void* stream) {
-  muon_status_t st;
-  if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
-  if (!(beta_s >= 0.f && beta_s < 1.f)) return fail(MUON_ERR_INVALID_VALUE, "beta_s %g outside [0, 1)", beta_s);
-  const int64_t c = grad->count, m = grad->rows, n = grad->cols;
-  if (L && (st = check_f32(L, "L", c, m, m)) != MUON_OK) return st;
-  if (R && (st = check_f32(R, "R", c, n, n)) != MUON_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  // L <- b L + (1-b) G G^T, R <- b R + (1-b) G^T G, upper tiles mirrored
-  if (L)
-    SOAP_TRY(gemm(op_batch(grad, true), op_batch(grad, true), out_batch(L), m, m, n, c, 1.f - beta_s, beta_s, true, s),
-             "statistics L");
-  if (R)
-    SOAP_TRY(gemm(op_batch(grad, false), op_batch(grad, false), out_batch(R), n, n, m, c, 1.f - beta_s, beta_s, true,
-                  s),
-             "statistics R");
-  return done(s, "soap_statistics");
+  if (!grad) return fail(MUON_ERR_INVALID_VALUE, "grad: descriptor is NULL");
+  return statistics(1, grad, &L, &R, beta_s, stream, false);
+}
+
+muon_status_t soap_statistics_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* Ls,
+                                      const muon_batch_t* const* Rs, float beta_s, void* stream) {
+  return statistics(ngroups, grads, Ls, Rs, beta_s, stream, true);
 }
 
 size_t soap_refresh_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,

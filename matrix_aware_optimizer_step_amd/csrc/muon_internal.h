@@ -298,6 +298,19 @@ constexpr int kSgemmTile = 128;
 constexpr int kSgemmBK = 32;
 hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream);
 
+// Up to kSgemmMaxList products in one launch; tile_end[p] = the workgroups of
+// products 0..p (each: tiles of one matrix x count x splits).
+constexpr int kSgemmMaxList = 8;
+struct SgemmList {
+  SgemmArgs g[kSgemmMaxList];
+  int32_t tile_end[kSgemmMaxList];
+  int32_t n;
+  int32_t pad_;
+};
+// Enqueues n (at most 2 * kSgemmMaxList) independent products; the result of
+// each is what launch_sgemm gives for it, bit for bit.
+hipError_t launch_sgemm_list(const SgemmArgs* gs, int n, hipStream_t stream);
+
 // Householder QR, one 16-column panel of `count` n x n matrices (row-major,
 // ld n): columns c0 .. c0+nb-1 (nb = min(16, n - c0)), rows c0 .. n-1, of A
 // (read only) are reduced in the panel's slot of the reflector buffer,

@@ -19,6 +19,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <cstring>
 
 #include "muon_internal.h"
 
@@ -192,27 +193,14 @@ __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
 // TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.  At
 // least three workgroups per CU (accumulators in VGPRs, no AGPRs): a third
 // wave per SIMD covers the LDS reads before each step's products.
+// Tile (ti, tj) of batch entry and split z = bi * splits + sp.
 template <int TM, int CFG>
-__global__ __launch_bounds__(kThreads, 3) void sgemm_kernel(SgemmArgs a) {
+__device__ __forceinline__ void sgemm_tile(const SgemmArgs& a, int ti, int tj, int z) {
   using F = FastCfg<CFG>;
   constexpr int WM = TM >= 64 ? 2 : 1, WN = 4 / WM;
   constexpr int FI = TM / WM / 32, FJ = kT / WN / 32;
   constexpr int kPA = TM + 4;
-  int tj = blockIdx.x, ti = blockIdx.y;
-  if (a.sym) {
-    // A symmetric product launches only its upper-triangle tiles: blockIdx.x
-    // enumerates them row by row.  (A full grid whose lower half returns at
-    // once ran the remaining tiles at half their rate.)
-    const int T = (a.N + kT - 1) / kT;
-    int p = blockIdx.x;
-    ti = 0;
-    while (p >= T - ti) {
-      p -= T - ti;
-      ++ti;
-    }
-    tj = ti + p;
-  }
-  const int bi = blockIdx.z / a.splits, sp = blockIdx.z % a.splits;
+  const int bi = z / a.splits, sp = z % a.splits;
   const int kbeg = sp * a.ksplit;
   const int kend = min(a.K, kbeg + a.ksplit);
   const char* pa = entry(a.a, bi);
@@ -290,6 +278,51 @@ __global__ __launch_bounds__(kThreads, 3) void sgemm_kernel(SgemmArgs a) {
         *cij = v;
         if (a.sym && i != j) C[static_cast<int64_t>(j) * a.ldc + i] = v;
       }
+}
+
+// Tile t of one matrix's grid: row-major over T x tn tiles, or for a
+// symmetric product over the upper triangle only, row by row.  (A full grid
+// whose lower half returns at once ran the remaining tiles at half their
+// rate.)
+__device__ __forceinline__ void tile_coords(const SgemmArgs& a, int t, int tn, int* ti, int* tj) {
+  if (a.sym) {
+    const int T = (a.N + kT - 1) / kT;
+    int r = 0;
+    while (t >= T - r) {
+      t -= T - r;
+      ++r;
+    }
+    *ti = r;
+    *tj = r + t;
+  } else {
+    *ti = t / tn;
+    *tj = t % tn;
+  }
+}
+
+// One product: blockIdx.x = tile of the matrix grid, blockIdx.z = batch
+// entry and split.
+template <int TM, int CFG>
+__global__ __launch_bounds__(kThreads, 3) void sgemm_kernel(SgemmArgs a) {
+  int ti = blockIdx.y, tj = blockIdx.x;
+  if (a.sym) tile_coords(a, blockIdx.x, 0, &ti, &tj);
+  sgemm_tile<TM, CFG>(a, ti, tj, blockIdx.z);
+}
+
+// Several products in one launch (128-row tiles): product p owns the linear
+// workgroups [tile_end[p-1], tile_end[p]), batch entry and split major, tile
+// minor.
+template <int CFG>
+__global__ __launch_bounds__(kThreads, 3) void sgemm_list_kernel(SgemmList l) {
+  int p = 0;
+  while (p + 1 < l.n && static_cast<int>(blockIdx.x) >= l.tile_end[p]) ++p;
+  const SgemmArgs& a = l.g[p];
+  const int q = blockIdx.x - (p ? l.tile_end[p - 1] : 0);
+  const int tn = (a.N + kT - 1) / kT;
+  const int per = a.sym ? tn * (tn + 1) / 2 : tn * ((a.M + kT - 1) / kT);
+  int ti, tj;
+  tile_coords(a, q % per, tn, &ti, &tj);
+  sgemm_tile<kT, CFG>(a, ti, tj, q / per);
 }
 
 // --------------------------------------------------------------- QR panel
@@ -760,6 +793,16 @@ void launch_fast(int cfg, const SgemmArgs& a, dim3 grid, hipStream_t stream) {
   }
 }
 
+template <int CFG = -1>
+void launch_list(int cfg, const SgemmList& l, int tiles, hipStream_t stream) {
+  if constexpr (CFG < 16) {
+    if (cfg == CFG)
+      hipLaunchKernelGGL((sgemm_list_kernel<CFG>), dim3(tiles), dim3(kThreads), 0, stream, l);
+    else
+      launch_list<CFG + 1>(cfg, l, tiles, stream);
+  }
+}
+
 // The fast path needs every 4-element run aligned and inside its row: both
 // operands' vector flag, and K plus each operand's outer extent along its
 // contiguous index a multiple of 4.
@@ -789,6 +832,51 @@ hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t stream) {
       launch_cfg<kT, -1>(a, grid, stream);
   }
   return hipGetLastError();
+}
+
+int64_t sgemm_list_tiles(const SgemmArgs& a) {
+  const int64_t tn = (a.N + kT - 1) / kT;
+  const int64_t per = a.sym ? tn * (tn + 1) / 2 : tn * ((a.M + kT - 1) / kT);
+  return per * a.count * a.splits;
+}
+
+hipError_t launch_sgemm_list(const SgemmArgs* gs, int n, hipStream_t stream) {
+  // Products that take the 32-row tiles, and products with a fast-path
+  // configuration of their own, launch apart; the rest go in lists of at
+  // most kSgemmMaxList, longest reduction first.
+  bool done[kSgemmMaxList * 2] = {};
+  if (n < 1 || n > kSgemmMaxList * 2) return hipErrorInvalidValue;
+  for (int i = 0; i < n; ++i) {
+    if (done[i]) continue;
+    const int cfg = fast_cfg(gs[i]);
+    if (gs[i].M <= 32 && !gs[i].sym) {
+      done[i] = true;
+      const hipError_t e = launch_sgemm(gs[i], stream);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    int idx[kSgemmMaxList * 2], m = 0;
+    for (int j = i; j < n; ++j)
+      if (!done[j] && !(gs[j].M <= 32 && !gs[j].sym) && fast_cfg(gs[j]) == cfg) idx[m++] = j;
+    std::sort(idx, idx + m, [&](int x, int y) { return gs[x].ksplit > gs[y].ksplit || (gs[x].ksplit == gs[y].ksplit && x < y); });
+    for (int b = 0; b < m; b += kSgemmMaxList) {
+      SgemmList l;
+      std::memset(&l, 0, sizeof(l));
+      int64_t tiles = 0;
+      l.n = std::min(kSgemmMaxList, m - b);
+      for (int k = 0; k < l.n; ++k) {
+        l.g[k] = gs[idx[b + k]];
+        done[idx[b + k]] = true;
+        tiles += sgemm_list_tiles(l.g[k]);
+        if (tiles > INT32_MAX) return hipErrorInvalidValue;
+        l.tile_end[k] = static_cast<int32_t>(tiles);
+      }
+      if (tiles > 0) launch_list(cfg, l, static_cast<int>(tiles), stream);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t stream) {

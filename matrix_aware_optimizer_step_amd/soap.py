@@ -45,6 +45,15 @@ def statistics(grad, Lstat=None, Rstat=None, beta_s: float = BETA_S, stream=None
     L.soap_statistics(*map(_desc, bs), beta_s, _stream(stream))
 
 
+def statistics_grouped(grads, Lstats, Rstats, beta_s: float = BETA_S, stream=None) -> None:
+    """statistics() for up to 8 groups in one call: the products of all
+    groups share launches."""
+    bg = [batch(x) for x in grads]
+    bl, br = ([None if x is None else batch(x) for x in xs] for xs in (Lstats, Rstats))
+    L.soap_statistics_grouped([b.desc for b in bg], [_desc(b) for b in bl], [_desc(b) for b in br], beta_s,
+                              _stream(stream))
+
+
 def qr(a, q, ws: torch.Tensor | None = None, stream=None) -> None:
     """q = the Q factor of a (square, f32), R's diagonal non-negative."""
     ba, bq = batch(a), batch(q)
@@ -97,7 +106,8 @@ class SoapStep:
     direction D; an axis longer than ``max_dim`` keeps the identity basis.
     ``step()`` runs, per group and in this order: the statistics, the basis
     refresh on steps 1, 1 + freq, ..., the rotated Adam direction, and
-    W <- (1 - lr*wd) W - lr D.
+    W <- (1 - lr*wd) W - lr D.  The statistics and the refreshes of up to 8
+    preconditioned groups share each call.
     """
 
     def __init__(self, groups, *, lr: float = 3e-4, weight_decay: float = 0.0, betas=(BETA1, BETA2),
@@ -172,8 +182,9 @@ class SoapStep:
                 events[i].record(st)
 
         rec(0)
-        for g in self.groups:
-            statistics(g["G"], g["L"], g["R"], self.beta_s, stream=s)
+        for ch in self.chunks:
+            gs = [self.groups[i] for i in ch]
+            statistics_grouped([g["G"] for g in gs], [g["L"] for g in gs], [g["R"] for g in gs], self.beta_s, stream=s)
         rec(1)
         if (self.t - 1) % self.freq == 0:
             for ch in self.chunks:

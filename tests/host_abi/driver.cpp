@@ -158,6 +158,11 @@ void soap_cases() {
       pr[g] = wr[g] ? &R[g] : nullptr;
       pqr[g] = wr[g] ? &QR[g] : nullptr;
     }
+    std::vector<muon_batch_t> grads;
+    for (int g = 0; g < 4; ++g) grads.push_back(batch(counts[g], rows[g], cols[g], MUON_BF16));
+    expect(soap_statistics_grouped(4, grads.data(), pl, pr, 0.9f, nullptr), MUON_OK, "soap_statistics_grouped");
+    expect(soap_statistics_grouped(9, grads.data(), pl, pr, 0.9f, nullptr), MUON_ERR_INVALID_VALUE,
+           "soap_statistics_grouped, 9 groups");
     const size_t need = soap_refresh_grouped_workspace(4, counts, rows, cols, wl, wr);
     stub_set_workspace(kWs, need);
     expect(soap_refresh_grouped(4, pl, pr, pql, pqr, mb.data(), kWs, need, nullptr), MUON_OK, "soap_refresh_grouped");

@@ -245,6 +245,15 @@ hipError_t launch_sgemm(const SgemmArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_sgemm_list(const SgemmArgs* gs, int n, hipStream_t s) {
+  if (n < 1 || n > 2 * kSgemmMaxList) die("sgemm list of %d products", n);
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_sgemm(gs[i], s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_qr_panel(const QrPanelArgs& a, int64_t count, hipStream_t) {
   ++g_launches;
   if (a.n < 1 || a.c0 < 0 || a.c0 >= a.n || a.c0 % kQrPanel) die("qr panel: n %d, c0 %d", a.n, a.c0);

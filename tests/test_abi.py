@@ -292,6 +292,23 @@ def test_soap_statistics_rejects_bad_arguments():
     assert status_of(lambda: L.soap_statistics(desc(count=0), None, None, 0.9, 0)) == INVALID
 
 
+def test_soap_statistics_grouped_rejects_bad_arguments():
+    g = desc(count=2, rows=64, cols=96)
+    Ls, Rs = desc(count=2, rows=64, cols=64), desc(count=2, rows=96, cols=96)
+    grouped = L.soap_statistics_grouped
+    assert status_of(lambda: grouped([], [], [], 0.9, 0)) == INVALID
+    assert status_of(lambda: grouped([g] * 9, [Ls] * 9, [Rs] * 9, 0.9, 0)) == INVALID
+    assert status_of(lambda: grouped([g, g], [Ls, Ls], [Rs, Rs], 1.0, 0)) == INVALID
+    # the second group's R has the wrong order: the error names group 1
+    assert status_of(lambda: grouped([g, g], [Ls, None], [Rs, Ls], 0.9, 0)) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: grouped([g, desc(count=0)], [Ls, None], [Rs, None], 0.9, 0)) == INVALID
+    assert status_of(lambda: grouped([g], [desc(count=2, rows=64, cols=64, dtype=L.MUON_BF16)], [None], 0.9,
+                                     0)) == UNSUPPORTED
+    with pytest.raises(ValueError):
+        grouped([g, g], [Ls], [Rs, Rs], 0.9, 0)
+
+
 def test_soap_qr_rejects_bad_arguments():
     a = desc(count=2, rows=64, cols=64)
     assert status_of(lambda: L.soap_qr(desc(count=2, rows=64, cols=32), a, FAKE, 1 << 30, 0)) == INVALID
