@@ -539,35 +539,45 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
   __shared__ float partn[kRegWaves];  // norm partials: apart from part, which the dot products reuse
   __shared__ float tot[16];
   __shared__ float Ts[kQrPanel][kQrPanel + 1];
+  __shared__ float sgs[kQrPanel];
   __shared__ float par[1];
 
-  float x[kRegRows][kQrPanel];
+  // one panel row per 16-float vector; 16-byte loads where every row of
+  // the panel starts 16-byte aligned
+  f32x16_t x[kRegRows];
+  const bool vec = nb == kQrPanel && n % 4 == 0 && (reinterpret_cast<uintptr_t>(A) & 15) == 0;
 #pragma unroll
   for (int k = 0; k < kRegRows; ++k) {
     const int r = tid + kRegThreads * k;
     const float* row = A + static_cast<int64_t>(c0 + (r < h ? r : 0)) * n + c0;
+    if (vec) {
 #pragma unroll
-    for (int q = 0; q < kQrPanel; ++q) x[k][q] = (r < h && q < nb) ? row[q < nb ? q : 0] : 0.f;
+      for (int q = 0; q < kQrPanel; q += 4) {
+        const float4 v = r < h ? *reinterpret_cast<const float4*>(row + q) : make_float4(0.f, 0.f, 0.f, 0.f);
+        x[k][q] = v.x;
+        x[k][q + 1] = v.y;
+        x[k][q + 2] = v.z;
+        x[k][q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kQrPanel; ++q) x[k][q] = (r < h && q < nb) ? row[q < nb ? q : 0] : 0.f;
+    }
   }
 
-  // x is only indexed by constants (column j is picked out with selects),
-  // so it stays in registers; v is recomputed from x where needed rather
-  // than held across the reductions
-  auto column = [&](int k, int j) {
-    float c = 0.f;
-#pragma unroll
-    for (int q = 0; q < kQrPanel; ++q) c = q == j ? x[k][q] : c;
-    return c;
-  };
-  // three barriers per column: every thread forms the reflector's factors
-  // from the wave partials itself, and the next column's writes go to LDS
-  // words that this column has finished reading before its last barrier
+  // Each row's 16 values are one vector; column j (uniform over the
+  // workgroup) is read and written by a register-relative move.  Three
+  // barriers per column: every thread forms the reflector's factors from the
+  // wave partials itself, and the next column's writes go to LDS words that
+  // this column has finished reading before its last barrier.
   for (int j = 0; j < nb; ++j) {
     float s = 0.f;
+    float vk[kRegRows];
 #pragma unroll
     for (int k = 0; k < kRegRows; ++k) {
       const int r = tid + kRegThreads * k;
-      const float c = column(k, j);
+      const float c = x[k][j];
+      vk[k] = c;
       s += (r > j && r < h) ? c * c : 0.f;
       if (k == 0 && tid == j) par[0] = c;  // alpha: row j is thread j's first row (j < 16)
     }
@@ -585,12 +595,13 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
       tau = (beta - alpha) / beta;
       scale = 1.f / (alpha - beta);
     }
-    if (tid == 0) {
-      sg[c0 + j] = beta < 0.f ? -1.f : 1.f;
-      tg[c0 + j] = tau;
+    if (tid == 0) {  // to global memory after the loop: a barrier waits for pending stores
+      sgs[j] = beta < 0.f ? -1.f : 1.f;
       Ts[j][j] = tau;
     }
 
+    // v (1 on the diagonal, x * scale below, 0 above) replaces column j
+    // below the diagonal; w = v^T x for every column (w[j] is not used)
     float w[16];
 #pragma unroll
     for (int q = 0; q < 16; ++q) w[q] = 0.f;
@@ -598,12 +609,10 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
     for (int k = 0; k < kRegRows; ++k) {
       const int r = tid + kRegThreads * k;
       const bool below = r > j && r < h;
-      const float vk = below ? column(k, j) * scale : (r == j ? 1.f : 0.f);
+      vk[k] = below ? vk[k] * scale : (r == j ? 1.f : 0.f);
+      if (below) x[k][j] = vk[k];
 #pragma unroll
-      for (int q = 0; q < kQrPanel; ++q) {
-        if (q == j && below) x[k][q] = vk;
-        w[q] += q == j ? 0.f : vk * x[k][q];
-      }
+      for (int q = 0; q < kQrPanel; ++q) w[q] += vk[k] * x[k][q];
     }
     block_sum16(w, part, tot);
 
@@ -612,16 +621,20 @@ __global__ __launch_bounds__(kRegThreads) void qr_panel_reg_kernel(QrPanelArgs a
       for (int k = tid; k < j; ++k) t += Ts[tid][k] * tot[k];
       Ts[tid][j] = -tau * t;
     }
+    // columns right of j: x_q -= tau (v^T x_q) v
+    float cq[kQrPanel];
 #pragma unroll
-    for (int k = 0; k < kRegRows; ++k) {
-      const int r = tid + kRegThreads * k;
-      const float vk = (r > j && r < h) ? column(k, j) : (r == j ? 1.f : 0.f);
+    for (int q = 0; q < kQrPanel; ++q) cq[q] = q > j ? tau * tot[q] : 0.f;
 #pragma unroll
-      for (int q = 0; q < kQrPanel; ++q)
-        if (q > j) x[k][q] -= tau * tot[q] * vk;
-    }
+    for (int k = 0; k < kRegRows; ++k)
+#pragma unroll
+      for (int q = 0; q < kQrPanel; ++q) x[k][q] = q > j ? x[k][q] - cq[q] * vk[k] : x[k][q];
   }
   __syncthreads();
+  if (tid < nb) {
+    sg[c0 + tid] = sgs[tid];
+    tg[c0 + tid] = Ts[tid][tid];
+  }
 
   // explicit reflectors, column-major in the slot (coalesced across lanes)
 #pragma unroll
