@@ -285,8 +285,8 @@ def bench_soap(args):
                         "traffic": measured_traffic("soap_sgemm_8b-dense-layer_hbm_traffic.md", "soap.hip",
                                                     "soap_products_bytes_per_step")
                         if cfg.slug == "8b-dense-layer" else None,
-                        "kernel": "sgemm_kernel (statistics and rotation products; timed with the rotated-Adam "
-                                  "kernel of the precondition phase)"},
+                        "kernel": "sgemm_list_kernel and sgemm_kernel (statistics and rotation products; timed "
+                                  "with the rotated-Adam kernel of the precondition phase)"},
            "cpu_baseline": cpu}
     print(json.dumps(out), flush=True)
 
