@@ -370,6 +370,23 @@ muon_status_t soap_precondition(const muon_batch_t* grad, const muon_batch_t* QL
                                 int64_t step, float beta1, float beta2, float eps, void* workspace,
                                 size_t ws_bytes, void* stream);
 
+/* soap_precondition for up to 8 groups (shape classes) at once, with one
+ * step count and one set of hyperparameters: grads, mbars, vbars and dirs
+ * are host arrays of ngroups descriptors, QLs and QRs host arrays of
+ * ngroups pointers (NULL: identity).  Each rotation stage launches the
+ * products of all groups together; every direction is bit-identical to
+ * soap_precondition on its group.  The workspace holds two m x n
+ * temporaries per group (the sum of the groups' soap_precondition
+ * workspaces).  Errors name the group; nothing is enqueued unless every
+ * group is valid. */
+size_t soap_precondition_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
+                                           const int64_t* cols);
+muon_status_t soap_precondition_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* QLs,
+                                        const muon_batch_t* const* QRs, const muon_batch_t* mbars,
+                                        const muon_batch_t* vbars, const muon_batch_t* dirs, int64_t step,
+                                        float beta1, float beta2, float eps, void* workspace, size_t ws_bytes,
+                                        void* stream);
+
 /* Static text for a status code. */
 const char* muon_status_string(muon_status_t status);
 /* Thread-local detail of the last non-OK return on this thread ("" if none). */

@@ -29,7 +29,8 @@ EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_m
             "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
             "soap_statistics_grouped", "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
             "soap_refresh_grouped_workspace", "soap_refresh_grouped",
-            "soap_precondition_workspace", "soap_precondition")
+            "soap_precondition_workspace", "soap_precondition", "soap_precondition_grouped_workspace",
+            "soap_precondition_grouped")
 
 ADAMW_CHUNK = 4096  # MUON_ADAMW_CHUNK
 
@@ -98,6 +99,10 @@ def load() -> ctypes.CDLL:
                                                 ctypes.POINTER(P), ctypes.POINTER(P), P, vp, sz, vp]),
         "soap_precondition_workspace": (sz, [i64, i64, i64]),
         "soap_precondition": (ctypes.c_int, [P, P, P, P, P, P, i64, f32, f32, f32, vp, sz, vp]),
+        "soap_precondition_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                                     ctypes.POINTER(i64)]),
+        "soap_precondition_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(P), ctypes.POINTER(P), P, P, P,
+                                                     i64, f32, f32, f32, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -268,3 +273,23 @@ def soap_precondition(grad: MuonBatch, QL: MuonBatch | None, QR: MuonBatch | Non
     st = load().soap_precondition(_ref(grad), _ref(QL), _ref(QR), _ref(mbar), _ref(vbar), _ref(direction), step,
                                   beta1, beta2, eps, workspace_ptr, ws_bytes, stream)
     _check(st, "soap_precondition")
+
+
+def soap_precondition_grouped_workspace(counts, rows, cols) -> int:
+    n = len(counts)
+    i64 = ctypes.c_int64 * n
+    return load().soap_precondition_grouped_workspace(n, i64(*counts), i64(*rows), i64(*cols))
+
+
+def soap_precondition_grouped(grads, QLs, QRs, mbars, vbars, dirs, step: int, beta1: float, beta2: float,
+                              eps: float, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    """grads, mbars, vbars, dirs: per-group MuonBatch; QLs, QRs: per-group MuonBatch or None."""
+    n = len(grads)
+    if not (len(QLs) == len(QRs) == len(mbars) == len(vbars) == len(dirs) == n):
+        raise ValueError("per-group lists differ in length")
+    PB = ctypes.POINTER(MuonBatch)
+    arr = lambda xs: (PB * n)(*[PB() if x is None else ctypes.pointer(x) for x in xs])
+    vec = lambda xs: (MuonBatch * n)(*xs)
+    st = load().soap_precondition_grouped(n, vec(grads), arr(QLs), arr(QRs), vec(mbars), vec(vbars), vec(dirs), step,
+                                          beta1, beta2, eps, workspace_ptr, ws_bytes, stream)
+    _check(st, "soap_precondition_grouped")

@@ -1051,6 +1051,125 @@ muon_status_t statistics(int ngroups, const muon_batch_t* grads, const muon_batc
   return done(s, grouped ? "soap_statistics_grouped" : "soap_statistics");
 }
 
+
+// soap_precondition and soap_precondition_grouped.  Per group, with
+// temporaries w1, w2 (m x n each) at the group's place in the workspace:
+//   Gbar = QL^T G QR (a side without a basis skipped), Dbar = Adam's
+//   direction in the rotated basis, D = QL Dbar QR^T.
+// Every rotation stage launches the products of all groups together.
+muon_status_t precondition(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* QLs,
+                           const muon_batch_t* const* QRs, const muon_batch_t* mbars, const muon_batch_t* vbars,
+                           const muon_batch_t* dirs, int64_t step, float beta1, float beta2, float eps,
+                           void* workspace, size_t ws_bytes, void* stream, bool grouped) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!grads || !QLs || !QRs || !mbars || !vbars || !dirs)
+    return fail(MUON_ERR_INVALID_VALUE, "the per-group arrays must not be NULL");
+  auto tag = [&](muon_status_t st, int g) { return grouped ? in_group(st, g) : st; };
+  muon_status_t st;
+  int64_t counts[kMaxGroups], rows[kMaxGroups], cols[kMaxGroups];
+  for (int g = 0; g < ngroups; ++g) {
+    const muon_batch_t* grad = &grads[g];
+    if ((st = check_batch(grad, "grad", true)) != MUON_OK) return tag(st, g);
+    const int64_t c = grad->count, m = grad->rows, n = grad->cols;
+    if (QLs[g] && (st = check_f32(QLs[g], "QL", c, m, m)) != MUON_OK) return tag(st, g);
+    if (QRs[g] && (st = check_f32(QRs[g], "QR", c, n, n)) != MUON_OK) return tag(st, g);
+    if ((st = check_f32(&mbars[g], "mbar", c, m, n)) != MUON_OK) return tag(st, g);
+    if ((st = check_f32(&vbars[g], "vbar", c, m, n)) != MUON_OK) return tag(st, g);
+    if ((st = check_f32(&dirs[g], "dir", c, m, n)) != MUON_OK) return tag(st, g);
+    counts[g] = c;
+    rows[g] = m;
+    cols[g] = n;
+  }
+  if (step < 1) return fail(MUON_ERR_INVALID_VALUE, "step %lld < 1", (long long)step);
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f))
+    return fail(MUON_ERR_INVALID_VALUE, "betas must lie in [0, 1)");
+  if (!(finite(eps) && eps >= 0.f)) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
+  const size_t need = soap_precondition_grouped_workspace(ngroups, counts, rows, cols);
+  if (need == 0) return fail(MUON_ERR_UNSUPPORTED, "sizes outside the supported range");
+  if ((st = check_workspace(workspace, ws_bytes, need)) != MUON_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  float* w1[kMaxGroups];
+  float* w2[kMaxGroups];
+  int64_t wm[kMaxGroups];
+  float* cur = static_cast<float*>(workspace);
+  for (int g = 0; g < ngroups; ++g) {
+    wm[g] = round64(rows[g] * cols[g]);
+    w1[g] = cur;
+    w2[g] = cur + counts[g] * wm[g];
+    cur += 2 * counts[g] * wm[g];
+  }
+  SgemmArgs gs[kMaxGroups];
+  int np = 0;
+  auto flush = [&](const char* what) -> muon_status_t {
+    if (np > 0) {
+      const hipError_t e = launch_sgemm_list(gs, np, s);
+      np = 0;
+      if (e != hipSuccess) return launch_status(e, what);
+    }
+    return MUON_OK;
+  };
+  // Gbar: the left rotation (or the right one alone) ...
+  for (int g = 0; g < ngroups; ++g) {
+    const muon_batch_t* grad = &grads[g];
+    const int64_t c = counts[g], m = rows[g], n = cols[g];
+    if (QLs[g])
+      gs[np++] = gemm_args(op_batch(QLs[g], false), op_batch(grad, false), out_ws(QRs[g] ? w1[g] : w2[g], wm[g], n),
+                           m, n, m, c, 1.f, 0.f, false);
+    else if (QRs[g])
+      gs[np++] = gemm_args(op_batch(grad, true), op_batch(QRs[g], false), out_ws(w2[g], wm[g], n), m, n, n, c, 1.f,
+                           0.f, false);
+  }
+  if ((st = flush("rotate in")) != MUON_OK) return st;
+  // ... then the right rotation of the two-sided groups
+  for (int g = 0; g < ngroups; ++g)
+    if (QLs[g] && QRs[g])
+      gs[np++] = gemm_args(op_ws(w1[g], wm[g], cols[g], true), op_batch(QRs[g], false), out_ws(w2[g], wm[g], cols[g]),
+                           rows[g], cols[g], cols[g], counts[g], 1.f, 0.f, false);
+  if ((st = flush("rotate in, right")) != MUON_OK) return st;
+  // Adam in the rotated basis: Dbar into w2 (in place over Gbar), or into
+  // dir when both bases are the identity
+  const float c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
+  const float c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
+  for (int g = 0; g < ngroups; ++g) {
+    const bool rot = QLs[g] || QRs[g];
+    const MatBatch tmp{reinterpret_cast<char*>(w2[g]), wm[g] * 4, nullptr, cols[g], MUON_F32, 0};
+    RotAdamArgs ra;
+    std::memset(&ra, 0, sizeof(ra));
+    ra.G = rot ? tmp : to_mat(&grads[g]);
+    ra.M = to_mat(&mbars[g]);
+    ra.V = to_mat(&vbars[g]);
+    ra.out = rot ? tmp : to_mat(&dirs[g]);
+    ra.rows = static_cast<int32_t>(rows[g]);
+    ra.cols = static_cast<int32_t>(cols[g]);
+    ra.beta1 = beta1;
+    ra.beta2 = beta2;
+    ra.eps = eps;
+    ra.c1 = c1;
+    ra.c2 = c2;
+    SOAP_TRY(launch_rot_adam(ra, counts[g], s), "rotated adam");
+  }
+  // D = QL Dbar QR^T: the left rotation back (or the right one alone) ...
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t c = counts[g], m = rows[g], n = cols[g];
+    if (QLs[g])
+      gs[np++] = gemm_args(op_batch(QLs[g], true), op_ws(w2[g], wm[g], n, false),
+                           QRs[g] ? out_ws(w1[g], wm[g], n) : out_batch(&dirs[g]), m, n, m, c, 1.f, 0.f, false);
+    else if (QRs[g])
+      gs[np++] = gemm_args(op_ws(w2[g], wm[g], n, true), op_batch(QRs[g], true), out_batch(&dirs[g]), m, n, n, c,
+                           1.f, 0.f, false);
+  }
+  if ((st = flush("rotate back")) != MUON_OK) return st;
+  // ... then the right rotation back of the two-sided groups
+  for (int g = 0; g < ngroups; ++g)
+    if (QLs[g] && QRs[g])
+      gs[np++] = gemm_args(op_ws(w1[g], wm[g], cols[g], true), op_batch(QRs[g], true), out_batch(&dirs[g]), rows[g],
+                           cols[g], cols[g], counts[g], 1.f, 0.f, false);
+  if ((st = flush("rotate back, right")) != MUON_OK) return st;
+  return done(s, grouped ? "soap_precondition_grouped" : "soap_precondition");
+}
+
 }  // namespace
 
 extern "C" {
@@ -1237,74 +1356,37 @@ muon_status_t soap_refresh(const muon_batch_t* L, const muon_batch_t* R, const m
 }
 
 size_t soap_precondition_workspace(int64_t count, int64_t rows, int64_t cols) {
-  if (count < 1 || count > 65535 || rows < 1 || cols < 1 || rows > kMaxElems / cols) return 0;
-  return static_cast<size_t>(2 * count * round64(rows * cols) * 4);
+  return soap_precondition_grouped_workspace(1, &count, &rows, &cols);
+}
+
+size_t soap_precondition_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows,
+                                           const int64_t* cols) {
+  if (ngroups < 1 || ngroups > kMaxGroups || !counts || !rows || !cols) return 0;
+  int64_t total = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t c = counts[g], m = rows[g], n = cols[g];
+    if (c < 1 || c > 65535 || m < 1 || n < 1 || m > kMaxElems / n) return 0;
+    total += 2 * c * round64(m * n);
+  }
+  return static_cast<size_t>(total * 4);
 }
 
 muon_status_t soap_precondition(const muon_batch_t* grad, const muon_batch_t* QL, const muon_batch_t* QR,
                                 const muon_batch_t* mbar, const muon_batch_t* vbar, const muon_batch_t* dir,
                                 int64_t step, float beta1, float beta2, float eps, void* workspace,
                                 size_t ws_bytes, void* stream) {
-  muon_status_t st;
-  if ((st = check_batch(grad, "grad", true)) != MUON_OK) return st;
-  const int64_t c = grad->count, m = grad->rows, n = grad->cols;
-  if (QL && (st = check_f32(QL, "QL", c, m, m)) != MUON_OK) return st;
-  if (QR && (st = check_f32(QR, "QR", c, n, n)) != MUON_OK) return st;
-  if ((st = check_f32(mbar, "mbar", c, m, n)) != MUON_OK) return st;
-  if ((st = check_f32(vbar, "vbar", c, m, n)) != MUON_OK) return st;
-  if ((st = check_f32(dir, "dir", c, m, n)) != MUON_OK) return st;
-  if (step < 1) return fail(MUON_ERR_INVALID_VALUE, "step %lld < 1", (long long)step);
-  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f))
-    return fail(MUON_ERR_INVALID_VALUE, "betas must lie in [0, 1)");
-  if (!(finite(eps) && eps >= 0.f)) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
-  if ((st = check_workspace(workspace, ws_bytes, soap_precondition_workspace(c, m, n))) != MUON_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const int64_t wm = round64(m * n);
-  float* w1 = static_cast<float*>(workspace);
-  float* w2 = w1 + c * wm;
-  // Gbar = QL^T G QR (sides without a basis skipped)
-  MatBatch gbar = to_mat(grad);
-  if (QL) {
-    float* dst = QR ? w1 : w2;
-    SOAP_TRY(gemm(op_batch(QL, false), op_batch(grad, false), out_ws(dst, wm, n), m, n, m, c, 1.f, 0.f, false, s),
-             "rotate left");
-    gbar = MatBatch{reinterpret_cast<char*>(dst), wm * 4, nullptr, n, MUON_F32, 0};
-  }
-  if (QR) {
-    const SgemmOperand src = QL ? op_ws(w1, wm, n, true) : op_batch(grad, true);
-    SOAP_TRY(gemm(src, op_batch(QR, false), out_ws(w2, wm, n), m, n, n, c, 1.f, 0.f, false, s), "rotate right");
-    gbar = MatBatch{reinterpret_cast<char*>(w2), wm * 4, nullptr, n, MUON_F32, 0};
-  }
-  // Adam in the rotated basis: Dbar into w2 (in place over Gbar), or into
-  // dir when both bases are the identity
-  RotAdamArgs ra;
-  std::memset(&ra, 0, sizeof(ra));
-  ra.G = gbar;
-  ra.M = to_mat(mbar);
-  ra.V = to_mat(vbar);
-  ra.out = (QL || QR) ? MatBatch{reinterpret_cast<char*>(w2), wm * 4, nullptr, n, MUON_F32, 0} : to_mat(dir);
-  ra.rows = static_cast<int32_t>(m);
-  ra.cols = static_cast<int32_t>(n);
-  ra.beta1 = beta1;
-  ra.beta2 = beta2;
-  ra.eps = eps;
-  ra.c1 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta1), static_cast<double>(step))));
-  ra.c2 = static_cast<float>(1.0 / (1.0 - std::pow(static_cast<double>(beta2), static_cast<double>(step))));
-  SOAP_TRY(launch_rot_adam(ra, c, s), "rotated adam");
-  // D = QL Dbar QR^T
-  if (QL && QR) {
-    SOAP_TRY(gemm(op_batch(QL, true), op_ws(w2, wm, n, false), out_ws(w1, wm, n), m, n, m, c, 1.f, 0.f, false, s),
-             "rotate back left");
-    SOAP_TRY(gemm(op_ws(w1, wm, n, true), op_batch(QR, true), out_batch(dir), m, n, n, c, 1.f, 0.f, false, s),
-             "rotate back right");
-  } else if (QL) {
-    SOAP_TRY(gemm(op_batch(QL, true), op_ws(w2, wm, n, false), out_batch(dir), m, n, m, c, 1.f, 0.f, false, s),
-             "rotate back left");
-  } else if (QR) {
-    SOAP_TRY(gemm(op_ws(w2, wm, n, true), op_batch(QR, true), out_batch(dir), m, n, n, c, 1.f, 0.f, false, s),
-             "rotate back right");
-  }
-  return done(s, "soap_precondition");
+  if (!grad || !mbar || !vbar || !dir) return fail(MUON_ERR_INVALID_VALUE, "a required descriptor is NULL");
+  return precondition(1, grad, &QL, &QR, mbar, vbar, dir, step, beta1, beta2, eps, workspace, ws_bytes, stream,
+                      false);
+}
+
+muon_status_t soap_precondition_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* const* QLs,
+                                        const muon_batch_t* const* QRs, const muon_batch_t* mbars,
+                                        const muon_batch_t* vbars, const muon_batch_t* dirs, int64_t step,
+                                        float beta1, float beta2, float eps, void* workspace, size_t ws_bytes,
+                                        void* stream) {
+  return precondition(ngroups, grads, QLs, QRs, mbars, vbars, dirs, step, beta1, beta2, eps, workspace, ws_bytes,
+                      stream, true);
 }
 
 }  // extern "C"

@@ -193,6 +193,12 @@ __device__ __forceinline__ const char* entry(const SgemmOperand& o, int b) {
 // TM = 32 (products with at most 32 rows) as 1 x 4 waves of 32 x 32.  At
 // least three workgroups per CU (accumulators in VGPRs, no AGPRs): a third
 // wave per SIMD covers the LDS reads before each step's products.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // Tile (ti, tj) of batch entry and split z = bi * splits + sp.
 template <int TM, int CFG>
 __device__ __forceinline__ void sgemm_tile(const SgemmArgs& a, int ti, int tj, int z) {
@@ -224,10 +230,16 @@ __device__ __forceinline__ void sgemm_tile(const SgemmArgs& a, int ti, int tj, i
       for (int r = 0; r < 16; ++r) acc[x][y][r] = 0.f;
 
   float ra[(TM * kBK / 4 + kThreads - 1) / kThreads * 4], rb[(kT * kBK / 4 + kThreads - 1) / kThreads * 4];
+  // The fast path's address arguments, taken into scalar registers once: read
+  // from the argument block at a runtime offset (the product-list kernel),
+  // the compiler would otherwise reload them every slice, and the wait for
+  // those loads also waits for the slice's LDS stores.
+  const int64_t lda = uniform64(a.a.ld), ldb = uniform64(a.b.ld);
+  const int Mu = __builtin_amdgcn_readfirstlane(a.M), Nu = __builtin_amdgcn_readfirstlane(a.N);
   auto load = [&](int k0) {
     if constexpr (F::kOn) {
-      load_slice_fast<TM, F::kAB, F::kAK>(pa, a.a.ld, a.M, kend, i0, k0, ra);
-      load_slice_fast<kT, F::kBB, F::kBK>(pb, a.b.ld, a.N, kend, j0, k0, rb);
+      load_slice_fast<TM, F::kAB, F::kAK>(pa, lda, Mu, kend, i0, k0, ra);
+      load_slice_fast<kT, F::kBB, F::kBK>(pb, ldb, Nu, kend, j0, k0, rb);
     } else {
       load_slice<TM>(pa, a.a, a.M, kend, i0, k0, ra);
       load_slice<kT>(pb, a.b, a.N, kend, j0, k0, rb);

@@ -97,6 +97,21 @@ def precondition(grad, mbar, vbar, out, step: int, QL=None, QR=None, beta1: floa
     L.soap_precondition(*map(_desc, bs), step, beta1, beta2, eps, ws.data_ptr(), ws.numel(), _stream(stream))
 
 
+def precondition_grouped(grads, mbars, vbars, outs, step: int, QLs, QRs, beta1: float = BETA1, beta2: float = BETA2,
+                         eps: float = EPS, ws: torch.Tensor | None = None, stream=None) -> None:
+    """precondition() for up to 8 groups in one call: every rotation stage
+    launches the products of all groups together."""
+    bg, bm, bv, bo = ([batch(x) for x in xs] for xs in (grads, mbars, vbars, outs))
+    bl, br = ([None if x is None else batch(x) for x in xs] for xs in (QLs, QRs))
+    if ws is None:
+        need = L.soap_precondition_grouped_workspace([b.count for b in bg], [b.rows for b in bg],
+                                                     [b.cols for b in bg])
+        ws = workspace(need, bg[0].keep[-1].device)
+    L.soap_precondition_grouped([b.desc for b in bg], [_desc(b) for b in bl], [_desc(b) for b in br],
+                                [b.desc for b in bm], [b.desc for b in bv], [b.desc for b in bo], step, beta1, beta2,
+                                eps, ws.data_ptr(), ws.numel(), _stream(stream))
+
+
 class SoapStep:
     """SOAP state and buffers for groups of same-shape weights.
 
@@ -106,8 +121,8 @@ class SoapStep:
     direction D; an axis longer than ``max_dim`` keeps the identity basis.
     ``step()`` runs, per group and in this order: the statistics, the basis
     refresh on steps 1, 1 + freq, ..., the rotated Adam direction, and
-    W <- (1 - lr*wd) W - lr D.  The statistics and the refreshes of up to 8
-    preconditioned groups share each call.
+    W <- (1 - lr*wd) W - lr D.  The statistics, the refreshes and the
+    rotated Adam directions of up to 8 groups share each call.
     """
 
     def __init__(self, groups, *, lr: float = 3e-4, weight_decay: float = 0.0, betas=(BETA1, BETA2),
@@ -136,11 +151,16 @@ class SoapStep:
                   "QR": eye(n) if n <= max_dim else None,
                   "mbar": torch.zeros(c, m, n, **f), "vbar": torch.zeros(c, m, n, **f),
                   "D": torch.empty(c, m, n, **f)}
-            need = max(need, L.soap_precondition_workspace(c, m, n))
             self.groups.append(st)
         self.chunks = [[i for i in range(k, min(k + 8, len(self.groups))) if self._preconditioned(i)]
                        for k in range(0, len(self.groups), 8)]
         self.chunks = [ch for ch in self.chunks if ch]
+        # the rotated Adam direction of every group, 8 groups to a call
+        self.all_chunks = [list(range(k, min(k + 8, len(self.groups)))) for k in range(0, len(self.groups), 8)]
+        for ch in self.all_chunks:
+            ds = [self.groups[i]["D"].shape for i in ch]
+            need = max(need, L.soap_precondition_grouped_workspace([d[0] for d in ds], [d[1] for d in ds],
+                                                                   [d[2] for d in ds]))
         for ch in self.chunks:
             gs = [self.groups[i] for i in ch]
             need = max(need, L.soap_refresh_grouped_workspace(
@@ -192,9 +212,11 @@ class SoapStep:
                 refresh_grouped([g["mbar"] for g in gs], [g["L"] for g in gs], [g["R"] for g in gs],
                                 [g["QL"] for g in gs], [g["QR"] for g in gs], ws=self.ws, stream=s)
         rec(2)
-        for g in self.groups:
-            precondition(g["G"], g["mbar"], g["vbar"], g["D"], self.t, g["QL"], g["QR"], self.beta1, self.beta2,
-                         self.eps, ws=self.ws, stream=s)
+        for ch in self.all_chunks:
+            gs = [self.groups[i] for i in ch]
+            precondition_grouped([g["G"] for g in gs], [g["mbar"] for g in gs], [g["vbar"] for g in gs],
+                                 [g["D"] for g in gs], self.t, [g["QL"] for g in gs], [g["QR"] for g in gs],
+                                 self.beta1, self.beta2, self.eps, ws=self.ws, stream=s)
         rec(3)
         for g in self.groups:
             bw, bd = batch(g["W"]), batch(g["D"])

@@ -163,6 +163,21 @@ void soap_cases() {
     expect(soap_statistics_grouped(4, grads.data(), pl, pr, 0.9f, nullptr), MUON_OK, "soap_statistics_grouped");
     expect(soap_statistics_grouped(9, grads.data(), pl, pr, 0.9f, nullptr), MUON_ERR_INVALID_VALUE,
            "soap_statistics_grouped, 9 groups");
+    {
+      std::vector<muon_batch_t> vb, dirs;
+      for (int g = 0; g < 4; ++g) {
+        vb.push_back(batch(counts[g], rows[g], cols[g], MUON_F32));
+        dirs.push_back(batch(counts[g], rows[g], cols[g], MUON_F32));
+      }
+      const size_t pneed = soap_precondition_grouped_workspace(4, counts, rows, cols);
+      stub_set_workspace(kWs, pneed);
+      expect(soap_precondition_grouped(4, grads.data(), pql, pqr, mb.data(), vb.data(), dirs.data(), 2, 0.9f, 0.999f,
+                                       1e-8f, kWs, pneed, nullptr),
+             MUON_OK, "soap_precondition_grouped");
+      expect(soap_precondition_grouped(4, grads.data(), pql, pqr, mb.data(), vb.data(), dirs.data(), 2, 0.9f, 0.999f,
+                                       1e-8f, kWs, pneed - 1, nullptr),
+             MUON_ERR_WORKSPACE, "soap_precondition_grouped, short workspace");
+    }
     const size_t need = soap_refresh_grouped_workspace(4, counts, rows, cols, wl, wr);
     stub_set_workspace(kWs, need);
     expect(soap_refresh_grouped(4, pl, pr, pql, pqr, mb.data(), kWs, need, nullptr), MUON_OK, "soap_refresh_grouped");

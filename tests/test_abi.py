@@ -227,7 +227,8 @@ int main(void) {
   int64_t counts[2] = {2, 1}, rows[2] = {768, 4096}, cols[2] = {2048, 14336};
   size_t g = muon_momentum_grouped_workspace(2, counts, rows, cols);
   size_t q = soap_qr_workspace(2, 4096), r = soap_refresh_workspace(1, 1024, 4096, 1, 1);
-  if (w == 0 || m == 0 || g == 0 || q == 0 || r == 0) return 2;
+  size_t p = soap_precondition_grouped_workspace(2, counts, rows, cols);
+  if (w == 0 || m == 0 || g == 0 || q == 0 || r == 0 || p == 0) return 2;
   /* an invalid descriptor is rejected before anything reaches the GPU */
   muon_batch_t bad = {NULL, NULL, 0, 1, 64, 64, 64, MUON_F32, 0};
   muon_status_t st = muon_apply(&bad, &bad, 1e-3f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, NULL);
@@ -267,6 +268,11 @@ def test_soap_workspace_queries():
     assert L.soap_qr_workspace(2, 100) == 2 * L.soap_qr_workspace(1, 100)
     assert L.soap_precondition_workspace(3, 64, 96) == 2 * 3 * 64 * 96 * 4
     assert L.soap_precondition_workspace(1, 0, 5) == 0
+    # the grouped call holds every group's two temporaries at once
+    assert L.soap_precondition_grouped_workspace([3, 1], [64, 100], [96, 30]) == \
+        L.soap_precondition_workspace(3, 64, 96) + 2 * 3008 * 4
+    assert L.soap_precondition_grouped_workspace([1] * 9, [8] * 9, [8] * 9) == 0
+    assert L.soap_precondition_grouped_workspace([1, 0], [8, 8], [8, 8]) == 0
     # the refresh holds two moment temporaries plus the largest batched QR
     # (both sides of one order factor together)
     assert L.soap_refresh_workspace(1, 64, 128, 1, 1) == 2 * 64 * 128 * 4 + L.soap_qr_workspace(1, 128)
@@ -354,6 +360,28 @@ def test_soap_precondition_rejects_bad_arguments(kw, code):
     need = L.soap_precondition_workspace(c, m, n) + a["ws"]
     assert status_of(lambda: L.soap_precondition(g, ql, qr, st, st, d, a["step"], a["beta1"], a["beta2"], a["eps"],
                                                  FAKE, need, 0)) == code
+
+
+def test_soap_precondition_grouped_rejects_bad_arguments():
+    shapes = [(2, 64, 96), (1, 40, 72)]
+    g = [desc(count=c, rows=m, cols=n, dtype=L.MUON_BF16) for c, m, n in shapes]
+    st = [desc(count=c, rows=m, cols=n) for c, m, n in shapes]
+    ql = [desc(count=2, rows=64, cols=64), None]
+    qr = [desc(count=2, rows=96, cols=96), desc(count=1, rows=72, cols=72)]
+    need = L.soap_precondition_grouped_workspace(*zip(*shapes))
+    call = lambda **kw: L.soap_precondition_grouped(kw.get("g", g), kw.get("ql", ql), kw.get("qr", qr), st, st,
+                                                    kw.get("d", st), kw.get("step", 1), 0.9, 0.999, 1e-8, FAKE,
+                                                    kw.get("ws", need), 0)
+    assert status_of(lambda: call(ws=need - 1)) == WORKSPACE
+    assert status_of(lambda: call(step=0)) == INVALID
+    # group 1's right basis has the wrong order: the error names group 1
+    assert status_of(lambda: call(qr=[qr[0], desc(count=1, rows=40, cols=40)])) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: call(d=[st[0], desc(count=1, rows=40, cols=72, dtype=L.MUON_BF16)])) == UNSUPPORTED
+    assert status_of(lambda: L.soap_precondition_grouped([], [], [], [], [], [], 1, 0.9, 0.999, 1e-8, FAKE, need,
+                                                         0)) == INVALID
+    with pytest.raises(ValueError):
+        L.soap_precondition_grouped(g, ql, qr[:1], st, st, st, 1, 0.9, 0.999, 1e-8, FAKE, need, 0)
 
 
 def test_soap_refresh_grouped_rejects_bad_arguments():

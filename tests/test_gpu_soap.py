@@ -320,3 +320,45 @@ def test_grouped_statistics_bit_identical_to_per_group(mx):
                 S0 = 0.5 * np.eye(G.shape[side])
                 want = S.statistics(S0, None, G, 0.9)[0] if side == 0 else S.statistics(None, S0, G, 0.9)[1]
                 assert rel(f64(b[i]), want) <= 1e-6, (k, side, i)
+
+
+@pytest.mark.gpu
+def test_grouped_precondition_bit_identical_to_per_group(mx):
+    """soap_precondition_grouped launches each rotation stage for all groups
+    together; every direction and moment is bit-identical to one call per
+    group.  The groups cover both sides, the left or the right side alone,
+    and neither (the identity bases: plain Adam), with bf16 and fp32
+    gradients.  The oracle checks one step's direction."""
+    from matrix_aware_optimizer_step_amd import soap
+    torch.manual_seed(12)
+    shapes = [(2, 96, 160), (1, 130, 64), (3, 48, 200), (1, 40, 36)]
+    sides = [(True, True), (True, False), (False, True), (False, False)]
+    dts = [torch.bfloat16, torch.float32, torch.float32, torch.bfloat16]
+    orth = lambda c, d: torch.linalg.qr(torch.randn(c, d, d, dtype=torch.float64))[0].float().contiguous().cuda()
+    grads = [torch.randn(c, m, n, device="cuda").to(dt) for (c, m, n), dt in zip(shapes, dts)]
+    QLs = [orth(c, m) if wl else None for (c, m, n), (wl, _) in zip(shapes, sides)]
+    QRs = [orth(c, n) if wr else None for (c, m, n), (_, wr) in zip(shapes, sides)]
+    m0 = [0.1 * torch.randn(c, m, n, device="cuda") for c, m, n in shapes]
+    v0 = [0.01 * torch.rand(c, m, n, device="cuda") for c, m, n in shapes]
+    runs = []
+    for grouped in (False, True):
+        mb = [x.clone() for x in m0]
+        vb = [x.clone() for x in v0]
+        D = [torch.empty(c, m, n, device="cuda") for c, m, n in shapes]
+        print(f"precondition grouped={grouped}", flush=True)
+        if grouped:
+            soap.precondition_grouped(grads, mb, vb, D, 3, QLs, QRs, eps=1e-2)
+        else:
+            for k in range(len(shapes)):
+                soap.precondition(grads[k], mb[k], vb[k], D[k], 3, QLs[k], QRs[k], eps=1e-2)
+        torch.cuda.synchronize()
+        runs.append((mb, vb, D))
+    for k, (c, m, n) in enumerate(shapes):
+        for j in range(3):
+            assert torch.equal(runs[0][j][k], runs[1][j][k]), (k, j)
+        for i in range(c):
+            QL = f64(QLs[k][i]) if QLs[k] is not None else np.eye(m)
+            QR = f64(QRs[k][i]) if QRs[k] is not None else np.eye(n)
+            want, _, _ = S.precondition(f64(grads[k][i]), QL, QR, f64(m0[k][i]), f64(v0[k][i]), 3, S.BETA1, S.BETA2,
+                                        1e-2)
+            assert rel(f64(runs[1][2][k][i]), want) <= 1e-3, (k, i, rel(f64(runs[1][2][k][i]), want))
