@@ -177,17 +177,23 @@ def soap_flops(m, n, with_l, with_r, refresh=False):
     """Algorithmic flops of one SOAP update of an m x n matrix: the
     statistics (upper triangles), the rotations of G into the basis and of
     the direction back; with ``refresh`` the power-iteration product, the
-    Householder QR (4/3 d^3 to factor, 4/3 d^3 to form Q) and the two
-    products that carry the first moment into the new basis, per side."""
+    Householder QR (4/3 d^3 to factor, 4/3 d^3 to form Q) and the products
+    that carry the first moment into the new basis, per side (two of m x n
+    by d, or for one side alone on the shorter axis the d x d basis change
+    and one of m x n by d)."""
     f = 0
     if with_l:
         f += m * (m + 1) * n + 2 * (2 * m * m * n)
         if refresh:
-            f += 2 * m ** 3 + (8 * m ** 3) // 3 + 2 * (2 * m * m * n)
+            # the moment's re-rotation: QL_new^T (QL_old mbar), or with the left
+            # side alone and n > m, (QL_new^T QL_old) mbar
+            carry = 2 * m ** 3 + 2 * m * m * n if (not with_r and n > m) else 2 * (2 * m * m * n)
+            f += 2 * m ** 3 + (8 * m ** 3) // 3 + carry
     if with_r:
         f += n * (n + 1) * m + 2 * (2 * m * n * n)
         if refresh:
-            f += 2 * n ** 3 + (8 * n ** 3) // 3 + 2 * (2 * m * n * n)
+            carry = 2 * n ** 3 + 2 * m * n * n if (not with_l and m > n) else 2 * (2 * m * n * n)
+            f += 2 * n ** 3 + (8 * n ** 3) // 3 + carry
     return f
 
 

@@ -1297,29 +1297,48 @@ muon_status_t soap_refresh_grouped(int ngroups, const muon_batch_t* const* Ls, c
     int nouts = 0;
     int64_t first = 0;
     // power-iteration products and the first moment in the old bases:
-    // t1 = QL_old mbar, or mbar QR_old^T, or (both sides of this order) t2 = QL_old mbar QR_old^T
+    // t1 = QL_old mbar, or mbar QR_old^T, or (both sides of this order) t2 = QL_old mbar QR_old^T.
+    // A group with one side whose other axis is longer (ql / qr) instead
+    // keeps mbar (t1) and the old basis (t2), and carries mbar through the
+    // small product C = QL_new^T QL_old (or QR_old^T QR_new) after the QR:
+    // 2 d^3 + 2 m n d flops instead of 4 m n d.
+    int64_t slot[kMaxGroups];
     for (int g = 0; g < ngroups; ++g) {
       const int64_t c = counts[g], m = rows[g], n = cols[g], tm = round64(m * n);
       const bool l = wl[g] && m == d, r = wr[g] && n == d;
+      const bool ql = l && !wr[g] && n > m, qr = r && !wl[g] && m > n;
+      if (ql || qr) {
+        SOAP_TRY(launch_gather(to_mat(&mbars[g]), t1[g], tm, static_cast<int32_t>(m), static_cast<int32_t>(n), c, s),
+                 "refresh moment copy");
+        SOAP_TRY(launch_gather(to_mat(ql ? QLs[g] : QRs[g]), t2[g], tm, static_cast<int32_t>(d),
+                               static_cast<int32_t>(d), c, s),
+                 "refresh old basis copy");
+      }
       if (l) {
         SOAP_TRY(gemm(op_batch(Ls[g], true), op_batch(QLs[g], false), out_ws(P + first * pm, pm, m), m, m, m, c, 1.f,
                       0.f, false, s),
                  "refresh power step L");
         outs[nouts++] = QrOut{QLs[g], first, c};
+        slot[g] = first;
         first += c;
-        SOAP_TRY(gemm(op_batch(QLs[g], true), op_batch(&mbars[g], false), out_ws(t1[g], tm, n), m, n, m, c, 1.f, 0.f,
-                      false, s),
-                 "refresh moment L");
+        if (!ql)
+          SOAP_TRY(gemm(op_batch(QLs[g], true), op_batch(&mbars[g], false), out_ws(t1[g], tm, n), m, n, m, c, 1.f,
+                        0.f, false, s),
+                   "refresh moment L");
       }
       if (r) {
         SOAP_TRY(gemm(op_batch(Rs[g], true), op_batch(QRs[g], false), out_ws(P + first * pm, pm, n), n, n, n, c, 1.f,
                       0.f, false, s),
                  "refresh power step R");
         outs[nouts++] = QrOut{QRs[g], first, c};
+        slot[g] = first;
         first += c;
-        const SgemmOperand src = l ? op_ws(t1[g], tm, n, true) : op_batch(&mbars[g], true);
-        SOAP_TRY(gemm(src, op_batch(QRs[g], true), out_ws(l ? t2[g] : t1[g], tm, n), m, n, n, c, 1.f, 0.f, false, s),
-                 "refresh moment R");
+        if (!qr) {
+          const SgemmOperand src = l ? op_ws(t1[g], tm, n, true) : op_batch(&mbars[g], true);
+          SOAP_TRY(gemm(src, op_batch(QRs[g], true), out_ws(l ? t2[g] : t1[g], tm, n), m, n, n, c, 1.f, 0.f, false,
+                        s),
+                   "refresh moment R");
+        }
       }
     }
     if ((st = qr_enqueue(P, pm, d, total, qws, outs, nouts, s)) != MUON_OK) return st;
@@ -1334,10 +1353,28 @@ muon_status_t soap_refresh_grouped(int ngroups, const muon_batch_t* const* Ls, c
         SOAP_TRY(gemm(op_ws(t1[g], tm, n, true), op_batch(QRs[g], false), out_batch(&mbars[g]), m, n, n, c, 1.f, 0.f,
                       false, s),
                  "refresh moment R'");
+      } else if (l && !wr[g] && n > m) {
+        // C = QL_new^T QL_old in the group's QR input slot (free after the QR), then mbar = C t1
+        float* C = P + slot[g] * pm;
+        SOAP_TRY(gemm(op_batch(QLs[g], false), op_ws(t2[g], tm, m, false), out_ws(C, pm, m), m, m, m, c, 1.f, 0.f,
+                      false, s),
+                 "refresh basis change L");
+        SOAP_TRY(gemm(op_ws(C, pm, m, true), op_ws(t1[g], tm, n, false), out_batch(&mbars[g]), m, n, m, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment L'");
       } else if (l) {
         SOAP_TRY(gemm(op_batch(QLs[g], false), op_ws(t1[g], tm, n, false), out_batch(&mbars[g]), m, n, m, c, 1.f, 0.f,
                       false, s),
                  "refresh moment L'");
+      } else if (r && !wl[g] && m > n) {
+        // C = QR_old^T QR_new in the group's QR input slot, then mbar = t1 C
+        float* C = P + slot[g] * pm;
+        SOAP_TRY(gemm(op_ws(t2[g], tm, n, false), op_batch(QRs[g], false), out_ws(C, pm, n), n, n, n, c, 1.f, 0.f,
+                      false, s),
+                 "refresh basis change R");
+        SOAP_TRY(gemm(op_ws(t1[g], tm, n, true), op_ws(C, pm, n, false), out_batch(&mbars[g]), m, n, n, c, 1.f, 0.f,
+                      false, s),
+                 "refresh moment R'");
       } else if (r) {
         SOAP_TRY(gemm(op_ws(t1[g], tm, n, true), op_batch(QRs[g], false), out_batch(&mbars[g]), m, n, n, c, 1.f, 0.f,
                       false, s),
