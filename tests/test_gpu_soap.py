@@ -170,7 +170,7 @@ def run_steps(mx, m, n, steps, *, count=2, max_dim=4096, freq=2, eps=1e-2, wdtyp
     return worst, worst_q
 
 
-@pytest.mark.parametrize("m,n", [(64, 96), (96, 64), (130, 70), (33, 200)])
+@pytest.mark.parametrize("m,n", [(64, 96), (96, 64), (130, 70), (33, 200), (20, 64)])
 def test_soap_steps_match_oracle(mx, m, n):
     print(f"soap steps {m}x{n}", flush=True)
     run_steps(mx, m, n, steps=4, freq=2)
