@@ -33,8 +33,9 @@ Pin status: every function here is pinned by the CPU tests against values
 the pages print (worked 2x2 example, scalar trajectories, the 64x256 band and
 update RMS), against closed forms (Lemma 3 via an SVD, the exact polar factor,
 the EMA geometric sum, the decay product) and against invariants (transpose
-equivariance, scale invariance, odd symmetry).  No function is
-"parity unpinned".
+equivariance, scale invariance, odd symmetry); the checker
+``relative_frobenius_error`` is pinned to hand-computed values on integer
+matrices.  No function is "parity unpinned".
 """
 
 from __future__ import annotations
@@ -188,9 +189,14 @@ def muon_step(weight, mom, grad, *, beta: float = BETA, nesterov: bool = True,
 
 
 def relative_frobenius_error(got, want) -> float:
-    """||got - want||_F / ||want||_F (0 when both are zero)."""
+    """||got - want||_F / ||want||_F, entries paired by position; ||got||_F
+    when ``want`` is zero.  This is the measure the parity tolerances are
+    stated in (relative Frobenius error).  Both arguments must have the same
+    shape: NumPy would otherwise broadcast (n, 1) against (1, n)."""
     g = _f64(got)
     w = _f64(want)
+    if g.shape != w.shape:
+        raise ValueError(f"shapes differ: {g.shape} vs {w.shape}")
     den = math.sqrt(float(np.sum(w * w)))
     num = math.sqrt(float(np.sum((g - w) ** 2)))
     if den == 0.0:
