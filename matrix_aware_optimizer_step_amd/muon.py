@@ -35,6 +35,7 @@ class Batch:
     rows: int
     cols: int
     keep: list = field(default_factory=list)
+    owned: list = field(default_factory=list)  # device tensors batch() allocated (the pointer array)
 
 
 def batch(x) -> Batch:
@@ -57,7 +58,7 @@ def batch(x) -> Batch:
         ptrs = torch.tensor([t.data_ptr() for t in x], dtype=torch.int64, device=t0.device)
         d = L.MuonBatch(ptrs.data_ptr(), None, 0, len(x), t0.shape[0], t0.shape[1], t0.stride(0),
                         dtype_code(t0), 0)
-        return Batch(d, len(x), t0.shape[0], t0.shape[1], [ptrs, *x])
+        return Batch(d, len(x), t0.shape[0], t0.shape[1], [ptrs, *x], [ptrs])
     t = x
     if t.is_sparse:
         raise RuntimeError("dense gradients required")
@@ -85,15 +86,43 @@ def workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
+def _stream_object(stream):
+    """The torch stream object of a ``stream=`` argument (None: the current
+    stream, which needs no bookkeeping)."""
+    if stream is None or hasattr(stream, "cuda_stream"):
+        return stream
+    return torch.cuda.ExternalStream(int(stream))
+
+
+def _record_on(stream, tensors) -> None:
+    """Tensors this module allocated for one call and drops on return (a
+    workspace, the device pointer array of a list input) are still read by
+    the kernels enqueued on ``stream``.  The caching allocator ties a block
+    to the stream it was allocated on (the current one); recording the
+    launch stream keeps the block from going to new work before the kernels
+    on that stream are done."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None and getattr(t, "is_cuda", False):
+            t.record_stream(stream)
+
+
+def _owned(batches) -> list:
+    return [t for b in batches if b is not None for t in b.owned]
+
+
 def momentum(grad, mom, nout, sumsq: torch.Tensor, beta: float = 0.95, nesterov: bool = True,
              ws: torch.Tensor | None = None, stream=None) -> None:
     g, m = batch(grad), batch(mom)
     n = batch(nout) if nout is not None else None
     need = L.muon_momentum_workspace(g.count, g.rows, g.cols)
+    own_ws = ws is None
     if ws is None:
         ws = workspace(need, sumsq.device)
     L.muon_momentum(g.desc, m.desc, n.desc if n else None, sumsq.data_ptr(), beta, nesterov,
                     ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned([g, m, n]))
 
 
 def momentum_grouped(grads, moms, nouts, sumsqs, beta: float = 0.95, nesterov: bool = True,
@@ -103,23 +132,27 @@ def momentum_grouped(grads, moms, nouts, sumsqs, beta: float = 0.95, nesterov: b
     bg = [batch(x) for x in grads]
     bm = [batch(x) for x in moms]
     bn = None if nouts is None else [batch(x) for x in nouts]
+    own_ws = ws is None
     if ws is None:
         need = L.muon_momentum_grouped_workspace([b.count for b in bg], [b.rows for b in bg], [b.cols for b in bg])
         ws = workspace(need, sumsqs[0].device)
     L.muon_momentum_grouped([b.desc for b in bg], [b.desc for b in bm], None if bn is None else [b.desc for b in bn],
                             [s.data_ptr() for s in sumsqs], beta, nesterov, ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bg + bm + (bn or [])))
 
 
 def orthogonalize(inp, out, sumsq: torch.Tensor | None = None, steps: int = 5, coeffs=QUINTIC,
                   eps: float = EPS, compute: int = L.MUON_BF16, ws: torch.Tensor | None = None,
                   stream=None, device=None) -> None:
     i, o = batch(inp), batch(out)
+    own_ws = ws is None
     if ws is None:
         need = L.muon_orthogonalize_workspace(i.count, i.rows, i.cols, compute)
         ws = workspace(need, device or (sumsq.device if sumsq is not None else i.keep[-1].device))
     a, b, c = coeffs
     L.muon_orthogonalize(i.desc, sumsq.data_ptr() if sumsq is not None else None, o.desc, steps, a, b, c,
                          eps, compute, ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned([i, o]))
 
 
 def orthogonalize_grouped(ins, outs, sumsqs=None, steps: int = 5, coeffs=QUINTIC, eps: float = EPS,
@@ -127,6 +160,7 @@ def orthogonalize_grouped(ins, outs, sumsqs=None, steps: int = 5, coeffs=QUINTIC
                           device=None) -> None:
     bi = [batch(x) for x in ins]
     bo = [batch(x) for x in outs]
+    own_ws = ws is None
     if ws is None:
         need = L.muon_orthogonalize_grouped_workspace([b.count for b in bi], [b.rows for b in bi],
                                                       [b.cols for b in bi], compute)
@@ -135,12 +169,14 @@ def orthogonalize_grouped(ins, outs, sumsqs=None, steps: int = 5, coeffs=QUINTIC
     sp = None if sumsqs is None else [s.data_ptr() if s is not None else 0 for s in sumsqs]
     L.muon_orthogonalize_grouped([x.desc for x in bi], sp, [x.desc for x in bo], steps, a, b, c, eps, compute,
                                  ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bi + bo))
 
 
 def apply(weight, ortho, lr: float, weight_decay: float, mode: int = L.MUON_SCALE_MATCH_RMS,
           coeff: float = 0.2, stream=None) -> None:
     w, o = batch(weight), batch(ortho)
     L.muon_apply(w.desc, o.desc, lr, weight_decay, mode, coeff, _stream(stream))
+    _record_on(_stream_object(stream), _owned([w, o]))
 
 
 def apply_grouped(weights, orthos, lr: float, weight_decay: float, mode: int = L.MUON_SCALE_MATCH_RMS,
@@ -151,6 +187,7 @@ def apply_grouped(weights, orthos, lr: float, weight_decay: float, mode: int = L
     bw = [batch(x) for x in weights]
     bo = [batch(x) for x in orthos]
     L.muon_apply_grouped([b.desc for b in bw], [b.desc for b in bo], lr, weight_decay, mode, coeff, _stream(stream))
+    _record_on(_stream_object(stream), _owned(bw + bo))
 
 
 class MuonStep:
@@ -342,13 +379,39 @@ class AdamW:
 
 # ------------------------------------------------------ routing helper
 
-DEFAULT_ADAMW_NAMES = ("embed", "wte", "wpe", "lm_head", "head", "output")
+# Module names that mark an embedding or the output head wherever they sit
+# in a parameter's dotted name (Hugging Face, GPT-2 and Meta Llama naming).
+EMBEDDING_OR_HEAD_MODULES = frozenset({
+    "embed", "embeds", "embedding", "embeddings", "embed_tokens", "tok_embeddings", "word_embeddings",
+    "position_embeddings", "token_type_embeddings", "embed_positions", "wte", "wpe", "lm_head"})
+# Names that are the output head only as a top-level module ("output.weight",
+# "head.weight"); deeper in a model they name hidden projections (BERT's
+# "attention.output.dense", an MLP's "output" layer) that belong to Muon.
+TOP_LEVEL_HEAD_MODULES = frozenset({"output", "head", "classifier", "score"})
 
 
-def is_muon_param(name: str, p: torch.Tensor, adamw_names=DEFAULT_ADAMW_NAMES) -> bool:
+def is_muon_param(name: str, p: torch.Tensor, embedding_or_head_modules=EMBEDDING_OR_HEAD_MODULES,
+                  top_level_head_modules=TOP_LEVEL_HEAD_MODULES) -> bool:
     """Muon takes the 2-D hidden weight matrices; embeddings, the output head
-    and every tensor that is not 2-D (norms, biases) stay with AdamW."""
-    return p.dim() == 2 and not any(k in name.lower() for k in adamw_names)
+    and every tensor that is not 2-D (norms, biases) stay with AdamW ("LLM
+    Optimizers: From SGD and AdamW to SOAP, Muon, and Scalable Training",
+    sections 5-6 and 11.5).
+
+    ``name`` is the parameter's dotted name.  Whole components are matched,
+    never substrings: a module listed in ``embedding_or_head_modules``
+    anywhere on the path marks an embedding or head; a module listed in
+    ``top_level_head_modules`` does so only when it is the top-level module
+    that owns the parameter (the path is ``<module>.<parameter>``).
+    """
+    if p.dim() != 2:
+        return False
+    parts = [c.lower() for c in name.split(".")]
+    modules = parts[:-1]  # the last component names the parameter itself
+    if any(c in embedding_or_head_modules for c in modules):
+        return False
+    if len(modules) == 1 and modules[0] in top_level_head_modules:
+        return False
+    return True
 
 
 class OptimizerStep:

@@ -14,7 +14,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib as L
-from .muon import _stream, batch, workspace
+from .muon import _owned, _record_on, _stream, _stream_object, batch, workspace
 
 # Adam's defaults ("LLM Optimizers", section 6); 0.9 for the statistics as
 # reported for the SOAP-Muon records ("初探优化器（一）", 7.2); refresh
@@ -43,6 +43,7 @@ def statistics(grad, Lstat=None, Rstat=None, beta_s: float = BETA_S, stream=None
     """L <- b L + (1-b) G G^T and R <- b R + (1-b) G^T G (either may be None)."""
     bs = _batches(grad, Lstat, Rstat)
     L.soap_statistics(*map(_desc, bs), beta_s, _stream(stream))
+    _record_on(_stream_object(stream), _owned(bs))
 
 
 def statistics_grouped(grads, Lstats, Rstats, beta_s: float = BETA_S, stream=None) -> None:
@@ -52,15 +53,18 @@ def statistics_grouped(grads, Lstats, Rstats, beta_s: float = BETA_S, stream=Non
     bl, br = ([None if x is None else batch(x) for x in xs] for xs in (Lstats, Rstats))
     L.soap_statistics_grouped([b.desc for b in bg], [_desc(b) for b in bl], [_desc(b) for b in br], beta_s,
                               _stream(stream))
+    _record_on(_stream_object(stream), _owned(bg + bl + br))
 
 
 def qr(a, q, ws: torch.Tensor | None = None, stream=None) -> None:
     """q = the Q factor of a (square, f32), R's diagonal non-negative."""
     ba, bq = batch(a), batch(q)
     need = L.soap_qr_workspace(ba.count, ba.rows)
+    own_ws = ws is None
     if ws is None:
         ws = workspace(need, bq.keep[-1].device)
     L.soap_qr(ba.desc, bq.desc, ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned([ba, bq]))
 
 
 def refresh(mbar, Lstat=None, Rstat=None, QL=None, QR=None, ws: torch.Tensor | None = None, stream=None) -> None:
@@ -68,9 +72,11 @@ def refresh(mbar, Lstat=None, Rstat=None, QL=None, QR=None, ws: torch.Tensor | N
     bs = _batches(Lstat, Rstat, QL, QR, mbar)
     bm = bs[-1]
     need = L.soap_refresh_workspace(bm.count, bm.rows, bm.cols, Lstat is not None, Rstat is not None)
+    own_ws = ws is None
     if ws is None:
         ws = workspace(need, bm.keep[-1].device)
     L.soap_refresh(*map(_desc, bs), ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bs))
 
 
 def refresh_grouped(mbars, Lstats, Rstats, QLs, QRs, ws: torch.Tensor | None = None, stream=None) -> None:
@@ -78,12 +84,14 @@ def refresh_grouped(mbars, Lstats, Rstats, QLs, QRs, ws: torch.Tensor | None = N
     all groups and sides runs as one batched factorization."""
     bm = [batch(x) for x in mbars]
     bl, br, bql, bqr = ([None if x is None else batch(x) for x in xs] for xs in (Lstats, Rstats, QLs, QRs))
+    own_ws = ws is None
     if ws is None:
         need = L.soap_refresh_grouped_workspace([b.count for b in bm], [b.rows for b in bm], [b.cols for b in bm],
                                                 [x is not None for x in Lstats], [x is not None for x in Rstats])
         ws = workspace(need, bm[0].keep[-1].device)
     L.soap_refresh_grouped([_desc(b) for b in bl], [_desc(b) for b in br], [_desc(b) for b in bql],
                            [_desc(b) for b in bqr], [b.desc for b in bm], ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bm + bl + br + bql + bqr))
 
 
 def precondition(grad, mbar, vbar, out, step: int, QL=None, QR=None, beta1: float = BETA1, beta2: float = BETA2,
@@ -92,9 +100,11 @@ def precondition(grad, mbar, vbar, out, step: int, QL=None, QR=None, beta1: floa
     bs = _batches(grad, QL, QR, mbar, vbar, out)
     bg = bs[0]
     need = L.soap_precondition_workspace(bg.count, bg.rows, bg.cols)
+    own_ws = ws is None
     if ws is None:
         ws = workspace(need, bg.keep[-1].device)
     L.soap_precondition(*map(_desc, bs), step, beta1, beta2, eps, ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bs))
 
 
 def precondition_grouped(grads, mbars, vbars, outs, step: int, QLs, QRs, beta1: float = BETA1, beta2: float = BETA2,
@@ -103,6 +113,7 @@ def precondition_grouped(grads, mbars, vbars, outs, step: int, QLs, QRs, beta1: 
     launches the products of all groups together."""
     bg, bm, bv, bo = ([batch(x) for x in xs] for xs in (grads, mbars, vbars, outs))
     bl, br = ([None if x is None else batch(x) for x in xs] for xs in (QLs, QRs))
+    own_ws = ws is None
     if ws is None:
         need = L.soap_precondition_grouped_workspace([b.count for b in bg], [b.rows for b in bg],
                                                      [b.cols for b in bg])
@@ -110,6 +121,7 @@ def precondition_grouped(grads, mbars, vbars, outs, step: int, QLs, QRs, beta1: 
     L.soap_precondition_grouped([b.desc for b in bg], [_desc(b) for b in bl], [_desc(b) for b in br],
                                 [b.desc for b in bm], [b.desc for b in bv], [b.desc for b in bo], step, beta1, beta2,
                                 eps, ws.data_ptr(), ws.numel(), _stream(stream))
+    _record_on(_stream_object(stream), ([ws] if own_ws else []) + _owned(bg + bm + bv + bo + bl + br))
 
 
 class SoapStep:
