@@ -11,7 +11,12 @@ also carries the Newton-Schulz TFLOP/s (algorithmic flops: upper-triangle
 Gram and square, full update product), the roofline of the dominant kernel
 family and the fp64 CPU oracle timed on a bounded sample.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b-dense-layer]
+The default workload is the 32-layer dense set (224 matrices); the timed
+region is exactly K steps enqueued back to back between two device
+synchronizations, split by events into up to five blocks whose rates give
+the median and spread.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 8b-dense-32-layers]
 """
 
 from __future__ import annotations
@@ -327,7 +332,10 @@ def cpu_baseline(cfg, grads_host, budget_s=20.0, coeffs=COEFFS["quintic"][0], st
     sec_per_step = spent * total_flops / done_flops
     return {"value": 1.0 / sec_per_step, "unit": "steps/s", "cores": int(threads), "kind": "oracle",
             "sample": f"fp64 NumPy oracle muon_step on one matrix each of [{', '.join(names)}] "
-                      f"({spent:.1f} s), scaled by Newton-Schulz flops to the whole workload",
+                      f"({spent:.1f} s), scaled by Newton-Schulz flops to the whole workload "
+                      f"({cfg.matrices} matrices): extrapolated x{total_flops / done_flops:.1f}",
+            "extrapolated": True, "scale_factor": total_flops / done_flops,
+            "blas_threads": int(threads), "host_cpu_count": os.cpu_count(),
             "seconds_per_step": sec_per_step}
 
 
@@ -338,7 +346,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="8b-dense-layer", choices=BENCH_WORKLOADS)
+    ap.add_argument("--workload", default="8b-dense-32-layers", choices=BENCH_WORKLOADS)
     ap.add_argument("--coeffs", default="quintic", choices=sorted(COEFFS),
                     help="Newton-Schulz coefficient set (quintic: the Muon default)")
     ap.add_argument("--ns-steps", type=int, default=None, help="Newton-Schulz steps (default: the set's usual count)")
@@ -394,17 +402,29 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] {args.warmup} warmup steps done")
 
+    # exactly K steps, enqueued back to back; events on the same stream cut
+    # them into up to five blocks of nearly equal step counts
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    nblocks = max(1, min(5, args.steps))
+    sizes = [args.steps // nblocks + (1 if b < args.steps % nblocks else 0) for b in range(nblocks)]
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(nblocks + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        one_step(events[k])
+    bev[0].record()
+    k = 0
+    for b, size in enumerate(sizes):
+        for _ in range(size):
+            one_step(events[k])
+            k += 1
+        bev[b + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     log(f"[bench] {args.steps} timed steps done in {wall:.3f} s")
+    block_rates = [sizes[b] / (bev[b].elapsed_time(bev[b + 1]) * 1e-3) for b in range(nblocks)]
 
     t_mom = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    t_ns = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ns_times = sorted(e[1].elapsed_time(e[2]) for e in events)
+    t_ns = sum(ns_times) / args.steps
     t_app = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
@@ -451,8 +471,13 @@ def main():
                                        "scale": f"{stepper.coeff}*sqrt(max(m,n))", "momentum_dtype": "f32",
                                        "ns_input_dtype": "f32"},
                    "parallelism": "single GPU"},
+        "repeats": {"blocks": nblocks, "steps_per_block": sizes, "steps_per_s": block_rates,
+                    "median_steps_per_s": float(np.median(block_rates)), "min_steps_per_s": min(block_rates),
+                    "max_steps_per_s": max(block_rates)},
         "newton_schulz": {"tflops_algorithmic": ns_tflops, "tflops_nominal_4m2n_2m3": ns_tflops_nominal,
                           "frac_bf16_peak": ns_tflops / PEAK_BF16_TFLOPS, "ms": t_ns,
+                          "ms_median": float(np.median(ns_times)), "ms_min": ns_times[0], "ms_max": ns_times[-1],
+                          "tflops_algorithmic_median": algo / (float(np.median(ns_times)) * 1e-3) / 1e12,
                           "flops_algorithmic": algo, "flops_nominal": nominal},
         "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
                         "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},

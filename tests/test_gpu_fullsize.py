@@ -15,6 +15,11 @@ seeded Gaussian of the same shape, which keeps the launch identical while
 sparing the host the cost of generating what is not checked.  Sampled
 indices include the last matrix of large groups, so per-matrix offsets far
 from the base are exercised.
+
+The 32-layer set is checked on every matrix of three whole layers: the
+first, the last and one drawn from a fixed seed (21 matrices).  Its GPU step
+runs once per module; each layer is then one test, so that the fp64 oracle's
+work (about a minute per layer on the host) stays within one test's time.
 """
 
 import time
@@ -33,9 +38,21 @@ TOL_EW = 1e-6
 TOL_BF16 = 3e-2
 
 # workload -> {group name: matrix indices within the group to check}
+# the 32-layer set: layers 0 and 31 and one seeded layer, all 7 matrices of each
+# (layer L holds wq_wo 2L, 2L+1; wk_wv 2L, 2L+1; gate_up 2L, 2L+1; down L)
+LAYERS_32 = (0, int(np.random.default_rng(3_000_000).integers(1, 31)), 31)
+
+
+def layer_picks(layers):
+    return {"wq_wo": [i for L in layers for i in (2 * L, 2 * L + 1)],
+            "wk_wv": [i for L in layers for i in (2 * L, 2 * L + 1)],
+            "gate_up": [i for L in layers for i in (2 * L, 2 * L + 1)],
+            "down": list(layers)}
+
+
 SAMPLES = {
     "8b-dense-layer": {"wq_wo": [0], "wk_wv": [1], "gate_up": [1], "down": [0]},
-    "8b-dense-32-layers": {"wq_wo": [63], "wk_wv": [0], "gate_up": [37], "down": [31]},
+    "8b-dense-32-layers": layer_picks(LAYERS_32),
     "moe-30b-a3b-layer": {"gate_up": list(range(0, 256, 16)) + [255], "down": list(range(3, 128, 16)) + [127]},
     "qkv-heads-kappa1e4": {"qkv_heads": list(range(96)), "gate_up": [1], "down": [0]},
 }
@@ -81,7 +98,7 @@ def gradients(cfg, dev, picks):
     return out
 
 
-@pytest.mark.parametrize("workload", list(synth.BENCH_WORKLOADS))
+@pytest.mark.parametrize("workload", [w for w in synth.BENCH_WORKLOADS if w != "8b-dense-32-layers"])
 def test_full_size_step_matches_oracle(mx, workload):
     cfg = synth.WORKLOADS[workload]
     picks = SAMPLES[workload]
@@ -124,3 +141,65 @@ def test_full_size_step_matches_oracle(mx, workload):
           f"(median over {len(ortho_errs)} sampled matrices {float(np.median(ortho_errs)):.2e})", flush=True)
     del stepper, grads, weights
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------ the 32-layer set
+
+ERRS_32 = []
+
+
+@pytest.fixture(scope="module")
+def step_32(mx):
+    """One optimizer step of the whole 32-layer set through the benchmark's
+    launches; host copies of the sampled matrices' inputs and outputs."""
+    workload = "8b-dense-32-layers"
+    cfg = synth.WORKLOADS[workload]
+    picks = SAMPLES[workload]
+    dev = torch.device("cuda:0")
+    print(f"[fullsize] {workload}: layers {LAYERS_32}, generating inputs", flush=True)
+    grads = gradients(cfg, dev, picks)
+    weights = synth.initial_weights(cfg, device=dev)
+    host = {}
+    for gi, grp in enumerate(cfg.groups):
+        for k in picks[grp.name]:
+            host[(grp.name, k)] = {"G": grads[gi][k].cpu(), "W0": weights[gi][k].cpu()}
+    stepper = bench.make_stepper(mx, weights, grads)
+    stepper.step()
+    torch.cuda.synchronize()
+    print(f"[fullsize] {workload}: GPU step done", flush=True)
+    for gi, grp in enumerate(cfg.groups):
+        for k in picks[grp.name]:
+            host[(grp.name, k)].update(M=stepper.momentum_buffers[gi][k].cpu(), O=stepper.ortho_buffers[gi][k].cpu(),
+                                      W=weights[gi][k].cpu(), sumsq=float(stepper.sumsq_buffers[gi][k]))
+    lr, wd = stepper.lr, stepper.weight_decay
+    del stepper, grads, weights
+    torch.cuda.empty_cache()
+    return host, lr, wd
+
+
+@pytest.mark.parametrize("layer", LAYERS_32)
+def test_32_layer_set_sampled_layer_matches_oracle(step_32, layer):
+    host, lr, wd = step_32
+    picks = layer_picks([layer])
+    t0 = time.perf_counter()
+    for name, ks in picks.items():
+        for k in ks:
+            h = host[(name, k)]
+            G, W0 = f64(h["G"]), f64(h["W0"])
+            W_new, M_new, O_want, ss_want = O.muon_step(W0, np.zeros_like(G), G, lr=lr, weight_decay=wd)
+            where = f"8b-dense-32-layers layer {layer} {name}[{k}] {G.shape[0]}x{G.shape[1]}"
+            e_mom = O.relative_frobenius_error(f64(h["M"]), M_new)
+            e_ss = abs(h["sumsq"] - ss_want) / ss_want
+            O_got = f64(h["O"])
+            e_o = O.relative_frobenius_error(O_got, O_want)
+            ERRS_32.append(e_o)
+            print(f"[fullsize] {where}: Newton-Schulz {e_o:.3e} momentum {e_mom:.1e} sumsq {e_ss:.1e}", flush=True)
+            assert e_mom <= TOL_EW, f"{where}: momentum error {e_mom:.3g}"
+            assert e_ss <= TOL_EW, f"{where}: sum of squares error {e_ss:.3g}"
+            assert e_o <= TOL_BF16, f"{where}: Newton-Schulz error {e_o:.3g}"
+            W_exact = O.apply_update(W0, O_got, lr, wd)
+            tol = bf16_ulp(W_exact) + TOL_EW * np.max(np.abs(W_exact))
+            assert np.all(np.abs(f64(h["W"]) - bf16_of(W_exact)) <= tol), f"{where}: updated weight"
+    print(f"[fullsize] 8b-dense-32-layers layer {layer}: oracle {time.perf_counter() - t0:.1f} s; over the "
+          f"{len(ERRS_32)} matrices checked so far Newton-Schulz worst {max(ERRS_32):.3e} "
+          f"median {float(np.median(ERRS_32)):.3e}", flush=True)

@@ -9,10 +9,15 @@ Frobenius error per matrix, from the fp32 arithmetic:
 * statistics (sums of up to a few hundred products): 1e-6;
 * QR of a well-conditioned matrix (condition number ~10): 1e-5, with
   Q^T Q = I to 1e-5;
-* the direction D and the updated weight: 1e-3.  A refresh takes the QR of
-  L Q; the forward error of an fp32 Householder QR is of order n u kappa(L)
-  (n <= 200, u = 6e-8, kappa(L) <= ~50 here: up to ~6e-4 per basis), and the
-  direction carries both bases.  The errors measured are printed.
+* the direction D and the updated weight: 1e-4.  A refresh takes the QR of
+  L Q; the forward error of an fp32 Householder QR is at most of order
+  n u kappa(L) per basis (n <= 200, u = 6e-8), and the direction carries
+  both bases.  On these inputs (Gaussian gradients, statistics from the
+  prior I, kappa(L) of a few tens) the measured errors are 1e-6 to 5e-5,
+  which the bound holds with a factor of two; a wrong moment carry or a
+  transposed basis change shows up at 1e-2 or more.  The errors measured
+  are printed;
+* one rotated-Adam direction from given bases (no QR): 1e-5.
 
 The multi-step runs start from statistics L_0 = I, R_0 = I (a damping prior,
 as Shampoo's eps*I).  From zero statistics one side of a non-square gradient
@@ -121,7 +126,7 @@ def test_statistics_match_oracle(mx, m, n, gdtype):
 
 
 def run_steps(mx, m, n, steps, *, count=2, max_dim=4096, freq=2, eps=1e-2, wdtype=torch.float32,
-              gdtype=torch.float32, lr=0.5, wd=0.2, check_each=True, tol=1e-3, seed=0, prior=1.0):
+              gdtype=torch.float32, lr=0.5, wd=0.2, check_each=True, tol=1e-4, seed=0, prior=1.0):
     """Run SoapStep and the oracle side by side from statistics prior*I;
     compare D and W; return the worst D error and the worst basis error."""
     from matrix_aware_optimizer_step_amd import soap
@@ -192,7 +197,7 @@ def test_soap_identity_bases_is_adamw(mx):
 
 def test_soap_default_eps_after_three_steps(mx):
     print("soap default eps", flush=True)
-    run_steps(mx, 96, 128, steps=3, freq=2, eps=1e-8, check_each=False, tol=1e-3)
+    run_steps(mx, 96, 128, steps=3, freq=2, eps=1e-8, check_each=False, tol=1e-4)
 
 
 def test_soap_bf16_weight_and_gradient(mx):
@@ -361,4 +366,4 @@ def test_grouped_precondition_bit_identical_to_per_group(mx):
             QR = f64(QRs[k][i]) if QRs[k] is not None else np.eye(n)
             want, _, _ = S.precondition(f64(grads[k][i]), QL, QR, f64(m0[k][i]), f64(v0[k][i]), 3, S.BETA1, S.BETA2,
                                         1e-2)
-            assert rel(f64(runs[1][2][k][i]), want) <= 1e-3, (k, i, rel(f64(runs[1][2][k][i]), want))
+            assert rel(f64(runs[1][2][k][i]), want) <= 1e-5, (k, i, rel(f64(runs[1][2][k][i]), want))

@@ -21,14 +21,14 @@ tiny-256x128-f32 [1]: one 256x128 fp32 gradient, entries N(0,1), three
    gate, up 14336x4096; down 4096x14336.  G = D X^T with D (m x 4096) and
    X (n x 4096) N(0,1): a sum of 4096 rank-1 outer products.
 8b-dense-32-layers [3]: all 32 layers of those shapes (224 matrices), G = U diag(1/k) V^T with
-   Haar-random U, V: a power-law spectrum.
+   random orthogonal U, V (random_orthogonal): a power-law spectrum.
 moe-30b-a3b-layer [4]: an MoE layer: 128 experts x (gate 768x2048, up 768x2048, down
    2048x768), G_e = c_e * Z_e with Z_e N(0,1) and c_e the expert's token
    count under top-8-of-128 routing of 65536 tokens with N(0,1) logits.
 qkv-heads-kappa1e4 [5]: per-head: the 96 row blocks (128x4096) of Wq, Wk, Wv of a 4096-wide,
    32-head layer, plus gate, up (14336x4096) and down (4096x14336); every
    matrix G = U diag(sigma) V^T with sigma geometric from 1 to 1e-4
-   (condition number 1e4).
+   (condition number 1e4) and random orthogonal U, V.
 """
 
 from __future__ import annotations
@@ -106,18 +106,57 @@ def rank1_sum(rows: int, cols: int, seed: int, inner: int = 4096, device="cpu") 
     return d @ x.T
 
 
-def haar(n: int, k: int, gen: torch.Generator, device) -> torch.Tensor:
-    """n x k with orthonormal columns: QR of a Gaussian, signs fixed by R."""
-    z = torch.randn(n, k, generator=gen, device=device, dtype=torch.float32)
+def haar_host(n: int, gen: torch.Generator) -> torch.Tensor:
+    """n x n Haar-distributed orthogonal matrix on the host (fp64): QR of a
+    Gaussian with the signs fixed by R's diagonal."""
+    z = torch.randn(n, n, generator=gen, dtype=torch.float64)
     q, r = torch.linalg.qr(z)
     return q * torch.sign(torch.diagonal(r)).unsqueeze(0)
 
 
+def _split(n: int):
+    """n = p * q with p the largest divisor of n not above sqrt(n)."""
+    p = int(n ** 0.5)
+    while n % p:
+        p -= 1
+    return p, n // p
+
+
+def _kron_apply(A: torch.Tensor, B: torch.Tensor, Y: torch.Tensor) -> torch.Tensor:
+    """(A kron B) @ Y for A (p x p), B (q x q), Y (p*q x k), without forming
+    the Kronecker product: row i*q + j of the result is
+    sum over a, b of A[i, a] B[j, b] Y[a*q + b]."""
+    p, q, k = A.shape[0], B.shape[0], Y.shape[1]
+    T = (A @ Y.reshape(p, q * k)).reshape(p, q, k)
+    return torch.matmul(B, T).reshape(p * q, k)
+
+
+def random_orthogonal(n: int, k: int, gen: torch.Generator, device) -> torch.Tensor:
+    """n x k fp32 with orthonormal columns (k <= n).
+
+    Up to n = 512, and when n has no divisor other than 1 and itself: the
+    first k columns of a Haar matrix drawn on the host.  Above that, the
+    first k columns of P1 (A1 kron B1) P2 (A2 kron B2) with A_i (p x p) and
+    B_i (q x q) Haar, n = p*q, and P_i random row permutations: a dense,
+    well-mixed orthogonal matrix whose only host work is four QRs of order
+    about sqrt(n), applied on the device by matrix products.  No LAPACK
+    routine runs on the device."""
+    p, q = _split(n)
+    if n <= 512 or p == 1:
+        return haar_host(n, gen)[:, :k].to(device=device, dtype=torch.float32)
+    A1, B1, A2, B2 = (haar_host(d, gen).to(device=device, dtype=torch.float32) for d in (p, q, p, q))
+    perm1 = torch.randperm(n, generator=gen).to(device)
+    perm2 = torch.randperm(n, generator=gen).to(device)
+    Y = torch.eye(n, k, device=device, dtype=torch.float32)
+    Y = _kron_apply(A2, B2, Y)[perm2]
+    return _kron_apply(A1, B1, Y)[perm1]
+
+
 def with_spectrum(rows: int, cols: int, sigma: torch.Tensor, seed: int, device="cpu") -> torch.Tensor:
-    g = _gen(seed, device)
+    g = _gen(seed, "cpu")
     r = sigma.numel()
-    u = haar(rows, r, g, device)
-    v = haar(cols, r, g, device)
+    u = random_orthogonal(rows, r, g, device)
+    v = random_orthogonal(cols, r, g, device)
     return (u * sigma.to(device=device, dtype=torch.float32).unsqueeze(0)) @ v.T
 
 
