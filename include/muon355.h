@@ -153,6 +153,35 @@ muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads,
                                     int nesterov, void* workspace,
                                     size_t ws_bytes, void* stream);
 
+/*
+ * Allocation-free form of muon_momentum_grouped, for callers that cannot
+ * allocate device memory or hand the library a workspace: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ *
+ * Same arguments, meaning, validation and results (bit for bit) as
+ * muon_momentum_grouped, without `workspace` and `ws_bytes`: the per-block
+ * partial sums go to a static device array of MUON_NOALLOC_SCRATCH_BYTES
+ * that the library holds on each GPU it runs on until the process ends (its
+ * address is looked up on the first call on a device).  The call allocates
+ * and frees nothing.
+ *
+ * Limit: muon_momentum_grouped_workspace(...) of the call must not exceed
+ * MUON_NOALLOC_SCRATCH_BYTES (8 MiB: about two million partial sums, i.e.
+ * up to about 1.7e10 matrix elements per call); larger calls return
+ * MUON_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap
+ * on a GPU (unordered streams, several host threads) race on it and must be
+ * serialized by the caller.  Nothing in the array needs to start at zero:
+ * each call writes every partial it reads.
+ */
+#define MUON_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+muon_status_t muon_momentum_grouped_noalloc(int ngroups, const muon_batch_t* grads,
+                                            const muon_batch_t* moms,
+                                            const muon_batch_t* nouts,
+                                            float* const* sumsqs, float beta,
+                                            int nesterov, void* stream);
+
 /* Bytes of device workspace muon_orthogonalize needs for `count` matrices
  * of stored shape rows x cols computed in `compute` (MUON_BF16 or MUON_F32).
  * Returns 0 for invalid arguments. */

@@ -24,7 +24,7 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
           3: "MUON_ERR_WORKSPACE", 4: "MUON_ERR_LAUNCH"}
 
 EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
-            "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped",
+            "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped", "muon_momentum_grouped_noalloc",
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
             "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
             "soap_statistics_grouped", "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
@@ -77,6 +77,8 @@ def load() -> ctypes.CDLL:
                                                  ctypes.POINTER(i64)]),
         "muon_momentum_grouped": (ctypes.c_int, [ctypes.c_int, P, P, P, ctypes.POINTER(vp), f32, ctypes.c_int, vp,
                                                  sz, vp]),
+        "muon_momentum_grouped_noalloc": (ctypes.c_int, [ctypes.c_int, P, P, P, ctypes.POINTER(vp), f32, ctypes.c_int,
+                                                         vp]),
         "muon_orthogonalize_workspace": (sz, [i64, i64, i64, i32]),
         "muon_orthogonalize": (ctypes.c_int, [P, vp, P, ctypes.c_int, f32, f32, f32, f32, i32, vp, sz, vp]),
         "muon_orthogonalize_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
@@ -153,6 +155,21 @@ def muon_momentum_grouped(grads, moms, nouts, sumsq_ptrs, beta: float, nesterov:
                                       (ctypes.c_void_p * n)(*sumsq_ptrs), beta, int(bool(nesterov)),
                                       workspace_ptr, ws_bytes, stream)
     _check(st, "muon_momentum_grouped")
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # MUON_NOALLOC_SCRATCH_BYTES
+
+
+def muon_momentum_grouped_noalloc(grads, moms, nouts, sumsq_ptrs, beta: float, nesterov: bool,
+                                  stream: int) -> None:
+    n = len(grads)
+    if len(moms) != n or len(sumsq_ptrs) != n or (nouts is not None and len(nouts) != n):
+        raise ValueError("per-group lists differ in length")
+    no = None if nouts is None else (MuonBatch * n)(*nouts)
+    st = load().muon_momentum_grouped_noalloc(n, (MuonBatch * n)(*grads), (MuonBatch * n)(*moms), no,
+                                              (ctypes.c_void_p * n)(*sumsq_ptrs), beta, int(bool(nesterov)),
+                                              stream)
+    _check(st, "muon_momentum_grouped_noalloc")
 
 
 def muon_orthogonalize_workspace(count: int, rows: int, cols: int, compute: int) -> int:

@@ -628,9 +628,16 @@ size_t muon_momentum_grouped_workspace(int ngroups, const int64_t* counts, const
   return total;
 }
 
-muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
-                                    const muon_batch_t* nouts, float* const* sumsqs, float beta, int nesterov,
-                                    void* workspace, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// muon_momentum_grouped and its allocation-free form.  With noalloc the
+// workspace arguments are ignored and the partials go to the library's
+// static scratch array of the current device, after every check has passed.
+muon_status_t momentum_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
+                               const muon_batch_t* nouts, float* const* sumsqs, float beta, int nesterov,
+                               void* workspace, size_t ws_bytes, bool noalloc, void* stream, const char* name) {
   if (ngroups < 1 || ngroups > kMaxGroups)
     return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
   if (!grads || !moms || !sumsqs) return fail(MUON_ERR_INVALID_VALUE, "grads, moms and sumsqs must not be NULL");
@@ -651,27 +658,61 @@ muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads, cons
     rows[g] = grads[g].rows;
     cols[g] = grads[g].cols;
   }
-  if ((st = check_workspace(workspace, ws_bytes, muon_momentum_grouped_workspace(ngroups, counts, rows, cols))) !=
-      MUON_OK)
+  const size_t need = muon_momentum_grouped_workspace(ngroups, counts, rows, cols);
+  if (noalloc) {
+    if (need > MUON_NOALLOC_SCRATCH_BYTES)
+      return fail(MUON_ERR_WORKSPACE, "%s: %zu bytes of partial sums needed, the static scratch holds %zu", name,
+                  need, static_cast<size_t>(MUON_NOALLOC_SCRATCH_BYTES));
+  } else if ((st = check_workspace(workspace, ws_bytes, need)) != MUON_OK) {
     return st;
+  }
   char* ws = static_cast<char*>(workspace);
+  for (int g = 0; g < ngroups; ++g) {
+    const int64_t blocks = counts[g] * G.g[g].blocks_per_mat;
+    G.first[g + 1] = G.first[g] + blocks;
+  }
+  if (G.first[ngroups] > INT32_MAX)
+    return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)G.first[ngroups]);
+  if (noalloc) {
+    size_t have = 0;
+    void* p = nullptr;
+    const hipError_t e = noalloc_scratch(&p, &have);
+    if (e != hipSuccess) return launch_status(e, "static scratch lookup");
+    if (need > have) return fail(MUON_ERR_WORKSPACE, "%s: static scratch of %zu bytes too small", name, have);
+    ws = static_cast<char*>(p);
+  }
   for (int g = 0; g < ngroups; ++g) {
     G.g[g].partials = reinterpret_cast<float*>(ws);
     ws += muon_momentum_workspace(counts[g], rows[g], cols[g]);
-    G.first[g + 1] = G.first[g] + counts[g] * G.g[g].blocks_per_mat;
     F.first[g + 1] = F.first[g] + counts[g];
     F.per[g] = G.g[g].blocks_per_mat;
     F.partials[g] = G.g[g].partials;
     F.sumsq[g] = sumsqs[g];
   }
-  if (G.first[ngroups] > INT32_MAX)
-    return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)G.first[ngroups]);
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = launch_momentum_grouped(G, s);
   if (e != hipSuccess) return launch_status(e, "momentum");
   e = launch_sumsq_finalize_grouped(F, s);
   if (e != hipSuccess) return launch_status(e, "sumsq finalize");
-  return done(s, "muon_momentum_grouped");
+  return done(s, name);
+}
+
+}  // namespace
+
+extern "C" {
+
+muon_status_t muon_momentum_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
+                                    const muon_batch_t* nouts, float* const* sumsqs, float beta, int nesterov,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  return momentum_grouped(ngroups, grads, moms, nouts, sumsqs, beta, nesterov, workspace, ws_bytes, false, stream,
+                          "muon_momentum_grouped");
+}
+
+muon_status_t muon_momentum_grouped_noalloc(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
+                                            const muon_batch_t* nouts, float* const* sumsqs, float beta,
+                                            int nesterov, void* stream) {
+  return momentum_grouped(ngroups, grads, moms, nouts, sumsqs, beta, nesterov, nullptr, 0, true, stream,
+                          "muon_momentum_grouped_noalloc");
 }
 
 size_t muon_orthogonalize_workspace(int64_t count, int64_t rows, int64_t cols, int32_t compute) {

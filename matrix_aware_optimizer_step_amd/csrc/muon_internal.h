@@ -182,6 +182,10 @@ struct MomentumGroups {
 };
 hipError_t launch_momentum_grouped(const MomentumGroups& a, hipStream_t stream);
 
+// The static device scratch array of the allocation-free entry point on the
+// current device: its address (looked up once per device) and size.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 struct FinalizeGroups {
   int32_t ngroups;
   int32_t per[kMaxGroups];  // partials per matrix

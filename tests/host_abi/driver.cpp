@@ -93,6 +93,15 @@ void momentum_and_apply_cases() {
          "momentum_grouped");
   expect(muon_momentum_grouped(3, gs.data(), ms.data(), ns.data(), sums.data(), 0.95f, 1, kWs, need - 1, nullptr),
          MUON_ERR_WORKSPACE, "momentum_grouped workspace");
+  expect(muon_momentum_grouped_noalloc(3, gs.data(), ms.data(), ns.data(), sums.data(), 0.95f, 1, nullptr), MUON_OK,
+         "momentum_grouped_noalloc");
+  {
+    // 17 matrices of 2^30 elements need 8.5 MiB of partial sums: over the static scratch
+    muon_batch_t big = batch(17, 32768, 32768, MUON_F32);
+    float* s17[1] = {sumsq};
+    expect(muon_momentum_grouped_noalloc(1, &big, &big, &big, s17, 0.95f, 1, nullptr), MUON_ERR_WORKSPACE,
+           "momentum_grouped_noalloc over the scratch");
+  }
   expect(muon_apply(&ws[0], &os[0], 3e-4f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, nullptr), MUON_OK, "apply");
   expect(muon_apply_grouped(3, ws.data(), os.data(), 3e-4f, 0.1f, MUON_SCALE_ORIGINAL, 0.2f, nullptr), MUON_OK,
          "apply_grouped");

@@ -77,6 +77,17 @@ hipError_t launch_momentum_grouped(const MomentumGroups& a, hipStream_t) {
   return hipSuccess;
 }
 
+// The static scratch of the allocation-free entry point: a fake device
+// range of MUON_NOALLOC_SCRATCH_BYTES; the launches that follow are checked
+// against it as against a caller's workspace.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  static const uintptr_t kScratch = uintptr_t{0x7f0000000000};
+  *ptr = reinterpret_cast<void*>(kScratch);
+  *bytes = size_t{8} << 20;
+  stub_set_workspace(*ptr, *bytes);
+  return hipSuccess;
+}
+
 hipError_t launch_sumsq_partials(const SumsqArgs& a, int64_t count, bool, hipStream_t) {
   ++g_launches;
   in_ws(a.partials, 1, 0, count * a.blocks_per_mat * 4, "sum-of-squares partials");

@@ -130,6 +130,31 @@ def test_momentum_grouped_rejects_bad_arguments():
     assert L.muon_momentum_grouped_workspace([1, 0], [4, 4], [4, 4]) == 0
 
 
+def test_momentum_grouped_noalloc_rejects_bad_arguments_and_oversize():
+    """The allocation-free momentum validates like muon_momentum_grouped and
+    refuses a call whose partial sums would not fit its static scratch, all
+    before anything touches the GPU."""
+    gs, ms, ns = [desc(), desc(rows=32)], [desc(), desc(rows=32)], [desc(), desc(rows=32)]
+    call = lambda **kw: L.muon_momentum_grouped_noalloc(kw.get("g", gs), kw.get("m", ms), kw.get("n", ns),
+                                                        kw.get("ss", [FAKE, FAKE]), kw.get("beta", 0.95),
+                                                        kw.get("nest", True), 0)
+    assert status_of(lambda: call(beta=1.0)) == INVALID
+    assert status_of(lambda: call(n=None)) == INVALID
+    assert status_of(lambda: call(m=[desc(), desc(rows=31)])) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: call(ss=[FAKE, None])) == INVALID
+    # 2^30-element matrices need 512 KiB of partial sums each: 16 fit, 17 do not
+    per = L.muon_momentum_workspace(1, 32768, 32768)
+    fits = L.NOALLOC_SCRATCH_BYTES // per
+    assert fits == 16
+    big = desc(count=fits + 1, rows=32768, cols=32768)
+    assert L.muon_momentum_grouped_workspace([fits + 1], [32768], [32768]) > L.NOALLOC_SCRATCH_BYTES
+    assert status_of(lambda: L.muon_momentum_grouped_noalloc([big], [big], [big], [FAKE], 0.9, True, 0)) == WORKSPACE
+    assert "static scratch" in L.load().muon_last_error().decode()
+    nine = [desc()] * 9
+    assert status_of(lambda: L.muon_momentum_grouped_noalloc(nine, nine, nine, [FAKE] * 9, 0.9, True, 0)) == INVALID
+
+
 def test_apply_grouped_rejects_bad_arguments():
     ws, os_ = [desc(), desc(cols=40)], [desc(), desc(cols=40)]
     call = lambda **kw: L.muon_apply_grouped(kw.get("w", ws), kw.get("o", os_), kw.get("lr", 1e-3), 0.1,
