@@ -46,6 +46,31 @@ def ns_flops(count, rows, cols, steps=5):
     return count * steps * algo, count * steps * nominal
 
 
+def momentum_bytes(cfg, packed):
+    """Algorithmic bytes of the momentum phase: G (bf16) read, M (fp32) read
+    and written, and the Newton-Schulz input written.  Unpacked, that input
+    is N in fp32 (4 B per element).  Packed, it is written once into the
+    padded Newton-Schulz buffers (tile 128 for a short side up to 128, else
+    256): the bf16 high part (2 B), the 8-bit residual with one exponent byte
+    per 16 codes (1.0625 B) and, unless every matrix of the tile class pads
+    its short side to at most 2048 (the update then reads X itself), the
+    transposed high part (2 B)."""
+    def pad(x, t):
+        return (x + t - 1) // t * t
+    base = cfg.elements * (2 + 8)
+    if not packed:
+        return base + cfg.elements * 4
+    tiles = {g.name: (128 if min(g.rows, g.cols) <= 128 else 256) for g in cfg.groups}
+    kmajor = {t: all(pad(min(g.rows, g.cols), t) <= 2048 for g in cfg.groups if tiles[g.name] == t)
+              for t in set(tiles.values())}
+    out = base
+    for g in cfg.groups:
+        t = tiles[g.name]
+        padded = pad(min(g.rows, g.cols), t) * pad(max(g.rows, g.cols), t)
+        out += g.count * padded * (2 + 1.0625 + (0 if kmajor[t] else 2))
+    return out
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -436,7 +461,7 @@ def main():
     ns_tflops = algo / (t_ns * 1e-3) / 1e12
     ns_tflops_nominal = nominal / (t_ns * 1e-3) / 1e12
     elems = cfg.elements
-    mom_bytes = elems * (2 + 8 + 4)   # G bf16 read, M fp32 read+write, N fp32 write
+    mom_bytes = momentum_bytes(cfg, stepper.packed)
     app_bytes = elems * (4 + 2)       # W bf16 read+write, O bf16 read
     mom_gbs = mom_bytes / (t_mom * 1e-3) / 1e9
     app_gbs = app_bytes / (t_app * 1e-3) / 1e9

@@ -242,6 +242,48 @@ muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins,
                                          size_t ws_bytes, void* stream);
 
 /*
+ * The momentum and the Newton-Schulz input in one pass ("packed" pair).
+ *
+ * muon_momentum_packed_grouped does what muon_momentum_grouped does for M and
+ * the sums of squares (same arithmetic: M is bit-identical; the sums of
+ * squares are added per 64 x 64 tile instead of per block, then in fp64 in
+ * a fixed order), but instead of writing the Nesterov blend N to a caller
+ * buffer it writes N straight into `workspace` in the layout the
+ * Newton-Schulz kernels read (bf16 high part and 8-bit residual with
+ * MUON_BF16; fp32 with MUON_F32; padded, and transposed when rows > cols).
+ * muon_orthogonalize_packed_grouped then runs the iteration of
+ * muon_orthogonalize_grouped from that workspace, dividing by
+ * sqrt(sumsq) + eps inside its first step ([GUIDE] 11.4, X_0 equation: the
+ * Gram of step 0 is scaled by 1/(||N||+eps)^2 and its update by
+ * 1/(||N||+eps)), so N never makes a round trip through memory.
+ *
+ * Contract: both calls take the same groups (the shapes of grads[g] in the
+ * first are the shapes of outs[g] in the second), the same compute and the
+ * same workspace of at least muon_packed_grouped_workspace bytes (16-byte
+ * aligned), in this order on one stream; the workspace carries the packed
+ * input from the first call to the second.  sumsqs[g]: device float[count]
+ * written by the first call, read by the second.  steps >= 1 (steps == 0
+ * takes the separate calls).  Arguments, hyperparameters, outputs and
+ * errors otherwise as muon_momentum_grouped and muon_orthogonalize_grouped.
+ * The result differs from the separate calls only by rounding (the input is
+ * scaled after its bf16 rounding instead of before).
+ */
+size_t muon_packed_grouped_workspace(int ngroups, const int64_t* counts,
+                                     const int64_t* rows, const int64_t* cols,
+                                     int32_t compute);
+muon_status_t muon_momentum_packed_grouped(int ngroups, const muon_batch_t* grads,
+                                           const muon_batch_t* moms,
+                                           float* const* sumsqs, float beta,
+                                           int nesterov, int32_t compute,
+                                           void* workspace, size_t ws_bytes,
+                                           void* stream);
+muon_status_t muon_orthogonalize_packed_grouped(int ngroups, const float* const* sumsqs,
+                                                const muon_batch_t* outs, int steps,
+                                                float a, float b, float c, float eps,
+                                                int32_t compute, void* workspace,
+                                                size_t ws_bytes, void* stream);
+
+/*
  * Parameter update ([GUIDE] 11.5 update equation; [LESSON] "Muon" step 4):
  *   W <- (1 - lr*weight_decay) * W - lr * s * O
  * with s from `mode` and `coeff` (see muon_scale_t) and (m, n) = (rows,

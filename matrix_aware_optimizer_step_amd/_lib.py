@@ -26,7 +26,8 @@ STATUS = {0: "MUON_OK", 1: "MUON_ERR_INVALID_VALUE", 2: "MUON_ERR_UNSUPPORTED",
 EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_momentum_workspace",
             "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped", "muon_momentum_grouped_noalloc",
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
-            "muon_orthogonalize_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
+            "muon_orthogonalize_grouped", "muon_packed_grouped_workspace", "muon_momentum_packed_grouped",
+            "muon_orthogonalize_packed_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
             "soap_statistics_grouped", "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
             "soap_refresh_grouped_workspace", "soap_refresh_grouped",
             "soap_precondition_workspace", "soap_precondition", "soap_precondition_grouped_workspace",
@@ -85,6 +86,12 @@ def load() -> ctypes.CDLL:
                                                       ctypes.POINTER(i64), i32]),
         "muon_orthogonalize_grouped": (ctypes.c_int, [ctypes.c_int, P, ctypes.POINTER(vp), P, ctypes.c_int,
                                                       f32, f32, f32, f32, i32, vp, sz, vp]),
+        "muon_packed_grouped_workspace": (sz, [ctypes.c_int, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                               ctypes.POINTER(i64), i32]),
+        "muon_momentum_packed_grouped": (ctypes.c_int, [ctypes.c_int, P, P, ctypes.POINTER(vp), f32, ctypes.c_int,
+                                                        i32, vp, sz, vp]),
+        "muon_orthogonalize_packed_grouped": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(vp), P, ctypes.c_int, f32,
+                                                             f32, f32, f32, i32, vp, sz, vp]),
         "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
         "muon_apply_grouped": (ctypes.c_int, [ctypes.c_int, P, P, f32, f32, i32, f32, vp]),
         "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
@@ -203,6 +210,33 @@ def muon_orthogonalize_grouped(ins, sumsq_ptrs, outs, steps: int, a: float, b: f
     st = load().muon_orthogonalize_grouped(n, ins_arr, ss, outs_arr, steps, a, b, c, eps, compute,
                                            workspace_ptr, ws_bytes, stream)
     _check(st, "muon_orthogonalize_grouped")
+
+
+def muon_packed_grouped_workspace(counts, rows, cols, compute: int) -> int:
+    n = len(counts)
+    arr = ctypes.c_int64 * n
+    return load().muon_packed_grouped_workspace(n, arr(*counts), arr(*rows), arr(*cols), compute)
+
+
+def muon_momentum_packed_grouped(grads, moms, sumsq_ptrs, beta: float, nesterov: bool, compute: int,
+                                 workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    n = len(grads)
+    if len(moms) != n or len(sumsq_ptrs) != n:
+        raise ValueError("per-group lists differ in length")
+    st = load().muon_momentum_packed_grouped(n, (MuonBatch * n)(*grads), (MuonBatch * n)(*moms),
+                                             (ctypes.c_void_p * n)(*sumsq_ptrs), beta, int(bool(nesterov)), compute,
+                                             workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_momentum_packed_grouped")
+
+
+def muon_orthogonalize_packed_grouped(sumsq_ptrs, outs, steps: int, a: float, b: float, c: float, eps: float,
+                                      compute: int, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    n = len(outs)
+    if len(sumsq_ptrs) != n:
+        raise ValueError("per-group lists differ in length")
+    st = load().muon_orthogonalize_packed_grouped(n, (ctypes.c_void_p * n)(*sumsq_ptrs), (MuonBatch * n)(*outs),
+                                                  steps, a, b, c, eps, compute, workspace_ptr, ws_bytes, stream)
+    _check(st, "muon_orthogonalize_packed_grouped")
 
 
 def muon_apply(weight: MuonBatch, ortho: MuonBatch, lr: float, weight_decay: float, mode: int, coeff: float,

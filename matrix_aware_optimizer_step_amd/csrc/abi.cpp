@@ -151,6 +151,7 @@ struct GroupPlan {
   int64_t xlo, xloe, xc[2], xt[2], a, b, sumsq, partials;  // xlo, xloe: low part of X, codes and
                                                             // exponents (bf16 compute)
   int32_t blocks_per_mat;
+  int32_t pack_tiles;   // 64 x 64 tiles of the padded stored extent
 };
 
 struct Plan {
@@ -158,8 +159,10 @@ struct Plan {
   int64_t bytes = 0;
 };
 
+// packed: the momentum kernel writes N into the buffers (momentum_pack_kernel),
+// with one partial sum of squares per 64 x 64 tile of the padded stored extent.
 bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,
-               int32_t compute, const bool* need_sumsq, Plan* plan) {
+               int32_t compute, const bool* need_sumsq, Plan* plan, bool packed = false) {
   if (ngroups < 1 || ngroups > kMaxGroups) return false;
   if (compute != MUON_F32 && compute != MUON_BF16) return false;
   const int64_t es = compute == MUON_BF16 ? 2 : 4;
@@ -215,7 +218,11 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.a = take(p.count * mm * es);
     p.b = take(p.count * mm * es);
     p.blocks_per_mat = elementwise_blocks_per_matrix(p.rows, p.cols);
-    if (need_sumsq == nullptr || need_sumsq[i]) {
+    p.pack_tiles = (p.Pr / 64) * (p.Pc / 64);
+    if (packed) {
+      p.sumsq = -1;
+      p.partials = take(p.count * p.pack_tiles * 4);
+    } else if (need_sumsq == nullptr || need_sumsq[i]) {
       p.sumsq = take(p.count * 4);
       p.partials = take(p.count * p.blocks_per_mat * 4);
     } else {
@@ -241,10 +248,13 @@ GemmGroup base_group(const GroupPlan& p, int tiles_per_mat, int tiles_m, int til
   return G;
 }
 
+// packed: there is no `ins`; the momentum kernel has written N (not yet
+// normalized) into the workspace and the sums of squares into sumsqs, and
+// step 0 applies the scale.
 muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const float* const* sumsqs,
                                 const muon_batch_t* outs, int steps, float a, float b, float c,
                                 float eps, int32_t compute, void* workspace, size_t ws_bytes,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool packed = false) {
   if (ngroups < 1 || ngroups > kMaxGroups)
     return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
   if (compute != MUON_F32 && compute != MUON_BF16)
@@ -252,22 +262,29 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
   if (steps < 0) return fail(MUON_ERR_INVALID_VALUE, "steps %d < 0", steps);
   if (!finite(a) || !finite(b) || !finite(c)) return fail(MUON_ERR_INVALID_VALUE, "coefficients must be finite");
   if (!finite(eps) || eps < 0.0f) return fail(MUON_ERR_INVALID_VALUE, "eps must be finite and >= 0");
-  if (!ins || !outs) return fail(MUON_ERR_INVALID_VALUE, "ins/outs is NULL");
+  if ((!packed && !ins) || !outs) return fail(MUON_ERR_INVALID_VALUE, "ins/outs is NULL");
+  if (packed && steps < 1) return fail(MUON_ERR_INVALID_VALUE, "the packed form needs steps >= 1");
+  if (packed && !sumsqs) return fail(MUON_ERR_INVALID_VALUE, "sumsqs is NULL");
   std::vector<int64_t> counts(ngroups), rows(ngroups), cols(ngroups);
   bool need[kMaxGroups];
   for (int g = 0; g < ngroups; ++g) {
-    muon_status_t st = check_batch(&ins[g], "in", true);
-    if (st != MUON_OK) return st;
+    muon_status_t st;
+    if (!packed) {
+      st = check_batch(&ins[g], "in", true);
+      if (st != MUON_OK) return st;
+    }
     st = check_batch(&outs[g], "out", true);
     if (st != MUON_OK) return st;
-    if (!same_shape(&ins[g], &outs[g])) return fail(MUON_ERR_INVALID_VALUE, "in and out shapes differ (group %d)", g);
-    counts[g] = ins[g].count;
-    rows[g] = ins[g].rows;
-    cols[g] = ins[g].cols;
-    need[g] = sumsqs == nullptr || sumsqs[g] == nullptr;
+    if (!packed && !same_shape(&ins[g], &outs[g]))
+      return fail(MUON_ERR_INVALID_VALUE, "in and out shapes differ (group %d)", g);
+    if (packed && !sumsqs[g]) return fail(MUON_ERR_INVALID_VALUE, "sumsqs[%d] is NULL", g);
+    counts[g] = outs[g].count;
+    rows[g] = outs[g].rows;
+    cols[g] = outs[g].cols;
+    need[g] = !packed && (sumsqs == nullptr || sumsqs[g] == nullptr);
   }
   Plan plan;
-  if (!make_plan(ngroups, counts.data(), rows.data(), cols.data(), compute, need, &plan))
+  if (!make_plan(ngroups, counts.data(), rows.data(), cols.data(), compute, need, &plan, packed))
     return fail(MUON_ERR_UNSUPPORTED, "a padded Newton-Schulz shape exceeds 2^30 elements");
   if (!workspace || ws_bytes < static_cast<size_t>(plan.bytes))
     return fail(MUON_ERR_WORKSPACE, "workspace of %zu bytes given, %lld needed", ws_bytes, (long long)plan.bytes);
@@ -316,8 +333,9 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
     return done(stream, "run_orthogonalize");
   }
 
-  // 2. X_0 = N / (||N|| + eps) into the padded buffers (X, and X^T where the update reads it)
-  for (int g = 0; g < ngroups; ++g) {
+  // 2. X_0 = N / (||N|| + eps) into the padded buffers (X, and X^T where the
+  // update reads it); the packed form has N there already
+  for (int g = 0; g < ngroups && !packed; ++g) {
     const GroupPlan& p = plan.g[g];
     const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
     PackArgs pa;
@@ -434,6 +452,10 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
               G.ot_mat = mn * es;
               G.ldot = p.Mp;
             }
+          }
+          if (packed && k == 0) {  // X_0 = N / (||N|| + eps), applied in step 0's three stages
+            G.xs_sumsq = ssq[g];
+            G.xs_eps = eps;
           }
           L.g[L.ngroups++] = G;
         }
@@ -744,6 +766,98 @@ muon_status_t muon_orthogonalize_grouped(int ngroups, const muon_batch_t* ins, c
                                          void* stream) {
   return run_orthogonalize(ngroups, ins, sumsqs, outs, steps, a, b, c, eps, compute, workspace, ws_bytes,
                            static_cast<hipStream_t>(stream));
+}
+
+size_t muon_packed_grouped_workspace(int ngroups, const int64_t* counts, const int64_t* rows, const int64_t* cols,
+                                     int32_t compute) {
+  if (!counts || !rows || !cols) return 0;
+  Plan plan;
+  if (!make_plan(ngroups, counts, rows, cols, compute, nullptr, &plan, true)) return 0;
+  return static_cast<size_t>(plan.bytes);
+}
+
+muon_status_t muon_momentum_packed_grouped(int ngroups, const muon_batch_t* grads, const muon_batch_t* moms,
+                                           float* const* sumsqs, float beta, int nesterov, int32_t compute,
+                                           void* workspace, size_t ws_bytes, void* stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!grads || !moms || !sumsqs) return fail(MUON_ERR_INVALID_VALUE, "grads, moms and sumsqs must not be NULL");
+  if (compute != MUON_F32 && compute != MUON_BF16)
+    return fail(MUON_ERR_INVALID_VALUE, "compute %d is not MUON_F32 or MUON_BF16", compute);
+  int64_t counts[kMaxGroups], rows[kMaxGroups], cols[kMaxGroups];
+  MomentumArgs ma[kMaxGroups];
+  muon_status_t st;
+  for (int g = 0; g < ngroups; ++g) {
+    bool vec;
+    // the checks of muon_momentum without N (the packed buffers take its place)
+    st = prepare_momentum(&grads[g], &moms[g], nullptr, sumsqs[g], beta, 0, &ma[g], &vec);
+    if (st != MUON_OK) return in_group(st, g);
+    if (nesterov != 0 && nesterov != 1) return fail(MUON_ERR_INVALID_VALUE, "nesterov must be 0 or 1");
+    counts[g] = grads[g].count;
+    rows[g] = grads[g].rows;
+    cols[g] = grads[g].cols;
+  }
+  Plan plan;
+  if (!make_plan(ngroups, counts, rows, cols, compute, nullptr, &plan, true))
+    return fail(MUON_ERR_UNSUPPORTED, "a padded Newton-Schulz shape exceeds 2^30 elements");
+  if ((st = check_workspace(workspace, ws_bytes, static_cast<size_t>(plan.bytes))) != MUON_OK) return st;
+  char* ws = static_cast<char*>(workspace);
+  const int64_t es = compute == MUON_BF16 ? 2 : 4;
+  MomentumPackGroups P;
+  FinalizeGroups F;
+  std::memset(&P, 0, sizeof(P));
+  std::memset(&F, 0, sizeof(F));
+  P.ngroups = F.ngroups = ngroups;
+  for (int g = 0; g < ngroups; ++g) {
+    const GroupPlan& p = plan.g[g];
+    const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
+    MomentumPackArgs& a = P.g[g];
+    a.G = to_mat(&grads[g]);
+    a.M = to_mat(&moms[g]);
+    a.beta = beta;
+    a.nesterov = nesterov;
+    a.rows = p.rows;
+    a.cols = p.cols;
+    a.Pr = p.Pr;
+    a.Pc = p.Pc;
+    a.compute = compute;
+    a.tall = p.tall;
+    a.vec = vec4_ok(&grads[g]) && vec4_ok(&moms[g]);
+    a.tiles_c = p.Pc / 64;
+    a.tiles_per_mat = p.pack_tiles;
+    a.lo_bm = p.tile;
+    a.lo_tiles_n = p.Np / p.tile;
+    a.partials = reinterpret_cast<float*>(ws + p.partials);
+    // the same buffers as the pack step of run_orthogonalize: X is whichever
+    // orientation is wide, X^T only where the update reads it
+    a.S = p.tall ? (p.kmajor ? nullptr : ws + p.xt[0]) : ws + p.xc[0];
+    a.T = p.tall ? ws + p.xc[0] : (p.kmajor ? nullptr : ws + p.xt[0]);
+    a.s_mat = a.t_mat = mn * es;
+    a.Lo = compute == MUON_BF16 ? reinterpret_cast<int8_t*>(ws + p.xlo) : nullptr;
+    a.lo_mat = mn;
+    a.LoE = compute == MUON_BF16 ? reinterpret_cast<uint8_t*>(ws + p.xloe) : nullptr;
+    a.loe_mat = mn / kLoExpPerCodes;
+    P.first[g + 1] = P.first[g] + counts[g] * p.pack_tiles;
+    F.first[g + 1] = F.first[g] + counts[g];
+    F.per[g] = p.pack_tiles;
+    F.partials[g] = a.partials;
+    F.sumsq[g] = sumsqs[g];
+  }
+  if (P.first[ngroups] > INT32_MAX)
+    return fail(MUON_ERR_UNSUPPORTED, "%lld workgroups exceed one launch", (long long)P.first[ngroups]);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_momentum_pack_grouped(P, s);
+  if (e != hipSuccess) return launch_status(e, "momentum pack");
+  e = launch_sumsq_finalize_grouped(F, s);
+  if (e != hipSuccess) return launch_status(e, "sumsq finalize");
+  return done(s, "muon_momentum_packed_grouped");
+}
+
+muon_status_t muon_orthogonalize_packed_grouped(int ngroups, const float* const* sumsqs, const muon_batch_t* outs,
+                                                int steps, float a, float b, float c, float eps, int32_t compute,
+                                                void* workspace, size_t ws_bytes, void* stream) {
+  return run_orthogonalize(ngroups, nullptr, sumsqs, outs, steps, a, b, c, eps, compute, workspace, ws_bytes,
+                           static_cast<hipStream_t>(stream), true);
 }
 
 muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,

@@ -358,6 +358,28 @@ __global__ __launch_bounds__(kThreads) void apply_grouped_kernel(const ApplyGrou
 
 constexpr int kTile = 64;
 
+// The low part of a 64 x 64 tile of X staged in `tile` (stored orientation;
+// X is its transpose when tall): thread t encodes lane (t % 64) of the
+// update kernel's 32x32 block (t / 64) of this tile, as pack_kernel does.
+__device__ __forceinline__ void store_low_part(const float (*tile)[kTile + 1], bool tall, uint32_t r0, uint32_t c0,
+                                               int8_t* Lo, uint8_t* LoE, int bm, int tiles_n) {
+  const uint32_t i0 = tall ? c0 : r0;
+  const uint32_t j0 = tall ? r0 : c0;
+  const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hf = lane >> 5, jl = (b & 1) * 32 + (lane & 31);
+  float x[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int il = (b >> 1) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+    x[r] = tall ? tile[jl][il] : tile[il][jl];
+  }
+  const Lo8 c = lo8_encode(x);
+  int8_t* run = Lo + lo_index(i0, j0, bm, tiles_n);
+  *reinterpret_cast<uint4*>(run + (b * 64 + lane) * 16) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
+  LoE[lo_exp_index(i0 + (b >> 1) * 32 + 4 * hf, j0 + (b & 1) * 32 + (lane & 31), bm, tiles_n)] =
+      static_cast<uint8_t>(c.e);
+}
+
 // grid: (Pc/64, Pr/64, count).  Each workgroup moves one 64x64 tile of the
 // padded stored-orientation extent.  Global accesses are 4-element pieces:
 // 16 threads cover a 64-element row (N rows read, S rows written) or a
@@ -402,29 +424,97 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(const PackArgs a) {
     if (S) store4(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, v);
   }
   __syncthreads();
-  if (a.Lo) {
-    // The low part of X in the update kernel's accumulator order: this 64 x 64
-    // tile of X is four consecutive 32x32 blocks of one wave there.  Thread t
-    // encodes lane (t % 64) of block (t / 64): its 16 values, rows
-    // 8*(r/4) + 4*half + r%4 of the block, leave as one 16-byte store of
-    // codes and one exponent byte.
-    const uint32_t i0 = a.tall ? c0 : r0;  // top-left corner of this tile in X
-    const uint32_t j0 = a.tall ? r0 : c0;
-    const int b = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int hf = lane >> 5, jl = (b & 1) * 32 + (lane & 31);
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int il = (b >> 1) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-      x[r] = a.tall ? tile[jl][il] : tile[il][jl];  // X[i][j] = S[j][i] when tall
-    }
-    const Lo8 c = lo8_encode(x);
-    int8_t* run = a.Lo + mat * a.lo_mat + lo_index(i0, j0, a.lo_bm, a.lo_tiles_n);
-    *reinterpret_cast<uint4*>(run + (b * 64 + lane) * 16) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
-    a.LoE[mat * a.loe_mat + lo_exp_index(i0 + (b >> 1) * 32 + 4 * hf, j0 + (b & 1) * 32 + (lane & 31), a.lo_bm,
-                                         a.lo_tiles_n)] = static_cast<uint8_t>(c.e);
-  }
+  // The low part of X in the update kernel's accumulator order: this 64 x 64
+  // tile of X is four consecutive 32x32 blocks of one wave there.
+  if (a.Lo) store_low_part(tile, a.tall != 0, r0, c0, a.Lo + mat * a.lo_mat, a.LoE + mat * a.loe_mat, a.lo_bm,
+                           a.lo_tiles_n);
   // write rows of T = columns of the tile (if wanted)
+  if (!a.T) return;
+  char* T = a.T + mat * a.t_mat;
+#pragma unroll
+  for (int k = 0; k < kTile / 16; ++k) {
+    const int cc = rq + 16 * k;
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = tile[4 * q + e][cc];
+    store4(T + (static_cast<int64_t>(c0 + cc) * a.Pr + r0 + 4 * q) * esz, a.compute, v);
+  }
+}
+
+// ------------------------------------------------------------ momentum + pack
+
+// Flat grid over the groups' tiles: workgroup b is 64 x 64 tile t of the
+// padded stored extent of matrix `mat`.  Reads G and M once, writes M once,
+// and writes N (not yet divided by its norm: the first Newton-Schulz step
+// applies that scale) straight into the Newton-Schulz buffers, so N never
+// makes a round trip through memory.  Global accesses are 4-element pieces,
+// 16 threads per 64-element row; the tile transposes through LDS for X^T
+// and the low part, as in pack_kernel.
+__global__ __launch_bounds__(kThreads) void momentum_pack_kernel(const MomentumPackGroups P) {
+  __shared__ float tile[kTile][kTile + 1];
+  __shared__ float red[kThreads / 64];
+  const int64_t b = blockIdx.x;
+  const int gi = group_of(P.first, P.ngroups, b);
+  const MomentumPackArgs& a = P.g[gi];
+  const int64_t local = b - P.first[gi];
+  const int64_t mat = local / a.tiles_per_mat;
+  const int t = static_cast<int>(local - mat * a.tiles_per_mat);
+  const int tr = t / a.tiles_c;
+  const int r0 = tr * kTile;
+  const int c0 = (t - tr * a.tiles_c) * kTile;
+  const char* g = mat_ptr(a.G, mat);
+  char* m = mat_ptr(a.M, mat);
+  const int gsz = a.G.dtype ? 2 : 4;
+  const float beta = a.beta;
+  const float omb = 1.0f - a.beta;
+  const int q = threadIdx.x & 15;   // 4-element piece of a 64-element row
+  const int rq = threadIdx.x >> 4;  // 0..15
+  const int esz = a.compute ? 2 : 4;
+  char* S = a.S ? a.S + mat * a.s_mat : nullptr;
+  float ss = 0.0f;
+#pragma unroll
+  for (int k = 0; k < kTile / 16; ++k) {
+    const int rr = rq + 16 * k;
+    const int r = r0 + rr;
+    const int c = c0 + 4 * q;
+    float nv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (r < a.rows) {
+      const char* gp = g + (static_cast<int64_t>(r) * a.G.ld + c) * gsz;
+      float* mp = reinterpret_cast<float*>(m + (static_cast<int64_t>(r) * a.M.ld + c) * 4);
+      if (a.vec && c + 3 < a.cols) {
+        float gv[4], mv[4];
+        load4(gp, a.G.dtype, gv);
+        load4(reinterpret_cast<const char*>(mp), 0, mv);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          mv[e] = beta * mv[e] + omb * gv[e];
+          nv[e] = a.nesterov ? omb * gv[e] + beta * mv[e] : mv[e];
+        }
+        store4(reinterpret_cast<char*>(mp), 0, mv);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (c + e < a.cols) {
+            const float gv = load1(gp + e * gsz, a.G.dtype);
+            const float mv = beta * mp[e] + omb * gv;
+            nv[e] = a.nesterov ? omb * gv + beta * mv : mv;
+            mp[e] = mv;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss += nv[e] * nv[e];
+      tile[rr][4 * q + e] = nv[e];
+    }
+    if (S) store4(S + (static_cast<int64_t>(r) * a.Pc + c) * esz, a.compute, nv);
+  }
+  // block_sum's barrier also makes the whole tile visible in LDS
+  const float part = block_sum(ss, red);
+  if (threadIdx.x == 0) a.partials[mat * a.tiles_per_mat + t] = part;
+  if (a.Lo) store_low_part(tile, a.tall != 0, r0, c0, a.Lo + mat * a.lo_mat, a.LoE + mat * a.loe_mat, a.lo_bm,
+                           a.lo_tiles_n);
   if (!a.T) return;
   char* T = a.T + mat * a.t_mat;
 #pragma unroll
@@ -522,6 +612,12 @@ hipError_t launch_apply_grouped(const ApplyGroups& a, hipStream_t stream) {
 hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream) {
   dim3 grid(a.Pc / kTile, a.Pr / kTile, static_cast<unsigned>(count));
   hipLaunchKernelGGL(pack_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_momentum_pack_grouped(const MomentumPackGroups& a, hipStream_t stream) {
+  hipLaunchKernelGGL(momentum_pack_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

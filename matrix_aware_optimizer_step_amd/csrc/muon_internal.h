@@ -68,7 +68,12 @@ struct GemmGroup {
   MatBatch user;
   int32_t tall;                  // 1: user output is X^T
   int32_t ms, ns;                // true (unpadded) Newton-Schulz shape
-  int32_t pad4_;
+  // Step 0 from an unnormalized packed input (the momentum kernel wrote
+  // N itself): with xs = 1/(sqrt(xs_sumsq[mat]) + xs_eps), the Gram's
+  // products are multiplied by xs^2, the polynomial uses xs*b and xs*c and
+  // the update xs*a; null: xs = 1.
+  float xs_eps;
+  const float* xs_sumsq;
 };
 
 // The low part of X (bf16 compute): the residual X - bf16(X), kept as int8
@@ -228,6 +233,37 @@ struct PackArgs {
   int32_t lo_bm, lo_tiles_n;      // update tile size and tile columns of X
 };
 hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t stream);
+
+// Momentum fused with the packing of the Newton-Schulz input: per 64x64
+// tile of the padded stored extent of one matrix, M <- beta*M + (1-beta)*G,
+// the Nesterov blend N (the same arithmetic as momentum_kernel), one partial
+// sum of N^2 per tile, and N itself (not yet normalized) into the padded
+// buffers as PackArgs describes them (S, T, Lo, LoE).
+struct MomentumPackArgs {
+  MatBatch G, M;
+  float beta;
+  int32_t nesterov;
+  int32_t rows, cols;      // stored m, n
+  int32_t Pr, Pc;          // padded
+  int32_t compute, tall;
+  int32_t vec;             // G's and M's rows and matrices start on 4-element boundaries
+  int32_t tiles_c;         // Pc / 64
+  int32_t tiles_per_mat;   // (Pr / 64) * (Pc / 64)
+  int32_t lo_bm, lo_tiles_n;
+  int32_t pad_;
+  float* partials;         // [count * tiles_per_mat]
+  char* S; int64_t s_mat;
+  char* T; int64_t t_mat;
+  int8_t* Lo; int64_t lo_mat;
+  uint8_t* LoE; int64_t loe_mat;
+};
+struct MomentumPackGroups {
+  int32_t ngroups;
+  int32_t pad_;
+  int64_t first[kMaxGroups + 1];  // first workgroup of each group (one per tile)
+  MomentumPackArgs g[kMaxGroups];
+};
+hipError_t launch_momentum_pack_grouped(const MomentumPackGroups& a, hipStream_t stream);
 
 // Zero-step output: out = N / (sqrt(sumsq) + eps), both in the stored
 // orientation.

@@ -458,6 +458,17 @@ void ns_gemm_kernel(const GemmLaunch L) {
     static_assert(!kAddXInLoop || (kNH * BK == WTM && kFPK * 32 == BK && RC == 2 * kFPK * 2),
                   "wave rows must split into whole k-tiles of whole 32-row blocks");
     const int kt_x0 = (ti * BM + wm * WTM) / BK;
+    // Step 0 from a packed, unnormalized input N (the momentum kernel wrote
+    // N itself): X_0 = xs*N with xs = 1/(||N|| + eps).  The Gram is then xs^2
+    // times its product, the polynomial takes xs*b and xs*c (B_0 is stored
+    // already multiplied by xs) and the update xs*a, so that
+    // X_1 = xs*a*N + (xs*B_0)*N.  Otherwise xs = 1 and these are the
+    // coefficients themselves.
+    float xs = 1.0f;
+    if (G.xs_sumsq != nullptr) xs = 1.0f / (sqrtf(G.xs_sumsq[mat]) + G.xs_eps);
+    const float at = L.a * xs;
+    const float bt = L.b * xs;
+    const float ct = L.c * xs;
     int st = 0;  // stage holding k-tile kt
     for (int kt = 0; kt < nk; ++kt) {
       const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
@@ -495,10 +506,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
                         sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
                     v = u32x2_t{u.x, u.y};
                   }
-                  acc[fi][fj][4 * q + 0] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x));
-                  acc[fi][fj][4 * q + 1] += L.a * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
-                  acc[fi][fj][4 * q + 2] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y));
-                  acc[fi][fj][4 * q + 3] += L.a * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
+                  acc[fi][fj][4 * q + 0] += at * bf16_to_f32(static_cast<uint16_t>(v.x));
+                  acc[fi][fj][4 * q + 1] += at * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
+                  acc[fi][fj][4 * q + 2] += at * bf16_to_f32(static_cast<uint16_t>(v.y));
+                  acc[fi][fj][4 * q + 3] += at * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
                 }
           }
         }
@@ -565,6 +576,16 @@ void ns_gemm_kernel(const GemmLaunch L) {
     // pieces of 128-byte row segments.
     const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
     const int gj0 = tj * BN + wn * WTN;  // first column
+
+    if constexpr (EPI == EPI_GRAM) {  // A_0 = xs^2 N N^T (see xs above)
+      const float x2 = xs * xs;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= x2;
+    }
 
     // 1. finish the values, one 32x32 block at a time, and store what leaves
     //    from registers.  The epilogue operand (X, or A for the polynomial)
@@ -640,10 +661,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
         const float* e = ebuf[blk % (PF + 1)];
         if constexpr (EPI == EPI_POLY) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.b * e[r] + L.c * acc[fi][fj][r];
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = bt * e[r] + ct * acc[fi][fj][r];
         } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = L.a * e[r] + acc[fi][fj][r];
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = at * e[r] + acc[fi][fj][r];
         }
       }
       if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {

@@ -195,25 +195,29 @@ class MuonStep:
 
     ``groups`` is a list of ``(weights, grads)`` pairs, each element anything
     ``batch()`` accepts (a 2-D or 3-D tensor or a list of 2-D tensors).  The
-    fp32 momentum, the Newton-Schulz input/output buffers, the sums of
-    squares and the workspaces are allocated once here; ``step()`` only
-    enqueues the library's kernels on the current stream.
+    fp32 momentum, the Newton-Schulz output buffers, the sums of squares and
+    the workspaces are allocated once here; ``step()`` only enqueues the
+    library's kernels on the current stream.
+
+    With ``packed`` (the default, for K >= 1 Newton-Schulz steps) the momentum
+    kernel writes the Newton-Schulz input straight into the iteration's
+    workspace (muon_momentum_packed_grouped, then
+    muon_orthogonalize_packed_grouped), so N is never stored; otherwise N is
+    an fp32 buffer between muon_momentum_grouped and
+    muon_orthogonalize_grouped.
     """
 
     def __init__(self, groups, *, compute: int = L.MUON_BF16, beta: float = 0.95, nesterov: bool = True,
                  steps: int = 5, coeffs=QUINTIC, eps: float = EPS, lr: float = 3e-4,
-                 weight_decay: float = 0.1, mode: int = L.MUON_SCALE_MATCH_RMS, coeff: float = 0.2):
+                 weight_decay: float = 0.1, mode: int = L.MUON_SCALE_MATCH_RMS, coeff: float = 0.2,
+                 packed: bool = True):
         if not groups:
             raise ValueError("no parameter groups")
         self.compute, self.beta, self.nesterov = compute, beta, nesterov
         self.steps, self.coeffs, self.eps = steps, coeffs, eps
         self.lr, self.weight_decay, self.mode, self.coeff = lr, weight_decay, mode, coeff
-        self.w, self.g, self.m, self.n, self.o, self.ss, self.mws = [], [], [], [], [], [], []
+        self.w, self.g, self.m, self.n, self.o, self.ss = [], [], [], [], [], []
         dev = None
-        # The Newton-Schulz input stays fp32 on both paths: the bf16 path's
-        # high/low copy of X starts from it, and a bf16-rounded start is the
-        # error that the iteration amplifies most on ill-conditioned inputs.
-        nbuf_dtype = torch.float32
         for weights, grads in groups:
             w, g = batch(weights), batch(grads)
             if (w.count, w.rows, w.cols) != (g.count, g.rows, g.cols):
@@ -223,21 +227,37 @@ class MuonStep:
             self.w.append(w)
             self.g.append(g)
             self.m.append(batch(torch.zeros(shape, dtype=torch.float32, device=dev)))
-            self.n.append(batch(torch.empty(shape, dtype=nbuf_dtype, device=dev)))
             self.o.append(batch(torch.empty(shape, dtype=w.keep[-1].dtype, device=dev)))
             self.ss.append(torch.empty(w.count, dtype=torch.float32, device=dev))
         self.device = dev
         # each stage runs the groups together, at most 8 per grouped launch
         self.chunks = [list(range(i, min(i + 8, len(self.w)))) for i in range(0, len(self.w), 8)]
+        self.packed = bool(packed)
+        self.pws, self.mws, self.ows = [], [], []
+        if self.packed:
+            for ch in self.chunks:
+                need = L.muon_packed_grouped_workspace([self.g[i].count for i in ch], [self.g[i].rows for i in ch],
+                                                       [self.g[i].cols for i in ch], compute)
+                self.pws.append(workspace(need, dev))
+        else:
+            self._unpacked_buffers()
+
+    def _unpacked_buffers(self) -> None:
+        """N (fp32 on both paths: the bf16 path's high/low copy of X starts
+        from it, and a bf16-rounded start is the error that the iteration
+        amplifies most on ill-conditioned inputs) and the workspaces of the
+        separate calls; made on first use."""
+        if self.mws:
+            return
+        for g in self.g:
+            self.n.append(batch(torch.empty((g.count, g.rows, g.cols), dtype=torch.float32, device=self.device)))
         for ch in self.chunks:
             need = L.muon_momentum_grouped_workspace([self.g[i].count for i in ch], [self.g[i].rows for i in ch],
                                                      [self.g[i].cols for i in ch])
-            self.mws.append(workspace(need, dev))
-        self.ows = []
-        for ch in self.chunks:
-            need = L.muon_orthogonalize_grouped_workspace([self.n[i].count for i in ch], [self.n[i].rows for i in ch],
-                                                          [self.n[i].cols for i in ch], compute)
-            self.ows.append(workspace(need, dev))
+            self.mws.append(workspace(need, self.device))
+            need = L.muon_orthogonalize_grouped_workspace([self.g[i].count for i in ch], [self.g[i].rows for i in ch],
+                                                          [self.g[i].cols for i in ch], self.compute)
+            self.ows.append(workspace(need, self.device))
 
     @property
     def momentum_buffers(self):
@@ -278,19 +298,36 @@ class MuonStep:
         apply and after apply (phase timing on the same stream)."""
         st = stream if stream is not None else torch.cuda.current_stream()
         s = _stream(st)
+        packed = self.packed and self.steps >= 1
+        if not packed:
+            self._unpacked_buffers()
+        a, b, c = self.coeffs
         if events is not None:
             events[0].record(st)
-        for ch, ws in zip(self.chunks, self.mws):
-            L.muon_momentum_grouped([self.g[i].desc for i in ch], [self.m[i].desc for i in ch],
-                                    [self.n[i].desc for i in ch], [self.ss[i].data_ptr() for i in ch], self.beta,
-                                    self.nesterov, ws.data_ptr(), ws.numel(), s)
+        for k, ch in enumerate(self.chunks):
+            sums = [self.ss[i].data_ptr() for i in ch]
+            if packed:
+                ws = self.pws[k]
+                L.muon_momentum_packed_grouped([self.g[i].desc for i in ch], [self.m[i].desc for i in ch], sums,
+                                               self.beta, self.nesterov, self.compute, ws.data_ptr(), ws.numel(), s)
+            else:
+                ws = self.mws[k]
+                L.muon_momentum_grouped([self.g[i].desc for i in ch], [self.m[i].desc for i in ch],
+                                        [self.n[i].desc for i in ch], sums, self.beta, self.nesterov, ws.data_ptr(),
+                                        ws.numel(), s)
         if events is not None:
             events[1].record(st)
-        a, b, c = self.coeffs
-        for ch, ws in zip(self.chunks, self.ows):
-            L.muon_orthogonalize_grouped([self.n[i].desc for i in ch], [self.ss[i].data_ptr() for i in ch],
-                                         [self.o[i].desc for i in ch], self.steps, a, b, c, self.eps,
-                                         self.compute, ws.data_ptr(), ws.numel(), s)
+        for k, ch in enumerate(self.chunks):
+            sums = [self.ss[i].data_ptr() for i in ch]
+            if packed:
+                ws = self.pws[k]
+                L.muon_orthogonalize_packed_grouped(sums, [self.o[i].desc for i in ch], self.steps, a, b, c, self.eps,
+                                                    self.compute, ws.data_ptr(), ws.numel(), s)
+            else:
+                ws = self.ows[k]
+                L.muon_orthogonalize_grouped([self.n[i].desc for i in ch], sums, [self.o[i].desc for i in ch],
+                                             self.steps, a, b, c, self.eps, self.compute, ws.data_ptr(), ws.numel(),
+                                             s)
         if events is not None:
             events[2].record(st)
         for ch in self.chunks:

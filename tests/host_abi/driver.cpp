@@ -61,6 +61,29 @@ void orthogonalize_cases() {
     expect(muon_orthogonalize_grouped(5, ins.data(), nullptr, outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
                                       kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_grouped, shapes");
   }
+  // the packed pair: momentum into the Newton-Schulz buffers, then the iteration from them
+  for (int32_t compute : {MUON_BF16, MUON_F32}) {
+    const size_t need = muon_packed_grouped_workspace(5, counts, rows, cols, compute);
+    stub_set_workspace(kWs, need);
+    std::vector<muon_batch_t> gs, ms, outs;
+    std::vector<float*> sums;
+    for (int g = 0; g < 5; ++g) {
+      gs.push_back(batch(counts[g], rows[g], cols[g], MUON_BF16));
+      ms.push_back(batch(counts[g], rows[g], cols[g], MUON_F32));
+      outs.push_back(batch(counts[g], rows[g], cols[g], MUON_BF16));
+      sums.push_back(reinterpret_cast<float*>(kDev));
+    }
+    expect(muon_momentum_packed_grouped(5, gs.data(), ms.data(), sums.data(), 0.95f, 1, compute, kWs, need, nullptr),
+           MUON_OK, "momentum_packed_grouped");
+    expect(muon_momentum_packed_grouped(5, gs.data(), ms.data(), sums.data(), 0.95f, 1, compute, kWs, need - 1,
+                                        nullptr), MUON_ERR_WORKSPACE, "momentum_packed_grouped, short workspace");
+    expect(muon_orthogonalize_packed_grouped(5, sums.data(), outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
+                                             kWs, need, nullptr), MUON_OK, "orthogonalize_packed_grouped");
+    expect(muon_orthogonalize_packed_grouped(5, sums.data(), outs.data(), 0, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
+                                             kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_packed, K 0");
+    expect(muon_orthogonalize_packed_grouped(5, nullptr, outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
+                                             kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_packed, sums");
+  }
   expect(muon_orthogonalize_workspace(1, 65536, 65536, MUON_F32) == 0 ? MUON_OK : MUON_ERR_LAUNCH, MUON_OK,
          "padded-size limit");
   expect(muon_orthogonalize_workspace(int64_t{1} << 40, 64, 64, MUON_BF16) == 0 ? MUON_OK : MUON_ERR_LAUNCH, MUON_OK,

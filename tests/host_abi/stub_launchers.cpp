@@ -136,6 +136,31 @@ hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_momentum_pack_grouped(const MomentumPackGroups& a, hipStream_t) {
+  ++g_launches;
+  if (a.ngroups < 1 || a.ngroups > kMaxGroups || a.first[0] != 0) die("momentum pack groups: %d", a.ngroups);
+  for (int g = 0; g < a.ngroups; ++g) {
+    const MomentumPackArgs& p = a.g[g];
+    const int64_t n = a.first[g + 1] - a.first[g];
+    if (p.Pr % 64 || p.Pc % 64 || p.Pr < p.rows || p.Pc < p.cols) die("momentum pack %d: padded %d x %d", g, p.Pr, p.Pc);
+    if (p.tiles_c != p.Pc / 64 || p.tiles_per_mat != (p.Pr / 64) * p.tiles_c) die("momentum pack %d: tile grid", g);
+    if (n <= 0 || n % p.tiles_per_mat) die("momentum pack group %d: %lld tiles", g, (long long)n);
+    const int64_t count = n / p.tiles_per_mat;
+    const int64_t elems = static_cast<int64_t>(p.Pr) * p.Pc;
+    const int es = p.compute ? 2 : 4;
+    in_ws(p.partials, 1, 0, n * 4, "momentum pack partials");
+    if (!p.S && !p.T) die("momentum pack %d writes no X", g);
+    if (p.S) in_ws(p.S, count, p.s_mat, elems * es, "momentum pack S");
+    if (p.T) in_ws(p.T, count, p.t_mat, elems * es, "momentum pack T");
+    if (p.compute != (p.Lo != nullptr)) die("momentum pack %d: low part with compute %d", g, p.compute);
+    if (p.Lo) {
+      in_ws(p.Lo, count, p.lo_mat, elems, "momentum pack low-part codes");
+      in_ws(p.LoE, count, p.loe_mat, elems / kLoExpPerCodes, "momentum pack low-part exponents");
+    }
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t) {
   ++g_launches;
   if (count < 1 || a.rows < 1 || a.cols < 1) die("copy_out shape");

@@ -155,6 +155,29 @@ def test_momentum_grouped_noalloc_rejects_bad_arguments_and_oversize():
     assert status_of(lambda: L.muon_momentum_grouped_noalloc(nine, nine, nine, [FAKE] * 9, 0.9, True, 0)) == INVALID
 
 
+def test_packed_pair_rejects_bad_arguments():
+    gs, ms = [desc(), desc(rows=96)], [desc(), desc(rows=96)]
+    need = L.muon_packed_grouped_workspace([1, 1], [64, 96], [64, 64], L.MUON_BF16)
+    assert need > L.muon_orthogonalize_grouped_workspace([1, 1], [64, 96], [64, 64], L.MUON_BF16) - 4096
+    mom = lambda **kw: L.muon_momentum_packed_grouped(kw.get("g", gs), kw.get("m", ms), kw.get("ss", [FAKE, FAKE]),
+                                                      kw.get("beta", 0.95), True, kw.get("compute", L.MUON_BF16),
+                                                      kw.get("ws", FAKE), kw.get("wsb", need), 0)
+    assert status_of(lambda: mom(beta=1.0)) == INVALID
+    assert status_of(lambda: mom(m=[desc(), desc(rows=95)])) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: mom(ss=[FAKE, None])) == INVALID
+    assert status_of(lambda: mom(compute=5)) == INVALID
+    assert status_of(lambda: mom(wsb=need - 1)) == WORKSPACE
+    assert status_of(lambda: mom(m=[desc(dtype=L.MUON_BF16), desc(rows=96)])) == UNSUPPORTED  # momentum is fp32
+    orth = lambda **kw: L.muon_orthogonalize_packed_grouped(kw.get("ss", [FAKE, FAKE]), kw.get("o", gs),
+                                                            kw.get("steps", 5), 3.4445, -4.775, 2.0315, 1e-7,
+                                                            L.MUON_BF16, FAKE, kw.get("wsb", need), 0)
+    assert status_of(lambda: orth(steps=0)) == INVALID
+    assert status_of(lambda: orth(ss=[FAKE, None])) == INVALID
+    assert status_of(lambda: orth(wsb=need - 1)) == WORKSPACE
+    assert L.muon_packed_grouped_workspace([1] * 9, [4] * 9, [4] * 9, 1) == 0
+
+
 def test_apply_grouped_rejects_bad_arguments():
     ws, os_ = [desc(), desc(cols=40)], [desc(), desc(cols=40)]
     call = lambda **kw: L.muon_apply_grouped(kw.get("w", ws), kw.get("o", os_), kw.get("lr", 1e-3), 0.1,
