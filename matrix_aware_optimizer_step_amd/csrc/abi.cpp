@@ -51,11 +51,26 @@ muon_status_t ok() {
 constexpr int64_t kAlign = 256;
 static_assert(kAdamWChunk == MUON_ADAMW_CHUNK, "chunk size of the AdamW tensor list");
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
+constexpr int64_t kSplitGramWorkgroups = 512;  // see gram_splits
 // Longest update reduction (padded short side) that takes the k-major bf16
 // update; longer ones read X^T.
 constexpr int kKMajorMaxK = 2048;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// A group whose Gram has few tiles (the 96 per-head 128 x 4096 blocks are 96
+// tiles; the GPU holds 512 of that size at once) splits its reduction in
+// slices: up to kSplitGramWorkgroups workgroups, each slice at least 512 deep
+// and a whole number of 64-deep k-tiles.  Decided per group from its own
+// shape and count only, so a group's results do not depend on the groups it
+// is launched with.
+int gram_splits(int64_t count, int64_t T, int64_t Np) {
+  const int64_t tiles = count * T * (T + 1) / 2;
+  int S = 1;
+  if (tiles > 128) return S;
+  while (S < 8 && tiles * S * 2 <= kSplitGramWorkgroups && Np % (S * 2 * 64) == 0 && Np / (S * 2) >= 512) S *= 2;
+  return S;
+}
 int esize(int32_t dtype) { return dtype == MUON_BF16 ? 2 : 4; }
 
 muon_status_t check_batch(const muon_batch_t* b, const char* name, bool allow_bf16) {
@@ -152,6 +167,8 @@ struct GroupPlan {
                                                             // exponents (bf16 compute)
   int32_t blocks_per_mat;
   int32_t pack_tiles;   // 64 x 64 tiles of the padded stored extent
+  int32_t gram_splits;  // the Gram's reduction in this many slices (1: not split)
+  int64_t part;         // byte offset of the split Gram's partial sums
 };
 
 struct Plan {
@@ -217,6 +234,8 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.xt[1] = p.kmajor ? -1 : take(p.count * mn * es);
     p.a = take(p.count * mm * es);
     p.b = take(p.count * mm * es);
+    p.gram_splits = gram_splits(p.count, p.Mp / p.tile, p.Np);
+    p.part = p.gram_splits > 1 ? take(p.count * p.gram_splits * mm * 4) : -1;
     p.blocks_per_mat = elementwise_blocks_per_matrix(p.rows, p.cols);
     p.pack_tiles = (p.Pr / 64) * (p.Pc / 64);
     if (packed) {
@@ -387,7 +406,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
           const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
           GemmGroup G;
           if (stage == 0) {  // A = X X^T
-            G = base_group(p, T * (T + 1) / 2, T, T, 1);
+            G = base_group(p, T * (T + 1) / 2 * p.gram_splits, T, T, 1);
             G.P = G.Q = ws + p.xc[cur];
             G.p_mat = G.q_mat = mn * es;
             G.ldp = G.ldq = p.Np;
@@ -395,6 +414,11 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             G.O0 = ws + p.a;
             G.o0_mat = mm * es;
             G.ldo0 = p.Mp;
+            G.splits = p.gram_splits;
+            if (p.gram_splits > 1) {
+              G.part = reinterpret_cast<float*>(ws + p.part);
+              G.part_mat = p.gram_splits * mm * 4;
+            }
           } else if (stage == 1) {  // B = b A + c A A
             G = base_group(p, T * (T + 1) / 2, T, T, 1);
             G.P = G.Q = ws + p.a;
@@ -471,6 +495,30 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
         const int epi = stage == 0 ? EPI_GRAM : stage == 1 ? EPI_POLY : (last ? EPI_FINAL : EPI_UPDATE);
         if ((e = launch_ns_gemm(compute, tile, epi, km != 0, L, stream)) != hipSuccess)
           return launch_status(e, "newton-schulz gemm");
+        if (stage == 0) {  // add the slices of split Grams
+          GramReduce R;
+          std::memset(&R, 0, sizeof(R));
+          for (int g = 0; g < ngroups; ++g) {
+            const GroupPlan& p = plan.g[g];
+            if (p.tile != tile || p.gram_splits < 2) continue;
+            const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
+            GramReduceGroup& r = R.g[R.ngroups];
+            r.part = reinterpret_cast<const float*>(ws + p.part);
+            r.part_mat = p.gram_splits * mm * 4;
+            r.A = ws + p.a;
+            r.a_mat = mm * es;
+            r.xs_sumsq = packed && k == 0 ? ssq[g] : nullptr;
+            r.xs_eps = eps;
+            r.Mp = p.Mp;
+            r.tile = tile;
+            r.splits = p.gram_splits;
+            r.compute = compute;
+            R.first[R.ngroups + 1] = R.first[R.ngroups] + p.count * (mm / 1024);
+            ++R.ngroups;
+          }
+          if (R.ngroups > 0 && (e = launch_gram_reduce(R, stream)) != hipSuccess)
+            return launch_status(e, "split gram reduce");
+        }
       }
       }
     }

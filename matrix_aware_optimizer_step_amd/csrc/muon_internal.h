@@ -74,7 +74,36 @@ struct GemmGroup {
   // the update xs*a; null: xs = 1.
   float xs_eps;
   const float* xs_sumsq;
+  // Gram with the reduction split in `splits` slices (1: not split): each
+  // tile of each slice stores its fp32 partial sums, unscaled and not
+  // mirrored, at part + mat*part_mat + slice*ldo0*ldo0*4 (row-major, ldo0 =
+  // the padded order), and gram_reduce adds the slices.
+  int32_t splits;
+  int32_t pad6_;
+  float* part; int64_t part_mat;  // bytes per matrix
 };
+
+// A = scale * (sum over the slices of the split Gram's partials), for every
+// element of the padded order-Mp matrices of up to kMaxGroups groups; an
+// element below the diagonal tile row reads the mirrored partial (only tiles
+// with ti <= tj were computed).  scale = xs^2 of step 0 of the packed input,
+// else 1.  Workgroup b of the flat grid handles 1024 elements of group g
+// (first[g] <= b < first[g+1]).
+struct GramReduceGroup {
+  const float* part; int64_t part_mat;  // bytes per matrix
+  char* A; int64_t a_mat;               // bytes per matrix; row-major, ld Mp
+  const float* xs_sumsq;                // null: scale 1
+  float xs_eps;
+  int32_t Mp, tile, splits, compute;
+  int32_t pad_;
+};
+struct GramReduce {
+  int32_t ngroups;
+  int32_t pad_;
+  int64_t first[kMaxGroups + 1];
+  GramReduceGroup g[kMaxGroups];
+};
+hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t stream);
 
 // The low part of X (bf16 compute): the residual X - bf16(X), kept as int8
 // codes in multiples of a step shared by the 16 values one lane holds in one

@@ -249,6 +249,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
     }
     const int mat = lt / G.tiles_per_mat;
     int tt = lt - mat * G.tiles_per_mat;
+    int slice = 0;  // split Gram: slice of the reduction this tile sums
+    if (G.splits > 1) {
+      slice = tt % G.splits;
+      tt /= G.splits;
+    }
     int ti, tj;
     constexpr int R = BM / BN;  // column tiles per row tile
     static_assert(R * BN == BM, "BN must divide BM");
@@ -280,10 +285,12 @@ void ns_gemm_kernel(const GemmLaunch L) {
 
     const int ldp = G.ldp;
     const int ldq = G.ldq;
-    const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T);
+    const int ksl = G.splits > 1 ? G.K / G.splits : G.K;  // reduction length of this tile
+    const int64_t k0 = static_cast<int64_t>(slice) * ksl * sizeof(T);  // (the split Gram is never k-major)
+    const char* Pt = G.P + mat * G.p_mat + static_cast<int64_t>(ti) * BM * ldp * sizeof(T) + k0;
     // a k-major Q starts at the tile's first column, an n-major one at its first row
-    const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * (kQN ? 1 : ldq) * sizeof(T);
-    const int nk = G.K / BK;
+    const char* Qt = G.Q + mat * G.q_mat + static_cast<int64_t>(tj) * BN * (kQN ? 1 : ldq) * sizeof(T) + k0;
+    const int nk = ksl / BK;
     // A diagonal tile of a symmetric product multiplies a block of rows by
     // itself: its Q tile is the P tile already in LDS, so only P is loaded.
     // Not on a persistent grid: there the workgroups walk their tiles nearly
@@ -464,8 +471,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
     // already multiplied by xs) and the update xs*a, so that
     // X_1 = xs*a*N + (xs*B_0)*N.  Otherwise xs = 1 and these are the
     // coefficients themselves.
-    float xs = 1.0f;
-    if (G.xs_sumsq != nullptr) xs = 1.0f / (sqrtf(G.xs_sumsq[mat]) + G.xs_eps);
+    // (The Gram needs xs only in its epilogue: computed there, it holds no
+    // register through the main loop, where the Gram uses all 256.)
+    auto scale_of = [&]() { return G.xs_sumsq != nullptr ? 1.0f / (sqrtf(G.xs_sumsq[mat]) + G.xs_eps) : 1.0f; };
+    const float xs = EPI == EPI_GRAM ? 1.0f : scale_of();
     const float at = L.a * xs;
     const float bt = L.b * xs;
     const float ct = L.c * xs;
@@ -577,8 +586,12 @@ void ns_gemm_kernel(const GemmLaunch L) {
     const int gi0 = ti * BM + wm * WTM;  // first row of this wave's sub-tile
     const int gj0 = tj * BN + wn * WTN;  // first column
 
+    // split Gram: the tile stores its fp32 partial sums, unscaled and
+    // unmirrored, into its slice; gram_reduce adds the slices, scales and mirrors
+    const bool split = EPI == EPI_GRAM && G.splits > 1;
     if constexpr (EPI == EPI_GRAM) {  // A_0 = xs^2 N N^T (see xs above)
-      const float x2 = xs * xs;
+      const float xg = split ? 1.0f : scale_of();
+      const float x2 = xg * xg;
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -668,12 +681,22 @@ void ns_gemm_kernel(const GemmLaunch L) {
         }
       }
       if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
-        char* Om = G.O0 + mat * G.o0_mat;
         const uint32_t ldo = G.ldo0;
+        if (split) {  // (a slice holds at most 3840^2 floats: 32-bit offsets)
+          char* Pm = reinterpret_cast<char*>(G.part) + mat * G.part_mat +
+                     static_cast<int64_t>(slice) * ldo * ldo * static_cast<int64_t>(sizeof(float));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-          Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+            *reinterpret_cast<float*>(Pm + (i * ldo + j) * 4u) = acc[fi][fj][r];
+          }
+        } else {
+          char* Om = G.O0 + mat * G.o0_mat;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
+            Elem<T>::store(Om + (i * ldo + j) * static_cast<uint32_t>(sizeof(T)), acc[fi][fj][r]);
+          }
         }
       } else if constexpr (EPI == EPI_UPDATE) {
         char* O0m = G.O0 + mat * G.o0_mat;  // X' (fp32) or its bf16 low part
@@ -718,7 +741,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
     } else if constexpr (EPI == EPI_FINAL) {
       transposed = sizeof(T) == 2 || G.tall != 0;  // bf16: staged either way (row or column segments)
     } else {
-      transposed = tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
+      transposed = !split && tj >= R * (ti + 1);  // the mirror of a tile off the diagonal block
     }
     if (!transposed) continue;  // uniform over the workgroup
     static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
@@ -845,6 +868,45 @@ void ns_gemm_kernel(const GemmLaunch L) {
   }  // tiles
 }
 
+// ---------------------------------------------------------------- split Gram
+
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const GramReduce R) {
+  const int64_t b = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < R.ngroups && b >= R.first[gi + 1]) ++gi;
+  const GramReduceGroup& g = R.g[gi];
+  const int64_t per = (static_cast<int64_t>(g.Mp) * g.Mp) / 1024;  // workgroups per matrix
+  const int64_t local = b - R.first[gi];
+  const int64_t mat = local / per;
+  const int64_t e0 = (local - mat * per) * 1024 + threadIdx.x * 4;  // four consecutive elements of one row
+  const int i = static_cast<int>(e0 / g.Mp);
+  const int j0 = static_cast<int>(e0 - static_cast<int64_t>(i) * g.Mp);
+  const float* part = reinterpret_cast<const float*>(reinterpret_cast<const char*>(g.part) + mat * g.part_mat);
+  const int64_t slice = static_cast<int64_t>(g.Mp) * g.Mp;
+  float scale = 1.0f;
+  if (g.xs_sumsq != nullptr) {
+    const float xs = 1.0f / (sqrtf(g.xs_sumsq[mat]) + g.xs_eps);
+    scale = xs * xs;
+  }
+  float v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int j = j0 + e;
+    // computed tiles have tile row <= tile column; below that, the mirror
+    const bool up = i / g.tile <= j / g.tile;
+    const int64_t at = up ? static_cast<int64_t>(i) * g.Mp + j : static_cast<int64_t>(j) * g.Mp + i;
+    float sum = 0.0f;
+    for (int s = 0; s < g.splits; ++s) sum += part[s * slice + at];  // fixed order
+    v[e] = scale * sum;
+  }
+  char* A = g.A + mat * g.a_mat;
+  if (g.compute) {
+    Elem<uint16_t>::store4(A + (static_cast<int64_t>(i) * g.Mp + j0) * 2, v[0], v[1], v[2], v[3]);
+  } else {
+    Elem<float>::store4(A + (static_cast<int64_t>(i) * g.Mp + j0) * 4, v[0], v[1], v[2], v[3]);
+  }
+}
+
 // Workgroups of a tile size that are resident on the current device at once
 // (one 256-tile or two 128-tile workgroups per CU: LDS bound), rounded down
 // to a multiple of the 8 XCDs; 0 if the device cannot be queried.
@@ -902,6 +964,12 @@ hipError_t launch_t(int epi, bool kmajor, const GemmLaunch& L, hipStream_t strea
 }
 
 }  // namespace
+
+hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t stream) {
+  if (a.first[a.ngroups] <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
   if (L.total_tiles <= 0) return hipSuccess;

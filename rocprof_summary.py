@@ -14,6 +14,9 @@ arguments.
   traffic  <fetch dir> <write dir>   --pmc FETCH_SIZE and --pmc WRITE_SIZE, each
                                      scaled by what the counter reads for the 1 GiB
                                      calibration copy in the same run
+  counters <dir> [<dir> ...]         several --pmc passes of memory-pipeline counters:
+                                     L2 latency and hit rate, address translation,
+                                     texture-addresser and LDS activity
 
 The optimizer steps in a run are counted as the dispatches of the momentum
 kernel (one per step).  ``--command`` records the commands that produced the
@@ -67,7 +70,7 @@ def label(name: str) -> str:
     return base
 
 
-LIBRARY_KERNELS = ("ns_gemm", "momentum", "pack", "apply", "finalize", "sumsq", "copy_out", "adamw", "sgemm", "qr_",
+LIBRARY_KERNELS = ("ns_gemm", "gram_reduce", "momentum", "pack", "apply", "finalize", "sumsq", "copy_out", "adamw", "sgemm", "qr_",
                    "rot_adam", "eye", "gather", "sign_copy", "ns_")
 
 
@@ -142,7 +145,7 @@ def cmd_trace(a):
         tot = sum(v) / 1e6
         per = tot / steps if steps else float("nan")
         lines.append(f"| {k} | {len(v)} | {statistics.mean(v) / 1e3:.1f} | {tot:.2f} | {per:.3f} |")
-        if k.startswith(("ns_gemm", "pack", "ns_")):
+        if k.startswith(("ns_gemm", "gram_reduce", "pack", "ns_")):
             ns_total += per
     lines += ["", f"Newton-Schulz kernels (every ns_gemm launch and the operand packing) per step: {ns_total:.3f} ms.",
               ""]
@@ -228,9 +231,57 @@ def cmd_traffic(a):
     return lines
 
 
+# derived quantities of the memory-pipeline counters: (name, numerator, denominator, scale)
+DERIVED = [("L2 read latency, cycles per request", "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", 1),
+           ("L2 write latency, cycles per request", "TCP_TCC_WRITE_REQ_LATENCY_sum", "TCP_TCC_WRITE_REQ_sum", 1),
+           ("L2 hit rate %", "TCC_HIT_sum", ("TCC_HIT_sum", "TCC_MISS_sum"), 100),
+           ("address translation miss rate %", "TCP_UTCL1_TRANSLATION_MISS_sum",
+            ("TCP_UTCL1_TRANSLATION_MISS_sum", "TCP_UTCL1_TRANSLATION_HIT_sum"), 100),
+           ("TA busy % (average TA over one XCD's active cycles)", "TA_BUSY_avr", "GRBM_GUI_ACTIVE/8", 100),
+           ("LDS bank conflicts % of LDS-active cycles", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", 100),
+           ("waves waiting on LDS instructions % of wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", 100)]
+
+
+def cmd_counters(a):
+    """Several --pmc passes of the same command: per launch family the mean
+    of every counter over its dispatches, and the derived quantities."""
+    fams = OrderedDict()
+    for d in a.dirs:
+        for e in counters(d):
+            if not e["label"].startswith(LIBRARY_KERNELS):
+                continue
+            f = fams.setdefault(e["label"], {})
+            for c, v in e.items():
+                if c not in ("label", "start", "end"):
+                    f.setdefault(c, []).append(v)
+    note = ("Means over each launch family's dispatches, one --pmc pass per line of the commands (a counter "
+            "taken in several passes is averaged over all of them); counters ending in _sum are summed over "
+            "the GPU's instances, _avr averaged over them; GRBM_GUI_ACTIVE is summed over the 8 XCDs.")
+    lines = header(a.title, a.command, note)
+    names = [n for n, *_ in DERIVED]
+    lines += ["| kernel | " + " | ".join(names) + " |", "|---|" + "---:|" * len(names)]
+
+    def val(f, key):
+        if key == "GRBM_GUI_ACTIVE/8":
+            return statistics.mean(f["GRBM_GUI_ACTIVE"]) / XCDS if "GRBM_GUI_ACTIVE" in f else None
+        if isinstance(key, tuple):
+            parts = [val(f, k) for k in key]
+            return None if None in parts else sum(parts)
+        return statistics.mean(f[key]) if key in f else None
+
+    for k, f in fams.items():
+        cells = []
+        for _, num, den, sc in DERIVED:
+            n, d = val(f, num), val(f, den)
+            cells.append("-" if n is None or not d else f"{sc * n / d:.1f}")
+        lines.append(f"| {k} | " + " | ".join(cells) + " |")
+    lines.append("")
+    return lines
+
+
 def main():
     ap = argparse.ArgumentParser()
-    ap.add_argument("kind", choices=["trace", "mfma", "traffic"])
+    ap.add_argument("kind", choices=["trace", "mfma", "traffic", "counters"])
     ap.add_argument("dirs", nargs="+")
     ap.add_argument("--trace", help="kernel-trace directory of the same command (mfma)")
     ap.add_argument("--title", required=True)
@@ -238,7 +289,7 @@ def main():
     ap.add_argument("--workload", default="", help="workload name for the traffic record")
     ap.add_argument("--out")
     a = ap.parse_args()
-    lines = {"trace": cmd_trace, "mfma": cmd_mfma, "traffic": cmd_traffic}[a.kind](a)
+    lines = {"trace": cmd_trace, "mfma": cmd_mfma, "traffic": cmd_traffic, "counters": cmd_counters}[a.kind](a)
     text = "\n".join(lines)
     if a.out:
         with open(a.out, "w") as f:

@@ -136,6 +136,22 @@ hipError_t launch_pack(const PackArgs& a, int64_t count, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t) {
+  ++g_launches;
+  if (a.ngroups < 1 || a.ngroups > kMaxGroups || a.first[0] != 0) die("gram reduce groups: %d", a.ngroups);
+  for (int g = 0; g < a.ngroups; ++g) {
+    const GramReduceGroup& r = a.g[g];
+    const int64_t mm = static_cast<int64_t>(r.Mp) * r.Mp;
+    const int64_t n = a.first[g + 1] - a.first[g];
+    if (r.Mp % r.tile || mm % 1024 || n <= 0 || n % (mm / 1024)) die("gram reduce %d: order %d, %lld blocks", g, r.Mp,
+                                                                       (long long)n);
+    const int64_t count = n / (mm / 1024);
+    in_ws(r.part, count, r.part_mat, r.splits * mm * 4, "gram reduce partials");
+    in_ws(r.A, count, r.a_mat, mm * (r.compute ? 2 : 4), "gram reduce output");
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_momentum_pack_grouped(const MomentumPackGroups& a, hipStream_t) {
   ++g_launches;
   if (a.ngroups < 1 || a.ngroups > kMaxGroups || a.first[0] != 0) die("momentum pack groups: %d", a.ngroups);
@@ -184,7 +200,14 @@ hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const Gem
     if (G.tile_begin != begin) die("group %d starts at tile %d, expected %lld", g, G.tile_begin, (long long)begin);
     const int64_t rows = static_cast<int64_t>(G.tiles_m) * tile, cols = static_cast<int64_t>(G.tiles_n) * tile;
     const int64_t want = G.sym ? static_cast<int64_t>(G.tiles_m) * (G.tiles_m + 1) / 2 : static_cast<int64_t>(G.tiles_m) * G.tiles_n;
-    if (G.tiles_per_mat != want) die("group %d: %d tiles per matrix, expected %lld", g, G.tiles_per_mat, (long long)want);
+    const int splits = G.splits > 1 ? G.splits : 1;
+    if (splits > 1 && (epi != EPI_GRAM || !G.sym)) die("group %d: split reduction outside the Gram", g);
+    if (G.tiles_per_mat != want * splits)
+      die("group %d: %d tiles per matrix, expected %lld", g, G.tiles_per_mat, (long long)(want * splits));
+    if (splits > 1) {
+      if (G.K % (splits * 64) != 0) die("group %d: K %d in %d slices", g, G.K, splits);
+      in_ws(G.part, G.count, G.part_mat, splits * rows * rows * 4, "split Gram partials");
+    }
     if (G.K < 64 || G.K % 64) die("group %d: K %d", g, G.K);
     if (G.ms < 1 || G.ms > rows) die("group %d: short side %d beyond %lld padded rows", g, G.ms, (long long)rows);
     if (epi >= EPI_UPDATE && (G.ns < G.ms || G.ns > cols)) die("group %d: long side %d, %lld padded columns", g, G.ns, (long long)cols);

@@ -213,10 +213,15 @@ def test_workspace_queries():
     lo = mn + mn // 16
     assert lo + mn * 4 * 2 + 2 * mm * 2 <= b < lo + mn * 4 * 2 + 2 * mm * 2 + (1 << 20)
     assert mn * 4 * 4 + 2 * mm * 4 <= f < mn * 4 * 4 + 2 * mm * 4 + (1 << 20)
+    # one 768 x 2048 matrix: 6 Gram tiles, so its 2048-deep reduction is split
+    # in 4 slices whose fp32 partial sums (4 x 768^2) are also in the workspace
     k = L.muon_orthogonalize_workspace(1, 768, 2048, L.MUON_BF16)
     mn, mm = 768 * 2048, 768 * 768
     lo = mn + mn // 16
-    assert lo + mn * 2 * 2 + 2 * mm * 2 <= k < lo + mn * 2 * 2 + 2 * mm * 2 + (1 << 20)
+    assert lo + mn * 2 * 2 + 2 * mm * 2 + 4 * mm * 4 <= k < lo + mn * 2 * 2 + 2 * mm * 2 + 4 * mm * 4 + (1 << 20)
+    # 256 of them have 1536 Gram tiles: no split
+    k256 = L.muon_orthogonalize_workspace(256, 768, 2048, L.MUON_BF16)
+    assert k256 < 256 * (lo + mn * 2 * 2 + 2 * mm * 2) + (1 << 20)
     # tall and wide of one shape pad to the same Newton-Schulz problem
     assert L.muon_orthogonalize_workspace(3, 700, 300, 1) == L.muon_orthogonalize_workspace(3, 300, 700, 1)
     g = L.muon_orthogonalize_grouped_workspace([2, 1], [4096, 1024], [4096, 4096], L.MUON_BF16)
