@@ -51,23 +51,19 @@ def momentum_bytes(cfg, packed):
     and written, and the Newton-Schulz input written.  Unpacked, that input
     is N in fp32 (4 B per element).  Packed, it is written once into the
     padded Newton-Schulz buffers (tile 128 for a short side up to 128, else
-    256): the bf16 high part (2 B), the 8-bit residual with one exponent byte
-    per 16 codes (1.0625 B) and, unless every matrix of the tile class pads
-    its short side to at most 2048 (the update then reads X itself), the
-    transposed high part (2 B)."""
+    256): the bf16 high part (2 B) and the 8-bit residual with one exponent
+    byte per 16 codes (1.0625 B); the bf16 update reads X itself, so no
+    transposed copy is written."""
     def pad(x, t):
         return (x + t - 1) // t * t
     base = cfg.elements * (2 + 8)
     if not packed:
         return base + cfg.elements * 4
-    tiles = {g.name: (128 if min(g.rows, g.cols) <= 128 else 256) for g in cfg.groups}
-    kmajor = {t: all(pad(min(g.rows, g.cols), t) <= 2048 for g in cfg.groups if tiles[g.name] == t)
-              for t in set(tiles.values())}
     out = base
     for g in cfg.groups:
-        t = tiles[g.name]
+        t = 128 if min(g.rows, g.cols) <= 128 else 256
         padded = pad(min(g.rows, g.cols), t) * pad(max(g.rows, g.cols), t)
-        out += g.count * padded * (2 + 1.0625 + (0 if kmajor[t] else 2))
+        out += g.count * padded * (2 + 1.0625)
     return out
 
 

@@ -52,9 +52,6 @@ constexpr int64_t kAlign = 256;
 static_assert(kAdamWChunk == MUON_ADAMW_CHUNK, "chunk size of the AdamW tensor list");
 constexpr int64_t kMaxElems = (int64_t{1} << 31) - 1;
 constexpr int64_t kSplitGramWorkgroups = 512;  // see gram_splits
-// Longest update reduction (padded short side) that takes the k-major bf16
-// update; longer ones read X^T.
-constexpr int kKMajorMaxK = 2048;
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 
@@ -190,20 +187,11 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     return o;
   };
   plan->g.clear();
-  // With bf16 compute and short update reductions (the padded short side
-  // Mp) the update reads X itself, k-major through LDS transpose reads, and
-  // X^T is never written: the saved X'^T stores outweigh the transpose reads'
-  // slower main loop up to about 2048-deep reductions (MI355X measurements).
-  // The choice is made per tile class, so that every update launch holds all
-  // of its class's groups (a class split in two leaves the smaller launch
-  // unable to fill the GPU).
-  bool kmajor_class[2] = {compute == MUON_BF16, compute == MUON_BF16};  // tile 256, 128
-  for (int i = 0; i < ngroups; ++i) {
-    if (rows[i] < 1 || cols[i] < 1) return false;
-    const int64_t ms = std::min(rows[i], cols[i]);
-    const int tile = ms <= 128 ? 128 : 256;
-    if (align_up(ms, tile) > kKMajorMaxK) kmajor_class[tile == 128] = false;
-  }
+  // With bf16 compute the update reads X itself, k-major through LDS
+  // transpose reads, and X^T is never written (on MI355X this beat reading a
+  // kept X^T at every reduction length measured, 128 to 4096 deep: the saved
+  // X'^T stores and transposed staging outweigh the transpose reads).  The
+  // fp32 update reads X^T.
   for (int i = 0; i < ngroups; ++i) {
     if (counts[i] < 1 || counts[i] > 65535 || rows[i] < 1 || cols[i] < 1) return false;
     if (rows[i] > kMaxElems / cols[i]) return false;
@@ -217,7 +205,7 @@ bool make_plan(int ngroups, const int64_t* counts, const int64_t* rows, const in
     p.tile = p.ms <= 128 ? 128 : 256;
     p.Mp = static_cast<int32_t>(align_up(p.ms, p.tile));
     p.Np = static_cast<int32_t>(align_up(p.ns, p.tile));
-    p.kmajor = kmajor_class[p.tile == 128];
+    p.kmajor = compute == MUON_BF16;
     // per-matrix byte offsets inside the GEMM kernels are 32-bit: an fp32
     // padded matrix must stay below 4 GiB
     if (static_cast<int64_t>(p.Mp) * p.Np > (int64_t{1} << 30)) return false;
@@ -384,14 +372,13 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
   }
 
   // 3. the K-step loop: Gram, polynomial, update; one launch per stage and
-  // tile class (the update also per operand layout)
+  // tile class
   for (int k = 0; k < steps; ++k) {
     const int cur = k & 1;
     const int nxt = cur ^ 1;
     const bool last = k + 1 == steps;
     for (int stage = 0; stage < 3; ++stage) {
       for (int tile : {256, 128}) {
-      for (int km = 0; km < (stage == 2 ? 2 : 1); ++km) {
         GemmLaunch L;
         std::memset(&L, 0, sizeof(L));
         L.a = a;
@@ -400,7 +387,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
         int total = 0;
         for (int g = 0; g < ngroups; ++g) {
           const GroupPlan& p = plan.g[g];
-          if (p.tile != tile || (stage == 2 && p.kmajor != km)) continue;  // (a class has one layout)
+          if (p.tile != tile) continue;
           const int T = p.Mp / tile;
           const int64_t mn = static_cast<int64_t>(p.Mp) * p.Np;
           const int64_t mm = static_cast<int64_t>(p.Mp) * p.Mp;
@@ -493,7 +480,7 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
         }
         L.total_tiles = total;
         const int epi = stage == 0 ? EPI_GRAM : stage == 1 ? EPI_POLY : (last ? EPI_FINAL : EPI_UPDATE);
-        if ((e = launch_ns_gemm(compute, tile, epi, km != 0, L, stream)) != hipSuccess)
+        if ((e = launch_ns_gemm(compute, tile, epi, compute == MUON_BF16, L, stream)) != hipSuccess)
           return launch_status(e, "newton-schulz gemm");
         if (stage == 0) {  // add the slices of split Grams
           GramReduce R;
@@ -519,7 +506,6 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
           if (R.ngroups > 0 && (e = launch_gram_reduce(R, stream)) != hipSuccess)
             return launch_status(e, "split gram reduce");
         }
-      }
       }
     }
   }

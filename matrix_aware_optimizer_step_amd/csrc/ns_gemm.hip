@@ -7,13 +7,12 @@
 //
 //   Gram    A = X X^T         P = Q = X            (symmetric: upper tiles)
 //   poly    B = b A + c A A   P = Q = A  (A = A^T) (symmetric: upper tiles)
-//   update  X' = a X + B X    P = B, Q = X^T       (X^T kept alongside X)
+//   update  X' = a X + B X    P = B, Q = X^T       (fp32: X^T kept alongside X)
 //
 // so one kernel template serves all three, with the stage's epilogue fused.
-// With bf16 compute and short update reductions (a tile class whose padded
-// short side is at most 2048, chosen by the host) the update instead reads X
-// itself as a k-major second operand (row k of X holds the tile's columns
-// contiguously) through LDS transpose reads, and no X^T is written.
+// With bf16 compute the update instead reads X itself as a k-major second
+// operand (row k of X holds the tile's columns contiguously) through LDS
+// transpose reads, and no X^T is kept.
 //
 // Tiling: a workgroup computes a BM x BM output tile (BM = 256 with eight
 // wave64s in a 2x4 grid, each owning 128x64; BM = 128 with four wave64s in a
@@ -147,9 +146,17 @@ __device__ __forceinline__ int swizzle(int row, int c) {
   return SWZ ? (c ^ ((row / kPhase) & (RC - 1))) : (c ^ (row & (RC - 1)));
 }
 
-__device__ __forceinline__ void lds_dma16(const char* g, char* l) {
-  __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(g),
-                                   (__attribute__((address_space(3))) void*)(l), 16, 0, 0);
+// Global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane i's
+// 16 bytes at base + off land at LDS address l + 16 i.  Issued as inline asm:
+// after the intrinsic form the compiler puts a wait for every outstanding
+// vector load (vmcnt 0) in front of each later ds_read_b64_tr_b16, which
+// would make the k-major update wait for the next k-tile's copy in every
+// k-tile.  The kernel orders these copies itself (barrier_keep_vm); nothing
+// reads a register written by them.
+__device__ __forceinline__ void lds_dma16(const char* base, uint32_t off, char* l) {
+  const uint32_t la = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)(l)));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(la))
+               : "memory");
 }
 
 template <int N>
@@ -215,6 +222,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
   // 16-byte chunks XOR-swizzled in groups of four by (row % 4), so that the
   // transpose reads of 4 consecutive rows x 64 bytes hit all 64 banks once.
   constexpr bool kQN = QN && (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
+  static_assert(kQN || sizeof(T) == 4 || !(EPI == EPI_UPDATE || EPI == EPI_FINAL), "the bf16 update reads X k-major");
   constexpr int QROWB = BN * 2;
   constexpr int QRC = QROWB / 16;
   static_assert(!kQN || (DMA && QRC >= 16 && BK * QROWB == BN * ROWB), "k-major Q tile: same bytes as n-major");
@@ -349,10 +357,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
       char* lp = smem + st * STB + wave * IPW * 1024;
       char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
-      for (int r = 0; r < IPW; ++r) lds_dma16(pk + dofs_p[r], lp + r * 1024);
+      for (int r = 0; r < IPW; ++r) lds_dma16(pk, dofs_p[r], lp + r * 1024);
       if (!same_pq) {
 #pragma unroll
-        for (int r = 0; r < IPWQ; ++r) lds_dma16(qk + dofs_q[r], lq + r * 1024);
+        for (int r = 0; r < IPWQ; ++r) lds_dma16(qk, dofs_q[r], lq + r * 1024);
       }
     };
     auto reg_load = [&](int kt) {
@@ -456,8 +464,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
     };
     frags(smem, 0, af[0], bfr[0]);
     // bf16 update: the high part of a*X enters from the operand tiles (below),
-    // the epilogue adds only the low part.  k-tile kt_x0 + hh of Q (X k-major,
-    // or X^T) holds rows [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e.
+    // the epilogue adds only the low part.  k-tile kt_x0 + hh of Q (X,
+    // k-major) holds rows [hh*BK, (hh+1)*BK) of this wave's sub-tile, i.e.
     // kFPK of its 32-row blocks, at the wave's columns.
     constexpr bool kAddXInLoop = (EPI == EPI_UPDATE || EPI == EPI_FINAL) && sizeof(T) == 2;
     constexpr int kFPK = BK / 32;
@@ -493,9 +501,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
       const char* sb = smem + st * STB;
       const int stn = (st + 1 == STAGES) ? 0 : st + 1;
       if constexpr (kAddXInLoop) {
-        // a * X[i][j] = a * Q[k = i][j] (k-major) or a * Q[j][k = i] (X^T):
-        // the k-tiles that cover this wave's rows hold the bf16 high part of
-        // X for its output elements.
+        // a * X[i][j] = a * Q[k = i][j]: the k-tiles that cover this wave's
+        // rows hold the bf16 high part of X for its output elements.
 #pragma unroll
         for (int hh = 0; hh < kNH; ++hh) {
           if (kt == kt_x0 + hh) {  // uniform over the wave
@@ -507,14 +514,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
                 for (int q = 0; q < 4; ++q) {
                   // rows f*32 + 8q + 4*half + 0..3 of the k-tile, column l%32 of block fj
                   const int fi = hh * kFPK + f;
-                  u32x2_t v;
-                  if constexpr (kQN) {
-                    v = lds_read_tr(sb + OPB + qn_off[fj] + (f * 32 + 8 * q + 4 * half) * QROWB);
-                  } else {  // X^T tile: the four values are consecutive in row l%32
-                    const uint2 u = *reinterpret_cast<const uint2*>(
-                        sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], f * 4 + q) << 4) + 8 * half);
-                    v = u32x2_t{u.x, u.y};
-                  }
+                  const u32x2_t v = lds_read_tr(sb + OPB + qn_off[fj] + (f * 32 + 8 * q + 4 * half) * QROWB);
                   acc[fi][fj][4 * q + 0] += at * bf16_to_f32(static_cast<uint16_t>(v.x));
                   acc[fi][fj][4 * q + 1] += at * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
                   acc[fi][fj][4 * q + 2] += at * bf16_to_f32(static_cast<uint16_t>(v.y));
@@ -941,24 +941,13 @@ void launch_one(const GemmLaunch& L, hipStream_t stream) {
 }
 
 template <typename T, int BM, int WGM, int WGN>
-hipError_t launch_t(int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
+hipError_t launch_t(int epi, const GemmLaunch& L, hipStream_t stream) {
   switch (epi) {
     case EPI_GRAM: launch_one<T, BM, WGM, WGN, EPI_GRAM>(L, stream); break;
     case EPI_POLY: launch_one<T, BM, WGM, WGN, EPI_POLY>(L, stream); break;
-    case EPI_UPDATE:
-      if (kmajor && sizeof(T) == 2) {
-        launch_one<T, BM, WGM, WGN, EPI_UPDATE, 1>(L, stream);
-      } else {
-        launch_one<T, BM, WGM, WGN, EPI_UPDATE>(L, stream);
-      }
-      break;
-    default:
-      if (kmajor && sizeof(T) == 2) {
-        launch_one<T, BM, WGM, WGN, EPI_FINAL, 1>(L, stream);
-      } else {
-        launch_one<T, BM, WGM, WGN, EPI_FINAL>(L, stream);
-      }
-      break;
+    // the bf16 update reads X k-major, the fp32 update X^T
+    case EPI_UPDATE: launch_one<T, BM, WGM, WGN, EPI_UPDATE, sizeof(T) == 2>(L, stream); break;
+    default: launch_one<T, BM, WGM, WGN, EPI_FINAL, sizeof(T) == 2>(L, stream); break;
   }
   return hipGetLastError();
 }
@@ -973,12 +962,12 @@ hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t stream) {
 
 hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
   if (L.total_tiles <= 0) return hipSuccess;
+  // the update's second operand: X k-major with bf16 compute, X^T with fp32
+  if ((epi == EPI_UPDATE || epi == EPI_FINAL) && kmajor != (compute == 1)) return hipErrorInvalidValue;
   if (compute == 1) {
-    return tile == 256 ? launch_t<uint16_t, 256, 2, 4>(epi, kmajor, L, stream)
-                       : launch_t<uint16_t, 128, 2, 2>(epi, kmajor, L, stream);
+    return tile == 256 ? launch_t<uint16_t, 256, 2, 4>(epi, L, stream) : launch_t<uint16_t, 128, 2, 2>(epi, L, stream);
   }
-  return tile == 256 ? launch_t<float, 256, 2, 4>(epi, false, L, stream)
-                     : launch_t<float, 128, 2, 2>(epi, false, L, stream);
+  return tile == 256 ? launch_t<float, 256, 2, 4>(epi, L, stream) : launch_t<float, 128, 2, 2>(epi, L, stream);
 }
 
 }  // namespace muon

@@ -239,7 +239,10 @@ DERIVED = [("L2 read latency, cycles per request", "TCP_TCC_READ_REQ_LATENCY_sum
             ("TCP_UTCL1_TRANSLATION_MISS_sum", "TCP_UTCL1_TRANSLATION_HIT_sum"), 100),
            ("TA busy % (average TA over one XCD's active cycles)", "TA_BUSY_avr", "GRBM_GUI_ACTIVE/8", 100),
            ("LDS bank conflicts % of LDS-active cycles", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", 100),
-           ("waves waiting on LDS instructions % of wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", 100)]
+           ("waves waiting on LDS instructions % of wave cycles", "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES", 100),
+           ("waves waiting (s_waitcnt, barriers) % of wave cycles", "SQ_WAIT_ANY", "SQ_WAVE_CYCLES", 100),
+           ("waves with an instruction ready but not issued % of wave cycles", "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES",
+            100)]
 
 
 def cmd_counters(a):

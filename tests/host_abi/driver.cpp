@@ -45,7 +45,7 @@ void orthogonalize_cases() {
     expect(muon_orthogonalize(&in, nullptr, &out, c.steps, 3.4445f, -4.775f, 2.0315f, 1e-7f, c.compute, kWs, need - 1,
                               nullptr), MUON_ERR_WORKSPACE, "orthogonalize, short workspace");
   }
-  // grouped, both tile classes, wide and tall, k-major and X^T classes
+  // grouped, both tile classes, wide and tall; bf16 (X read k-major) and fp32 (X^T kept)
   const int64_t counts[] = {2, 1, 96, 3, 1}, rows[] = {4096, 14336, 128, 520, 2300}, cols[] = {4096, 4096, 4096, 700, 2050};
   for (int32_t compute : {MUON_BF16, MUON_F32}) {
     const size_t need = muon_orthogonalize_grouped_workspace(5, counts, rows, cols, compute);

@@ -193,6 +193,7 @@ hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const Gem
   ++g_launches;
   const int64_t es = compute ? 2 : 4;
   if (tile != 128 && tile != 256) die("tile %d", tile);
+  if ((epi == EPI_UPDATE || epi == EPI_FINAL) && kmajor != (compute == 1)) die("update layout %d for compute %d", kmajor, compute);
   if (L.ngroups < 1 || L.ngroups > kMaxGroups) die("ngroups %d", L.ngroups);
   int64_t begin = 0;
   for (int g = 0; g < L.ngroups; ++g) {

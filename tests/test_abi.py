@@ -203,15 +203,14 @@ def test_apply_rejects_bad_arguments():
 def test_workspace_queries():
     assert L.muon_momentum_workspace(0, 4, 4) == 0
     assert L.muon_momentum_workspace(2, 4096, 14336) >= 2 * (4096 * 14336 // 8192) * 4
-    # X and X^T twice each (bf16 compute: plus the low part of X, one int8 code
-    # per element and one exponent byte per 16), and A and B (4096^2 each).  A
-    # bf16 problem whose short side pads to at most 2048 keeps no X^T: its
-    # update reads X itself, k-major.
+    # fp32: X and X^T twice each, and A and B (4096^2 each).  bf16: X twice
+    # (its update reads X itself, k-major: no X^T is kept) plus the low part
+    # of X, one int8 code per element and one exponent byte per 16.
     b = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_BF16)
     f = L.muon_orthogonalize_workspace(1, 4096, 14336, L.MUON_F32)
     mn, mm = 4096 * 14336, 4096 * 4096
     lo = mn + mn // 16
-    assert lo + mn * 4 * 2 + 2 * mm * 2 <= b < lo + mn * 4 * 2 + 2 * mm * 2 + (1 << 20)
+    assert lo + mn * 2 * 2 + 2 * mm * 2 <= b < lo + mn * 2 * 2 + 2 * mm * 2 + (1 << 20)
     assert mn * 4 * 4 + 2 * mm * 4 <= f < mn * 4 * 4 + 2 * mm * 4 + (1 << 20)
     # one 768 x 2048 matrix: 6 Gram tiles, so its 2048-deep reduction is split
     # in 4 slices whose fp32 partial sums (4 x 768^2) are also in the workspace

@@ -404,13 +404,11 @@ def test_grouped_equals_separate_calls(mx):
         assert torch.equal(a, b)
 
 
-def test_grouped_mixed_update_layouts(mx):
-    """With bf16 compute a tile class whose every group pads its short side to
-    at most 2048 updates with X read k-major (no X^T kept); otherwise with X^T.
-    Alone, the first and last shapes here go k-major; grouped with the others
-    they share the X^T layout.  Both layouts give every lane the same k values
-    for every MFMA, so the grouped call must equal the separate calls bit for
-    bit, wide and tall, and match the oracle."""
+def test_grouped_update_reduction_lengths(mx):
+    """The bf16 update reads X itself, k-major, at every reduction length: here
+    padded short sides of 768, 2304 and 2048 in one grouped call, wide and
+    tall, ragged against the 256 tiles.  The grouped call must equal the
+    separate calls bit for bit and match the oracle."""
     shapes = [(2, 520, 700), (1, 2100, 2200), (1, 2300, 2050), (1, 1900, 2040)]
     Ns = [randn(s, 70 + k, torch.bfloat16) for k, s in enumerate(shapes)]
     sep = [run_ns(mx, N, mx.MUON_BF16) for N in Ns]
