@@ -490,7 +490,8 @@ def main():
                                        "abc": [float(x) for x in stepper.coeffs], "lr": stepper.lr,
                                        "weight_decay": stepper.weight_decay,
                                        "scale": f"{stepper.coeff}*sqrt(max(m,n))", "momentum_dtype": "f32",
-                                       "ns_input_dtype": "f32"},
+                                       "ns_input_dtype": ("bf16 high part + 8-bit residual, written by the momentum "
+                                                          "kernel" if stepper.packed else "f32")},
                    "parallelism": "single GPU"},
         "repeats": {"blocks": nblocks, "steps_per_block": sizes, "steps_per_s": block_rates,
                     "median_steps_per_s": float(np.median(block_rates)), "min_steps_per_s": min(block_rates),
@@ -505,7 +506,9 @@ def main():
         "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"ns_gemm_{cfg.slug}_hbm_traffic.md", "ns_gemm.hip",
                                                                     "ns_gemm_bytes_per_step"),
-                     "kernel": "ns_gemm_kernel (Gram, polynomial and update launches of muon_orthogonalize_grouped)"},
+                     "kernel": ("ns_gemm_kernel (Gram, polynomial and update launches of "
+                                f"{'muon_orthogonalize_packed_grouped' if stepper.packed else 'muon_orthogonalize_grouped'}"
+                                "; achieved over the whole call, traffic over the ns_gemm_kernel launches)")},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -500,7 +500,8 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             r.tile = tile;
             r.splits = p.gram_splits;
             r.compute = compute;
-            R.first[R.ngroups + 1] = R.first[R.ngroups] + p.count * (mm / 1024);
+            const int64_t T = p.Mp / tile, nb = tile / 64;  // 64x64 blocks of the computed tiles
+            R.first[R.ngroups + 1] = R.first[R.ngroups] + p.count * (T * (T + 1) / 2 * nb * nb);
             ++R.ngroups;
           }
           if (R.ngroups > 0 && (e = launch_gram_reduce(R, stream)) != hipSuccess)

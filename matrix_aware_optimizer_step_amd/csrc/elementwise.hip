@@ -547,6 +547,78 @@ __global__ __launch_bounds__(kThreads) void copy_out_kernel(const CopyOutArgs a)
   }
 }
 
+// ------------------------------------------------------------ split Gram
+
+// One workgroup per 64x64 block of a computed tile (tile row <= tile
+// column) of one matrix: adds the S slices' partial sums in a fixed order,
+// scales (step 0 of the packed path), stores the block, and for a tile off
+// the diagonal also its mirror, transposed through LDS.  Thread t sums 16
+// consecutive elements of row t/4 of the block (float4 reads of each slice).
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const GramReduce R) {
+  __shared__ float tr[64][65];
+  const int64_t b = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < R.ngroups && b >= R.first[gi + 1]) ++gi;
+  const GramReduceGroup& g = R.g[gi];
+  const int T = g.Mp / g.tile;
+  const int nb = g.tile / 64;                                            // 64-blocks per tile side
+  const int64_t per = static_cast<int64_t>(T) * (T + 1) / 2 * nb * nb;  // workgroups per matrix
+  const int64_t local = b - R.first[gi];
+  const int64_t mat = local / per;
+  const int r = static_cast<int>(local - mat * per);
+  const int sub = r % (nb * nb);
+  int tt = r / (nb * nb);
+  int ti = 0;
+  while (tt >= T - ti) {
+    tt -= T - ti;
+    ++ti;
+  }
+  const int tj = ti + tt;
+  const int r0 = ti * g.tile + (sub / nb) * 64;
+  const int c0 = tj * g.tile + (sub % nb) * 64;
+  const int row = threadIdx.x >> 2;
+  const int cq = (threadIdx.x & 3) * 16;
+  const float* part = reinterpret_cast<const float*>(reinterpret_cast<const char*>(g.part) + mat * g.part_mat) +
+                      static_cast<int64_t>(r0 + row) * g.Mp + c0 + cq;
+  const int64_t slice = static_cast<int64_t>(g.Mp) * g.Mp;
+  float scale = 1.0f;
+  if (g.xs_sumsq != nullptr) {
+    const float xs = 1.0f / (sqrtf(g.xs_sumsq[mat]) + g.xs_eps);
+    scale = xs * xs;
+  }
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = 0.0f;
+  for (int s = 0; s < g.splits; ++s) {  // fixed order
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 x = *reinterpret_cast<const float4*>(part + s * slice + 4 * q);
+      v[4 * q] += x.x;
+      v[4 * q + 1] += x.y;
+      v[4 * q + 2] += x.z;
+      v[4 * q + 3] += x.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] *= scale;
+  char* A = g.A + mat * g.a_mat;
+  const int es = g.compute ? 2 : 4;  // compute 1 = bf16, as the dtype of store8
+  auto put16 = [&](int i, int j, const float* w) {  // 16 consecutive elements of row i from column j
+    char* p = A + (static_cast<int64_t>(i) * g.Mp + j) * es;
+    store8(p, g.compute, w);
+    store8(p + 8 * es, g.compute, w + 8);
+  };
+  put16(r0 + row, c0 + cq, v);
+  if (ti == tj) return;  // a diagonal tile's partial sums hold both of its halves
+#pragma unroll
+  for (int e = 0; e < 16; ++e) tr[row][cq + e] = v[e];
+  __syncthreads();
+  float w[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) w[e] = tr[cq + e][row];  // mirror row c0 + row, columns r0 + cq ..
+  put16(c0 + row, r0 + cq, w);
+}
+
 }  // namespace
 
 int elementwise_blocks_per_matrix(int64_t rows, int64_t cols) {
@@ -624,6 +696,12 @@ hipError_t launch_momentum_pack_grouped(const MomentumPackGroups& a, hipStream_t
 hipError_t launch_copy_out(const CopyOutArgs& a, int64_t count, hipStream_t stream) {
   dim3 grid((a.cols + kTile - 1) / kTile, (a.rows + kTile - 1) / kTile, static_cast<unsigned>(count));
   hipLaunchKernelGGL(copy_out_kernel, grid, dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t stream) {
+  if (a.first[a.ngroups] <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -868,45 +868,6 @@ void ns_gemm_kernel(const GemmLaunch L) {
   }  // tiles
 }
 
-// ---------------------------------------------------------------- split Gram
-
-__global__ __launch_bounds__(256) void gram_reduce_kernel(const GramReduce R) {
-  const int64_t b = blockIdx.x;
-  int gi = 0;
-  while (gi + 1 < R.ngroups && b >= R.first[gi + 1]) ++gi;
-  const GramReduceGroup& g = R.g[gi];
-  const int64_t per = (static_cast<int64_t>(g.Mp) * g.Mp) / 1024;  // workgroups per matrix
-  const int64_t local = b - R.first[gi];
-  const int64_t mat = local / per;
-  const int64_t e0 = (local - mat * per) * 1024 + threadIdx.x * 4;  // four consecutive elements of one row
-  const int i = static_cast<int>(e0 / g.Mp);
-  const int j0 = static_cast<int>(e0 - static_cast<int64_t>(i) * g.Mp);
-  const float* part = reinterpret_cast<const float*>(reinterpret_cast<const char*>(g.part) + mat * g.part_mat);
-  const int64_t slice = static_cast<int64_t>(g.Mp) * g.Mp;
-  float scale = 1.0f;
-  if (g.xs_sumsq != nullptr) {
-    const float xs = 1.0f / (sqrtf(g.xs_sumsq[mat]) + g.xs_eps);
-    scale = xs * xs;
-  }
-  float v[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int j = j0 + e;
-    // computed tiles have tile row <= tile column; below that, the mirror
-    const bool up = i / g.tile <= j / g.tile;
-    const int64_t at = up ? static_cast<int64_t>(i) * g.Mp + j : static_cast<int64_t>(j) * g.Mp + i;
-    float sum = 0.0f;
-    for (int s = 0; s < g.splits; ++s) sum += part[s * slice + at];  // fixed order
-    v[e] = scale * sum;
-  }
-  char* A = g.A + mat * g.a_mat;
-  if (g.compute) {
-    Elem<uint16_t>::store4(A + (static_cast<int64_t>(i) * g.Mp + j0) * 2, v[0], v[1], v[2], v[3]);
-  } else {
-    Elem<float>::store4(A + (static_cast<int64_t>(i) * g.Mp + j0) * 4, v[0], v[1], v[2], v[3]);
-  }
-}
-
 // Workgroups of a tile size that are resident on the current device at once
 // (one 256-tile or two 128-tile workgroups per CU: LDS bound), rounded down
 // to a multiple of the 8 XCDs; 0 if the device cannot be queried.
@@ -953,12 +914,6 @@ hipError_t launch_t(int epi, const GemmLaunch& L, hipStream_t stream) {
 }
 
 }  // namespace
-
-hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t stream) {
-  if (a.first[a.ngroups] <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gram_reduce_kernel, dim3(static_cast<unsigned>(a.first[a.ngroups])), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
 
 hipError_t launch_ns_gemm(int compute, int tile, int epi, bool kmajor, const GemmLaunch& L, hipStream_t stream) {
   if (L.total_tiles <= 0) return hipSuccess;

@@ -41,7 +41,8 @@ SRC = os.path.join(ROOT, "matrix_aware_optimizer_step_amd", "csrc")
 PEAK_BF16_TFLOPS = 2500.0
 SIMDS = 1024            # 256 CUs x 4 SIMDs
 XCDS = 8
-STEP_KERNEL = "momentum_grouped_kernel"
+# one dispatch per optimizer step: the momentum kernel of the packed pair, or of the separate calls
+STEP_KERNELS = ("momentum_pack_kernel", "momentum_grouped_kernel")
 EPI = {0: "Gram A=XX^T", 1: "poly B=bA+cAA", 2: "update X=aX+BX", 3: "update, last step (caller output)"}
 
 
@@ -71,7 +72,7 @@ def label(name: str) -> str:
 
 
 LIBRARY_KERNELS = ("ns_gemm", "gram_reduce", "momentum", "pack", "apply", "finalize", "sumsq", "copy_out", "adamw", "sgemm", "qr_",
-                   "rot_adam", "eye", "gather", "sign_copy", "ns_")
+                   "rot_adam", "eye", "gather_kernel", "sign_copy", "ns_")
 
 
 def find(d, suffix):
@@ -101,7 +102,7 @@ def trace_table(d):
             n = col(r, "Kernel_Name", "KernelName", "Name")
             t = int(col(r, "End_Timestamp", "EndNs")) - int(col(r, "Start_Timestamp", "BeginNs"))
             durs[label(n)].append(t)
-    steps = len(durs.get(STEP_KERNEL, []))
+    steps = sum(len(durs.get(k, [])) for k in STEP_KERNELS)
     return durs, steps
 
 
@@ -136,7 +137,7 @@ def header(title, commands, note=None):
 def cmd_trace(a):
     durs, steps = trace_table(a.dirs[0])
     lines = header(a.title, a.command, f"The trace covers {steps} optimizer steps (the dispatches of "
-                                       f"{STEP_KERNEL}); kernels that are not the library's (input generation) are "
+                                       f"{' or '.join(STEP_KERNELS)}); kernels that are not the library's (input generation) are "
                                        f"omitted.")
     lines += ["| kernel | calls | avg us | total ms | ms per step |", "|---|---:|---:|---:|---:|"]
     ours = {k: v for k, v in durs.items() if k.startswith(LIBRARY_KERNELS)}
@@ -155,7 +156,7 @@ def cmd_trace(a):
 def cmd_mfma(a):
     disp = counters(a.dirs[0])
     tdurs, _ = trace_table(a.trace) if a.trace else ({}, 0)
-    steps = sum(1 for e in disp if e["label"] == STEP_KERNEL)
+    steps = sum(1 for e in disp if e["label"] in STEP_KERNELS)
     fam = OrderedDict()
     for e in disp:
         if not e["label"].startswith("ns_gemm"):
@@ -202,7 +203,7 @@ def cmd_traffic(a):
         sys.exit("no calibration copy kernel in the counter output (run the benchmark with --copy-calibration)")
     gib_kb = 1 << 20
     fs, ws = gib_kb / max(cal_f), gib_kb / max(cal_w)
-    steps = sum(1 for e in fetch if e["label"] == STEP_KERNEL)
+    steps = sum(1 for e in fetch if e["label"] in STEP_KERNELS)
     note = (f"Calibration: the 1 GiB device copy reads FETCH_SIZE = {max(cal_f):.0f} KB and WRITE_SIZE = "
             f"{max(cal_w):.0f} KB against {gib_kb} KB moved each way; the factors applied below are {fs:.3f} (fetch) "
             f"and {ws:.3f} (write).")

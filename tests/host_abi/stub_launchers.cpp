@@ -143,9 +143,10 @@ hipError_t launch_gram_reduce(const GramReduce& a, hipStream_t) {
     const GramReduceGroup& r = a.g[g];
     const int64_t mm = static_cast<int64_t>(r.Mp) * r.Mp;
     const int64_t n = a.first[g + 1] - a.first[g];
-    if (r.Mp % r.tile || mm % 1024 || n <= 0 || n % (mm / 1024)) die("gram reduce %d: order %d, %lld blocks", g, r.Mp,
-                                                                       (long long)n);
-    const int64_t count = n / (mm / 1024);
+    if ((r.tile != 128 && r.tile != 256) || r.Mp % r.tile) die("gram reduce %d: order %d, tile %d", g, r.Mp, r.tile);
+    const int64_t T = r.Mp / r.tile, nb = r.tile / 64, per = T * (T + 1) / 2 * nb * nb;
+    if (n <= 0 || n % per) die("gram reduce %d: order %d, %lld blocks", g, r.Mp, (long long)n);
+    const int64_t count = n / per;
     in_ws(r.part, count, r.part_mat, r.splits * mm * 4, "gram reduce partials");
     in_ws(r.A, count, r.a_mat, mm * (r.compute ? 2 : 4), "gram reduce output");
   }
