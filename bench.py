@@ -1,10 +1,13 @@
 """Benchmark of one Muon optimizer step on one MI355X.
 
 A step is the whole hot path over every matrix of the workload:
-muon_momentum (fp32 momentum, Nesterov blend, sum of squares) ->
-muon_orthogonalize_grouped (5 quintic Newton-Schulz steps, bf16 MFMA with
-fp32 accumulation) -> muon_apply (0.2*sqrt(max(m,n)) shape factor,
-decoupled weight decay), with inputs resident in HBM.
+momentum (fp32 momentum, Nesterov blend, sum of squares; it writes the
+Newton-Schulz input) -> 5 quintic Newton-Schulz steps (bf16 MFMA with fp32
+accumulation) -> the update (0.2*sqrt(max(m,n)) shape factor, decoupled
+weight decay), with inputs resident in HBM.  By default the update is
+applied by the last Newton-Schulz step (muon_momentum_packed_grouped, then
+muon_orthogonalize_apply_packed_grouped); --separate-apply runs it as its own
+kernel (muon_orthogonalize_packed_grouped, then muon_apply_grouped).
 
 Prints one JSON line.  ``value`` is optimizer steps per second; the line
 also carries the Newton-Schulz TFLOP/s (algorithmic flops: upper-triangle
@@ -76,12 +79,20 @@ def log(msg):
 COEFFS = {"quintic": ((3.4445, -4.7750, 2.0315), 5), "track3": ((2.0, -1.5, 0.5), 12), "cubic": ((1.5, -0.5, 0.0), 5)}
 
 
-def make_stepper(mx, weights, grads, coeffs="quintic", steps=None):
+def make_stepper(mx, weights, grads, coeffs="quintic", steps=None, fused_apply=True):
     """The optimizer step this benchmark times: every group of the workload
-    in one MuonStep (grouped Newton-Schulz launches, bf16 MFMA)."""
+    in one MuonStep (grouped Newton-Schulz launches, bf16 MFMA; by default
+    the update applied by the last Newton-Schulz step's epilogue)."""
     abc, k = COEFFS[coeffs]
     return mx.MuonStep(list(zip(weights, grads)), compute=mx.MUON_BF16, lr=LR, weight_decay=WD, coeffs=abc,
-                       steps=k if steps is None else steps)
+                       steps=k if steps is None else steps, fused_apply=fused_apply)
+
+
+def ns_call(stepper):
+    """The entry point that runs the Newton-Schulz steps of a MuonStep."""
+    if stepper.packed and stepper.fused_apply:
+        return "muon_orthogonalize_apply_packed_grouped"
+    return "muon_orthogonalize_packed_grouped" if stepper.packed else "muon_orthogonalize_grouped"
 
 
 def measured_traffic(profile, source, key):
@@ -375,6 +386,9 @@ def main():
                     help="muon: the Muon step of --workload (default); adamw: the AdamW step over the 8B-style "
                          "model's embeddings, head and norms; soap: SOAP steps over --workload's matrices")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-apply", action="store_true",
+                    help="apply the update with its own kernel (muon_apply_grouped) instead of in the last "
+                         "Newton-Schulz step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB device-to-device copy before the warmup, so that profiler byte counters "
                          "can be scaled against a kernel of known traffic")
@@ -410,7 +424,8 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f} s")
 
-    stepper = make_stepper(mx, weights, grads, args.coeffs, args.ns_steps)
+    stepper = make_stepper(mx, weights, grads, args.coeffs, args.ns_steps, fused_apply=not args.separate_apply)
+    fused = stepper.fused_apply
     ns_steps = stepper.steps
     if args.copy_calibration:
         calibration_copy(dev)
@@ -460,7 +475,7 @@ def main():
     mom_bytes = momentum_bytes(cfg, stepper.packed)
     app_bytes = elems * (4 + 2)       # W bf16 read+write, O bf16 read
     mom_gbs = mom_bytes / (t_mom * 1e-3) / 1e9
-    app_gbs = app_bytes / (t_app * 1e-3) / 1e9
+    app_gbs = None if fused else app_bytes / (t_app * 1e-3) / 1e9
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -502,12 +517,15 @@ def main():
                           "tflops_algorithmic_median": algo / (float(np.median(ns_times)) * 1e-3) / 1e12,
                           "flops_algorithmic": algo, "flops_nominal": nominal},
         "elementwise": {"momentum_ms": t_mom, "momentum_gbs": mom_gbs, "momentum_frac_hbm": mom_gbs / PEAK_HBM_GBS,
-                        "apply_ms": t_app, "apply_gbs": app_gbs, "apply_frac_hbm": app_gbs / PEAK_HBM_GBS},
+                        "apply_ms": None if fused else t_app, "apply_gbs": app_gbs,
+                        "apply_frac_hbm": None if fused else app_gbs / PEAK_HBM_GBS,
+                        "apply": ("in the last Newton-Schulz step's epilogue (reads and writes W, O never stored; "
+                                  "its time is in newton_schulz.ms)" if fused else "muon_apply_grouped")},
         "roofline": {"bound": "mfma", "achieved": ns_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": ns_tflops / PEAK_BF16_TFLOPS, "traffic": measured_traffic(f"ns_gemm_{cfg.slug}_hbm_traffic.md", "ns_gemm.hip",
                                                                     "ns_gemm_bytes_per_step"),
                      "kernel": ("ns_gemm_kernel (Gram, polynomial and update launches of "
-                                f"{'muon_orthogonalize_packed_grouped' if stepper.packed else 'muon_orthogonalize_grouped'}"
+                                f"{ns_call(stepper)}"
                                 "; achieved over the whole call, traffic over the ns_gemm_kernel launches)")},
         "cpu_baseline": cpu,
     }

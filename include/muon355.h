@@ -284,6 +284,29 @@ muon_status_t muon_orthogonalize_packed_grouped(int ngroups, const float* const*
                                                 size_t ws_bytes, void* stream);
 
 /*
+ * The second call of the packed pair with the parameter update folded into
+ * its last step ([GUIDE] 11.5 update equation; [LESSON] "Muon" step 4):
+ * instead of writing O it updates each weight in place,
+ *   W <- (1 - lr*weight_decay) * W - lr * s * O,
+ * s from `mode` and `coeff` and (m, n) = (rows, cols) of W, as
+ * muon_apply_grouped does for an O of the same shape.  O is never stored:
+ * each value goes from the last GEMM's fp32 accumulator into the update, so
+ * the result differs from muon_orthogonalize_packed_grouped followed by
+ * muon_apply_grouped only by O's rounding to the dtype of a caller buffer
+ * (none for fp32 O).  weights[g] takes the place of outs[g] (same shapes,
+ * bf16 or fp32, read and written in place); every other argument, the
+ * workspace and the errors are those of muon_orthogonalize_packed_grouped,
+ * and lr, weight_decay, mode and coeff are checked as in muon_apply.
+ */
+muon_status_t muon_orthogonalize_apply_packed_grouped(int ngroups, const float* const* sumsqs,
+                                                      const muon_batch_t* weights, int steps,
+                                                      float a, float b, float c, float eps,
+                                                      float lr, float weight_decay, int32_t mode,
+                                                      float coeff, int32_t compute,
+                                                      void* workspace, size_t ws_bytes,
+                                                      void* stream);
+
+/*
  * Parameter update ([GUIDE] 11.5 update equation; [LESSON] "Muon" step 4):
  *   W <- (1 - lr*weight_decay) * W - lr * s * O
  * with s from `mode` and `coeff` (see muon_scale_t) and (m, n) = (rows,

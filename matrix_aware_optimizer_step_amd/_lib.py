@@ -27,7 +27,7 @@ EXPORTED = ("muon_abi_version", "muon_last_error", "muon_status_string", "muon_m
             "muon_momentum", "muon_momentum_grouped_workspace", "muon_momentum_grouped", "muon_momentum_grouped_noalloc",
             "muon_orthogonalize_workspace", "muon_orthogonalize", "muon_orthogonalize_grouped_workspace",
             "muon_orthogonalize_grouped", "muon_packed_grouped_workspace", "muon_momentum_packed_grouped",
-            "muon_orthogonalize_packed_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
+            "muon_orthogonalize_packed_grouped", "muon_orthogonalize_apply_packed_grouped", "muon_apply", "muon_apply_grouped", "muon_adamw", "soap_statistics",
             "soap_statistics_grouped", "soap_qr_workspace", "soap_qr", "soap_refresh_workspace", "soap_refresh",
             "soap_refresh_grouped_workspace", "soap_refresh_grouped",
             "soap_precondition_workspace", "soap_precondition", "soap_precondition_grouped_workspace",
@@ -92,6 +92,9 @@ def load() -> ctypes.CDLL:
                                                         i32, vp, sz, vp]),
         "muon_orthogonalize_packed_grouped": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(vp), P, ctypes.c_int, f32,
                                                              f32, f32, f32, i32, vp, sz, vp]),
+        "muon_orthogonalize_apply_packed_grouped": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(vp), P, ctypes.c_int,
+                                                                   f32, f32, f32, f32, f32, f32, i32, f32, i32, vp,
+                                                                   sz, vp]),
         "muon_apply": (ctypes.c_int, [P, P, f32, f32, i32, f32, vp]),
         "muon_apply_grouped": (ctypes.c_int, [ctypes.c_int, P, P, f32, f32, i32, f32, vp]),
         "muon_adamw": (ctypes.c_int, [ctypes.POINTER(MuonTensorList), i64, f32, f32, f32, f32, f32, vp]),
@@ -237,6 +240,19 @@ def muon_orthogonalize_packed_grouped(sumsq_ptrs, outs, steps: int, a: float, b:
     st = load().muon_orthogonalize_packed_grouped(n, (ctypes.c_void_p * n)(*sumsq_ptrs), (MuonBatch * n)(*outs),
                                                   steps, a, b, c, eps, compute, workspace_ptr, ws_bytes, stream)
     _check(st, "muon_orthogonalize_packed_grouped")
+
+
+def muon_orthogonalize_apply_packed_grouped(sumsq_ptrs, weights, steps: int, a: float, b: float, c: float,
+                                            eps: float, lr: float, weight_decay: float, mode: int, coeff: float,
+                                            compute: int, workspace_ptr: int, ws_bytes: int, stream: int) -> None:
+    n = len(weights)
+    if len(sumsq_ptrs) != n:
+        raise ValueError("per-group lists differ in length")
+    st = load().muon_orthogonalize_apply_packed_grouped(n, (ctypes.c_void_p * n)(*sumsq_ptrs),
+                                                        (MuonBatch * n)(*weights), steps, a, b, c, eps, lr,
+                                                        weight_decay, mode, coeff, compute, workspace_ptr, ws_bytes,
+                                                        stream)
+    _check(st, "muon_orthogonalize_apply_packed_grouped")
 
 
 def muon_apply(weight: MuonBatch, ortho: MuonBatch, lr: float, weight_decay: float, mode: int, coeff: float,

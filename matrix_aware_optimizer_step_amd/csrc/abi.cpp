@@ -261,7 +261,8 @@ GemmGroup base_group(const GroupPlan& p, int tiles_per_mat, int tiles_m, int til
 muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const float* const* sumsqs,
                                 const muon_batch_t* outs, int steps, float a, float b, float c,
                                 float eps, int32_t compute, void* workspace, size_t ws_bytes,
-                                hipStream_t stream, bool packed = false) {
+                                hipStream_t stream, bool packed = false, const float* ap_decay = nullptr,
+                                const float* ap_step = nullptr) {
   if (ngroups < 1 || ngroups > kMaxGroups)
     return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
   if (compute != MUON_F32 && compute != MUON_BF16)
@@ -444,6 +445,11 @@ muon_status_t run_orthogonalize(int ngroups, const muon_batch_t* ins, const floa
             }
             if (last) {
               G.user = to_mat(&outs[g]);
+              if (ap_decay != nullptr) {  // outs are the weights: W <- decay*W - step*O
+                G.ap = 1;
+                G.ap_decay = ap_decay[g];
+                G.ap_step = ap_step[g];
+              }
             } else if (compute == MUON_BF16) {
               // the low part is rewritten in place: each element is read
               // and written by the same lane of the same tile
@@ -621,16 +627,14 @@ muon_status_t check_workspace(void* workspace, size_t ws_bytes, size_t need) {
 }
 
 // Checks of one apply batch; fills the kernel arguments.
-muon_status_t prepare_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,
-                            int32_t mode, float coeff, ApplyArgs* a, bool* vec) {
-  muon_status_t st;
-  if ((st = check_batch(weight, "weight", true)) != MUON_OK) return st;
-  if ((st = check_batch(ortho, "ortho", true)) != MUON_OK) return st;
-  if (!same_shape(weight, ortho)) return fail(MUON_ERR_INVALID_VALUE, "weight and ortho shapes differ");
+// The update's factors for an m x n weight: decay = 1 - lr*weight_decay and
+// step = lr * s, s from the scale mode ("LLM Optimizers…" section 11.5).
+muon_status_t apply_factors(int64_t rows, int64_t cols, float lr, float weight_decay, int32_t mode, float coeff,
+                            float* decay, float* step) {
   if (!finite(lr) || !finite(weight_decay) || !finite(coeff))
     return fail(MUON_ERR_INVALID_VALUE, "lr, weight_decay and coeff must be finite");
-  const double m = static_cast<double>(weight->rows);
-  const double n = static_cast<double>(weight->cols);
+  const double m = static_cast<double>(rows);
+  const double n = static_cast<double>(cols);
   double s;
   switch (mode) {
     case MUON_SCALE_MATCH_RMS: s = static_cast<double>(coeff) * std::sqrt(m > n ? m : n); break;
@@ -638,14 +642,28 @@ muon_status_t prepare_apply(const muon_batch_t* weight, const muon_batch_t* orth
     case MUON_SCALE_NONE: s = 1.0; break;
     default: return fail(MUON_ERR_INVALID_VALUE, "unknown scale mode %d", mode);
   }
+  *decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
+  *step = static_cast<float>(static_cast<double>(lr) * s);
+  return MUON_OK;
+}
+
+muon_status_t prepare_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,
+                            int32_t mode, float coeff, ApplyArgs* a, bool* vec) {
+  muon_status_t st;
+  if ((st = check_batch(weight, "weight", true)) != MUON_OK) return st;
+  if ((st = check_batch(ortho, "ortho", true)) != MUON_OK) return st;
+  if (!same_shape(weight, ortho)) return fail(MUON_ERR_INVALID_VALUE, "weight and ortho shapes differ");
+  float decay, step;
+  if ((st = apply_factors(weight->rows, weight->cols, lr, weight_decay, mode, coeff, &decay, &step)) != MUON_OK)
+    return st;
   std::memset(a, 0, sizeof(*a));
   a->W = to_mat(weight);
   a->O = to_mat(ortho);
   a->rows = static_cast<int32_t>(weight->rows);
   a->cols = static_cast<int32_t>(weight->cols);
   a->cdiv = make_fastdiv(static_cast<uint32_t>(weight->cols));
-  a->decay = static_cast<float>(1.0 - static_cast<double>(lr) * weight_decay);
-  a->step = static_cast<float>(static_cast<double>(lr) * s);
+  a->decay = decay;
+  a->step = step;
   *vec = vec_ok(weight) && vec_ok(ortho);
   return MUON_OK;
 }
@@ -893,6 +911,25 @@ muon_status_t muon_orthogonalize_packed_grouped(int ngroups, const float* const*
                                                 void* workspace, size_t ws_bytes, void* stream) {
   return run_orthogonalize(ngroups, nullptr, sumsqs, outs, steps, a, b, c, eps, compute, workspace, ws_bytes,
                            static_cast<hipStream_t>(stream), true);
+}
+
+muon_status_t muon_orthogonalize_apply_packed_grouped(int ngroups, const float* const* sumsqs,
+                                                      const muon_batch_t* weights, int steps, float a, float b,
+                                                      float c, float eps, float lr, float weight_decay, int32_t mode,
+                                                      float coeff, int32_t compute, void* workspace, size_t ws_bytes,
+                                                      void* stream) {
+  if (ngroups < 1 || ngroups > kMaxGroups)
+    return fail(MUON_ERR_INVALID_VALUE, "ngroups %d outside [1, %d]", ngroups, kMaxGroups);
+  if (!weights) return fail(MUON_ERR_INVALID_VALUE, "weights is NULL");
+  float decay[kMaxGroups], step[kMaxGroups];
+  for (int g = 0; g < ngroups; ++g) {
+    muon_status_t st = check_batch(&weights[g], "weight", true);
+    if (st == MUON_OK)
+      st = apply_factors(weights[g].rows, weights[g].cols, lr, weight_decay, mode, coeff, &decay[g], &step[g]);
+    if (st != MUON_OK) return in_group(st, g);
+  }
+  return run_orthogonalize(ngroups, nullptr, sumsqs, weights, steps, a, b, c, eps, compute, workspace, ws_bytes,
+                           static_cast<hipStream_t>(stream), true, decay, step);
 }
 
 muon_status_t muon_apply(const muon_batch_t* weight, const muon_batch_t* ortho, float lr, float weight_decay,

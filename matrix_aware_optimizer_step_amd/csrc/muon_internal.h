@@ -68,6 +68,11 @@ struct GemmGroup {
   MatBatch user;
   int32_t tall;                  // 1: user output is X^T
   int32_t ms, ns;                // true (unpadded) Newton-Schulz shape
+  // FINAL with the parameter update folded in (ap = 1): `user` is the weight
+  // W, and the epilogue writes W <- ap_decay * W - ap_step * O in place of O
+  int32_t ap;
+  float ap_decay, ap_step;
+  int32_t pad7_;
   // Step 0 from an unnormalized packed input (the momentum kernel wrote
   // N itself): with xs = 1/(sqrt(xs_sumsq[mat]) + xs_eps), the Gram's
   // products are multiplied by xs^2, the polynomial uses xs*b and xs*c and

@@ -135,6 +135,50 @@ __device__ __forceinline__ void store_user(const MatBatch& u, char* base, int64_
   }
 }
 
+// The parameter update folded into the last step ("LLM Optimizers: From SGD
+// and AdamW to SOAP, Muon, and Scalable Training", section 11.5 update
+// equation): W <- decay * W - step * O on the caller's weight, read and
+// written in its own dtype, fp32 arithmetic as in the separate apply call.
+__device__ __forceinline__ void apply_user(const MatBatch& u, char* base, int64_t r, int64_t c, float v, float decay,
+                                           float step) {
+  char* p = base + (r * u.ld + c) * (u.dtype ? 2 : 4);
+  if (u.dtype) {
+    const float w = bf16_to_f32(*reinterpret_cast<const uint16_t*>(p));
+    *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(decay * w - step * v);
+  } else {
+    float* q = reinterpret_cast<float*>(p);
+    *q = decay * *q - step * v;
+  }
+}
+// ... eight consecutive elements (16-byte aligned)
+__device__ __forceinline__ void apply8(char* p, int dtype, float decay, float step, const float4& a,
+                                       const float4& b) {
+  const float o[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float w[8];
+  if (dtype) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t q[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      w[2 * k] = bf16_to_f32(static_cast<uint16_t>(q[k]));
+      w[2 * k + 1] = bf16_to_f32(static_cast<uint16_t>(q[k] >> 16));
+    }
+  } else {
+    const float4 x0 = reinterpret_cast<const float4*>(p)[0];
+    const float4 x1 = reinterpret_cast<const float4*>(p)[1];
+    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+    w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = decay * w[e] - step * o[e];
+  const float4 y0 = make_float4(w[0], w[1], w[2], w[3]), y1 = make_float4(w[4], w[5], w[6], w[7]);
+  if (dtype) {
+    Elem<uint16_t>::store8(p, y0, y1);
+  } else {
+    Elem<float>::store8(p, y0, y1);
+  }
+}
+
 // Physical 16-byte slot of logical chunk c in an LDS row of RC chunks.  A
 // ds_read_b128 from 16 consecutive rows at one logical chunk is one cycle of
 // the 64-bank (256-byte) gfx950 LDS when the 16 slots are distinct modulo
@@ -196,7 +240,7 @@ __device__ __forceinline__ void barrier_keep_vm() {
 //   QN:     1 = the bf16 update's second operand is X itself, k-major (read
 //           through LDS transpose reads); 0 = it is X^T, n-major.
 template <typename T, int BM, int WGM, int WGN, int EPI, int RC = 4, int STAGES = 4, int SWZ = 1, int DMA = 1,
-          int XCD = 0, int SCHED = 0, int GM = 1, int BN = BM, int QN = 0>
+          int XCD = 0, int SCHED = 0, int GM = 1, int BN = BM, int QN = 0, int AP = 0>
 __global__ __launch_bounds__(64 * WGM * WGN, 2)  // at least two waves per SIMD
 void ns_gemm_kernel(const GemmLaunch L) {
   constexpr int NW = WGM * WGN;          // waves
@@ -723,7 +767,12 @@ void ns_gemm_kernel(const GemmLaunch L) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int i = i_base + fi * 32 + 8 * (r >> 2) + (r & 3);
-            if (i < G.ms && j < G.ns) store_user(G.user, U, i, j, acc[fi][fj][r]);
+            if (i >= G.ms || j >= G.ns) continue;
+            if constexpr (AP) {
+              apply_user(G.user, U, i, j, acc[fi][fj][r], G.ap_decay, G.ap_step);
+            } else {
+              store_user(G.user, U, i, j, acc[fi][fj][r]);
+            }
           }
         }
       }  // EPI_FINAL, bf16 compute: the caller's output leaves from the LDS staging below
@@ -809,7 +858,9 @@ void ns_gemm_kernel(const GemmLaunch L) {
           if (orow >= rows) return;
           if (vec && ocol + 8 <= cols) {
             char* p = OTm + (static_cast<int64_t>(orow) * ldot + ocol) * es;
-            if (G.user.dtype) {
+            if constexpr (AP) {
+              apply8(p, G.user.dtype, G.ap_decay, G.ap_step, x0, x1);
+            } else if (G.user.dtype) {
               Elem<uint16_t>::store8(p, x0, x1);
             } else {
               Elem<float>::store8(p, x0, x1);
@@ -817,8 +868,14 @@ void ns_gemm_kernel(const GemmLaunch L) {
           } else {
             const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (ocol + e < cols) store_user(G.user, OTm, orow, ocol + e, xv[e]);
+            for (int e = 0; e < 8; ++e) {
+              if (ocol + e >= cols) continue;
+              if constexpr (AP) {
+                apply_user(G.user, OTm, orow, ocol + e, xv[e], G.ap_decay, G.ap_step);
+              } else {
+                store_user(G.user, OTm, orow, ocol + e, xv[e]);
+              }
+            }
           }
         };
         if (!G.tall) {
@@ -892,13 +949,13 @@ int resident_workgroups(int tile) {
 // k-tiles moved by LDS DMA through a two-stage ring, the 64-bank swizzle,
 // XCD-contiguous tile ranges and groups of four tile rows for the
 // non-symmetric product.
-template <typename T, int BM, int WGM, int WGN, int EPI, int QN = 0>
+template <typename T, int BM, int WGM, int WGN, int EPI, int QN = 0, int AP = 0>
 void launch_one(const GemmLaunch& L, hipStream_t stream) {
   constexpr int RC = 8, STAGES = 2, SWZ = 1, DMA = 1, XCD = 1, SCHED = 0, GM = 4;
   const int cap = resident_workgroups(BM);
   const int grid = (cap >= 8 && L.total_tiles >= 4 * cap) ? cap : L.total_tiles;
-  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM, BM, QN>), dim3(grid),
-                     dim3(64 * WGM * WGN), 0, stream, L);
+  hipLaunchKernelGGL((ns_gemm_kernel<T, BM, WGM, WGN, EPI, RC, STAGES, SWZ, DMA, XCD, SCHED, GM, BM, QN, AP>),
+                     dim3(grid), dim3(64 * WGM * WGN), 0, stream, L);
 }
 
 template <typename T, int BM, int WGM, int WGN>
@@ -908,7 +965,13 @@ hipError_t launch_t(int epi, const GemmLaunch& L, hipStream_t stream) {
     case EPI_POLY: launch_one<T, BM, WGM, WGN, EPI_POLY>(L, stream); break;
     // the bf16 update reads X k-major, the fp32 update X^T
     case EPI_UPDATE: launch_one<T, BM, WGM, WGN, EPI_UPDATE, sizeof(T) == 2>(L, stream); break;
-    default: launch_one<T, BM, WGM, WGN, EPI_FINAL, sizeof(T) == 2>(L, stream); break;
+    default:  // the last step writes O, or (ap) applies the update to W
+      if (L.g[0].ap) {
+        launch_one<T, BM, WGM, WGN, EPI_FINAL, sizeof(T) == 2, 1>(L, stream);
+      } else {
+        launch_one<T, BM, WGM, WGN, EPI_FINAL, sizeof(T) == 2>(L, stream);
+      }
+      break;
   }
   return hipGetLastError();
 }

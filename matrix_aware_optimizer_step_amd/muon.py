@@ -204,13 +204,16 @@ class MuonStep:
     workspace (muon_momentum_packed_grouped, then
     muon_orthogonalize_packed_grouped), so N is never stored; otherwise N is
     an fp32 buffer between muon_momentum_grouped and
-    muon_orthogonalize_grouped.
+    muon_orthogonalize_grouped.  With ``fused_apply`` as well, the update is
+    applied by the last Newton-Schulz step
+    (muon_orthogonalize_apply_packed_grouped): O is never stored, and
+    ``ortho_buffers`` are not written.
     """
 
     def __init__(self, groups, *, compute: int = L.MUON_BF16, beta: float = 0.95, nesterov: bool = True,
                  steps: int = 5, coeffs=QUINTIC, eps: float = EPS, lr: float = 3e-4,
                  weight_decay: float = 0.1, mode: int = L.MUON_SCALE_MATCH_RMS, coeff: float = 0.2,
-                 packed: bool = True):
+                 packed: bool = True, fused_apply: bool = False):
         if not groups:
             raise ValueError("no parameter groups")
         self.compute, self.beta, self.nesterov = compute, beta, nesterov
@@ -227,12 +230,14 @@ class MuonStep:
             self.w.append(w)
             self.g.append(g)
             self.m.append(batch(torch.zeros(shape, dtype=torch.float32, device=dev)))
-            self.o.append(batch(torch.empty(shape, dtype=w.keep[-1].dtype, device=dev)))
             self.ss.append(torch.empty(w.count, dtype=torch.float32, device=dev))
         self.device = dev
         # each stage runs the groups together, at most 8 per grouped launch
         self.chunks = [list(range(i, min(i + 8, len(self.w)))) for i in range(0, len(self.w), 8)]
         self.packed = bool(packed)
+        self.fused_apply = bool(fused_apply) and self.packed
+        if not self.fused_apply:
+            self._ortho()
         self.pws, self.mws, self.ows = [], [], []
         if self.packed:
             for ch in self.chunks:
@@ -241,6 +246,14 @@ class MuonStep:
                 self.pws.append(workspace(need, dev))
         else:
             self._unpacked_buffers()
+
+    def _ortho(self) -> None:
+        """The Newton-Schulz outputs O (the weights' dtype); made on first use
+        when the update is folded into the last step, which needs none."""
+        if self.o:
+            return
+        for w in self.w:
+            self.o.append(batch(torch.empty((w.count, w.rows, w.cols), dtype=w.keep[-1].dtype, device=self.device)))
 
     def _unpacked_buffers(self) -> None:
         """N (fp32 on both paths: the bf16 path's high/low copy of X starts
@@ -265,6 +278,7 @@ class MuonStep:
 
     @property
     def ortho_buffers(self):
+        self._ortho()
         return [o.keep[0] for o in self.o]
 
     @property
@@ -301,6 +315,8 @@ class MuonStep:
         packed = self.packed and self.steps >= 1
         if not packed:
             self._unpacked_buffers()
+        if not (packed and self.fused_apply):
+            self._ortho()
         a, b, c = self.coeffs
         if events is not None:
             events[0].record(st)
@@ -319,7 +335,12 @@ class MuonStep:
             events[1].record(st)
         for k, ch in enumerate(self.chunks):
             sums = [self.ss[i].data_ptr() for i in ch]
-            if packed:
+            if packed and self.fused_apply:
+                ws = self.pws[k]
+                L.muon_orthogonalize_apply_packed_grouped(sums, [self.w[i].desc for i in ch], self.steps, a, b, c,
+                                                          self.eps, self.lr, self.weight_decay, self.mode,
+                                                          self.coeff, self.compute, ws.data_ptr(), ws.numel(), s)
+            elif packed:
                 ws = self.pws[k]
                 L.muon_orthogonalize_packed_grouped(sums, [self.o[i].desc for i in ch], self.steps, a, b, c, self.eps,
                                                     self.compute, ws.data_ptr(), ws.numel(), s)
@@ -330,7 +351,7 @@ class MuonStep:
                                              s)
         if events is not None:
             events[2].record(st)
-        for ch in self.chunks:
+        for ch in (self.chunks if not (packed and self.fused_apply) else []):
             L.muon_apply_grouped([self.w[i].desc for i in ch], [self.o[i].desc for i in ch], self.lr,
                                  self.weight_decay, self.mode, self.coeff, s)
         if events is not None:

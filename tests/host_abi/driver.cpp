@@ -81,6 +81,13 @@ void orthogonalize_cases() {
                                              kWs, need, nullptr), MUON_OK, "orthogonalize_packed_grouped");
     expect(muon_orthogonalize_packed_grouped(5, sums.data(), outs.data(), 0, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
                                              kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_packed, K 0");
+    // ... with the update folded into the last step: the outputs are the weights
+    expect(muon_orthogonalize_apply_packed_grouped(5, sums.data(), outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f,
+                                                   1e-3f, 0.1f, MUON_SCALE_MATCH_RMS, 0.2f, compute, kWs, need,
+                                                   nullptr), MUON_OK, "orthogonalize_apply_packed_grouped");
+    expect(muon_orthogonalize_apply_packed_grouped(5, sums.data(), outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f,
+                                                   1e-3f, 0.1f, 9, 0.2f, compute, kWs, need, nullptr),
+           MUON_ERR_INVALID_VALUE, "orthogonalize_apply_packed_grouped, mode");
     expect(muon_orthogonalize_packed_grouped(5, nullptr, outs.data(), 5, 3.4445f, -4.775f, 2.0315f, 1e-7f, compute,
                                              kWs, need, nullptr), MUON_ERR_INVALID_VALUE, "orthogonalize_packed, sums");
   }

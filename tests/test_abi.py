@@ -176,6 +176,19 @@ def test_packed_pair_rejects_bad_arguments():
     assert status_of(lambda: orth(ss=[FAKE, None])) == INVALID
     assert status_of(lambda: orth(wsb=need - 1)) == WORKSPACE
     assert L.muon_packed_grouped_workspace([1] * 9, [4] * 9, [4] * 9, 1) == 0
+    # the same second call with the update folded in: the weights take the outputs' place
+    fused = lambda **kw: L.muon_orthogonalize_apply_packed_grouped(
+        kw.get("ss", [FAKE, FAKE]), kw.get("w", gs), kw.get("steps", 5), 3.4445, -4.775, 2.0315, 1e-7,
+        kw.get("lr", 1e-3), 0.1, kw.get("mode", 0), kw.get("coeff", 0.2), L.MUON_BF16, FAKE, kw.get("wsb", need), 0)
+    assert status_of(lambda: fused(lr=float("nan"))) == INVALID
+    assert status_of(lambda: fused(coeff=float("inf"))) == INVALID
+    assert status_of(lambda: fused(mode=7)) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 0:")
+    assert status_of(lambda: fused(w=[desc(), desc(rows=0)])) == INVALID
+    assert L.load().muon_last_error().decode().startswith("group 1:")
+    assert status_of(lambda: fused(steps=0)) == INVALID
+    assert status_of(lambda: fused(ss=[FAKE, None])) == INVALID
+    assert status_of(lambda: fused(wsb=need - 1)) == WORKSPACE
 
 
 def test_apply_grouped_rejects_bad_arguments():

@@ -10,6 +10,14 @@ run on the same seeded inputs:
 * the updated bf16 weight: within one bf16 rounding of the oracle's apply
   step evaluated on the GPU's own Newton-Schulz output.
 
+The benchmark applies the update in the last Newton-Schulz step, so its O
+is never stored.  Each test therefore runs that step first and keeps the
+sampled weights, puts the sampled matrices back to their starting values and
+runs a second step with the separate apply call, whose O and W are checked
+against the oracle as above; the first step's weights must lie within one
+bf16 unit plus lr*s*2^-8 |O| of the second's (the rounding of O to bf16 that
+only the separate call takes).
+
 Sampled matrices get their workload's gradient recipe; the others get a
 seeded Gaussian of the same shape, which keeps the launch identical while
 sparing the host the cost of generating what is not checked.  Sampled
@@ -81,6 +89,32 @@ def bf16_ulp(x: np.ndarray) -> np.ndarray:
     return np.where(ax > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
+def two_steps(mx, cfg, weights, grads, picks):
+    """The benchmark's step (update in the last Newton-Schulz step), then the
+    separate-apply step on the same inputs for the sampled matrices.  Returns
+    the second stepper and {(group index, k): weight after the first step}."""
+    w0 = {(gi, k): weights[gi][k].clone() for gi, grp in enumerate(cfg.groups) for k in picks.get(grp.name, ())}
+    fused = bench.make_stepper(mx, weights, grads)
+    assert fused.fused_apply
+    fused.step()
+    torch.cuda.synchronize()
+    w_fused = {key: weights[key[0]][key[1]].cpu() for key in w0}
+    del fused
+    for (gi, k), w in w0.items():
+        weights[gi][k].copy_(w)
+    sep = bench.make_stepper(mx, weights, grads, fused_apply=False)
+    sep.step()
+    torch.cuda.synchronize()
+    return sep, w_fused
+
+
+def check_fused(w_fused, w_sep, o_sep, lr, rows, cols, where):
+    step = lr * O.scale_factor(rows, cols, O.SCALE_MATCH_RMS, 0.2)
+    tol = bf16_ulp(np.maximum(np.abs(w_fused), np.abs(w_sep))) + step * 2.0 ** -8 * np.abs(o_sep)
+    bad = int((np.abs(w_fused - w_sep) > tol).sum())
+    assert bad == 0, f"{where}: {bad} elements of the fused update beyond one rounding of the separate apply"
+
+
 def gradients(cfg, dev, picks):
     """Per group a (count, rows, cols) tensor: the recipe for picked matrices,
     a seeded Gaussian filler elsewhere."""
@@ -107,10 +141,8 @@ def test_full_size_step_matches_oracle(mx, workload):
     grads = gradients(cfg, dev, picks)
     weights = synth.initial_weights(cfg, device=dev)
     w0 = {(gi, k): f64(weights[gi][k]) for gi, grp in enumerate(cfg.groups) for k in picks.get(grp.name, ())}
-    stepper = bench.make_stepper(mx, weights, grads)
-    stepper.step()
-    torch.cuda.synchronize()
-    print(f"[fullsize] {workload}: GPU step done", flush=True)
+    stepper, w_fused = two_steps(mx, cfg, weights, grads, picks)
+    print(f"[fullsize] {workload}: GPU steps done", flush=True)
 
     worst = {"mom": 0.0, "sumsq": 0.0, "ortho": 0.0}
     ortho_errs = []
@@ -134,6 +166,7 @@ def test_full_size_step_matches_oracle(mx, workload):
             W_got = f64(weights[gi][k])
             tol = bf16_ulp(W_exact) + TOL_EW * np.max(np.abs(W_exact))
             assert np.all(np.abs(W_got - bf16_of(W_exact)) <= tol), f"{where}: updated weight"
+            check_fused(f64(w_fused[(gi, k)]), W_got, O_got, stepper.lr, grp.rows, grp.cols, where)
             worst = {"mom": max(worst["mom"], e_mom), "sumsq": max(worst["sumsq"], e_ss),
                      "ortho": max(worst["ortho"], e_o)}
     print(f"[fullsize] {workload}: oracle checks {time.perf_counter() - t0:.1f} s, worst errors "
@@ -163,14 +196,13 @@ def step_32(mx):
     for gi, grp in enumerate(cfg.groups):
         for k in picks[grp.name]:
             host[(grp.name, k)] = {"G": grads[gi][k].cpu(), "W0": weights[gi][k].cpu()}
-    stepper = bench.make_stepper(mx, weights, grads)
-    stepper.step()
-    torch.cuda.synchronize()
-    print(f"[fullsize] {workload}: GPU step done", flush=True)
+    stepper, w_fused = two_steps(mx, cfg, weights, grads, picks)
+    print(f"[fullsize] {workload}: GPU steps done", flush=True)
     for gi, grp in enumerate(cfg.groups):
         for k in picks[grp.name]:
             host[(grp.name, k)].update(M=stepper.momentum_buffers[gi][k].cpu(), O=stepper.ortho_buffers[gi][k].cpu(),
-                                      W=weights[gi][k].cpu(), sumsq=float(stepper.sumsq_buffers[gi][k]))
+                                      W=weights[gi][k].cpu(), W_fused=w_fused[(gi, k)],
+                                      sumsq=float(stepper.sumsq_buffers[gi][k]))
     lr, wd = stepper.lr, stepper.weight_decay
     del stepper, grads, weights
     torch.cuda.empty_cache()
@@ -200,6 +232,7 @@ def test_32_layer_set_sampled_layer_matches_oracle(step_32, layer):
             W_exact = O.apply_update(W0, O_got, lr, wd)
             tol = bf16_ulp(W_exact) + TOL_EW * np.max(np.abs(W_exact))
             assert np.all(np.abs(f64(h["W"]) - bf16_of(W_exact)) <= tol), f"{where}: updated weight"
+            check_fused(f64(h["W_fused"]), f64(h["W"]), O_got, lr, G.shape[0], G.shape[1], where)
     print(f"[fullsize] 8b-dense-32-layers layer {layer}: oracle {time.perf_counter() - t0:.1f} s; over the "
           f"{len(ERRS_32)} matrices checked so far Newton-Schulz worst {max(ERRS_32):.3e} "
           f"median {float(np.median(ERRS_32)):.3e}", flush=True)
