@@ -60,7 +60,10 @@ def label(name: str) -> str:
         epi = int(args[4])
         bn = int(args[12]) if len(args) > 12 else bm
         qn = int(args[13]) if len(args) > 13 else 0
+        ap = int(args[14]) if len(args) > 14 else 0
         stage = EPI.get(epi, f"epi {epi}")
+        if epi == 3 and ap:
+            stage = "update, last step (applies the update to W)"
         if epi in (2, 3):
             stage += ", X k-major" if qn else ", X^T operand"
         return f"ns_gemm_kernel {dt} {bm}x{bn} [{stage}]"
