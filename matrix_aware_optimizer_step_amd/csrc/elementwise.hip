@@ -82,10 +82,10 @@ __device__ __forceinline__ void load8(const char* p, int dtype, float* v) {
 __device__ __forceinline__ void store8(char* p, int dtype, const float* v) {
   if (dtype) {
     uint4 u;
-    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
-    u.z = f32_to_bf16(v[4]) | (static_cast<uint32_t>(f32_to_bf16(v[5])) << 16);
-    u.w = f32_to_bf16(v[6]) | (static_cast<uint32_t>(f32_to_bf16(v[7])) << 16);
+    u.x = bf16_pair(v[0], v[1]);
+    u.y = bf16_pair(v[2], v[3]);
+    u.z = bf16_pair(v[4], v[5]);
+    u.w = bf16_pair(v[6], v[7]);
     *reinterpret_cast<uint4*>(p) = u;
   } else {
     reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -110,8 +110,8 @@ __device__ __forceinline__ void load4(const char* p, int dtype, float* v) {
 __device__ __forceinline__ void store4(char* p, int dtype, const float* v) {
   if (dtype) {
     uint2 u;
-    u.x = f32_to_bf16(v[0]) | (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
-    u.y = f32_to_bf16(v[2]) | (static_cast<uint32_t>(f32_to_bf16(v[3])) << 16);
+    u.x = bf16_pair(v[0], v[1]);
+    u.y = bf16_pair(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = u;
   } else {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);

@@ -80,17 +80,17 @@ struct Elem<uint16_t> {  // bf16 storage
   // eight consecutive elements (16 bytes)
   __device__ __forceinline__ static void store8(char* p, const float4& a, const float4& b) {
     uint4 u;
-    u.x = static_cast<uint32_t>(f32_to_bf16(a.x)) | (static_cast<uint32_t>(f32_to_bf16(a.y)) << 16);
-    u.y = static_cast<uint32_t>(f32_to_bf16(a.z)) | (static_cast<uint32_t>(f32_to_bf16(a.w)) << 16);
-    u.z = static_cast<uint32_t>(f32_to_bf16(b.x)) | (static_cast<uint32_t>(f32_to_bf16(b.y)) << 16);
-    u.w = static_cast<uint32_t>(f32_to_bf16(b.z)) | (static_cast<uint32_t>(f32_to_bf16(b.w)) << 16);
+    u.x = bf16_pair(a.x, a.y);
+    u.y = bf16_pair(a.z, a.w);
+    u.z = bf16_pair(b.x, b.y);
+    u.w = bf16_pair(b.z, b.w);
     *reinterpret_cast<uint4*>(p) = u;
   }
   // four consecutive elements
   __device__ __forceinline__ static void store4(char* p, float v0, float v1, float v2, float v3) {
     uint2 u;
-    u.x = static_cast<uint32_t>(f32_to_bf16(v0)) | (static_cast<uint32_t>(f32_to_bf16(v1)) << 16);
-    u.y = static_cast<uint32_t>(f32_to_bf16(v2)) | (static_cast<uint32_t>(f32_to_bf16(v3)) << 16);
+    u.x = bf16_pair(v0, v1);
+    u.y = bf16_pair(v2, v3);
     *reinterpret_cast<uint2*>(p) = u;
   }
 };
@@ -689,10 +689,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
         const char* Em = G.E0 + mat * G.e0_mat;
         const uint32_t lde = G.lde0;
         if constexpr (sizeof(T) == 2) {  // the high part was added in the main loop
+          // the codes; their step is folded into the coefficient a below
           const uint32_t w[4] = {lo_pre[blk].x, lo_pre[blk].y, lo_pre[blk].z, lo_pre[blk].w};
-          const float step = lo8_step((lo_exp[blk >> 2] >> (8 * (blk & 3))) & 0xffu);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = lo8_decode(w, r, step);
+          for (int r = 0; r < 16; ++r) e[r] = lo8_code(w, r);
         } else {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -720,8 +720,12 @@ void ns_gemm_kernel(const GemmLaunch L) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[fi][fj][r] = bt * e[r] + ct * acc[fi][fj][r];
         } else {
+          // a * Xlo: with bf16 compute e holds the low part's codes, and
+          // a * step is exact (a power-of-two step)
+          float ae = at;
+          if constexpr (kLoNative) ae = at * lo8_step((lo_exp[blk >> 2] >> (8 * (blk & 3))) & 0xffu);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = at * e[r] + acc[fi][fj][r];
+          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = ae * e[r] + acc[fi][fj][r];
         }
       }
       if constexpr (EPI == EPI_GRAM || EPI == EPI_POLY) {
