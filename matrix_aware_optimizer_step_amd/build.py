@@ -22,6 +22,13 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wall", "-Wno-unused-function"]
+# Per-source additions.  The GEMM kernel's epilogue loops carry
+# "#pragma unroll"; with the parameter update folded into the last step the
+# loop over the two staged halves outgrows LLVM's default size limit for a
+# pragma unroll, and a loop left rolled indexes the accumulators dynamically
+# (they go to scratch memory).  A larger limit keeps every instantiation
+# unrolled and the others unchanged.
+EXTRA = {"ns_gemm.hip": ["-mllvm", "-pragma-unroll-threshold=65536"]}
 
 
 def _hipcc() -> str:
@@ -33,7 +40,7 @@ def _hipcc() -> str:
 
 def _compile(hipcc: str, src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc, *COMMON, *EXTRA.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

@@ -882,7 +882,64 @@ void ns_gemm_kernel(const GemmLaunch L) {
             }
           }
         };
-        if (!G.tall) {
+        // bf16 weights in 16-byte segments and the wave's staged 64 x 64
+        // block inside the matrix (no bounds checks): each segment's old
+        // weights are loaded one segment ahead, so that a load is in flight
+        // while the previous segment is computed and stored.  (put8 below
+        // loads and stores one segment after the other: the compiler cannot
+        // move a load above the previous segment's store to the same array.)
+        const bool wpipe = AP && G.user.dtype && vec && gi0 + h * 64 + 64 <= G.ms && gj0 + 64 <= G.ns;
+        auto wl16 = [&](int orow, int ocol) {
+          return *reinterpret_cast<const uint4*>(OTm + (static_cast<int64_t>(orow) * ldot + ocol) * 2);
+        };
+        auto wput16 = [&](int orow, int ocol, const uint4& wq, const float4& x0, const float4& x1) {
+          const uint32_t q[4] = {wq.x, wq.y, wq.z, wq.w};
+          const float o[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          float w[8];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            w[2 * k] = bf16_to_f32(static_cast<uint16_t>(q[k]));
+            w[2 * k + 1] = bf16_to_f32(static_cast<uint16_t>(q[k] >> 16));
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) w[e] = G.ap_decay * w[e] - G.ap_step * o[e];
+          Elem<uint16_t>::store8(OTm + (static_cast<int64_t>(orow) * ldot + ocol) * 2,
+                                 make_float4(w[0], w[1], w[2], w[3]), make_float4(w[4], w[5], w[6], w[7]));
+        };
+        if (wpipe && !G.tall) {
+          const int rg = lane & 15;
+          uint4 wa = wl16(gi0 + h * 64 + 4 * rg, gj0 + 8 * (lane >> 4)), wb = wa;
+#pragma unroll
+          for (int it = 0; it < 2; ++it) {
+            const int c0 = 8 * (lane >> 4) + 32 * it;
+            float4 x[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const float4*>(wl + (c0 + t) * ES + 4 * rg);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int sn = 4 * it + e + 1;
+              if (sn < 8) wb = wl16(gi0 + h * 64 + 4 * rg + (sn & 3), gj0 + 8 * (lane >> 4) + 32 * (sn >> 2));
+              float v[8];
+#pragma unroll
+              for (int t = 0; t < 8; ++t) v[t] = e == 0 ? x[t].x : e == 1 ? x[t].y : e == 2 ? x[t].z : x[t].w;
+              wput16(gi0 + h * 64 + 4 * rg + e, gj0 + c0, wa, make_float4(v[0], v[1], v[2], v[3]),
+                     make_float4(v[4], v[5], v[6], v[7]));
+              wa = wb;
+            }
+          }
+        } else if (wpipe) {
+          const int rc = (lane & 7) * 8;
+          uint4 wa = wl16(gj0 + (lane >> 3), gi0 + h * 64 + rc), wb = wa;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            if (k + 1 < 8) wb = wl16(gj0 + (lane >> 3) + 8 * (k + 1), gi0 + h * 64 + rc);
+            const int c = (lane >> 3) + 8 * k;
+            const float4 x0 = *reinterpret_cast<const float4*>(wl + c * ES + rc);
+            const float4 x1 = *reinterpret_cast<const float4*>(wl + c * ES + rc + 4);
+            wput16(gj0 + c, gi0 + h * 64 + rc, wa, x0, x1);
+            wa = wb;
+          }
+        } else if (!G.tall) {
           // rows of X are rows of the output: 4-row x 8-column pieces
           const int rg = lane & 15;
 #pragma unroll
