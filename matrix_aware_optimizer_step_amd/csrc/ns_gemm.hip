@@ -516,6 +516,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
     constexpr int kNH = WTM / BK;
     static_assert(!kAddXInLoop || (kNH * BK == WTM && kFPK * 32 == BK && RC == 2 * kFPK * 2),
                   "wave rows must split into whole k-tiles of whole 32-row blocks");
+    static_assert(!(EPI == EPI_POLY && sizeof(T) == 2) || (kNH * BK == WTM && kFPK * 32 == BK && RC == 4 * kFPK),
+                  "the polynomial's in-loop term assumes whole k-tiles of whole 32-row blocks");
     const int kt_x0 = (ti * BM + wm * WTM) / BK;
     // Step 0 from a packed, unnormalized input N (the momentum kernel wrote
     // N itself): X_0 = xs*N with xs = 1/(||N|| + eps).  The Gram is then xs^2
@@ -530,6 +532,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
     const float at = L.a * xs;
     const float bt = L.b * xs;
     const float ct = L.c * xs;
+    // bf16 polynomial with c != 0: B = c * (A*A + (b/c) * A), and (b/c) * A
+    // enters the accumulator from the operand tiles, as the update's a * X
+    // does: A is symmetric, so the second operand's k-tiles that cover this
+    // wave's rows hold A[j][i] = A[i][j] for its output elements.  The
+    // epilogue then only scales by c and loads nothing.
+    const float bc = ct != 0.0f ? bt / ct : 0.0f;
+    const bool poly_in_loop = EPI == EPI_POLY && sizeof(T) == 2 && ct != 0.0f && __builtin_isfinite(bc);
     int st = 0;  // stage holding k-tile kt
     for (int kt = 0; kt < nk; ++kt) {
       const bool issue = DMA ? (kt + STAGES - 1 < nk) : (kt + 1 < nk);
@@ -544,6 +553,29 @@ void ns_gemm_kernel(const GemmLaunch L) {
       }
       const char* sb = smem + st * STB;
       const int stn = (st + 1 == STAGES) ? 0 : st + 1;
+      if constexpr (EPI == EPI_POLY && sizeof(T) == 2 && !kQN) {
+        // row j of the second operand's k-tile, k = i: chunk 4f + q holds
+        // k = 32f + 8q .. +7 of it, and this lane's four rows start 4*half in
+#pragma unroll
+        for (int hh = 0; hh < kNH; ++hh) {
+          if (poly_in_loop && kt == kt_x0 + hh) {  // uniform over the wave
+#pragma unroll
+            for (int f = 0; f < kFPK; ++f)
+#pragma unroll
+              for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const int fi = hh * kFPK + f;
+                  const u32x2_t v = *reinterpret_cast<const u32x2_t*>(
+                      sb + fb_off[fj] + (swizzle<SWZ, RC>(fb_row[fj], 4 * f + q) << 4) + 8 * half);
+                  acc[fi][fj][4 * q + 0] += bc * bf16_to_f32(static_cast<uint16_t>(v.x));
+                  acc[fi][fj][4 * q + 1] += bc * bf16_to_f32(static_cast<uint16_t>(v.x >> 16));
+                  acc[fi][fj][4 * q + 2] += bc * bf16_to_f32(static_cast<uint16_t>(v.y));
+                  acc[fi][fj][4 * q + 3] += bc * bf16_to_f32(static_cast<uint16_t>(v.y >> 16));
+                }
+          }
+        }
+      }
       if constexpr (kAddXInLoop) {
         // a * X[i][j] = a * Q[k = i][j]: the k-tiles that cover this wave's
         // rows hold the bf16 high part of X for its output elements.
@@ -703,8 +735,10 @@ void ns_gemm_kernel(const GemmLaunch L) {
       }
     };
     if constexpr (kHasE) {
+      if (!poly_in_loop) {
 #pragma unroll
-      for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
+        for (int b = 0; b < PF && b < NB; ++b) eload(b, ebuf[b]);
+      }
     }
     uint32_t new_exp[kLoNative ? NB / 4 : 1];
 #pragma unroll
@@ -714,11 +748,16 @@ void ns_gemm_kernel(const GemmLaunch L) {
       const int fi = blk / FN, fj = blk % FN;
       const int j = j_base + fj * 32;
       if constexpr (kHasE) {
-        if (blk + PF < NB) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
+        if (blk + PF < NB && !poly_in_loop) eload(blk + PF, ebuf[(blk + PF) % (PF + 1)]);
         const float* e = ebuf[blk % (PF + 1)];
         if constexpr (EPI == EPI_POLY) {
+          if (poly_in_loop) {  // b/c * A is already in the accumulator
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[fi][fj][r] = bt * e[r] + ct * acc[fi][fj][r];
+            for (int r = 0; r < 16; ++r) acc[fi][fj][r] = ct * acc[fi][fj][r];
+          } else {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[fi][fj][r] = bt * e[r] + ct * acc[fi][fj][r];
+          }
         } else {
           // a * Xlo: with bf16 compute e holds the low part's codes, and
           // a * step is exact (a power-of-two step)
