@@ -43,7 +43,8 @@ struct Lo8 {
   uint32_t w[4];
   uint32_t e;
 };
-__device__ __forceinline__ Lo8 lo8_encode(const float* x) {
+// With hi given, hi[k] receives bf16(x[2k]) | bf16(x[2k+1]) << 16 as well.
+__device__ __forceinline__ Lo8 lo8_encode(const float* x, uint32_t* hi = nullptr) {
   Lo8 o;
   float m = 0.0f;
 #pragma unroll
@@ -55,6 +56,7 @@ __device__ __forceinline__ Lo8 lo8_encode(const float* x) {
 #pragma unroll
   for (int r = 0; r < 16; r += 2) {
     const uint32_t hb = bf16_pair(x[r], x[r + 1]);
+    if (hi != nullptr) hi[r / 2] = hb;
     const float h0 = __builtin_bit_cast(float, hb << 16);
     const float h1 = __builtin_bit_cast(float, hb & 0xffff0000u);
     const float t0 = fminf(fmaxf(fmaf(x[r] - h0, inv, kMagic), kMagic - 127.0f), kMagic + 127.0f);

@@ -280,10 +280,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
   // Tiles t = blockIdx.x, + gridDim.x, ...: one tile per workgroup when the
   // grid covers the launch, several in turn when the host chose a persistent
   // grid (a multiple of 8, so every tile of a workgroup is on its XCD).
-  for (int t = blockIdx.x; t < L.total_tiles; t += gridDim.x) {
-    if (t != static_cast<int>(blockIdx.x)) __syncthreads();  // the previous tile is done with LDS
-    // ---- which tile of which matrix of which group
-    int gi = 0;
+  // ---- which tile of which matrix of which group
+  constexpr int R = BM / BN;  // column tiles per row tile
+  static_assert(R * BN == BM, "BN must divide BM");
+  auto decode = [&](int t, int& gi, int& mat, int& slice, int& ti, int& tj) {
+    gi = 0;
     while (gi + 1 < L.ngroups && t >= L.g[gi + 1].tile_begin) ++gi;
     const GemmGroup& G = L.g[gi];
     int lt = t - G.tile_begin;  // position within the group
@@ -299,16 +300,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
       for (int e = 0; e < f; ++e) start += (n - e + 7) >> 3;  // positions on XCDs ranked before
       lt = start + ((lt - f) >> 3);
     }
-    const int mat = lt / G.tiles_per_mat;
+    mat = lt / G.tiles_per_mat;
     int tt = lt - mat * G.tiles_per_mat;
-    int slice = 0;  // split Gram: slice of the reduction this tile sums
+    slice = 0;  // split Gram: slice of the reduction this tile sums
     if (G.splits > 1) {
       slice = tt % G.splits;
       tt /= G.splits;
     }
-    int ti, tj;
-    constexpr int R = BM / BN;  // column tiles per row tile
-    static_assert(R * BN == BM, "BN must divide BM");
     if (G.sym) {
       // upper tiles only: row tile ti keeps column tiles tj >= R*ti
       ti = 0;
@@ -328,6 +326,24 @@ void ns_gemm_kernel(const GemmLaunch L) {
       tj = in / rows;
       ti = grp * GM + (in - tj * rows);
     }
+  };
+
+  // bf16 update on a persistent grid: the next tile's first k-tile is copied
+  // into stage 0 during this tile's epilogue (which then stages in bf16 above
+  // stage 0), so that its latency is off the next tile's prologue
+  constexpr bool kXPF = EPI == EPI_UPDATE && sizeof(T) == 2 && DMA && STAGES == 2;
+  bool pf = false;  // this tile's first k-tile is already on its way
+  for (int t = blockIdx.x; t < L.total_tiles; t += gridDim.x) {
+    if (t != static_cast<int>(blockIdx.x)) {  // the previous tile is done with LDS
+      if constexpr (kXPF) {
+        barrier_keep_vm<63>();  // (its stores and the prefetch are waited for in the prologue)
+      } else {
+        __syncthreads();
+      }
+    }
+    int gi, mat, slice, ti, tj;
+    decode(t, gi, mat, slice, ti, tj);
+    const GemmGroup& G = L.g[gi];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -394,10 +410,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
     }
 
     // DMA: issue k-tile kt into LDS stage st (lands asynchronously; vmcnt).
-    auto dma_issue = [&](int kt, int st) {
+    // (dma_issue_at: the same for the tile whose operands start at P0, Q0)
+    auto dma_issue_at = [&](const char* P0, const char* Q0, int kt, int st) {
       const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
-      const char* pk = Pt + kb;
-      const char* qk = Qt + (kQN ? static_cast<int64_t>(kt) * BK * ldq * static_cast<int64_t>(sizeof(T)) : kb);
+      const char* pk = P0 + kb;
+      const char* qk = Q0 + (kQN ? static_cast<int64_t>(kt) * BK * ldq * static_cast<int64_t>(sizeof(T)) : kb);
       char* lp = smem + st * STB + wave * IPW * 1024;
       char* lq = smem + st * STB + OPB + wave * IPWQ * 1024;
 #pragma unroll
@@ -407,6 +424,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
         for (int r = 0; r < IPWQ; ++r) lds_dma16(qk, dofs_q[r], lq + r * 1024);
       }
     };
+    auto dma_issue = [&](int kt, int st) { dma_issue_at(Pt, Qt, kt, st); };
     auto reg_load = [&](int kt) {
       const int64_t kb = static_cast<int64_t>(kt) * BK * sizeof(T);
 #pragma unroll
@@ -443,12 +461,13 @@ void ns_gemm_kernel(const GemmLaunch L) {
     if constexpr (DMA) {
 #pragma unroll
       for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) dma_issue(s, s);
+        if (s < nk && !(kXPF && pf)) dma_issue(s, s);
       if (nk >= STAGES - 1) {
         barrier_keep_vm<(STAGES - 2) * kPerTile>();  // k-tile 0 has landed
       } else {
         barrier_keep_vm<0>();
       }
+      pf = false;
     } else {
       reg_load(0);
       reg_store(0);
@@ -741,6 +760,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
       }
     }
     uint32_t new_exp[kLoNative ? NB / 4 : 1];
+    uint32_t hiw[kXPF ? NB : 1][8];  // bf16 update: the high part of X', pairs of rows
 #pragma unroll
     for (int k = 0; k < (kLoNative ? NB / 4 : 1); ++k) new_exp[k] = 0;
 #pragma unroll
@@ -794,7 +814,7 @@ void ns_gemm_kernel(const GemmLaunch L) {
           float x[16];
 #pragma unroll
           for (int r = 0; r < 16; ++r) x[r] = acc[fi][fj][r];
-          const Lo8 c = lo8_encode(x);
+          const Lo8 c = lo8_encode(x, kXPF ? hiw[blk] : nullptr);
           *reinterpret_cast<uint4*>(O0m + lo_off + blk * 1024u) = make_uint4(c.w[0], c.w[1], c.w[2], c.w[3]);
           new_exp[blk >> 2] |= c.e << (8 * (blk & 3));
         } else {
@@ -840,6 +860,23 @@ void ns_gemm_kernel(const GemmLaunch L) {
     constexpr int ES = 68;  // floats per staged column
     __syncthreads();        // every wave is done with the operand stages
     float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
+    constexpr int ES2 = 68;  // bf16 update: bf16 values per staged column
+    char* wl2 = smem + STB + wave * 64 * ES2 * 2;
+    static_assert(!kXPF || STB + NW * 64 * ES2 * 2 <= SMEM, "bf16 staging above stage 0");
+    if constexpr (kXPF) {
+      // the next tile of this workgroup, if it is in the same group (same
+      // operand strides): its first k-tile goes into stage 0 now
+      const int tn = t + static_cast<int>(gridDim.x);
+      if (tn < L.total_tiles) {
+        int gn, mn, sn, tin, tjn;
+        decode(tn, gn, mn, sn, tin, tjn);
+        if (gn == gi) {
+          dma_issue_at(G.P + mn * G.p_mat + static_cast<int64_t>(tin) * BM * ldp * sizeof(T),
+                       G.Q + mn * G.q_mat + static_cast<int64_t>(tjn) * BN * sizeof(T), 0, 0);
+          pf = true;
+        }
+      }
+    }
     char* OTm;
     int64_t ldot;
     if constexpr (EPI == EPI_UPDATE) {
@@ -854,6 +891,44 @@ void ns_gemm_kernel(const GemmLaunch L) {
     }
 #pragma unroll
     for (int h = 0; h < WTM / 64; ++h) {
+      if constexpr (kXPF) {
+        // the high part of X', already bf16 (from the encoder): column-major
+        // in LDS, 4 rows of one column per 8-byte write, then read back as
+        // 4-row x 8-column pieces and stored as 16-byte row segments.  A
+        // half-wave reads columns c and c + 16 (68-element columns put them
+        // 32 banks apart); its writes cover the 64 banks once.
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int fj = 0; fj < FN; ++fj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int blk = (2 * h + f) * FN + fj;
+              *reinterpret_cast<u32x2_t*>(wl2 + ((fj * 32 + frow) * ES2 + f * 32 + 8 * q + 4 * half) * 2) =
+                  u32x2_t{hiw[blk][2 * q], hiw[blk][2 * q + 1]};
+            }
+        char* O1m = G.O1 + mat * G.o1_mat;
+        const uint32_t ldo1 = G.ldo1;
+        const int rg = lane & 15;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int c0 = 8 * it + 16 * ((lane >> 4) & 1) + 32 * (lane >> 5);
+          u32x2_t x[8];
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = *reinterpret_cast<const u32x2_t*>(wl2 + ((c0 + t) * ES2 + 4 * rg) * 2);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const uint32_t a = e < 2 ? x[2 * k].x : x[2 * k].y, b = e < 2 ? x[2 * k + 1].x : x[2 * k + 1].y;
+              w[k] = (e & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+            }
+            const uint32_t row = gi0 + h * 64 + 4 * rg + e;
+            *reinterpret_cast<uint4*>(O1m + (row * ldo1 + gj0 + c0) * 2u) = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        }
+      } else {
       // registers -> LDS column-major: 4 consecutive rows of one column per write
 #pragma unroll
       for (int f = 0; f < 2; ++f)
@@ -867,7 +942,8 @@ void ns_gemm_kernel(const GemmLaunch L) {
             *reinterpret_cast<float4*>(wl + c * ES + r) =
                 make_float4(acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2], acc[fi][fj][4 * q + 3]);
           }
-      if constexpr (EPI == EPI_UPDATE && sizeof(T) == 2) {
+      }
+      if constexpr (EPI == EPI_UPDATE && sizeof(T) == 2 && !kXPF) {
         // the high part of X' row-major: lanes read 4-row x 8-column pieces of
         // the staged half (16 lanes cover 256 consecutive bytes of LDS) and
         // store 16-byte row segments
