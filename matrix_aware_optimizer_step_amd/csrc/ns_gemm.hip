@@ -846,6 +846,26 @@ void ns_gemm_kernel(const GemmLaunch L) {
       for (int k = 0; k < NB / 4; ++k) Eo[k] = new_exp[k];
     }
 
+    if constexpr (kXPF) {
+      // The next tile of this workgroup, if it is in the same group (same
+      // operand strides): its first k-tile goes into stage 0 now, under this
+      // epilogue's stores.  No wave reads stage 0 any more: the last k-tile's
+      // barrier retired every read that matters (what follows it only
+      // prefetches fragments that are never used).  Issued after the last
+      // load this epilogue waits for: the compiler's counted waits do not see
+      // these copies, and vector memory operations complete in issue order.
+      const int tn = t + static_cast<int>(gridDim.x);
+      if (tn < L.total_tiles) {
+        int gn, mn, sn, tin, tjn;
+        decode(tn, gn, mn, sn, tin, tjn);
+        if (gn == gi) {
+          dma_issue_at(G.P + mn * G.p_mat + static_cast<int64_t>(tin) * BM * ldp * sizeof(T),
+                       G.Q + mn * G.q_mat + static_cast<int64_t>(tjn) * BN * sizeof(T), 0, 0);
+          pf = true;
+        }
+      }
+    }
+
     // 3. transposed stores through LDS
     bool transposed;
     if constexpr (EPI == EPI_UPDATE) {
@@ -858,25 +878,17 @@ void ns_gemm_kernel(const GemmLaunch L) {
     if (!transposed) continue;  // uniform over the workgroup
     static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
     constexpr int ES = 68;  // floats per staged column
-    __syncthreads();        // every wave is done with the operand stages
+    // every wave is done with the operand stages (the bf16 update waits for
+    // LDS reads only: its copy of the next k-tile may still be in flight)
+    if constexpr (kXPF) {
+      barrier_keep_vm<63>();
+    } else {
+      __syncthreads();
+    }
     float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
     constexpr int ES2 = 68;  // bf16 update: bf16 values per staged column
     char* wl2 = smem + STB + wave * 64 * ES2 * 2;
     static_assert(!kXPF || STB + NW * 64 * ES2 * 2 <= SMEM, "bf16 staging above stage 0");
-    if constexpr (kXPF) {
-      // the next tile of this workgroup, if it is in the same group (same
-      // operand strides): its first k-tile goes into stage 0 now
-      const int tn = t + static_cast<int>(gridDim.x);
-      if (tn < L.total_tiles) {
-        int gn, mn, sn, tin, tjn;
-        decode(tn, gn, mn, sn, tin, tjn);
-        if (gn == gi) {
-          dma_issue_at(G.P + mn * G.p_mat + static_cast<int64_t>(tin) * BM * ldp * sizeof(T),
-                       G.Q + mn * G.q_mat + static_cast<int64_t>(tjn) * BN * sizeof(T), 0, 0);
-          pf = true;
-        }
-      }
-    }
     char* OTm;
     int64_t ldot;
     if constexpr (EPI == EPI_UPDATE) {
