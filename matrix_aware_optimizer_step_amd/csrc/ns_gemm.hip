@@ -878,13 +878,11 @@ void ns_gemm_kernel(const GemmLaunch L) {
     if (!transposed) continue;  // uniform over the workgroup
     static_assert(WTN == 64 && WTM % 64 == 0, "transposed staging works on 64 x 64 wave blocks");
     constexpr int ES = 68;  // floats per staged column
-    // every wave is done with the operand stages (the bf16 update waits for
-    // LDS reads only: its copy of the next k-tile may still be in flight)
-    if constexpr (kXPF) {
-      barrier_keep_vm<63>();
-    } else {
-      __syncthreads();
-    }
+    // every wave is done with the operand stages.  The bf16 update needs no
+    // barrier here: each wave stages into its own part of the ring above
+    // stage 0, and after the last k-tile's barrier the other waves read only
+    // fragments they never use (the next tile's copy is in stage 0).
+    if constexpr (!kXPF) __syncthreads();
     float* wl = reinterpret_cast<float*>(smem) + wave * 64 * ES;
     constexpr int ES2 = 68;  // bf16 update: bf16 values per staged column
     char* wl2 = smem + STB + wave * 64 * ES2 * 2;
