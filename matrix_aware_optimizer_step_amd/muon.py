@@ -207,7 +207,7 @@ class MuonStep:
     muon_orthogonalize_grouped.  With ``fused_apply`` as well, the update is
     applied by the last Newton-Schulz step
     (muon_orthogonalize_apply_packed_grouped): O is never stored, and
-    ``ortho_buffers`` are not written.
+    ``ortho_buffers`` raises.
     """
 
     def __init__(self, groups, *, compute: int = L.MUON_BF16, beta: float = 0.95, nesterov: bool = True,
@@ -278,6 +278,9 @@ class MuonStep:
 
     @property
     def ortho_buffers(self):
+        if self.fused_apply and self.steps >= 1:
+            raise RuntimeError("with fused_apply the last Newton-Schulz step applies the update and O is never "
+                               "stored; use a MuonStep without fused_apply to read O")
         self._ortho()
         return [o.keep[0] for o in self.o]
 

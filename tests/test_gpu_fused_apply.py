@@ -97,6 +97,8 @@ def test_fused_apply_matches_oracle_and_separate_apply(mx, shape, dtype, compute
     W = randn(shape, 11, dtype, 0.02)
     G = torch.empty(shape, dtype=dtype, device="cuda")
     fused, plain, twin = pair(mx, [(W, G)], compute=compute, lr=lr, weight_decay=wd)
+    with pytest.raises(RuntimeError, match="never stored"):
+        fused.ortho_buffers
     Wu = twin[0][0]
     step = lr * O.scale_factor(m, n, O.SCALE_MATCH_RMS, 0.2)
     decay = np.float32(1.0 - lr * wd)
