@@ -354,6 +354,59 @@ def test_bf16_carry_of_x_round_trips(mx, shape):
         assert rel(f64(out[i]), x0) <= 3e-5
 
 
+def _bf16_rne(x32):
+    """bf16 rounding (to nearest, ties to even) of finite float32 values, as float32."""
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return r.astype(np.uint32).view(np.float32)
+
+
+def _carry_model(x32):
+    """High part plus decoded residual of the bf16 path's carry of X, from its
+    definition: per 32x32 block, lane-group of 16 values (one column, rows
+    8q + 4h + e of the block, q, e < 4, h = 0, 1), E = the largest exponent
+    field of their bf16 values, codes = residual / 2^(E-142) rounded to
+    nearest even and clamped to +-127 (0 when E < 16)."""
+    m, n = x32.shape
+    mp, np_ = -(-m // 32) * 32, -(-n // 32) * 32
+    x = np.zeros((mp, np_), np.float32)
+    x[:m, :n] = x32
+    hi = _bf16_rne(x)
+    out = hi.astype(np.float64)
+    for b in range(0, mp, 32):
+        for h in range(2):
+            rows = [b + 8 * q + 4 * h + e for q in range(4) for e in range(4)]
+            hb = hi[rows, :]                                       # 16 x columns
+            E = ((hb.view(np.uint32) >> 23) & 0xFF).max(axis=0).astype(np.int64)
+            step = np.where(E >= 16, np.ldexp(1.0, E - 142), 0.0)
+            inv = np.where(E >= 16, np.ldexp(1.0, 142 - E), 0.0)
+            code = np.clip(np.rint((x[rows, :].astype(np.float64) - hb) * inv), -127, 127)
+            out[rows, :] = hb + code * step
+    return out[:m, :n].astype(np.float32)
+
+
+@pytest.mark.parametrize("shape", [(2, 96, 200), (1, 256, 700), (1, 300, 520)])
+def test_bf16_carry_of_x_is_exact(mx, shape):
+    """The carry's format, bit for bit: with (a, b, c) = (1, 0, 0), one step,
+    eps = 0 and a given sum of squares of 64 (so X_0 = N / 8 exactly), the
+    fp32 output is the high part plus the decoded residual of every X_0
+    element, which a host model of the format computes exactly.  Values span
+    six decades so that blocks mix exponents."""
+    g = np.random.default_rng(7 + shape[1])
+    N = (g.standard_normal(shape) * 10.0 ** g.uniform(-3, 3, shape)).astype(np.float32)
+    N[:, 0, :5] = 0.0
+    Nt = torch.from_numpy(N).cuda()
+    ss = torch.full((shape[0],), 64.0, dtype=torch.float32, device="cuda")
+    out = torch.empty(shape, dtype=torch.float32, device="cuda")
+    mx.orthogonalize(Nt, out, ss, 1, (1.0, 0.0, 0.0), 0.0, mx.MUON_BF16, device="cuda")
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    for i in range(shape[0]):
+        want = _carry_model(N[i] / np.float32(8.0))
+        bad = np.argwhere(got[i].view(np.uint32) != want.view(np.uint32))
+        assert bad.size == 0, f"{shape} matrix {i}: {len(bad)} elements differ, first {bad[:3].tolist()}"
+
+
 @pytest.mark.parametrize("compute", [0, 1])
 def test_ns_scale_invariance_and_odd_symmetry(mx, compute):
     """Invariants of the method on the GPU path.  Multiplying N by a power of
